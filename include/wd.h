@@ -1,0 +1,193 @@
+/*
+ * wd.h -- C ABI of the KV-cached decoder step for AMD Instinct MI355X (gfx950).
+ *
+ * The library runs one decoder step of a Whisper-style speech-recognition
+ * decoder (token embedding + learned position, pre-LN causal self-attention
+ * over a K/V cache appended in place, cross-attention over per-window cross
+ * K/V, erf-GELU FFN, final LayerNorm, tied-embedding logits and argmax), or of
+ * a Qwen3-ASR-style causal LM (RMSNorm, GQA with per-head QK RMSNorm and NeoX
+ * RoPE, SwiGLU, tied head).  Every step of the computation runs in the
+ * library's own HIP kernels on the device.
+ *
+ * The calls follow the split the source pages make between weights and
+ * per-run state: load the weights once (wavo decoder.rs `Decoder::load`),
+ * compute the cross K/V once per audio window (wavo `record_cross`; Whisper
+ * tiny (Nest model page) README "Transcribing with caches", entry `listen`),
+ * then one call per token (wavo `record_step`; Nest entry `step`;
+ * transcribe.cpp qwen3_asr/decoder.h `StepBuildBatched`), with a beam
+ * rearrangement of the self caches (mlx-bun whisper.ts
+ * `WhisperKvCache.rearrange`) and a prompt prefill (Nest entry `prefill`;
+ * decoder.h `PrefillBuild`).
+ *
+ * Conventions for every call:
+ *   - Device pointers are plain HIP device addresses ("dev" below); host
+ *     pointers are marked "host".  The caller owns all device memory,
+ *     including the workspace; the library never allocates device memory.
+ *   - Calls are asynchronous on the stream given to wd_load, except
+ *     wd_check (synchronises) and wd_load (returns after its launches are
+ *     queued; the source tensors may be freed once the stream has synced).
+ *   - A context is bound to one stream and is not thread-safe.
+ *   - Errors detectable on the host return a non-zero wd_status at once and
+ *     leave the device state unchanged; wd_last_error gives a message.
+ *     Errors only visible on the device (a token id outside [0, vocab), a
+ *     position outside [0, context), a NaN logit) set a sticky device flag
+ *     that wd_check reports as WD_ERR_RANGE; the offending row's cache write
+ *     is skipped, so no out-of-bounds access happens.
+ *   - No C++ exception crosses this boundary (internal failures return
+ *     WD_ERR_INTERNAL).
+ */
+#ifndef WD_H
+#define WD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WD_ABI_VERSION 1
+#define WD_MAX_BATCH 64
+
+typedef struct wd_ctx wd_ctx;
+
+typedef enum {
+  WD_OK = 0,
+  WD_ERR_ARG = 1,      /* bad argument: null pointer, size, dtype, name, shape */
+  WD_ERR_STATE = 2,    /* call out of order (e.g. wd_step before wd_cross_kv) */
+  WD_ERR_RANGE = 3,    /* device flag: token/position/NaN out of range (wd_check) */
+  WD_ERR_HIP = 4,      /* a HIP runtime call failed */
+  WD_ERR_OOM = 5,      /* workspace smaller than wd_workspace_bytes */
+  WD_ERR_INTERNAL = 6
+} wd_status;
+
+typedef enum { WD_F32 = 0, WD_F16 = 1, WD_BF16 = 2 } wd_dtype;
+typedef enum { WD_ARCH_WHISPER = 0, WD_ARCH_QWEN3 = 1 } wd_arch;
+
+/* Model and run-size description.
+ *   arch        WD_ARCH_WHISPER or WD_ARCH_QWEN3
+ *   d_model     residual width d (multiple of 8)
+ *   n_heads     query heads; head_dim = 64 or 128
+ *   n_kv_heads  key/value heads (== n_heads for Whisper; divides n_heads)
+ *   n_layers, d_ff (multiple of 8), vocab, context (self-cache rows)
+ *   max_frames  cross-cache rows per encoder set (Whisper; 0 for Qwen3)
+ *   max_batch   rows per step, 1..WD_MAX_BATCH
+ *   n_enc       distinct encoder-state sets (Whisper): max_batch (one per
+ *               stream) or 1 (one set broadcast to all rows, as for beams;
+ *               this also reserves a second self cache for wd_reorder).
+ *               Row b reads set b / (max_batch / n_enc).  0 for Qwen3.
+ *   w_dtype     storage of the weight matrices and encoder states
+ *   cache_dtype storage of the self and cross K/V caches
+ *   norm_eps    LayerNorm / RMSNorm epsilon; rope_base (Qwen3 only)        */
+typedef struct {
+  int32_t arch, d_model, n_heads, n_kv_heads, head_dim, n_layers, d_ff, vocab;
+  int32_t context, max_frames, max_batch, n_enc;
+  int32_t w_dtype, cache_dtype;
+  float norm_eps, rope_base;
+} wd_config;
+
+/* One named weight tensor in caller device memory, row-major [out, in] for
+ * matrices.  Matrices must be in cfg.w_dtype; vectors (biases, norm gains
+ * and biases) may be any wd_dtype.  Canonical names (i = layer index):
+ *   Whisper: embed [vocab,d]  pos [context,d]  ln_f.g  ln_f.b
+ *     dec.i.ln1.g/.b  dec.i.self.q.w/.b  dec.i.self.k.w  dec.i.self.v.w/.b
+ *     dec.i.self.o.w/.b  dec.i.ln2.g/.b  dec.i.cross.q.w/.b  dec.i.cross.k.w
+ *     dec.i.cross.v.w/.b  dec.i.cross.o.w/.b  dec.i.ln3.g/.b
+ *     dec.i.fc1.w [d_ff,d]/.b  dec.i.fc2.w [d,d_ff]/.b
+ *   Key projections have no bias (Nest model page, README "The key
+ *   projection has no bias"; wavo `Decoder::load` zero-fills the K half of
+ *   the fused cross bias): any "*.k.b" name is rejected with WD_ERR_ARG.
+ *   Qwen3: embed [vocab,d]  norm_f.g  dec.i.norm1.g  dec.i.self.q.w
+ *     [Hq*hd,d]  dec.i.self.k.w/.v.w [Hkv*hd,d]  dec.i.self.o.w [d,Hq*hd]
+ *     dec.i.q_norm.g/.k_norm.g [hd]  dec.i.norm2.g  dec.i.mlp.gate.w/.up.w
+ *     [d_ff,d]  dec.i.mlp.down.w [d,d_ff]  (no biases).                  */
+typedef struct {
+  const char* name;
+  const void* data;    /* dev */
+  int64_t numel;
+  int32_t dtype;       /* wd_dtype */
+} wd_tensor;
+
+/* Library ABI version (WD_ABI_VERSION). */
+int32_t wd_abi_version(void);
+
+/* Bytes of workspace wd_load needs for cfg (repacked weights, self caches,
+ * cross caches, step scratch, device error word); 0 if cfg is invalid. */
+size_t wd_workspace_bytes(const wd_config* cfg);
+
+/* Validates cfg and the weight list, repacks the weights into `workspace`
+ * (dev, 256-byte aligned, ws_bytes >= wd_workspace_bytes(cfg)) on `stream`
+ * (a hipStream_t; NULL = the null stream) and returns a host-side context in
+ * *out.  Repacking fuses q|k|v (and gate|up) row blocks and the cross [k|v]
+ * projection with bias [0 | b_v] (wavo decoder.rs `Decoder::load`).
+ * Errors: WD_ERR_ARG (null, invalid dims, missing/unknown/misshaped name,
+ * wrong matrix dtype, misaligned workspace), WD_ERR_OOM, WD_ERR_HIP. */
+wd_status wd_load(const wd_config* cfg, const wd_tensor* weights, int32_t n_weights,
+                  void* workspace, size_t ws_bytes, void* stream, wd_ctx** out);
+
+/* Whisper: computes every layer's cross K/V once per window from encoder
+ * states `enc` (dev, [n_enc, frames, d] in w_dtype): K = enc Wk^T, V = enc
+ * Wv^T + b_v, rounded to cache_dtype (wavo `record_cross`; mlx-bun
+ * `decode` computes crossK/crossV once and reuses them).
+ * 1 <= frames <= max_frames.  Errors: ARG, STATE (Qwen3 context). */
+wd_status wd_cross_kv(wd_ctx* ctx, const void* enc, int32_t frames);
+
+/* One decoder step for rows 0..B-1 (1 <= B <= max_batch).
+ *   tokens    dev int32 [B]   token id per row (may alias `argmax` for
+ *                             on-device greedy decoding)
+ *   positions dev int32 [B]   cache row per row; the step writes K/V at that
+ *                             row and attends to rows 0..positions[b]
+ *                             inclusive (wavo `record_step` attends `pos + 1`
+ *                             rows after writing; decoder.h step graph masks
+ *                             rows beyond n_past); rows below it must have
+ *                             been written by earlier steps or a prefill.
+ *   logits    dev float [B, vocab] or NULL (NULL skips the logits write;
+ *                             decoder.h `StepBuild::out` returns only the id)
+ *   argmax    dev int32 [B]   index of the largest logit, lowest on ties.
+ * Whisper requires a prior wd_cross_kv.  Errors: ARG (B, nulls), STATE. */
+wd_status wd_step(wd_ctx* ctx, const int32_t* tokens, const int32_t* positions, int32_t B,
+                  float* logits, int32_t* argmax);
+
+/* Beam rearrangement: new self-cache row b <- old row beam_idx[b] for cache
+ * rows 0..n_rows-1 of every layer (mlx-bun `WhisperKvCache.rearrange`).
+ * beam_idx is host int32 [B]; identity returns at once; the broadcast cross
+ * cache is not touched.  Needs n_enc == 1 and max_batch > 1 (the spare self
+ * cache); the copy goes into the spare cache, which then becomes current.
+ * Errors: ARG (index outside [0,B), n_rows outside [0,context]), STATE. */
+wd_status wd_reorder(wd_ctx* ctx, const int32_t* beam_idx, int32_t B, int32_t n_rows);
+
+/* Prompt prefill for rows 0..B-1 at positions 0..T-1 (Nest entry `prefill`;
+ * decoder.h `PrefillBuild`).  tokens dev int32 [B, T]; embeds dev [B, A, d]
+ * in w_dtype or NULL: rows offset..offset+A-1 take these embeddings instead of
+ * the token embeddings (decoder.h "Audio injection").  Fills cache rows
+ * 0..T-1 and returns the logits (nullable) and argmax of the last position.
+ * Errors: ARG (T outside [1, context], offset/A outside [0, T]), STATE. */
+wd_status wd_prefill(wd_ctx* ctx, const int32_t* tokens, int32_t B, int32_t T,
+                     const void* embeds, int32_t A, int32_t offset,
+                     float* logits, int32_t* argmax);
+
+/* Synchronises the stream, reads and clears the sticky device flag:
+ * WD_OK, WD_ERR_RANGE (flag was set) or WD_ERR_HIP. */
+wd_status wd_check(wd_ctx* ctx);
+
+/* Message for the last non-OK status of ctx (ctx NULL: of the last failed
+ * wd_load on this thread).  Valid until the next call on ctx. */
+const char* wd_last_error(const wd_ctx* ctx);
+
+/* Releases the host-side context (events); never touches caller memory. */
+void wd_free(wd_ctx* ctx);
+
+/* --- measurement support ------------------------------------------------
+ * Records a pair of HIP events on the context's stream around every launch
+ * of kernel class `kernel` in layer `layer` (-1: all layers) during later
+ * wd_step / wd_cross_kv calls; wd_profile_read sums their elapsed times
+ * (synchronising first).  kernel: 0 cross-attention, 1 self-attention,
+ * 2 logits + argmax, 3 cross-K/V GEMM, 4 FFN fc1 projection.
+ * wd_profile(ctx, -1, 0) disables recording and clears the totals.        */
+wd_status wd_profile(wd_ctx* ctx, int32_t kernel, int32_t layer);
+wd_status wd_profile_read(wd_ctx* ctx, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WD_H */

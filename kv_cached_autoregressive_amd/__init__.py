@@ -1,0 +1,265 @@
+"""Python binding of the MI355X decoder-step library (``libwd.so``).
+
+The functions below carry the names of the C ABI in ``include/wd.h`` and only
+marshal arguments through ctypes; every step of the decoder runs in the
+library's HIP kernels.  PyTorch is used for device memory and streams only
+(``Decoder`` allocates the workspace and uploads weights with it).
+
+The library must have been built (``python -m kv_cached_autoregressive_amd._build``
+or ``__graft_entry__.build()``); importing a missing library raises at once --
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Dict, Iterable, Optional, Sequence
+
+__all__ = [
+    "WdError", "WdConfig", "WdTensor", "lib", "lib_path", "declared_functions",
+    "wd_abi_version", "wd_workspace_bytes", "wd_load", "wd_cross_kv", "wd_step", "wd_reorder",
+    "wd_prefill", "wd_check", "wd_last_error", "wd_free", "wd_profile", "wd_profile_read",
+    "config_from", "Decoder", "DTYPES", "STATUS",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(HERE)
+HEADER = os.path.join(_ROOT, "include", "wd.h")
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+ARCHS = {"whisper": 0, "qwen3": 1}
+STATUS = {0: "WD_OK", 1: "WD_ERR_ARG", 2: "WD_ERR_STATE", 3: "WD_ERR_RANGE", 4: "WD_ERR_HIP",
+          5: "WD_ERR_OOM", 6: "WD_ERR_INTERNAL"}
+# kernel classes for wd_profile
+K_CROSS_ATTN, K_SELF_ATTN, K_LOGITS, K_XKV_GEMM, K_FC1 = 0, 1, 2, 3, 4
+
+
+class WdError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class WdConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "arch", "d_model", "n_heads", "n_kv_heads", "head_dim", "n_layers", "d_ff", "vocab",
+        "context", "max_frames", "max_batch", "n_enc", "w_dtype", "cache_dtype")] + [
+        ("norm_eps", ctypes.c_float), ("rope_base", ctypes.c_float)]
+
+
+class WdTensor(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("data", ctypes.c_void_p), ("numel", ctypes.c_int64),
+                ("dtype", ctypes.c_int32)]
+
+
+def lib_path() -> str:
+    return os.environ.get("WD_LIB", os.path.join(HERE, "libwd.so"))
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        p = lib_path()
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is missing: build it with `python -m kv_cached_autoregressive_amd._build`")
+        L = ctypes.CDLL(p)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        sig = {
+            "wd_abi_version": (i32, []),
+            "wd_workspace_bytes": (sz, [ctypes.POINTER(WdConfig)]),
+            "wd_load": (i32, [ctypes.POINTER(WdConfig), ctypes.POINTER(WdTensor), i32, vp, sz, vp,
+                              ctypes.POINTER(vp)]),
+            "wd_cross_kv": (i32, [vp, vp, i32]),
+            "wd_step": (i32, [vp, vp, vp, i32, vp, vp]),
+            "wd_reorder": (i32, [vp, ctypes.POINTER(i32), i32, i32]),
+            "wd_prefill": (i32, [vp, vp, i32, i32, vp, i32, i32, vp, vp]),
+            "wd_check": (i32, [vp]),
+            "wd_last_error": (ctypes.c_char_p, [vp]),
+            "wd_free": (None, [vp]),
+            "wd_profile": (i32, [vp, i32, i32]),
+            "wd_profile_read": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _LIB = L
+    return _LIB
+
+
+def declared_functions() -> list:
+    """Names of the functions include/wd.h declares."""
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(wd_[a-z_]+)\s*\(", txt)))
+
+
+def _check(st: int, ctx=None):
+    if st != 0:
+        raise WdError(st, wd_last_error(ctx))
+
+
+# ---- the C ABI, one wrapper per entry point --------------------------------------------------
+
+def wd_abi_version() -> int:
+    return lib().wd_abi_version()
+
+
+def wd_workspace_bytes(cfg: WdConfig) -> int:
+    return lib().wd_workspace_bytes(ctypes.byref(cfg))
+
+
+def wd_load(cfg: WdConfig, tensors: Sequence[WdTensor], workspace: int, ws_bytes: int,
+            stream: int = 0):
+    arr = (WdTensor * max(1, len(tensors)))(*tensors)
+    out = ctypes.c_void_p()
+    st = lib().wd_load(ctypes.byref(cfg), arr if tensors else None, len(tensors),
+                       ctypes.c_void_p(workspace), ws_bytes, ctypes.c_void_p(stream), ctypes.byref(out))
+    _check(st)
+    return out.value
+
+
+def wd_cross_kv(ctx, enc: int, frames: int):
+    _check(lib().wd_cross_kv(ctx, ctypes.c_void_p(enc), frames), ctx)
+
+
+def wd_step(ctx, tokens: int, positions: int, B: int, logits: int, argmax: int):
+    _check(lib().wd_step(ctx, ctypes.c_void_p(tokens), ctypes.c_void_p(positions), B,
+                         ctypes.c_void_p(logits) if logits else None, ctypes.c_void_p(argmax)), ctx)
+
+
+def wd_reorder(ctx, beam_idx: Iterable[int], n_rows: int):
+    idx = list(beam_idx)
+    arr = (ctypes.c_int32 * max(1, len(idx)))(*idx)
+    _check(lib().wd_reorder(ctx, arr, len(idx), n_rows), ctx)
+
+
+def wd_prefill(ctx, tokens: int, B: int, T: int, embeds: int, A: int, offset: int, logits: int,
+               argmax: int):
+    _check(lib().wd_prefill(ctx, ctypes.c_void_p(tokens), B, T,
+                            ctypes.c_void_p(embeds) if embeds else None, A, offset,
+                            ctypes.c_void_p(logits) if logits else None, ctypes.c_void_p(argmax)), ctx)
+
+
+def wd_check(ctx) -> int:
+    """Returns the status (0, or WD_ERR_RANGE == 3 when the device flag was set)."""
+    return lib().wd_check(ctx)
+
+
+def wd_last_error(ctx=None) -> str:
+    r = lib().wd_last_error(ctx)
+    return r.decode() if r else ""
+
+
+def wd_free(ctx):
+    lib().wd_free(ctx)
+
+
+def wd_profile(ctx, kernel: int, layer: int = -1):
+    _check(lib().wd_profile(ctx, kernel, layer), ctx)
+
+
+def wd_profile_read(ctx):
+    t = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(lib().wd_profile_read(ctx, ctypes.byref(t), ctypes.byref(n)), ctx)
+    return t.value, n.value
+
+
+# ---- convenience: config and a torch-backed holder -------------------------------------------
+
+def config_from(w, max_batch: Optional[int] = None) -> WdConfig:
+    """WdConfig from any object with the workload attribute names (d, heads, ...)."""
+    c = WdConfig()
+    c.arch = ARCHS[w.arch]
+    c.d_model, c.n_heads, c.n_kv_heads, c.head_dim = w.d, w.heads, w.kv_heads, w.head_dim
+    c.n_layers, c.d_ff, c.vocab, c.context = w.layers, w.d_ff, w.vocab, w.context
+    c.max_frames = w.frames if w.arch == "whisper" else 0
+    c.max_batch = w.batch if max_batch is None else max_batch
+    c.n_enc = w.n_enc if w.arch == "whisper" else 0
+    c.w_dtype, c.cache_dtype = DTYPES[w.w_dtype], DTYPES[w.cache_dtype]
+    c.norm_eps = w.eps
+    c.rope_base = w.rope_base
+    return c
+
+
+def _torch_dtype(name: str):
+    import torch
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[name]
+
+
+class Decoder:
+    """Owns one context: the workspace (a torch uint8 tensor), the loaded weights
+    and the caches.  ``weights`` maps canonical names to arrays/tensors holding
+    values representable in the workload's w_dtype."""
+
+    def __init__(self, w, weights: Dict[str, object], device: str = "cuda", stream=None):
+        import numpy as np
+        import torch
+        self.w = w
+        self.cfg = config_from(w)
+        self.device = torch.device(device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        nbytes = wd_workspace_bytes(self.cfg)
+        if nbytes == 0:
+            raise WdError(1, "invalid configuration")
+        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        base = self.workspace.data_ptr()
+        self.ws_ptr = (base + 255) & ~255
+        wdt = _torch_dtype(w.w_dtype)
+        up, descs = [], []
+        with torch.cuda.stream(self.stream):
+            for name, arr in weights.items():
+                t = arr if isinstance(arr, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(arr))
+                t = t.to(device=self.device, dtype=wdt).contiguous()
+                up.append(t)
+                descs.append(WdTensor(name.encode(), t.data_ptr(), t.numel(), DTYPES[w.w_dtype]))
+        self.ctx = wd_load(self.cfg, descs, self.ws_ptr, nbytes, self.stream.cuda_stream)
+        self.stream.synchronize()
+        del up
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            wd_free(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def cross_kv(self, enc, frames: Optional[int] = None):
+        wd_cross_kv(self.ctx, enc.data_ptr(), enc.shape[1] if frames is None else frames)
+
+    def step(self, tokens, positions, logits=None, argmax=None):
+        """tokens, positions: int32 device tensors [B].  Returns (logits, argmax)."""
+        import torch
+        B = tokens.shape[0]
+        if argmax is None:
+            argmax = torch.empty(B, dtype=torch.int32, device=self.device)
+        wd_step(self.ctx, tokens.data_ptr(), positions.data_ptr(), B,
+                logits.data_ptr() if logits is not None else 0, argmax.data_ptr())
+        return logits, argmax
+
+    def prefill(self, tokens, embeds=None, offset: int = 0, logits=None, argmax=None):
+        import torch
+        B, T = tokens.shape
+        if argmax is None:
+            argmax = torch.empty(B, dtype=torch.int32, device=self.device)
+        A = 0 if embeds is None else embeds.shape[1]
+        wd_prefill(self.ctx, tokens.data_ptr(), B, T, embeds.data_ptr() if embeds is not None else 0,
+                   A, offset, logits.data_ptr() if logits is not None else 0, argmax.data_ptr())
+        return logits, argmax
+
+    def reorder(self, beam_idx, n_rows: int):
+        wd_reorder(self.ctx, [int(i) for i in beam_idx], n_rows)
+
+    def check(self) -> int:
+        return wd_check(self.ctx)
+
+    def last_error(self) -> str:
+        return wd_last_error(self.ctx)

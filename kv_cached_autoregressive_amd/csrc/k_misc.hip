@@ -1,0 +1,283 @@
+// Small kernels of the decoder step: weight repack, embedding, row norms,
+// Qwen3 per-head QK norm + RoPE + cache append, argmax finalisation and the
+// beam-reorder cache gather.  All are tiny next to the weight and cache
+// streams; they are written for coalesced 16-byte accesses where it matters.
+#include "wd_common.h"
+#include "wd_kernels.h"
+
+namespace wd {
+
+// ------------------------------------------------------------------------------------------
+// repack: row copy with dtype conversion and a row remap (fused q|k|v, gate|up blocks)
+// ------------------------------------------------------------------------------------------
+template <typename S, typename D>
+__global__ void k_copy_rows(const S* __restrict__ src, D* __restrict__ dst, int64_t rows,
+                            int64_t cols, int64_t row_mul, int64_t row_add) {
+  const int64_t n = rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / cols, c = i - r * cols;
+    dst[(r * row_mul + row_add) * cols + c] = from_f<D>(to_f(src[i]));
+  }
+}
+
+template <typename S>
+static hipError_t copy_rows_to(const S* src, void* dst, int dst_dtype, int64_t rows, int64_t cols,
+                               int64_t mul, int64_t add, hipStream_t s) {
+  const int64_t n = rows * cols;
+  const int blocks = (int)std::min<int64_t>((n + 255) / 256, 65536);
+  if (n <= 0) return hipSuccess;
+  switch (dst_dtype) {
+    case DT_F32: k_copy_rows<<<blocks, 256, 0, s>>>(src, (float*)dst, rows, cols, mul, add); break;
+    case DT_F16: k_copy_rows<<<blocks, 256, 0, s>>>(src, (f16_t*)dst, rows, cols, mul, add); break;
+    case DT_BF16: k_copy_rows<<<blocks, 256, 0, s>>>(src, (bf16_t*)dst, rows, cols, mul, add); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const void* src, int src_dtype, void* dst, int dst_dtype, int64_t rows,
+                            int64_t cols, int64_t row_mul, int64_t row_add, hipStream_t s) {
+  switch (src_dtype) {
+    case DT_F32: return copy_rows_to((const float*)src, dst, dst_dtype, rows, cols, row_mul, row_add, s);
+    case DT_F16: return copy_rows_to((const f16_t*)src, dst, dst_dtype, rows, cols, row_mul, row_add, s);
+    case DT_BF16: return copy_rows_to((const bf16_t*)src, dst, dst_dtype, rows, cols, row_mul, row_add, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+__global__ void k_fill(T* p, T v, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_fill<<<(int)std::min<int64_t>((n + 255) / 256, 4096), 256, 0, s>>>(p, v, n);
+  return hipGetLastError();
+}
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_fill<<<(int)std::min<int64_t>((n + 255) / 256, 4096), 256, 0, s>>>(p, v, n);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// embedding: token row + learned position row (Whisper) or token row (Qwen3), or an
+// embedding override row (prompt audio splice).  Out-of-range ids/positions raise the
+// device flag and produce a zero row.
+// ------------------------------------------------------------------------------------------
+template <typename WT>
+__global__ __launch_bounds__(256) void k_embed(float* __restrict__ x, const WT* __restrict__ E,
+                                               const WT* __restrict__ P, const int32_t* tok,
+                                               int tok_stride, const int32_t* pos,
+                                               const WT* __restrict__ ov, int64_t ov_stride, int d,
+                                               int V, int ctx, unsigned* err) {
+  const int b = blockIdx.x;
+  const int p = pos[b];
+  const bool bad_p = p < 0 || p >= ctx;
+  int t = 0;
+  bool bad_t = false;
+  if (!ov) {
+    t = tok[(int64_t)b * tok_stride];
+    bad_t = t < 0 || t >= V;
+  }
+  if (threadIdx.x == 0 && (bad_p || bad_t)) raise_err(err, (bad_p ? ERR_POS : 0u) | (bad_t ? ERR_TOKEN : 0u));
+  float* xr = x + (int64_t)b * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    float v = 0.f;
+    if (!bad_p && !bad_t) {
+      if (ov) {
+        v = to_f(ov[(int64_t)b * ov_stride + i]);
+      } else {
+        v = to_f(E[(int64_t)t * d + i]);
+        if (P) v += to_f(P[(int64_t)p * d + i]);
+      }
+    }
+    xr[i] = v;
+  }
+}
+
+hipError_t launch_embed(float* x, const void* E, const void* P, int w_dtype, const int32_t* tok,
+                        int tok_stride, const int32_t* pos, const void* ov, int64_t ov_stride,
+                        int B, int d, int V, int ctx, unsigned* err, hipStream_t s) {
+  if (B <= 0 || d <= 0 || (!ov && !tok) || !pos) return hipErrorInvalidValue;
+  switch (w_dtype) {
+    case DT_F32: k_embed<<<B, 256, 0, s>>>(x, (const float*)E, (const float*)P, tok, tok_stride, pos, (const float*)ov, ov_stride, d, V, ctx, err); break;
+    case DT_F16: k_embed<<<B, 256, 0, s>>>(x, (const f16_t*)E, (const f16_t*)P, tok, tok_stride, pos, (const f16_t*)ov, ov_stride, d, V, ctx, err); break;
+    case DT_BF16: k_embed<<<B, 256, 0, s>>>(x, (const bf16_t*)E, (const bf16_t*)P, tok, tok_stride, pos, (const bf16_t*)ov, ov_stride, d, V, ctx, err); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// row norms, one block per row; LayerNorm uses the two-pass (mean, then centred
+// variance) form, eps inside the square root.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, float* __restrict__ y,
+                                              const float* __restrict__ g,
+                                              const float* __restrict__ bvec, int d, float eps) {
+  __shared__ float red[4];
+  const float* xr = x + (int64_t)blockIdx.x * d;
+  float* yr = y + (int64_t)blockIdx.x * d;
+  float mean = 0.f;
+  if (bvec) {
+    float s = 0.f;
+    for (int i = threadIdx.x; i < d; i += 256) s += xr[i];
+    mean = block_sum<256>(s, red) / (float)d;
+  }
+  float s2 = 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) {
+    const float c = xr[i] - mean;
+    s2 += c * c;
+  }
+  const float var = block_sum<256>(s2, red) / (float)d;
+  const float rs = 1.0f / sqrtf(var + eps);
+  for (int i = threadIdx.x; i < d; i += 256) {
+    const float v = (xr[i] - mean) * rs * g[i];
+    yr[i] = bvec ? v + bvec[i] : v;
+  }
+}
+
+hipError_t launch_norm(const float* x, float* y, const float* g, const float* b, int B, int d,
+                       float eps, hipStream_t s) {
+  if (B <= 0 || d <= 0 || !g) return hipErrorInvalidValue;
+  k_norm<<<B, 256, 0, s>>>(x, y, g, b, d, eps);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Qwen3: per-head RMSNorm of q and k over head_dim, NeoX RoPE at the row's position,
+// q scaled by 1/sqrt(hd) into q_out, k and v appended to the cache row.  One wave per
+// (head slot, row): slots [0,Hq) are q heads, [Hq,Hq+Hkv) k heads, the rest v heads.
+// The rotation angle pos * base^(-2i/hd) and its sine/cosine are taken in double.
+// ------------------------------------------------------------------------------------------
+template <typename CT>
+__global__ __launch_bounds__(64) void k_qk_rope_append(const float* __restrict__ qkv, int Hq, int Hkv,
+                                                       int hd, const int32_t* pos, int ctx,
+                                                       const float* __restrict__ qn,
+                                                       const float* __restrict__ kn, float eps,
+                                                       float base, float qscale, float* q_out,
+                                                       CT* Kc, CT* Vc, int64_t kv_bstride) {
+  __shared__ float z[256];
+  const int slot = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int nslot = Hq + 2 * Hkv;
+  const float* src = qkv + ((int64_t)b * nslot + slot) * hd;
+  const int p = pos[b];
+  const bool ok = p >= 0 && p < ctx;
+  if (slot >= Hq + Hkv) {  // value head: plain append
+    if (!ok) return;
+    const int g = slot - Hq - Hkv;
+    CT* dst = Vc + (int64_t)b * kv_bstride + ((int64_t)g * ctx + p) * hd;
+    for (int c = lane; c < hd; c += 64) dst[c] = from_f<CT>(src[c]);
+    return;
+  }
+  const float* gain = slot < Hq ? qn : kn;
+  float ss = 0.f;
+  for (int c = lane; c < hd; c += 64) ss += src[c] * src[c];
+  ss = wave_sum(ss);
+  const float rs = 1.0f / sqrtf(ss / (float)hd + eps);
+  for (int c = lane; c < hd; c += 64) z[c] = src[c] * rs * gain[c];
+  __syncthreads();
+  const int half = hd / 2;
+  const double dpos = ok ? (double)p : 0.0;
+  for (int i = lane; i < half; i += 64) {
+    const double th = dpos * pow((double)base, -2.0 * (double)i / (double)hd);
+    const float cs = (float)cos(th), sn = (float)sin(th);
+    const float a = z[i], bb = z[i + half];
+    const float r0 = a * cs - bb * sn, r1 = bb * cs + a * sn;
+    if (slot < Hq) {
+      float* qo = q_out + ((int64_t)b * Hq + slot) * hd;
+      qo[i] = r0 * qscale;
+      qo[i + half] = r1 * qscale;
+    } else if (ok) {
+      const int g = slot - Hq;
+      CT* dst = Kc + (int64_t)b * kv_bstride + ((int64_t)g * ctx + p) * hd;
+      dst[i] = from_f<CT>(r0);
+      dst[i + half] = from_f<CT>(r1);
+    }
+  }
+}
+
+hipError_t launch_qk_rope_append(const float* qkv, int B, int Hq, int Hkv, int hd, const int32_t* pos,
+                                 int ctx, const float* qn, const float* kn, float eps, float base,
+                                 float qscale, float* q_out, void* Kc, void* Vc, int cache_dtype,
+                                 int64_t kv_bstride, hipStream_t s) {
+  if (B <= 0 || hd > 256 || (hd % 2) || Hq <= 0 || Hkv <= 0) return hipErrorInvalidValue;
+  dim3 grid(Hq + 2 * Hkv, B);
+  switch (cache_dtype) {
+    case DT_F32: k_qk_rope_append<<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, (float*)Kc, (float*)Vc, kv_bstride); break;
+    case DT_F16: k_qk_rope_append<<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, (f16_t*)Kc, (f16_t*)Vc, kv_bstride); break;
+    case DT_BF16: k_qk_rope_append<<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, (bf16_t*)Kc, (bf16_t*)Vc, kv_bstride); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// argmax: max over the per-block keys of each row; the key order makes the lowest
+// index win ties.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_argmax_final(const unsigned long long* __restrict__ amax,
+                                                      int nparts, int ldp, int32_t* out) {
+  __shared__ unsigned long long red[256];
+  const int b = blockIdx.x;
+  unsigned long long m = 0;
+  for (int i = threadIdx.x; i < nparts; i += 256) {
+    const unsigned long long k = amax[(int64_t)i * ldp + b];
+    m = k > m ? k : m;
+  }
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      const unsigned long long o = red[threadIdx.x + s];
+      if (o > red[threadIdx.x]) red[threadIdx.x] = o;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[b] = (int32_t)(0xffffffffu - (uint32_t)(red[0] & 0xffffffffull));
+}
+
+hipError_t launch_argmax_final(const unsigned long long* amax, int nparts, int ldp, int B,
+                               int32_t* out, hipStream_t s) {
+  if (B <= 0 || nparts <= 0 || ldp < B) return hipErrorInvalidValue;
+  k_argmax_final<<<B, 256, 0, s>>>(amax, nparts, ldp, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// beam reorder: for every (layer, K|V) block, new row b <- old row idx[b], cache rows
+// 0..n_rows-1 of every head, 16 bytes per thread.  Source and destination are the two
+// halves of the ping-pong cache, so the gather never reads what it writes.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_reorder(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                 BeamIdx idx, int H, int64_t slab_vec,
+                                                 int64_t copy_vec, int64_t block_vec) {
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh - (bh / H) * H;
+  const int64_t blk = (int64_t)blockIdx.z * block_vec;
+  const int64_t so = blk + ((int64_t)idx.v[b] * H + h) * slab_vec;
+  const int64_t dof = blk + ((int64_t)b * H + h) * slab_vec;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < copy_vec; i += (int64_t)gridDim.x * 256)
+    dst[dof + i] = src[so + i];
+}
+
+hipError_t launch_reorder(const void* src, void* dst, int elt_bytes, const BeamIdx& idx, int B, int Bmax,
+                          int H, int ctx, int hd, int n_rows, int n_blocks, hipStream_t s) {
+  if (B <= 0 || B > 64 || B > Bmax || n_rows < 0 || n_rows > ctx || n_blocks <= 0) return hipErrorInvalidValue;
+  if (((int64_t)hd * elt_bytes) % 16) return hipErrorInvalidValue;
+  for (int b = 0; b < B; ++b)
+    if (idx.v[b] < 0 || idx.v[b] >= B) return hipErrorInvalidValue;
+  if (n_rows == 0) return hipSuccess;
+  const int64_t row_vec = (int64_t)hd * elt_bytes / 16;
+  const int64_t slab_vec = (int64_t)ctx * row_vec;
+  const int64_t copy_vec = (int64_t)n_rows * row_vec;
+  const int64_t block_vec = (int64_t)Bmax * H * slab_vec;
+  dim3 grid((unsigned)std::min<int64_t>((copy_vec + 255) / 256, 64), B * H, n_blocks);
+  k_reorder<<<grid, 256, 0, s>>>((const uint4*)src, (uint4*)dst, idx, H, slab_vec, copy_vec, block_vec);
+  return hipGetLastError();
+}
+
+}  // namespace wd

@@ -1,0 +1,722 @@
+// Host runtime of the decoder step: configuration checks, workspace plan, weight
+// repack, and the launch sequence of one step.  Exports the C ABI of wd.h.
+//
+// Device layout inside the caller's workspace (every region 256-byte aligned):
+//   weights    per layer, row-major [out, in] in w_dtype, row blocks fused:
+//              Whisper q|k|v [3d, d], cross k|v [2d, d]; Qwen3 q|k|v
+//              [(Hq+2Hkv)hd, d], gate|up [2ff, d]; biases and norm vectors fp32
+//              (the K blocks of the fused biases are zero)
+//   self cache per buffer, per layer: K then V, each [max_batch][Hkv][context][hd]
+//              (head-major, one contiguous [context, hd] slab per row and head);
+//              two buffers when the rows share one encoder set (beam reorder)
+//   cross      per layer: K then V, each [n_enc][H][max_frames][hd]
+//   scratch    x, y, q, qkv, o, h (fp32), split partials, argmax keys, error word
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "wd.h"
+#include "wd_kernels.h"
+
+namespace {
+
+using wd::DT_BF16;
+using wd::DT_F16;
+using wd::DT_F32;
+
+thread_local std::string g_load_error;
+
+int dtype_bytes(int dt) { return dt == DT_F32 ? 4 : (dt == DT_F16 || dt == DT_BF16) ? 2 : 0; }
+
+struct LayerOff {
+  // Whisper
+  size_t wqkv, wo, wcq, wckv, wco, w1, w2;
+  size_t bqkv, bo, bcq, bckv, bco, b1, b2, ln1g, ln1b, ln2g, ln2b, ln3g, ln3b;
+  // Qwen3
+  size_t wgu, wdn, n1g, n2g, qn, kn;
+};
+
+struct Plan {
+  size_t total = 0;
+  std::vector<LayerOff> L;
+  size_t embed = 0, pos = 0, lnfg = 0, lnfb = 0;
+  size_t self[2] = {0, 0};
+  size_t self_slab = 0;   // bytes of one K (or V) block of one layer
+  int n_bufs = 1;
+  size_t cross = 0, cross_slab = 0;
+  size_t x = 0, y = 0, q = 0, qkv = 0, o = 0, h = 0, part = 0, amax = 0, err = 0, pos_tmp = 0;
+  int max_splits = 1, amax_parts = 1;
+};
+
+struct Bump {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    off = (off + 255) & ~size_t(255);
+    const size_t at = off;
+    off += bytes;
+    return at;
+  }
+};
+
+bool valid_dt(int dt) { return dt == DT_F32 || dt == DT_F16 || dt == DT_BF16; }
+
+// Returns an empty string when cfg is acceptable, else the reason.
+std::string check_config(const wd_config& c) {
+  if (c.arch != WD_ARCH_WHISPER && c.arch != WD_ARCH_QWEN3) return "arch must be 0 (whisper) or 1 (qwen3)";
+  if (c.d_model <= 0 || c.d_model % 32) return "d_model must be a positive multiple of 32";
+  if (c.head_dim != 64 && c.head_dim != 128) return "head_dim must be 64 or 128";
+  if (c.n_heads <= 0 || c.n_kv_heads <= 0 || c.n_heads % c.n_kv_heads) return "n_kv_heads must divide n_heads";
+  if (c.n_heads / c.n_kv_heads > 8) return "at most 8 query heads per kv head";
+  if (c.n_layers <= 0 || c.vocab <= 0 || c.context <= 0) return "n_layers, vocab, context must be positive";
+  if (c.d_ff <= 0 || c.d_ff % 8) return "d_ff must be a positive multiple of 8";
+  if (c.max_batch < 1 || c.max_batch > WD_MAX_BATCH) return "max_batch must be in [1, 64]";
+  if (!valid_dt(c.w_dtype) || !valid_dt(c.cache_dtype)) return "unknown dtype";
+  if (!(c.norm_eps > 0.f)) return "norm_eps must be positive";
+  if (c.arch == WD_ARCH_WHISPER) {
+    if (c.n_kv_heads != c.n_heads || c.n_heads * c.head_dim != c.d_model) return "whisper: heads * head_dim must equal d_model";
+    if (c.max_frames <= 0) return "whisper: max_frames must be positive";
+    if (c.n_enc <= 0 || c.max_batch % c.n_enc) return "whisper: n_enc must divide max_batch";
+    if (c.max_batch / c.n_enc > 8) return "whisper: at most 8 rows per encoder set";
+  } else {
+    if (!(c.rope_base > 0.f)) return "qwen3: rope_base must be positive";
+    if (c.n_enc != 0) return "qwen3: n_enc must be 0";
+  }
+  return "";
+}
+
+// Split of an attention over `rows` cache rows: aim at >= 2048 blocks in total, at
+// least 64 rows (one K/V tile of a few KB) per block, scores within the LDS budget.
+void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits) {
+  const int want = std::max(1, (2048 + slabs - 1) / slabs);
+  int r = (rows + want - 1) / want;
+  r = std::max(r, 64);
+  r = (r + 31) & ~31;
+  r = std::min(r, 12288 / std::max(nq, 1));
+  r = std::max(r, 1);
+  *split_rows = r;
+  *n_splits = std::max(1, (rows + r - 1) / r);
+}
+
+Plan make_plan(const wd_config& c) {
+  Plan p;
+  Bump b;
+  const size_t d = c.d_model, ff = c.d_ff, hd = c.head_dim, hq = c.n_heads, hkv = c.n_kv_heads;
+  const size_t wb = dtype_bytes(c.w_dtype), cb = dtype_bytes(c.cache_dtype), f4 = 4;
+  const size_t Bm = c.max_batch;
+  p.L.resize(c.n_layers);
+  for (auto& l : p.L) {
+    std::memset(&l, 0, sizeof(l));
+    if (c.arch == WD_ARCH_WHISPER) {
+      l.wqkv = b.take(3 * d * d * wb); l.wo = b.take(d * d * wb); l.wcq = b.take(d * d * wb);
+      l.wckv = b.take(2 * d * d * wb); l.wco = b.take(d * d * wb);
+      l.w1 = b.take(ff * d * wb); l.w2 = b.take(d * ff * wb);
+      l.bqkv = b.take(3 * d * f4); l.bo = b.take(d * f4); l.bcq = b.take(d * f4);
+      l.bckv = b.take(2 * d * f4); l.bco = b.take(d * f4); l.b1 = b.take(ff * f4); l.b2 = b.take(d * f4);
+      l.ln1g = b.take(d * f4); l.ln1b = b.take(d * f4); l.ln2g = b.take(d * f4);
+      l.ln2b = b.take(d * f4); l.ln3g = b.take(d * f4); l.ln3b = b.take(d * f4);
+    } else {
+      l.wqkv = b.take((hq + 2 * hkv) * hd * d * wb); l.wo = b.take(d * hq * hd * wb);
+      l.wgu = b.take(2 * ff * d * wb); l.wdn = b.take(d * ff * wb);
+      l.n1g = b.take(d * f4); l.n2g = b.take(d * f4); l.qn = b.take(hd * f4); l.kn = b.take(hd * f4);
+    }
+  }
+  p.embed = b.take((size_t)c.vocab * d * wb);
+  if (c.arch == WD_ARCH_WHISPER) {
+    p.pos = b.take((size_t)c.context * d * wb);
+    p.lnfb = b.take(d * f4);
+  }
+  p.lnfg = b.take(d * f4);
+  p.n_bufs = (c.arch == WD_ARCH_WHISPER && c.n_enc == 1 && c.max_batch > 1) ? 2 : 1;
+  p.self_slab = Bm * hkv * (size_t)c.context * hd * cb;
+  for (int i = 0; i < p.n_bufs; ++i) p.self[i] = b.take(2 * p.self_slab * c.n_layers);
+  if (c.arch == WD_ARCH_WHISPER) {
+    p.cross_slab = (size_t)c.n_enc * hq * (size_t)c.max_frames * hd * cb;
+    p.cross = b.take(2 * p.cross_slab * c.n_layers);
+  }
+  const size_t wide = std::max({d, 2 * ff, (hq + 2 * hkv) * hd});
+  p.x = b.take(Bm * d * f4);
+  p.y = b.take(Bm * wide * f4);
+  p.q = b.take(Bm * hq * hd * f4);
+  p.qkv = b.take(Bm * (hq + 2 * hkv) * hd * f4);
+  p.o = b.take(Bm * hq * hd * f4);
+  p.h = b.take(Bm * 2 * ff * f4);
+  const int rows_max = std::max(c.context, c.arch == WD_ARCH_WHISPER ? c.max_frames : 0);
+  p.max_splits = (rows_max + 63) / 64;
+  p.part = b.take(Bm * hq * (size_t)p.max_splits * (hd + 2) * f4);
+  p.amax_parts = wd::gemv_blocks(c.vocab, c.max_batch);
+  p.amax = b.take((size_t)p.amax_parts * Bm * 8);
+  p.err = b.take(64);
+  p.pos_tmp = b.take(Bm * 4);
+  p.total = (b.off + 255) & ~size_t(255);
+  return p;
+}
+
+struct ProfPair { hipEvent_t a, b; };
+
+}  // namespace
+
+struct wd_ctx {
+  wd_config cfg{};
+  Plan plan;
+  hipStream_t stream = nullptr;
+  char* ws = nullptr;
+  int cur = 0;               // current self-cache buffer
+  bool cross_ready = false;
+  int frames = 0;
+  std::string err;
+  // measurement
+  int prof_kernel = -1, prof_layer = -1;
+  std::vector<ProfPair> prof;
+  size_t prof_used = 0;
+
+  template <typename T = void>
+  T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+  void* self_k(int l) const { return ws + plan.self[cur] + (size_t)l * 2 * plan.self_slab; }
+  void* self_v(int l) const { return ws + plan.self[cur] + (size_t)l * 2 * plan.self_slab + plan.self_slab; }
+  void* cross_k(int l) const { return ws + plan.cross + (size_t)l * 2 * plan.cross_slab; }
+  void* cross_v(int l) const { return ws + plan.cross + (size_t)l * 2 * plan.cross_slab + plan.cross_slab; }
+};
+
+namespace {
+
+wd_status fail(wd_ctx* ctx, wd_status st, const std::string& msg) {
+  if (ctx) ctx->err = msg;
+  else g_load_error = msg;
+  return st;
+}
+
+#define HIPCHK(ctx, expr, what)                                                        \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(ctx, WD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+// kernel classes for measurement
+enum { PK_CROSS_ATTN = 0, PK_SELF_ATTN = 1, PK_LOGITS = 2, PK_XKV_GEMM = 3, PK_FC1 = 4 };
+
+bool prof_on(wd_ctx* c, int kind, int layer) {
+  return c->prof_kernel == kind && (c->prof_layer < 0 || c->prof_layer == layer) &&
+         c->prof_used < c->prof.size();
+}
+void prof_begin(wd_ctx* c, bool on) {
+  if (on) (void)hipEventRecord(c->prof[c->prof_used].a, c->stream);
+}
+void prof_end(wd_ctx* c, bool on) {
+  if (on) { (void)hipEventRecord(c->prof[c->prof_used].b, c->stream); ++c->prof_used; }
+}
+
+// Rows of one step share encoder sets in groups of q_per_kvb rows.
+int rows_per_set(const wd_config& c, int B) {
+  if (c.n_enc == 1) return B;
+  return c.max_batch / c.n_enc;
+}
+
+// One decoder step over rows 0..B-1.  tok: ids (stride tok_stride) or null with ov;
+// pos: device positions; ov: embedding override rows (stride ov_stride) or null.
+wd_status run_step(wd_ctx* c, const int32_t* tok, int tok_stride, const int32_t* pos, const void* ov,
+                   int64_t ov_stride, int B, float* logits, int32_t* argmax, bool head) {
+  const wd_config& g = c->cfg;
+  const Plan& P = c->plan;
+  hipStream_t s = c->stream;
+  const int d = g.d_model, hd = g.head_dim, hq = g.n_heads, hkv = g.n_kv_heads, ff = g.d_ff;
+  const bool whisper = g.arch == WD_ARCH_WHISPER;
+  float* x = c->at<float>(P.x);
+  float* y = c->at<float>(P.y);
+  float* q = c->at<float>(P.q);
+  float* qkv = c->at<float>(P.qkv);
+  float* o = c->at<float>(P.o);
+  float* h = c->at<float>(P.h);
+  float* part = c->at<float>(P.part);
+  unsigned* err = c->at<unsigned>(P.err);
+  const int64_t kv_bstride = (int64_t)hkv * g.context * hd;
+  const float qscale = 1.0f / sqrtf((float)hd);
+
+  HIPCHK(c, wd::launch_embed(x, c->at(P.embed), whisper ? c->at(P.pos) : nullptr, g.w_dtype, tok, tok_stride,
+                             pos, ov, ov_stride, B, d, g.vocab, g.context, err, s), "embed");
+
+  // self-attention split policy (positions live on the device, so split by context)
+  int s_rows, s_splits;
+  split_for(g.context, B * hkv, hq / hkv, &s_rows, &s_splits);
+  const int qpk = whisper ? rows_per_set(g, B) : 1;
+  int c_rows = 0, c_splits = 1;
+  if (whisper) split_for(c->frames, (B / qpk) * hkv, qpk, &c_rows, &c_splits);
+
+  for (int l = 0; l < g.n_layers; ++l) {
+    const LayerOff& L = P.L[l];
+    wd::GemvParams gp{};
+    gp.w_dtype = g.w_dtype;
+    gp.B = B;
+    gp.err = err;
+    gp.scale = 1.0f;
+    wd::AttnParams ap{};
+    ap.cache_dtype = g.cache_dtype;
+    ap.B = B;
+    ap.Hq = hq;
+    ap.Hkv = hkv;
+    ap.hd = hd;
+    ap.part = part;
+
+    if (whisper) {
+      HIPCHK(c, wd::launch_norm(x, y, c->at<float>(L.ln1g), c->at<float>(L.ln1b), B, d, g.norm_eps, s), "ln1");
+      gp.W = c->at(L.wqkv); gp.N = 3 * d; gp.K = d; gp.Y = y; gp.ldy = d; gp.ymode = wd::Y_PLAIN;
+      gp.epi = wd::EPI_QKV; gp.bias = c->at<float>(L.bqkv); gp.out = q; gp.ldo = d; gp.scale = qscale;
+      gp.d = d; gp.H = hq; gp.hd = hd; gp.ctx = g.context; gp.pos = pos;
+      gp.Kc = c->self_k(l); gp.Vc = c->self_v(l); gp.cache_dtype = g.cache_dtype; gp.kv_bstride = kv_bstride;
+      HIPCHK(c, wd::launch_gemv(gp, s), "qkv projection");
+    } else {
+      HIPCHK(c, wd::launch_norm(x, y, c->at<float>(L.n1g), nullptr, B, d, g.norm_eps, s), "norm1");
+      const int nqkv = (hq + 2 * hkv) * hd;
+      gp.W = c->at(L.wqkv); gp.N = nqkv; gp.K = d; gp.Y = y; gp.ldy = d; gp.ymode = wd::Y_PLAIN;
+      gp.epi = wd::EPI_STORE; gp.bias = nullptr; gp.out = qkv; gp.ldo = nqkv;
+      HIPCHK(c, wd::launch_gemv(gp, s), "qkv projection");
+      HIPCHK(c, wd::launch_qk_rope_append(qkv, B, hq, hkv, hd, pos, g.context, c->at<float>(L.qn),
+                                          c->at<float>(L.kn), g.norm_eps, g.rope_base, qscale, q,
+                                          c->self_k(l), c->self_v(l), g.cache_dtype, kv_bstride, s),
+             "qk norm/rope/append");
+    }
+    // self-attention over rows 0..pos of each row's own cache
+    ap.q = q; ap.q_ld = hq * hd; ap.K = c->self_k(l); ap.V = c->self_v(l);
+    ap.kvb_stride = kv_bstride; ap.rows_cap = g.context; ap.pos = pos; ap.n_rows_fixed = 0;
+    ap.q_per_kvb = 1; ap.split_rows = s_rows; ap.n_splits = s_splits; ap.out = o; ap.out_ld = hq * hd;
+    {
+      const bool on = prof_on(c, PK_SELF_ATTN, l);
+      prof_begin(c, on);
+      HIPCHK(c, wd::launch_attention(ap, s), "self attention");
+      prof_end(c, on);
+    }
+    HIPCHK(c, wd::launch_attention_combine(ap, s), "self attention combine");
+    // output projection + residual
+    gp.W = c->at(L.wo); gp.N = d; gp.K = hq * hd; gp.Y = o; gp.ldy = hq * hd; gp.ymode = wd::Y_PLAIN;
+    gp.epi = wd::EPI_RESID; gp.bias = whisper ? c->at<float>(L.bo) : nullptr; gp.out = x; gp.ldo = d;
+    HIPCHK(c, wd::launch_gemv(gp, s), "out projection");
+
+    if (whisper) {
+      // cross-attention: LN2, cross q, attend over all frames of the row's encoder set
+      HIPCHK(c, wd::launch_norm(x, y, c->at<float>(L.ln2g), c->at<float>(L.ln2b), B, d, g.norm_eps, s), "ln2");
+      gp.W = c->at(L.wcq); gp.N = d; gp.K = d; gp.Y = y; gp.ldy = d; gp.epi = wd::EPI_STORE;
+      gp.bias = c->at<float>(L.bcq); gp.out = q; gp.ldo = d; gp.scale = qscale;
+      HIPCHK(c, wd::launch_gemv(gp, s), "cross q projection");
+      gp.scale = 1.0f;
+      wd::AttnParams cp = ap;
+      cp.K = c->cross_k(l); cp.V = c->cross_v(l);
+      cp.kvb_stride = (int64_t)hq * g.max_frames * hd; cp.rows_cap = g.max_frames;
+      cp.pos = nullptr; cp.n_rows_fixed = c->frames; cp.q_per_kvb = qpk;
+      cp.split_rows = c_rows; cp.n_splits = c_splits;
+      {
+        const bool on = prof_on(c, PK_CROSS_ATTN, l);
+        prof_begin(c, on);
+        HIPCHK(c, wd::launch_attention(cp, s), "cross attention");
+        prof_end(c, on);
+      }
+      HIPCHK(c, wd::launch_attention_combine(cp, s), "cross attention combine");
+      gp.W = c->at(L.wco); gp.N = d; gp.K = d; gp.Y = o; gp.ldy = d; gp.epi = wd::EPI_RESID;
+      gp.bias = c->at<float>(L.bco); gp.out = x; gp.ldo = d;
+      HIPCHK(c, wd::launch_gemv(gp, s), "cross out projection");
+      // FFN
+      HIPCHK(c, wd::launch_norm(x, y, c->at<float>(L.ln3g), c->at<float>(L.ln3b), B, d, g.norm_eps, s), "ln3");
+      gp.W = c->at(L.w1); gp.N = ff; gp.K = d; gp.Y = y; gp.ldy = d; gp.epi = wd::EPI_GELU;
+      gp.bias = c->at<float>(L.b1); gp.out = h; gp.ldo = ff;
+      {
+        const bool on = prof_on(c, PK_FC1, l);
+        prof_begin(c, on);
+        HIPCHK(c, wd::launch_gemv(gp, s), "fc1");
+        prof_end(c, on);
+      }
+      gp.W = c->at(L.w2); gp.N = d; gp.K = ff; gp.Y = h; gp.ldy = ff; gp.epi = wd::EPI_RESID;
+      gp.bias = c->at<float>(L.b2); gp.out = x; gp.ldo = d;
+      HIPCHK(c, wd::launch_gemv(gp, s), "fc2");
+    } else {
+      HIPCHK(c, wd::launch_norm(x, y, c->at<float>(L.n2g), nullptr, B, d, g.norm_eps, s), "norm2");
+      gp.W = c->at(L.wgu); gp.N = 2 * ff; gp.K = d; gp.Y = y; gp.ldy = d; gp.epi = wd::EPI_STORE;
+      gp.bias = nullptr; gp.out = h; gp.ldo = 2 * ff;
+      {
+        const bool on = prof_on(c, PK_FC1, l);
+        prof_begin(c, on);
+        HIPCHK(c, wd::launch_gemv(gp, s), "gate|up projection");
+        prof_end(c, on);
+      }
+      gp.W = c->at(L.wdn); gp.N = d; gp.K = ff; gp.Y = h; gp.ldy = 2 * ff; gp.ymode = wd::Y_SWIGLU;
+      gp.epi = wd::EPI_RESID; gp.out = x; gp.ldo = d;
+      HIPCHK(c, wd::launch_gemv(gp, s), "down projection");
+    }
+  }
+  if (!head) return WD_OK;
+  // final norm, tied-embedding logits, argmax
+  HIPCHK(c, wd::launch_norm(x, y, c->at<float>(P.lnfg), whisper ? c->at<float>(P.lnfb) : nullptr, B, d,
+                            g.norm_eps, s), "final norm");
+  wd::GemvParams hp{};
+  hp.W = c->at(P.embed); hp.w_dtype = g.w_dtype; hp.N = g.vocab; hp.K = d; hp.Y = y; hp.ldy = d; hp.B = B;
+  hp.ymode = wd::Y_PLAIN; hp.epi = wd::EPI_LOGITS; hp.out = logits; hp.ldo = g.vocab; hp.scale = 1.0f;
+  hp.amax = c->at<unsigned long long>(P.amax); hp.ldp = g.max_batch; hp.err = err;
+  {
+    const bool on = prof_on(c, PK_LOGITS, -1);
+    prof_begin(c, on);
+    HIPCHK(c, wd::launch_gemv(hp, s), "logits");
+    prof_end(c, on);
+  }
+  HIPCHK(c, wd::launch_argmax_final(hp.amax, wd::gemv_blocks(g.vocab, B), g.max_batch, B, argmax, s), "argmax");
+  return WD_OK;
+}
+
+struct Need {
+  std::string name;
+  int64_t numel;
+  bool matrix;
+};
+
+std::vector<Need> required(const wd_config& c) {
+  std::vector<Need> n;
+  const int64_t d = c.d_model, ff = c.d_ff, hd = c.head_dim, hq = c.n_heads, hkv = c.n_kv_heads;
+  n.push_back({"embed", (int64_t)c.vocab * d, true});
+  if (c.arch == WD_ARCH_WHISPER) {
+    n.push_back({"pos", (int64_t)c.context * d, true});
+    n.push_back({"ln_f.g", d, false});
+    n.push_back({"ln_f.b", d, false});
+    for (int i = 0; i < c.n_layers; ++i) {
+      const std::string p = "dec." + std::to_string(i) + ".";
+      for (const char* ln : {"ln1", "ln2", "ln3"}) {
+        n.push_back({p + ln + ".g", d, false});
+        n.push_back({p + ln + ".b", d, false});
+      }
+      for (const char* a : {"self", "cross"}) {
+        for (const char* m : {"q", "k", "v", "o"}) n.push_back({p + a + "." + m + ".w", d * d, true});
+        for (const char* m : {"q", "v", "o"}) n.push_back({p + a + "." + m + ".b", d, false});
+      }
+      n.push_back({p + "fc1.w", ff * d, true});
+      n.push_back({p + "fc1.b", ff, false});
+      n.push_back({p + "fc2.w", d * ff, true});
+      n.push_back({p + "fc2.b", d, false});
+    }
+  } else {
+    n.push_back({"norm_f.g", d, false});
+    for (int i = 0; i < c.n_layers; ++i) {
+      const std::string p = "dec." + std::to_string(i) + ".";
+      n.push_back({p + "norm1.g", d, false});
+      n.push_back({p + "norm2.g", d, false});
+      n.push_back({p + "q_norm.g", hd, false});
+      n.push_back({p + "k_norm.g", hd, false});
+      n.push_back({p + "self.q.w", hq * hd * d, true});
+      n.push_back({p + "self.k.w", hkv * hd * d, true});
+      n.push_back({p + "self.v.w", hkv * hd * d, true});
+      n.push_back({p + "self.o.w", d * hq * hd, true});
+      n.push_back({p + "mlp.gate.w", ff * d, true});
+      n.push_back({p + "mlp.up.w", ff * d, true});
+      n.push_back({p + "mlp.down.w", d * ff, true});
+    }
+  }
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t wd_abi_version(void) { return WD_ABI_VERSION; }
+
+size_t wd_workspace_bytes(const wd_config* cfg) {
+  if (!cfg || !check_config(*cfg).empty()) return 0;
+  return make_plan(*cfg).total;
+}
+
+wd_status wd_load(const wd_config* cfg, const wd_tensor* weights, int32_t n_weights, void* workspace,
+                  size_t ws_bytes, void* stream, wd_ctx** out) {
+  try {
+    if (!cfg || !out) return fail(nullptr, WD_ERR_ARG, "wd_load: cfg and out must not be null");
+    *out = nullptr;
+    const std::string why = check_config(*cfg);
+    if (!why.empty()) return fail(nullptr, WD_ERR_ARG, "wd_load: " + why);
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255))
+      return fail(nullptr, WD_ERR_ARG, "wd_load: workspace must be a 256-byte aligned device pointer");
+    if (n_weights < 0 || (n_weights > 0 && !weights)) return fail(nullptr, WD_ERR_ARG, "wd_load: bad weight list");
+    const Plan plan = make_plan(*cfg);
+    if (ws_bytes < plan.total)
+      return fail(nullptr, WD_ERR_OOM, "wd_load: workspace of " + std::to_string(ws_bytes) + " bytes, need " +
+                                           std::to_string(plan.total));
+    // name -> tensor, with shape and dtype checks
+    std::map<std::string, const wd_tensor*> byname;
+    for (int i = 0; i < n_weights; ++i) {
+      const wd_tensor& t = weights[i];
+      if (!t.name) return fail(nullptr, WD_ERR_ARG, "wd_load: tensor with null name");
+      const std::string nm(t.name);
+      if (nm.size() >= 4 && nm.compare(nm.size() - 4, 4, ".k.b") == 0)
+        return fail(nullptr, WD_ERR_ARG, "wd_load: '" + nm + "': the key projections carry no bias");
+      if (byname.count(nm)) return fail(nullptr, WD_ERR_ARG, "wd_load: duplicate tensor '" + nm + "'");
+      byname[nm] = &t;
+    }
+    const auto need = required(*cfg);
+    if (byname.size() != need.size()) {
+      for (const auto& kv : byname) {
+        bool known = false;
+        for (const auto& n : need) known = known || n.name == kv.first;
+        if (!known) return fail(nullptr, WD_ERR_ARG, "wd_load: unknown tensor '" + kv.first + "'");
+      }
+    }
+    for (const auto& n : need) {
+      auto it = byname.find(n.name);
+      if (it == byname.end()) return fail(nullptr, WD_ERR_ARG, "wd_load: missing tensor '" + n.name + "'");
+      const wd_tensor& t = *it->second;
+      if (!t.data) return fail(nullptr, WD_ERR_ARG, "wd_load: '" + n.name + "' has a null data pointer");
+      if (t.numel != n.numel)
+        return fail(nullptr, WD_ERR_ARG, "wd_load: '" + n.name + "' has " + std::to_string(t.numel) +
+                                             " elements, expected " + std::to_string(n.numel));
+      if (!valid_dt(t.dtype)) return fail(nullptr, WD_ERR_ARG, "wd_load: '" + n.name + "' has an unknown dtype");
+      if (n.matrix && t.dtype != cfg->w_dtype)
+        return fail(nullptr, WD_ERR_ARG, "wd_load: matrix '" + n.name + "' must be in w_dtype");
+    }
+
+    wd_ctx* c = new (std::nothrow) wd_ctx();
+    if (!c) return fail(nullptr, WD_ERR_INTERNAL, "wd_load: out of host memory");
+    c->cfg = *cfg;
+    c->plan = plan;
+    c->stream = reinterpret_cast<hipStream_t>(stream);
+    c->ws = reinterpret_cast<char*>(workspace);
+    hipStream_t s = c->stream;
+    const int wdt = cfg->w_dtype;
+    auto T = [&](const std::string& nm) { return byname[nm]; };
+    auto cp = [&](const std::string& nm, size_t dst, int dst_dt, int64_t rows, int64_t cols, int64_t add) {
+      const wd_tensor* t = T(nm);
+      return wd::launch_copy_rows(t->data, t->dtype, c->ws + dst, dst_dt, rows, cols, 1, add, s);
+    };
+    auto vcopy = [&](const std::string& nm, size_t dst_byte, int64_t n) {
+      const wd_tensor* t = T(nm);
+      return wd::launch_copy_rows(t->data, t->dtype, c->ws + dst_byte, DT_F32, 1, n, 1, 0, s);
+    };
+    auto zero = [&](size_t dst_byte, int64_t nwords) {
+      return wd::launch_fill_u32(reinterpret_cast<uint32_t*>(c->ws + dst_byte), 0u, nwords, s);
+    };
+    const int64_t d = cfg->d_model, ff = cfg->d_ff, hd = cfg->head_dim, hq = cfg->n_heads, hkv = cfg->n_kv_heads;
+    hipError_t e = hipSuccess;
+    auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+    chk(cp("embed", plan.embed, wdt, cfg->vocab, d, 0));
+    if (cfg->arch == WD_ARCH_WHISPER) {
+      chk(cp("pos", plan.pos, wdt, cfg->context, d, 0));
+      chk(vcopy("ln_f.g", plan.lnfg, d));
+      chk(vcopy("ln_f.b", plan.lnfb, d));
+      for (int i = 0; i < cfg->n_layers && e == hipSuccess; ++i) {
+        const std::string p = "dec." + std::to_string(i) + ".";
+        const LayerOff& L = plan.L[i];
+        chk(cp(p + "self.q.w", L.wqkv, wdt, d, d, 0));
+        chk(cp(p + "self.k.w", L.wqkv, wdt, d, d, d));
+        chk(cp(p + "self.v.w", L.wqkv, wdt, d, d, 2 * d));
+        chk(cp(p + "self.o.w", L.wo, wdt, d, d, 0));
+        chk(cp(p + "cross.q.w", L.wcq, wdt, d, d, 0));
+        chk(cp(p + "cross.k.w", L.wckv, wdt, d, d, 0));
+        chk(cp(p + "cross.v.w", L.wckv, wdt, d, d, d));
+        chk(cp(p + "cross.o.w", L.wco, wdt, d, d, 0));
+        chk(cp(p + "fc1.w", L.w1, wdt, ff, d, 0));
+        chk(cp(p + "fc2.w", L.w2, wdt, d, ff, 0));
+        chk(vcopy(p + "self.q.b", L.bqkv, d));
+        chk(zero(L.bqkv + d * 4, d));                 // keys: no bias
+        chk(vcopy(p + "self.v.b", L.bqkv + 2 * d * 4, d));
+        chk(vcopy(p + "self.o.b", L.bo, d));
+        chk(vcopy(p + "cross.q.b", L.bcq, d));
+        chk(zero(L.bckv, d));                         // fused cross bias [0 | b_v]
+        chk(vcopy(p + "cross.v.b", L.bckv + d * 4, d));
+        chk(vcopy(p + "cross.o.b", L.bco, d));
+        chk(vcopy(p + "fc1.b", L.b1, ff));
+        chk(vcopy(p + "fc2.b", L.b2, d));
+        chk(vcopy(p + "ln1.g", L.ln1g, d)); chk(vcopy(p + "ln1.b", L.ln1b, d));
+        chk(vcopy(p + "ln2.g", L.ln2g, d)); chk(vcopy(p + "ln2.b", L.ln2b, d));
+        chk(vcopy(p + "ln3.g", L.ln3g, d)); chk(vcopy(p + "ln3.b", L.ln3b, d));
+      }
+    } else {
+      chk(vcopy("norm_f.g", plan.lnfg, d));
+      for (int i = 0; i < cfg->n_layers && e == hipSuccess; ++i) {
+        const std::string p = "dec." + std::to_string(i) + ".";
+        const LayerOff& L = plan.L[i];
+        chk(cp(p + "self.q.w", L.wqkv, wdt, hq * hd, d, 0));
+        chk(cp(p + "self.k.w", L.wqkv, wdt, hkv * hd, d, hq * hd));
+        chk(cp(p + "self.v.w", L.wqkv, wdt, hkv * hd, d, (hq + hkv) * hd));
+        chk(cp(p + "self.o.w", L.wo, wdt, d, hq * hd, 0));
+        chk(cp(p + "mlp.gate.w", L.wgu, wdt, ff, d, 0));
+        chk(cp(p + "mlp.up.w", L.wgu, wdt, ff, d, ff));
+        chk(cp(p + "mlp.down.w", L.wdn, wdt, d, ff, 0));
+        chk(vcopy(p + "norm1.g", L.n1g, d));
+        chk(vcopy(p + "norm2.g", L.n2g, d));
+        chk(vcopy(p + "q_norm.g", L.qn, hd));
+        chk(vcopy(p + "k_norm.g", L.kn, hd));
+      }
+    }
+    chk(zero(plan.err, 16));
+    if (e != hipSuccess) {
+      std::string m = std::string("wd_load: repack launch failed: ") + hipGetErrorString(e);
+      delete c;
+      return fail(nullptr, WD_ERR_HIP, m);
+    }
+    *out = c;
+    return WD_OK;
+  } catch (...) {
+    return fail(nullptr, WD_ERR_INTERNAL, "wd_load: internal error");
+  }
+}
+
+wd_status wd_cross_kv(wd_ctx* ctx, const void* enc, int32_t frames) {
+  if (!ctx) return WD_ERR_ARG;
+  try {
+    const wd_config& g = ctx->cfg;
+    if (g.arch != WD_ARCH_WHISPER) return fail(ctx, WD_ERR_STATE, "wd_cross_kv: no cross-attention in this arch");
+    if (!enc) return fail(ctx, WD_ERR_ARG, "wd_cross_kv: enc must not be null");
+    if (frames < 1 || frames > g.max_frames) return fail(ctx, WD_ERR_ARG, "wd_cross_kv: frames outside [1, max_frames]");
+    for (int l = 0; l < g.n_layers; ++l) {
+      const LayerOff& L = ctx->plan.L[l];
+      const bool on = prof_on(ctx, PK_XKV_GEMM, l);
+      prof_begin(ctx, on);
+      HIPCHK(ctx, wd::launch_cross_kv_gemm(enc, ctx->at(L.wckv), ctx->at<float>(L.bckv), g.w_dtype,
+                                           g.n_enc * frames, g.d_model, frames, g.max_frames, g.n_heads,
+                                           g.head_dim, ctx->cross_k(l), ctx->cross_v(l), g.cache_dtype,
+                                           ctx->stream), "cross K/V projection");
+      prof_end(ctx, on);
+    }
+    ctx->cross_ready = true;
+    ctx->frames = frames;
+    return WD_OK;
+  } catch (...) {
+    return fail(ctx, WD_ERR_INTERNAL, "wd_cross_kv: internal error");
+  }
+}
+
+static wd_status check_rows(wd_ctx* ctx, int32_t B, const char* who) {
+  const wd_config& g = ctx->cfg;
+  if (B < 1 || B > g.max_batch) return fail(ctx, WD_ERR_ARG, std::string(who) + ": B outside [1, max_batch]");
+  if (g.arch == WD_ARCH_WHISPER) {
+    if (!ctx->cross_ready) return fail(ctx, WD_ERR_STATE, std::string(who) + ": call wd_cross_kv first");
+    const int r = rows_per_set(g, B);
+    if (B % r) return fail(ctx, WD_ERR_ARG, std::string(who) + ": B must be a multiple of max_batch / n_enc");
+  }
+  return WD_OK;
+}
+
+wd_status wd_step(wd_ctx* ctx, const int32_t* tokens, const int32_t* positions, int32_t B, float* logits,
+                  int32_t* argmax) {
+  if (!ctx) return WD_ERR_ARG;
+  try {
+    if (!tokens || !positions || !argmax) return fail(ctx, WD_ERR_ARG, "wd_step: tokens, positions, argmax must not be null");
+    const wd_status st = check_rows(ctx, B, "wd_step");
+    if (st != WD_OK) return st;
+    return run_step(ctx, tokens, 1, positions, nullptr, 0, B, logits, argmax, true);
+  } catch (...) {
+    return fail(ctx, WD_ERR_INTERNAL, "wd_step: internal error");
+  }
+}
+
+wd_status wd_prefill(wd_ctx* ctx, const int32_t* tokens, int32_t B, int32_t T, const void* embeds, int32_t A,
+                     int32_t offset, float* logits, int32_t* argmax) {
+  if (!ctx) return WD_ERR_ARG;
+  try {
+    const wd_config& g = ctx->cfg;
+    if (!tokens || !argmax) return fail(ctx, WD_ERR_ARG, "wd_prefill: tokens and argmax must not be null");
+    if (T < 1 || T > g.context) return fail(ctx, WD_ERR_ARG, "wd_prefill: T outside [1, context]");
+    if (A < 0 || offset < 0 || offset + A > T || (A > 0 && !embeds))
+      return fail(ctx, WD_ERR_ARG, "wd_prefill: audio rows must lie inside the prompt");
+    const wd_status st = check_rows(ctx, B, "wd_prefill");
+    if (st != WD_OK) return st;
+    int32_t* ptmp = ctx->at<int32_t>(ctx->plan.pos_tmp);
+    const size_t eb = dtype_bytes(g.w_dtype);
+    for (int t = 0; t < T; ++t) {
+      HIPCHK(ctx, wd::launch_fill_i32(ptmp, t, B, ctx->stream), "prefill positions");
+      const void* ov = nullptr;
+      if (A > 0 && t >= offset && t < offset + A)
+        ov = reinterpret_cast<const char*>(embeds) + (size_t)(t - offset) * g.d_model * eb;
+      const wd_status r = run_step(ctx, tokens + t, T, ptmp, ov, (int64_t)A * g.d_model, B, logits, argmax, t == T - 1);
+      if (r != WD_OK) return r;
+    }
+    return WD_OK;
+  } catch (...) {
+    return fail(ctx, WD_ERR_INTERNAL, "wd_prefill: internal error");
+  }
+}
+
+wd_status wd_reorder(wd_ctx* ctx, const int32_t* beam_idx, int32_t B, int32_t n_rows) {
+  if (!ctx) return WD_ERR_ARG;
+  try {
+    const wd_config& g = ctx->cfg;
+    if (ctx->plan.n_bufs < 2) return fail(ctx, WD_ERR_STATE, "wd_reorder: needs n_enc == 1 and max_batch > 1");
+    if (!beam_idx) return fail(ctx, WD_ERR_ARG, "wd_reorder: beam_idx must not be null");
+    if (B < 1 || B > g.max_batch) return fail(ctx, WD_ERR_ARG, "wd_reorder: B outside [1, max_batch]");
+    if (n_rows < 0 || n_rows > g.context) return fail(ctx, WD_ERR_ARG, "wd_reorder: n_rows outside [0, context]");
+    wd::BeamIdx idx{};
+    bool ident = true;
+    for (int b = 0; b < B; ++b) {
+      if (beam_idx[b] < 0 || beam_idx[b] >= B) return fail(ctx, WD_ERR_ARG, "wd_reorder: beam index outside [0, B)");
+      idx.v[b] = beam_idx[b];
+      ident = ident && beam_idx[b] == b;
+    }
+    if (ident || n_rows == 0) return WD_OK;
+    const int nxt = 1 - ctx->cur;
+    HIPCHK(ctx, wd::launch_reorder(ctx->ws + ctx->plan.self[ctx->cur], ctx->ws + ctx->plan.self[nxt],
+                                   dtype_bytes(g.cache_dtype), idx, B, g.max_batch, g.n_kv_heads, g.context,
+                                   g.head_dim, n_rows, 2 * g.n_layers, ctx->stream), "beam reorder");
+    ctx->cur = nxt;
+    return WD_OK;
+  } catch (...) {
+    return fail(ctx, WD_ERR_INTERNAL, "wd_reorder: internal error");
+  }
+}
+
+wd_status wd_check(wd_ctx* ctx) {
+  if (!ctx) return WD_ERR_ARG;
+  HIPCHK(ctx, hipStreamSynchronize(ctx->stream), "wd_check: stream sync");
+  unsigned flag[4] = {0, 0, 0, 0};
+  HIPCHK(ctx, hipMemcpy(flag, ctx->ws + ctx->plan.err, sizeof(flag), hipMemcpyDeviceToHost), "wd_check: read flag");
+  if (flag[0]) {
+    HIPCHK(ctx, wd::launch_fill_u32(reinterpret_cast<uint32_t*>(ctx->ws + ctx->plan.err), 0u, 4, ctx->stream), "wd_check: clear");
+    HIPCHK(ctx, hipStreamSynchronize(ctx->stream), "wd_check: stream sync");
+    std::string m = "device range flag:";
+    if (flag[0] & wd::ERR_TOKEN) m += " token id outside [0, vocab)";
+    if (flag[0] & wd::ERR_POS) m += " position outside [0, context)";
+    if (flag[0] & wd::ERR_NAN) m += " NaN logit";
+    return fail(ctx, WD_ERR_RANGE, m);
+  }
+  return WD_OK;
+}
+
+const char* wd_last_error(const wd_ctx* ctx) {
+  return ctx ? ctx->err.c_str() : g_load_error.c_str();
+}
+
+void wd_free(wd_ctx* ctx) {
+  if (!ctx) return;
+  for (auto& pr : ctx->prof) {
+    (void)hipEventDestroy(pr.a);
+    (void)hipEventDestroy(pr.b);
+  }
+  delete ctx;
+}
+
+wd_status wd_profile(wd_ctx* ctx, int32_t kernel, int32_t layer) {
+  if (!ctx) return WD_ERR_ARG;
+  if (kernel < -1 || kernel > 4) return fail(ctx, WD_ERR_ARG, "wd_profile: unknown kernel class");
+  if (ctx->prof.empty() && kernel >= 0) {
+    ctx->prof.resize(4096);
+    for (auto& pr : ctx->prof) {
+      HIPCHK(ctx, hipEventCreate(&pr.a), "wd_profile: event");
+      HIPCHK(ctx, hipEventCreate(&pr.b), "wd_profile: event");
+    }
+  }
+  ctx->prof_kernel = kernel;
+  ctx->prof_layer = layer;
+  ctx->prof_used = 0;
+  return WD_OK;
+}
+
+wd_status wd_profile_read(wd_ctx* ctx, double* total_ms, int64_t* launches) {
+  if (!ctx || !total_ms || !launches) return WD_ERR_ARG;
+  HIPCHK(ctx, hipStreamSynchronize(ctx->stream), "wd_profile_read: sync");
+  double t = 0.0;
+  for (size_t i = 0; i < ctx->prof_used; ++i) {
+    float ms = 0.f;
+    HIPCHK(ctx, hipEventElapsedTime(&ms, ctx->prof[i].a, ctx->prof[i].b), "wd_profile_read: elapsed");
+    t += ms;
+  }
+  *total_ms = t;
+  *launches = (int64_t)ctx->prof_used;
+  ctx->prof_used = 0;
+  return WD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Host-side launchers of the decoder-step kernels.  Every launcher checks the
+// shapes its kernel assumes before launching and returns hipErrorInvalidValue
+// instead of launching when they do not hold.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wd {
+
+enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };  // same values as wd_dtype
+
+// sticky device error bits (reported by wd_check)
+enum : unsigned { ERR_TOKEN = 1u, ERR_POS = 2u, ERR_NAN = 4u };
+
+// ---- repack / utility -------------------------------------------------------------------
+// dst[(r*row_mul + row_add) * cols + c] = convert(src[r*cols + c]) for r < rows.
+hipError_t launch_copy_rows(const void* src, int src_dtype, void* dst, int dst_dtype,
+                            int64_t rows, int64_t cols, int64_t row_mul, int64_t row_add,
+                            hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+
+// ---- embedding ---------------------------------------------------------------------------
+// x[b] = ov ? ov[b*ov_stride ..] : E[tok[b*tok_stride]] + (P ? P[pos[b]] : 0); validates ranges.
+hipError_t launch_embed(float* x, const void* E, const void* P, int w_dtype, const int32_t* tok,
+                        int tok_stride, const int32_t* pos, const void* ov, int64_t ov_stride,
+                        int B, int d, int V, int ctx, unsigned* err, hipStream_t s);
+
+// ---- row norm: LayerNorm (b != nullptr) or RMSNorm (b == nullptr) ----------------------
+hipError_t launch_norm(const float* x, float* y, const float* g, const float* b, int B, int d,
+                       float eps, hipStream_t s);
+
+// ---- skinny GEMM (GEMV over B rows) with fused epilogues -----------------------------------
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_GELU = 2, EPI_QKV = 3, EPI_LOGITS = 4 };
+enum YMode : int { Y_PLAIN = 0, Y_SWIGLU = 1 };
+
+struct GemvParams {
+  const void* W; int w_dtype; int N; int K;   // W [N, K] row-major
+  const float* Y; int ldy; int B; int ymode;  // Y [B, ldy]; SWIGLU reads silu(Y[:,k]) * Y[:,K+k]
+  int epi;
+  const float* bias;                          // [N] or null
+  float* out; int ldo; float scale;           // STORE/GELU/RESID target; STORE multiplies by scale
+  // EPI_QKV (Whisper): rows [0,d) -> q (out, times scale), [d,2d) -> K cache, [2d,3d) -> V cache
+  int d; int H; int hd; int ctx; const int32_t* pos;
+  void* Kc; void* Vc; int cache_dtype; int64_t kv_bstride;
+  // EPI_LOGITS: out = logits [B, ldo] or null; per-block argmax keys amax[blockIdx.x * ldp + b]
+  unsigned long long* amax; int ldp;
+  unsigned* err;
+};
+// Returns the number of blocks along N (the number of argmax partials per row).
+int gemv_blocks(int N, int B);
+hipError_t launch_gemv(const GemvParams& p, hipStream_t s);
+hipError_t launch_argmax_final(const unsigned long long* amax, int nparts, int ldp, int B,
+                               int32_t* out, hipStream_t s);
+
+// ---- attention over a K/V cache --------------------------------------------------------------
+struct AttnParams {
+  const float* q; int q_ld;                   // q [B, q_ld]; head h at h*hd, pre-scaled
+  const void* K; const void* V; int cache_dtype;
+  int64_t kvb_stride; int rows_cap;           // cache [n_kvb][Hkv][rows_cap][hd]
+  const int32_t* pos; int n_rows_fixed;       // pos: rows 0..pos[b]; else n_rows_fixed rows
+  int B; int Hq; int Hkv; int hd; int q_per_kvb;
+  int split_rows; int n_splits;
+  float* out; int out_ld;                     // [B, out_ld] (head h at h*hd)
+  float* part;                                // [B*Hq][n_splits][hd+2] when n_splits > 1
+};
+// main kernel (writes o directly when n_splits == 1, else partials) ...
+hipError_t launch_attention(const AttnParams& p, hipStream_t s);
+// ... and the split combine (no-op when n_splits == 1)
+hipError_t launch_attention_combine(const AttnParams& p, hipStream_t s);
+
+// ---- Qwen3: per-head q/k RMSNorm + NeoX RoPE, K/V append -------------------------------------
+hipError_t launch_qk_rope_append(const float* qkv, int B, int Hq, int Hkv, int hd,
+                                 const int32_t* pos, int ctx, const float* qn, const float* kn,
+                                 float eps, float base, float qscale, float* q_out, void* Kc,
+                                 void* Vc, int cache_dtype, int64_t kv_bstride, hipStream_t s);
+
+// ---- beam reorder: cache-row gather -----------------------------------------------------------
+struct BeamIdx { int32_t v[64]; };
+hipError_t launch_reorder(const void* src, void* dst, int elt_bytes, const BeamIdx& idx, int B,
+                          int Bmax, int H, int ctx, int hd, int n_rows, int n_blocks,
+                          hipStream_t s);
+
+// ---- cross K/V projection (dense GEMM) with cache scatter ------------------------------------
+// C[m, n] = sum_k X[m,k] W[n,k] (+ bias[n]); m = e*frames + f; n < d -> K cache, else V cache;
+// caches [n_enc][H][max_frames][hd] in cache_dtype.
+hipError_t launch_cross_kv_gemm(const void* X, const void* W, const float* bias, int w_dtype,
+                                int M, int d, int frames, int max_frames, int H, int hd,
+                                void* Kc, void* Vc, int cache_dtype, hipStream_t s);
+
+}  // namespace wd

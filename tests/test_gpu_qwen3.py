@@ -1,0 +1,60 @@
+"""GPU parity of the Qwen3-ASR decoder step and prompt prefill (audio rows
+spliced into the prompt) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as WL
+from oracle import qwen3 as OQ
+
+from .gpu_helpers import GpuRun, compare_logits, need_gpu, say, to_dev, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+def _qwen_parity(w, T, steps, streams):
+    """Prefill T rows (audio at rows audio_offset.. of the workload, clipped to T)
+    on all rows, then `steps` teacher-forced decode steps; the sampled rows are
+    compared at the prefill's last position and at every decode step."""
+    need_gpu()
+    say(f"[qwen3] {w.describe()} T={T} steps={steps} rows={streams}")
+    W = WL.make_weights(w)
+    ids, audio = WL.make_qwen_prefill(w)
+    off = w.audio_offset
+    A = max(0, min(w.audio_rows, T - off))
+    ids = ids[:, :T]
+    audio = audio[:, :A]
+    dec_ids = WL.random_ids(w, steps)
+    G = GpuRun(w, W)
+    tok = torch.from_numpy(np.ascontiguousarray(ids)).to(device="cuda", dtype=torch.int32)
+    emb = to_dev(audio, torch_dtype(w.w_dtype)) if A > 0 else None
+    logits = torch.empty(w.batch, w.vocab, dtype=torch.float32, device="cuda")
+    G.dec.prefill(tok, emb, off, logits)
+    got = {b: [logits[b].cpu().numpy()] for b in streams}
+    for s in range(steps):
+        lg, _ = G.step(dec_ids[:, s], T + s, rows=list(streams))
+        for i, b in enumerate(streams):
+            got[b].append(lg[i])
+    assert G.check() == 0
+    G.close()
+    del G
+    torch.cuda.empty_cache()
+    D = OQ.dims_of(w)
+    worst = 0.0
+    for b in streams:
+        seq = np.concatenate([ids[b], dec_ids[b]])
+        ref = OQ.decode_full(D, W, seq, round_cache=True, embeds=audio[b] if A else None, offset=off)
+        e, _ = compare_logits(w, np.stack(got[b]), ref[T - 1:], f"row {b}")
+        worst = max(worst, e)
+    say(f"  worst err {worst:.3e}")
+
+
+def test_qwen3_reduced_layers_full_width():
+    w = WL.reduced(WL.by_name("qwen3asr_bf16_b8"), layers=3)
+    _qwen_parity(w, T=40, steps=6, streams=(0, 7))
+
+
+def test_qwen3_small_dims_context_end():
+    w = WL.reduced(WL.by_name("qwen3asr_bf16_b8"), layers=2, d=256, heads=4, kv_heads=2,
+                   d_ff=512, vocab=7001, context=48, batch=3, audio_offset=3, audio_rows=9)
+    _qwen_parity(w, T=20, steps=28, streams=(0, 1, 2))   # last step at position 47 = context - 1
