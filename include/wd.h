@@ -187,6 +187,14 @@ void wd_free(wd_ctx* ctx);
 wd_status wd_profile(wd_ctx* ctx, int32_t kernel, int32_t layer);
 wd_status wd_profile_read(wd_ctx* ctx, double* total_ms, int64_t* launches);
 
+/* --- test hook ------------------------------------------------------------
+ * Device address of one cache block of the current buffer, for checking the
+ * caches element by element (in the spirit of named intermediate dumps,
+ * transcribe.cpp qwen3_asr/decoder.h `DecoderDumps`).  which: 0 self K,
+ * 1 self V ([max_batch][n_kv_heads][context][head_dim]), 2 cross K, 3 cross V
+ * ([n_enc][n_heads][max_frames][head_dim]), in cache_dtype.  Errors: ARG.  */
+wd_status wd_debug_cache(wd_ctx* ctx, int32_t which, int32_t layer, void** dev_ptr);
+
 #ifdef __cplusplus
 }
 #endif

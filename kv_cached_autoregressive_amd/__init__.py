@@ -20,6 +20,7 @@ __all__ = [
     "WdError", "WdConfig", "WdTensor", "lib", "lib_path", "declared_functions",
     "wd_abi_version", "wd_workspace_bytes", "wd_load", "wd_cross_kv", "wd_step", "wd_reorder",
     "wd_prefill", "wd_check", "wd_last_error", "wd_free", "wd_profile", "wd_profile_read",
+    "wd_debug_cache",
     "config_from", "Decoder", "DTYPES", "STATUS",
 ]
 
@@ -82,6 +83,7 @@ def lib():
             "wd_free": (None, [vp]),
             "wd_profile": (i32, [vp, i32, i32]),
             "wd_profile_read": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
+            "wd_debug_cache": (i32, [vp, i32, i32, ctypes.POINTER(vp)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -167,6 +169,12 @@ def wd_profile_read(ctx):
     n = ctypes.c_int64()
     _check(lib().wd_profile_read(ctx, ctypes.byref(t), ctypes.byref(n)), ctx)
     return t.value, n.value
+
+
+def wd_debug_cache(ctx, which: int, layer: int) -> int:
+    p = ctypes.c_void_p()
+    _check(lib().wd_debug_cache(ctx, which, layer, ctypes.byref(p)), ctx)
+    return p.value
 
 
 # ---- convenience: config and a torch-backed holder -------------------------------------------
@@ -260,6 +268,23 @@ class Decoder:
 
     def check(self) -> int:
         return wd_check(self.ctx)
+
+    def cache(self, which: int, layer: int):
+        """A torch view of one cache block (test hook): which 0/1 self K/V
+        [max_batch, Hkv, context, hd], 2/3 cross K/V [n_enc, H, max_frames, hd]."""
+        import torch
+        w = self.w
+        ptr = wd_debug_cache(self.ctx, which, layer)
+        shape = ((w.batch, w.kv_heads, w.context, w.head_dim) if which < 2
+                 else (w.n_enc, w.heads, w.frames, w.head_dim))
+        dt = _torch_dtype(w.cache_dtype)
+        n = 1
+        for s_ in shape:
+            n *= s_
+        base = self.workspace.view(torch.uint8)
+        off = ptr - base.data_ptr()
+        esz = torch.tensor([], dtype=dt).element_size()
+        return base[off:off + n * esz].view(dt).view(*shape)
 
     def last_error(self) -> str:
         return wd_last_error(self.ctx)

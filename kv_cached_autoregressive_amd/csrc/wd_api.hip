@@ -719,4 +719,14 @@ wd_status wd_profile_read(wd_ctx* ctx, double* total_ms, int64_t* launches) {
   return WD_OK;
 }
 
+wd_status wd_debug_cache(wd_ctx* ctx, int32_t which, int32_t layer, void** dev_ptr) {
+  if (!ctx) return WD_ERR_ARG;
+  if (!dev_ptr || layer < 0 || layer >= ctx->cfg.n_layers || which < 0 || which > 3)
+    return fail(ctx, WD_ERR_ARG, "wd_debug_cache: bad argument");
+  if (which >= 2 && ctx->cfg.arch != WD_ARCH_WHISPER) return fail(ctx, WD_ERR_ARG, "wd_debug_cache: no cross cache");
+  *dev_ptr = which == 0 ? ctx->self_k(layer) : which == 1 ? ctx->self_v(layer)
+           : which == 2 ? ctx->cross_k(layer) : ctx->cross_v(layer);
+  return WD_OK;
+}
+
 }  // extern "C"

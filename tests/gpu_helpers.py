@@ -81,8 +81,10 @@ class GpuRun:
         self.amax = torch.empty(B, dtype=torch.int32, device="cuda")
 
     def cross(self, enc, frames=None):
-        e = to_dev(enc, torch_dtype(self.w.w_dtype))
-        self.dec.cross_kv(e, frames)
+        """enc [n_enc, >= frames, d]; the library takes [n_enc, frames, d] contiguous."""
+        F = enc.shape[1] if frames is None else frames
+        e = to_dev(np.ascontiguousarray(enc[:, :F]), torch_dtype(self.w.w_dtype))
+        self.dec.cross_kv(e, F)
         torch.cuda.synchronize()
 
     def step(self, tokens, pos, rows=None, B=None):

@@ -1,0 +1,86 @@
+"""Element-wise parity of the caches the GPU writes: the cross K/V from the
+once-per-window projection (MFMA GEMM for f16/bf16, VALU for fp32) and the self
+K/V rows appended by each step, against the oracle's rounded caches.
+
+A cache element is a rounding of a float sum; the device rounds its fp32 sum,
+the oracle its fp64 sum, so the two may land on different sides of a rounding
+boundary when the sum is within fp32 error of it.  The bar: every element equal,
+except a small fraction that differ by at most one unit in the last place of
+the cache dtype (fp32 caches: within a few fp32 ulps of the row scale)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as WL
+from oracle import whisper as OW
+
+from .gpu_helpers import GpuRun, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _ulp(r, dtype):
+    a = np.abs(r)
+    a = np.where(a == 0, 1e-30, a)
+    e = np.floor(np.log2(a))
+    if dtype == "bf16":
+        return 2.0 ** (np.maximum(e, -126) - 7)
+    if dtype == "f16":
+        return 2.0 ** (np.maximum(e, -14) - 10)
+    return 2.0 ** (e - 23)
+
+
+def _cmp(g, r, dtype, what, max_frac):
+    g = np.asarray(g, np.float64)
+    diff = np.abs(g - r)
+    if dtype == "f32":
+        scale = np.abs(r).max()
+        bad = diff > 1e-5 * scale
+        assert not bad.any(), f"{what}: {bad.sum()} elements off by > 1e-5 of the block scale"
+        return 0.0
+    mism = diff > 0
+    frac = mism.mean()
+    # one ulp of the cache dtype, plus the fp32 accumulation error of the sum (absolute,
+    # a few fp32 ulps of the block scale) which dominates for values near zero
+    allow = _ulp(r, dtype) * 1.0001 + 4e-6 * np.abs(r).max()
+    over = diff > allow
+    if over.any():
+        i = np.argmax(diff - allow)
+        raise AssertionError(f"{what}: {over.sum()} differences above one ulp; worst gpu {g.flat[i]:.6e} "
+                             f"oracle {r.flat[i]:.6e} diff {diff.flat[i]:.3e} allowed {allow.flat[i]:.3e}")
+    assert frac <= max_frac, f"{what}: {frac:.2e} of elements differ (by one ulp)"
+    return frac
+
+
+@pytest.mark.parametrize("w_dtype,cache_dtype", [("bf16", "bf16"), ("f16", "f16"), ("f32", "f32"),
+                                                 ("bf16", "f16"), ("f32", "bf16")])
+def test_cross_and_self_caches_match_oracle(w_dtype, cache_dtype):
+    need_gpu()
+    w = WL.reduced(WL.by_name("whisper_large_bf16_b64"), layers=2, batch=3, n_enc=3, d=384, heads=6,
+                   kv_heads=6, d_ff=768, vocab=3001, w_dtype=w_dtype, cache_dtype=cache_dtype,
+                   frames=333)
+    say(f"[caches] {w.describe()}")
+    W = WL.make_weights(w)
+    enc = WL.make_encoder_states(w)
+    O = OW.WhisperOracle(OW.dims_of(w), W)
+    O.cross_kv(enc)
+    O.reset(w.batch, enc_of=range(w.batch))
+    G = GpuRun(w, W)
+    G.cross(enc)
+    worst = 0.0
+    for l in range(w.layers):
+        for which, ref in ((2, O.Kc[l]), (3, O.Vc[l])):
+            g = G.dec.cache(which, l).float().cpu().numpy()[:, :, :w.frames]
+            r = ref.reshape(w.n_enc, w.frames, w.heads, w.head_dim).transpose(0, 2, 1, 3)
+            worst = max(worst, _cmp(g, r, cache_dtype, f"cross {'KV'[which - 2]} layer {l}", 2e-3))
+    ids = WL.random_ids(w, 5)
+    for p in range(5):
+        O.step(ids[:, p], np.full(w.batch, p))
+        G.step(ids[:, p], p)
+        # layer 0 sees identical inputs up to fp32 rounding: rows must match
+        for which, arr in ((0, O.Ks[0]), (1, O.Vs[0])):
+            g = G.dec.cache(which, 0).float().cpu().numpy()[:, :, :p + 1]
+            r = arr[:, :p + 1].reshape(w.batch, p + 1, w.heads, w.head_dim).transpose(0, 2, 1, 3)
+            worst = max(worst, _cmp(g, r, cache_dtype, f"self {'KV'[which]} pos {p}", 2e-2))
+    G.close()
+    say(f"  largest one-ulp fraction {worst:.2e}")

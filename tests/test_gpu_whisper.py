@@ -65,7 +65,7 @@ def test_f16_batch_rows_below_max():
 
 def test_bf16_small_dims_frames_1499():
     w = WL.reduced(WL.by_name("whisper_large_bf16_b64"), layers=2, batch=4, n_enc=4, d=256,
-                   heads=4, d_ff=1024, vocab=5003)
+                   heads=4, kv_heads=4, d_ff=1024, vocab=5003)
     _greedy_parity(w, steps=8, frames=1499)
 
 

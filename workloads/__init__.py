@@ -238,8 +238,9 @@ def make_encoder_states(w: Workload, streams: Optional[List[int]] = None) -> np.
 
 
 def make_prompt(w: Workload) -> np.ndarray:
-    """Whisper prompt ids [batch, 4] (the same 4 ids in every row)."""
-    return np.tile(np.array(WHISPER_PROMPT, dtype=np.int32), (w.batch, 1))
+    """Whisper prompt ids [batch, 4] (the same 4 ids in every row); reduced test
+    vocabularies take the ids modulo their size."""
+    return np.tile(np.array(WHISPER_PROMPT, dtype=np.int32) % w.vocab, (w.batch, 1)).astype(np.int32)
 
 
 def make_qwen_prefill(w: Workload, streams: Optional[List[int]] = None):
