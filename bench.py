@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Decoder-step throughput on one MI355X.
+
+One bench step is one whole audio window of the workload: the cross K/V
+projection of every layer (once per window), then every decode position of the
+window, each a wd_step over the B rows, greedy on the device (the argmax of a
+step is the next step's token buffer; the 4-token prompt is fed first), with no
+host synchronisation inside the window.  Inputs (weights, encoder states,
+prompts) are resident in HBM before the timed region.
+
+Printed: one JSON line.  value = B * positions * K / (time of K windows),
+tokens/s including the cross K/V projection; decode-only tokens/s, the
+algorithmic HBM bytes per window (weights once per step + self-cache rows
+0..pos + cross cache once per encoder set) and their rate against the 8 TB/s
+peak are extra fields.  `roofline` reports the dominant kernel (the
+cross-attention) from HIP events recorded around its launches in one layer
+during the timed region; `cpu_baseline` times the CPU oracle on a bounded sample
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as WL  # noqa: E402
+
+HBM_PEAK = 8.0e12
+DEFAULT = "whisper_large_bf16_b64"
+DT_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+ATTN_SRC = os.path.join(ROOT, "kv_cached_autoregressive_amd", "csrc", "k_attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cross_attention_traffic.json")
+
+
+def whisper_bytes_per_step(w, pos: int) -> int:
+    """Algorithmic HBM bytes of one decode step at position `pos`: every weight
+    once (projections, norms, biases, the tied head), the B embedding and
+    position rows, self-cache rows 0..pos of every row and layer, the cross
+    cache once per encoder set."""
+    d, ff, L = w.d, w.d_ff, w.layers
+    wb, cb = DT_BYTES[w.w_dtype], DT_BYTES[w.cache_dtype]
+    per_layer = (6 * d * d + 2 * d * ff + 12 * d + ff) * wb
+    glob = w.vocab * d * wb + 2 * d * wb + 2 * w.batch * d * wb
+    self_c = w.batch * L * (pos + 1) * 2 * d * cb
+    cross = w.n_enc * L * w.frames * 2 * d * cb
+    return L * per_layer + glob + self_c + cross
+
+
+def cross_attn_bytes_per_launch(w) -> int:
+    """Algorithmic bytes of one cross-attention launch (one layer): the K and V
+    blocks of every encoder set, read once."""
+    return w.n_enc * w.heads * w.frames * w.head_dim * 2 * DT_BYTES[w.cache_dtype]
+
+
+def traffic_per_launch():
+    """HBM bytes per cross-attention launch from the committed rocprofv3 counter
+    summary, or None when absent or taken on a different kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+        sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        if t.get("kernel_source_sha256") != sha:
+            return None
+        return int(t["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle as it is, on the host cores: one stream of the workload, its
+    cross K/V and as many decode steps as fit the time budget."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import whisper as OW
+    W = WL.make_weights(w)
+    enc = WL.make_encoder_states(w, streams=[0])
+    O = OW.WhisperOracle(OW.dims_of(w), W)
+    del W
+    t0 = time.perf_counter()
+    O.cross_kv(enc)
+    t_cross = time.perf_counter() - t0
+    O.reset(1)
+    prompt = WL.make_prompt(w)[:1]
+    tok = prompt[:, 0]
+    n, t_steps = 0, 0.0
+    while n < w.steps and (n < 2 or t_steps < budget_s):
+        t0 = time.perf_counter()
+        lg = O.step(tok, [n])
+        t_steps += time.perf_counter() - t0
+        tok = prompt[:, n + 1] if n + 1 < prompt.shape[1] else np.argmax(lg, -1)
+        n += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": n / t_steps, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 of {w.batch} streams, positions 0..{n - 1} of {w.steps} (float64 numpy); "
+                      f"the stream's cross K/V took {t_cross:.2f} s on top, not counted"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3, help="timed windows")
+    ap.add_argument("--warmup", type=int, default=1, help="untimed windows")
+    ap.add_argument("--config", default=DEFAULT)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle decode steps")
+    ap.add_argument("--profile-layer", type=int, default=0, help="layer whose cross-attention launches are timed")
+    ap.add_argument("--positions", type=int, default=0,
+                    help="profiling aid: decode only the first N positions of each window")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU: the decoder step is measured on a single MI355X and no "
+              "multi-GPU path is built (rows would shard by stream across GPUs).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kv_cached_autoregressive_amd as K
+
+    w = WL.by_name(args.config)
+    if args.positions:
+        w = WL.reduced(w, steps=min(args.positions, w.steps))
+    if w.arch != "whisper" or w.mode != "greedy":
+        print(f"bench.py times greedy Whisper-style windows; {w.name} is not one", file=sys.stderr)
+        sys.exit(2)
+    K.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    W = WL.make_weights(w)
+    enc_np = WL.make_encoder_states(w)
+    dec = K.Decoder(w, W)
+    del W
+    wdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.w_dtype]
+    enc = torch.from_numpy(enc_np).to(dev, wdt)
+    del enc_np
+    B, S = w.batch, w.steps
+    prompt = torch.from_numpy(WL.make_prompt(w).T.copy()).to(dev)          # [4, B]
+    pos_all = torch.arange(S, dtype=torch.int32, device=dev)[:, None].repeat(1, B).contiguous()
+    amax = torch.zeros(B, dtype=torch.int32, device=dev)
+    stream = dec.stream
+    ctx = dec.ctx
+
+    def window(ev=None):
+        K.wd_cross_kv(ctx, enc.data_ptr(), w.frames)
+        if ev is not None:
+            ev.record(stream)
+        for p in range(S):
+            tok = prompt[p] if p < prompt.shape[0] else amax
+            K.wd_step(ctx, tok.data_ptr(), pos_all[p].data_ptr(), B, 0, amax.data_ptr())
+
+    for _ in range(args.warmup):
+        window()
+    torch.cuda.synchronize()
+    if dec.check() != 0:
+        raise RuntimeError(dec.last_error())
+
+    K.wd_profile(ctx, K.K_CROSS_ATTN, args.profile_layer)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        window(mids[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    xkv_ms = sum(starts[i].elapsed_time(mids[i]) for i in range(args.steps)) / args.steps
+    attn_ms, attn_n = K.wd_profile_read(ctx)
+    K.wd_profile(ctx, -1, -1)
+    if dec.check() != 0:
+        raise RuntimeError(dec.last_error())
+
+    ms_window = total_ms / args.steps
+    dec_ms = ms_window - xkv_ms
+    tokens = B * S
+    bytes_window = sum(whisper_bytes_per_step(w, p) for p in range(S))
+    attn_bytes = cross_attn_bytes_per_launch(w)
+    attn_avg_s = attn_ms / 1e3 / max(attn_n, 1)
+    achieved = attn_bytes / attn_avg_s
+    xkv_flops = 2.0 * w.n_enc * w.frames * w.d * 2 * w.d * w.layers
+    traffic = traffic_per_launch()
+    out = {
+        "metric": "decoder tokens/sec at batch B; achieved HBM GB/s as % of MI355X peak",
+        "value": tokens / (ms_window / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_window,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.w_dtype,
+        "data": "synthetic (seeded random-init weights N(0,0.02), encoder states N(0,1))",
+        "config": {"workload": w.name, "batch": B, "positions": S, "frames": w.frames,
+                   "layers": w.layers, "d": w.d, "heads": w.heads, "d_ff": w.d_ff,
+                   "vocab": w.vocab, "w_dtype": w.w_dtype, "cache_dtype": w.cache_dtype,
+                   "step": "one window: cross K/V projection + all positions, greedy on device"},
+        "decode_tokens_per_s": tokens / (dec_ms / 1e3),
+        "decode_ms_per_window": dec_ms,
+        "hbm_bytes_per_window": bytes_window,
+        "hbm_gbps_decode": bytes_window / (dec_ms / 1e3) / 1e9,
+        "hbm_frac_decode": bytes_window / (dec_ms / 1e3) / HBM_PEAK,
+        "cross_kv_ms": xkv_ms,
+        "cross_kv_tflops": xkv_flops / (xkv_ms / 1e3) / 1e12,
+        "wall_s": wall,
+        "roofline": {"kernel": "k_attn (cross-attention, one layer per launch)", "bound": "hbm",
+                     "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK,
+                     "traffic": traffic,
+                     "bytes_per_launch": attn_bytes, "avg_launch_us": attn_avg_s * 1e6,
+                     "launches_timed": attn_n},
+        "cpu_baseline": None,
+    }
+    del dec, enc
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
