@@ -8,11 +8,12 @@
 // beams of a beam search sharing one broadcast encoder set, and the query
 // heads of a GQA group.
 //
-// Per block: pass 1 streams K rows (16 B per lane, a wave covers 4 or 8 whole
-// rows per load so loads are fully coalesced), dots them with the query slice
-// each lane holds in registers and reduces over the lanes of a row; scores go to
-// LDS.  Pass 2 takes the max and exp-sums (fp32).  Pass 3 streams V rows with
-// the same lane mapping and accumulates p_j * V_j.  With one split the block
+// Per block, one pass over its rows: K and V rows stream together (16 B per
+// lane; a wave covers 4 or 8 whole rows per load, fully coalesced), the lanes of
+// a row reduce the q.k dot product with shuffles, and each lane keeps an online
+// softmax state (running max, running exp-sum and its slice of the weighted V
+// sum), rescaled when the max grows.  The lanes' states are merged at the end
+// (shuffles within a wave, LDS across waves).  With one split the block
 // normalises and writes o; otherwise it writes (o, max, sum) partials that a
 // combine kernel rescales and adds.
 #include <algorithm>
@@ -22,14 +23,24 @@
 
 namespace wd {
 
+// o for (row bq, head h, channel c): fp32 row-major, or split fragment layout
+__device__ __forceinline__ void write_o(float* out, int out_ld, void* o_hi, void* o_lo, int o_dtype, int Hq,
+                                        int HD, int bq, int h, int c, float v) {
+  if (o_hi) {
+    const int64_t off = frag_offset(bq, (int64_t)h * HD + c, (int64_t)Hq * HD);
+    if (o_dtype == DT_BF16) store_split<bf16_t>(o_hi, o_lo, off, v);
+    else store_split<f16_t>(o_hi, o_lo, off, v);
+  } else {
+    out[(int64_t)bq * out_ld + h * HD + c] = v;
+  }
+}
+
 template <typename CT, int HD, int NQ>
 __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
-  constexpr int SEGS = HD / 8;          // lanes per cache row
+  constexpr int SEGS = HD / 8;          // lanes per cache row (16 bytes each)
   constexpr int RPP = 256 / SEGS;       // rows per block pass
-  constexpr int UNR = 4;                // independent row loads in flight per lane
-  extern __shared__ float sc[];         // scores [NQ][split_rows]
-  __shared__ float red[4][NQ][HD];
-  __shared__ float stat[2][NQ][4];
+  constexpr int UNR = 4;                // rows in flight per lane, for K and for V
+  __shared__ float red[4][NQ][HD + 2];
 
   const int s = blockIdx.x, g = blockIdx.y, kvb = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -45,7 +56,6 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
   }
   const int r_lo = s * p.split_rows;
   const int r_hi = min(r_lo + p.split_rows, n_rows);
-  const int SR = p.split_rows;
 
   auto qrow = [&](int qi) { return bq0 + qi / G; };
   auto qhead = [&](int qi) { return g * G + qi % G; };
@@ -55,7 +65,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
       const int qi = i / HD, c = i - qi * HD;
       const int bq = qrow(qi), h = qhead(qi);
       if (p.n_splits == 1) {
-        p.out[(int64_t)bq * p.out_ld + h * HD + c] = 0.f;
+        write_o(p.out, p.out_ld, p.o_hi, p.o_lo, p.o_dtype, p.Hq, HD, bq, h, c, 0.f);
       } else {
         float* pp = p.part + (((int64_t)bq * p.Hq + h) * p.n_splits + s) * (HD + 2);
         pp[c] = 0.f;
@@ -79,19 +89,30 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     }
   }
 
-  // ---- pass 1: scores -------------------------------------------------------------------
-  for (int r = r_lo + rr; r - rr < r_hi; r += RPP * UNR) {
-    Raw8<CT> raw[UNR];
+  // one pass over the rows: each lane keeps, per query, the running max m, the
+  // running sum l of exp(score - m) and its slice of sum exp(score - m) * V
+  float m[NQ], l[NQ], acc[NQ][8];
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi) {
+    m[qi] = -INFINITY;
+    l[qi] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[qi][j] = 0.f;
+  }
+  for (int r = r_lo + rr; r - rr < r_hi; r += RPP * UNR) {   // trip count uniform over the block
+    Raw8<CT> kr[UNR], vr[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int ru = min(r + u * RPP, r_hi - 1);
-      raw[u] = fetch8(Kp + (int64_t)ru * HD + seg * 8);
+      kr[u] = fetch8(Kp + (int64_t)ru * HD + seg * 8);
+      vr[u] = fetch8(Vp + (int64_t)ru * HD + seg * 8);
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      float kf[8];
-      unpack8(raw[u], kf);
-      const int ru = r + u * RPP;
+      const bool live = r + u * RPP < r_hi;
+      float kf[8], vf[8];
+      unpack8(kr[u], kf);
+      unpack8(vr[u], vf);
 #pragma unroll
       for (int qi = 0; qi < NQ; ++qi) {
         float d = 0.f;
@@ -99,112 +120,78 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
         for (int j = 0; j < 8; ++j) d = fmaf(qv[qi][j], kf[j], d);
 #pragma unroll
         for (int o = 1; o < SEGS; o <<= 1) d += __shfl_xor(d, o, WAVE);
-        if (seg == 0 && ru < r_hi && qi < nq) sc[qi * SR + (ru - r_lo)] = d;
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- pass 2: max and exp-sum per query ------------------------------------------------------
-  const int nr = r_hi - r_lo;
-  float mq[NQ], lq[NQ];
+        if (live && qi < nq) {
+          if (d > m[qi]) {  // new running max: rescale what was accumulated
+            const float sc = expf(m[qi] - d);
+            l[qi] *= sc;
 #pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) {
-    float m = -INFINITY;
-    if (qi < nq)
-      for (int i = t; i < nr; i += 256) m = fmaxf(m, sc[qi * SR + i]);
-    m = wave_max(m);
-    if (lane == 0) stat[0][qi][wv] = m;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int qi = 0; qi < NQ; ++qi)
-    mq[qi] = fmaxf(fmaxf(stat[0][qi][0], stat[0][qi][1]), fmaxf(stat[0][qi][2], stat[0][qi][3]));
-#pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) {
-    float l = 0.f;
-    if (qi < nq)
-      for (int i = t; i < nr; i += 256) {
-        const float e = expf(sc[qi * SR + i] - mq[qi]);
-        sc[qi * SR + i] = e;
-        l += e;
-      }
-    l = wave_sum(l);
-    if (lane == 0) stat[1][qi][wv] = l;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) lq[qi] = stat[1][qi][0] + stat[1][qi][1] + stat[1][qi][2] + stat[1][qi][3];
-
-  // ---- pass 3: weighted sum of V rows -------------------------------------------------------------
-  float acc[NQ][8];
-#pragma unroll
-  for (int qi = 0; qi < NQ; ++qi)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[qi][j] = 0.f;
-  for (int r = r_lo + rr; r - rr < r_hi; r += RPP * UNR) {
-    Raw8<CT> raw[UNR];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int ru = min(r + u * RPP, r_hi - 1);
-      raw[u] = fetch8(Vp + (int64_t)ru * HD + seg * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int ru = r + u * RPP;
-      if (ru < r_hi) {
-        float vf[8];
-        unpack8(raw[u], vf);
-#pragma unroll
-        for (int qi = 0; qi < NQ; ++qi) {
-          if (qi < nq) {
-            const float w = sc[qi * SR + (ru - r_lo)];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[qi][j] = fmaf(w, vf[j], acc[qi][j]);
+            for (int j = 0; j < 8; ++j) acc[qi][j] *= sc;
+            m[qi] = d;
           }
+          const float e = expf(d - m[qi]);
+          l[qi] += e;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[qi][j] = fmaf(e, vf[j], acc[qi][j]);
         }
       }
     }
   }
-  // reduce over the lanes of a wave that hold the same segment, then over waves
+  // merge the (m, l, acc) of the lanes holding the same segment: within the wave,
+  // then across the four waves through LDS
 #pragma unroll
-  for (int qi = 0; qi < NQ; ++qi)
+  for (int qi = 0; qi < NQ; ++qi) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float a = acc[qi][j];
+    for (int o = SEGS; o < 64; o <<= 1) {
+      const float m2 = __shfl_xor(m[qi], o, WAVE);
+      const float l2 = __shfl_xor(l[qi], o, WAVE);
+      const float mn = fmaxf(m[qi], m2);
+      const float f1 = mn == -INFINITY ? 0.f : expf(m[qi] - mn);
+      const float f2 = mn == -INFINITY ? 0.f : expf(m2 - mn);
+      l[qi] = l[qi] * f1 + l2 * f2;
 #pragma unroll
-      for (int o = SEGS; o < 64; o <<= 1) a += __shfl_xor(a, o, WAVE);
-      acc[qi][j] = a;
+      for (int j = 0; j < 8; ++j) {
+        const float a2 = __shfl_xor(acc[qi][j], o, WAVE);
+        acc[qi][j] = acc[qi][j] * f1 + a2 * f2;
+      }
+      m[qi] = mn;
     }
+  }
   if (lane < SEGS) {
 #pragma unroll
-    for (int qi = 0; qi < NQ; ++qi)
+    for (int qi = 0; qi < NQ; ++qi) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) red[wv][qi][seg * 8 + j] = acc[qi][j];
+      if (seg == 0) { red[wv][qi][HD] = m[qi]; red[wv][qi][HD + 1] = l[qi]; }
+    }
   }
   __syncthreads();
   for (int i = t; i < nq * HD; i += 256) {
     const int qi = i / HD, c = i - qi * HD;
-    float o = 0.f;
-    float m = 0.f, l = 1.f;
+    float M = -INFINITY;
 #pragma unroll
-    for (int q2 = 0; q2 < NQ; ++q2)
-      if (q2 == qi) { m = mq[q2]; l = lq[q2]; }
-    o = red[0][qi][c] + red[1][qi][c] + red[2][qi][c] + red[3][qi][c];
+    for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, red[w2][qi][HD]);
+    float L = 0.f, o = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      const float f = red[w2][qi][HD] == -INFINITY ? 0.f : expf(red[w2][qi][HD] - M);
+      L += f * red[w2][qi][HD + 1];
+      o += f * red[w2][qi][c];
+    }
     const int bq = qrow(qi), h = qhead(qi);
     if (p.n_splits == 1) {
-      p.out[(int64_t)bq * p.out_ld + h * HD + c] = o / l;
+      write_o(p.out, p.out_ld, p.o_hi, p.o_lo, p.o_dtype, p.Hq, HD, bq, h, c, o / L);
     } else {
       float* pp = p.part + (((int64_t)bq * p.Hq + h) * p.n_splits + s) * (HD + 2);
       pp[c] = o;
-      if (c == 0) { pp[HD] = m; pp[HD + 1] = l; }
+      if (c == 0) { pp[HD] = M; pp[HD + 1] = L; }
     }
   }
 }
 
 template <int HD>
 __global__ __launch_bounds__(HD) void k_attn_combine(const float* __restrict__ part, int n_splits,
-                                                     float* __restrict__ out, int out_ld, int Hq) {
+                                                     float* __restrict__ out, int out_ld, int Hq,
+                                                     void* o_hi, void* o_lo, int o_dtype) {
   const int bh = blockIdx.x, c = threadIdx.x;
   const int b = bh / Hq, h = bh - (bh / Hq) * Hq;
   const float* pp = part + (int64_t)bh * n_splits * (HD + 2);
@@ -219,18 +206,16 @@ __global__ __launch_bounds__(HD) void k_attn_combine(const float* __restrict__ p
       o += w * q[c];
     }
   }
-  out[(int64_t)b * out_ld + h * HD + c] = L > 0.f ? o / L : 0.f;
+  write_o(out, out_ld, o_hi, o_lo, o_dtype, Hq, HD, b, h, c, L > 0.f ? o / L : 0.f);
 }
 
 template <typename CT, int HD>
 static hipError_t run_hd(const AttnParams& p, int nq, hipStream_t s) {
   dim3 grid(p.n_splits, p.Hkv, p.B / p.q_per_kvb);
-  // the kernel touches score rows qi < nq only
-  const size_t smem = (size_t)p.split_rows * nq * sizeof(float);
-  if (nq <= 1) k_attn<CT, HD, 1><<<grid, 256, smem, s>>>(p);
-  else if (nq <= 2) k_attn<CT, HD, 2><<<grid, 256, smem, s>>>(p);
-  else if (nq <= 4) k_attn<CT, HD, 4><<<grid, 256, smem, s>>>(p);
-  else k_attn<CT, HD, 8><<<grid, 256, smem, s>>>(p);
+  if (nq <= 1) k_attn<CT, HD, 1><<<grid, 256, 0, s>>>(p);
+  else if (nq <= 2) k_attn<CT, HD, 2><<<grid, 256, 0, s>>>(p);
+  else if (nq <= 4) k_attn<CT, HD, 4><<<grid, 256, 0, s>>>(p);
+  else k_attn<CT, HD, 8><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -246,12 +231,14 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
     return hipErrorInvalidValue;
   const int nq = p.q_per_kvb * (p.Hq / p.Hkv);
   if (nq > 8 || p.split_rows <= 0 || p.n_splits <= 0) return hipErrorInvalidValue;
-  if ((size_t)p.split_rows * nq * sizeof(float) > 48 * 1024) return hipErrorInvalidValue;
   if (p.pos && p.q_per_kvb != 1) return hipErrorInvalidValue;  // per-row lengths need own slabs
   if (!p.pos && (p.n_rows_fixed < 0 || p.n_rows_fixed > p.rows_cap)) return hipErrorInvalidValue;
   if ((int64_t)p.split_rows * p.n_splits < (p.pos ? p.rows_cap : p.n_rows_fixed)) return hipErrorInvalidValue;
   if (p.n_splits > 1 && !p.part) return hipErrorInvalidValue;
-  if (!p.q || !p.K || !p.V || !p.out || (p.q_ld % 4) || (p.out_ld < p.Hq * p.hd)) return hipErrorInvalidValue;
+  if (!p.q || !p.K || !p.V || (p.q_ld % 4)) return hipErrorInvalidValue;
+  if (p.o_hi ? (!p.o_lo || (p.Hq * p.hd) % 32 || (p.o_dtype != DT_F16 && p.o_dtype != DT_BF16))
+             : (!p.out || p.out_ld < p.Hq * p.hd))
+    return hipErrorInvalidValue;
   switch (p.cache_dtype) {
     case DT_F32: return run_ct<float>(p, nq, s);
     case DT_F16: return run_ct<f16_t>(p, nq, s);
@@ -262,9 +249,9 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
 
 hipError_t launch_attention_combine(const AttnParams& p, hipStream_t s) {
   if (p.n_splits <= 1) return hipSuccess;
-  if (!p.part || !p.out) return hipErrorInvalidValue;
-  if (p.hd == 64) k_attn_combine<64><<<p.B * p.Hq, 64, 0, s>>>(p.part, p.n_splits, p.out, p.out_ld, p.Hq);
-  else if (p.hd == 128) k_attn_combine<128><<<p.B * p.Hq, 128, 0, s>>>(p.part, p.n_splits, p.out, p.out_ld, p.Hq);
+  if (!p.part || (!p.out && !p.o_hi)) return hipErrorInvalidValue;
+  if (p.hd == 64) k_attn_combine<64><<<p.B * p.Hq, 64, 0, s>>>(p.part, p.n_splits, p.out, p.out_ld, p.Hq, p.o_hi, p.o_lo, p.o_dtype);
+  else if (p.hd == 128) k_attn_combine<128><<<p.B * p.Hq, 128, 0, s>>>(p.part, p.n_splits, p.out, p.out_ld, p.Hq, p.o_hi, p.o_lo, p.o_dtype);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -1,0 +1,327 @@
+// Skinny GEMM on the matrix cores for 16-bit weights: out[b, n] = sum_k W[n,k] y[b,k]
+// over the B rows of one decoder step (B padded to 16, 32 or 64).
+//
+// The weights were repacked at load into MFMA fragment order, so each wave
+// fetches one contiguous 1 KB tile (16 rows x 32 k) per 16-byte lane load and
+// feeds it straight to v_mfma_f32_16x16x32 as the A operand.  The activations
+// arrive from their producer (norm, attention, GELU/SwiGLU epilogue) already in
+// the same fragment order and split into hi + lo 16-bit parts; every weight tile
+// meets both parts, so the product keeps ~16 bits of each fp32 activation while
+// the weights stream at their storage width.
+//
+// Work split: a wave owns NBW 16-row blocks and a 1/KS slice of K; the KS waves
+// of a row tile sit in one workgroup and add their partial tiles through LDS
+// (fixed order, so results are reproducible run to run).  Loads run one K step
+// ahead of the MFMAs.  Epilogues: bias, scale, residual add, erf-GELU or SwiGLU
+// written back in split fragment order for the next GEMM, the Whisper q|k|v split
+// with the K/V cache append, and tied-head logits with per-block argmax keys.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+
+#include "wd_common.h"
+#include "wd_kernels.h"
+
+namespace wd {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 mbf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 mf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float mf32x4_t;
+
+__device__ __forceinline__ mf32x4_t mma(const uint4& a, const uint4& b, const mf32x4_t& c, bf16_t*) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8_t, a), __builtin_bit_cast(mbf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ mf32x4_t mma(const uint4& a, const uint4& b, const mf32x4_t& c, f16_t*) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mf16x8_t, a), __builtin_bit_cast(mf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float m_gelu(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+__device__ __forceinline__ float m_silu(float z) { return z / (1.0f + expf(-z)); }
+
+template <typename CT>
+__device__ __forceinline__ void put_cache(void* base, int64_t idx, float v) {
+  reinterpret_cast<CT*>(base)[idx] = from_f<CT>(v);
+}
+
+template <typename T>
+__device__ __forceinline__ void epi_one(const MGemvParams& p, int n, int b, float v) {
+  const float bias = p.bias ? p.bias[n] : 0.f;
+  switch (p.epi) {
+    case EPI_STORE: p.out[(int64_t)b * p.ldo + n] = (v + bias) * p.scale; break;
+    case EPI_RESID: p.out[(int64_t)b * p.ldo + n] += v + bias; break;
+    case EPI_GELU_SPLIT: store_split<T>(p.yo_hi, p.yo_lo, frag_offset(b, n, p.N), m_gelu(v + bias)); break;
+    case EPI_QKV: {
+      const int seg = n / p.d, c_all = n - seg * p.d;
+      if (seg == 0) {
+        p.out[(int64_t)b * p.ldo + c_all] = (v + bias) * p.scale;
+      } else {
+        const int pos = p.pos[b];
+        if (pos < 0 || pos >= p.ctx) break;
+        const int h = c_all / p.hd, c = c_all - h * p.hd;
+        const int64_t at = (int64_t)b * p.kv_bstride + ((int64_t)h * p.ctx + pos) * p.hd + c;
+        void* base = seg == 1 ? p.Kc : p.Vc;
+        const float val = seg == 1 ? v : v + bias;  // keys carry no bias
+        if (p.cache_dtype == DT_F32) put_cache<float>(base, at, val);
+        else if (p.cache_dtype == DT_F16) put_cache<f16_t>(base, at, val);
+        else put_cache<bf16_t>(base, at, val);
+      }
+      break;
+    }
+    default: break;
+  }
+}
+
+constexpr int mg_waves(int KS) { return KS >= 4 ? KS : 4; }
+
+template <typename T, int NBW, int NBB, int KS, int D>
+__global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv(MGemvParams p) {
+  constexpr int RT = KS >= 4 ? 1 : 4 / KS;   // row tiles per workgroup (>= 4 waves)
+  constexpr int NW = RT * KS;                // waves per workgroup
+  constexpr int REDF = KS > 1 ? NW * NBW * NBB * 256 : 0;
+  constexpr int LDSF = REDF > NBB * 32 ? REDF : NBB * 32;   // argmax keys reuse the buffer
+  __shared__ __align__(16) float red[LDSF];
+  unsigned long long* kmax = reinterpret_cast<unsigned long long*>(red);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rt = w % RT, ks = w / RT;
+  const int tile = blockIdx.x * RT + rt;
+  const int NB = (p.N + 15) >> 4;
+  const int KST = p.K >> 5;
+  const int s0 = (ks * KST) / KS, s1 = ((ks + 1) * KST) / KS;
+  const uint4* __restrict__ Wv = reinterpret_cast<const uint4*>(p.W);
+  const uint4* __restrict__ Yh = reinterpret_cast<const uint4*>(p.Yhi);
+  const uint4* __restrict__ Yl = reinterpret_cast<const uint4*>(p.Ylo);
+
+  int64_t wbase[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) wbase[nb] = (int64_t)min(tile * NBW + nb, NB - 1) * KST * 64 + lane;
+
+  mf32x4_t acc[NBW][NBB];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int bb = 0; bb < NBB; ++bb) acc[nb][bb] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // ring of D k-steps of fragments: loads run D-1 steps ahead of the MFMAs
+  uint4 wr[D][NBW], hr[D][NBB], lr[D][NBB];
+  auto load = [&](int slot_unused, int st, uint4 (&wd)[NBW], uint4 (&hd)[NBB], uint4 (&ld)[NBB]) {
+    (void)slot_unused;
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) wd[nb] = Wv[wbase[nb] + (int64_t)st * 64];
+#pragma unroll
+    for (int bb = 0; bb < NBB; ++bb) {
+      const int64_t yi = ((int64_t)bb * KST + st) * 64 + lane;
+      hd[bb] = Yh[yi];
+      ld[bb] = Yl[yi];
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j)
+    if (s0 + j < s1) load(j, s0 + j, wr[j], hr[j], lr[j]);
+  for (int s = s0; s < s1; s += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int ss = s + j;
+      if (ss < s1) {
+        const int pre = ss + D - 1;
+        constexpr int dummy = 0;
+        (void)dummy;
+        if (pre < s1) load((j + D - 1) % D, pre, wr[(j + D - 1) % D], hr[(j + D - 1) % D], lr[(j + D - 1) % D]);
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+          for (int bb = 0; bb < NBB; ++bb) {
+            acc[nb][bb] = mma(wr[j][nb], hr[j][bb], acc[nb][bb], (T*)nullptr);
+            acc[nb][bb] = mma(wr[j][nb], lr[j][bb], acc[nb][bb], (T*)nullptr);
+          }
+      }
+    }
+  }
+
+  if constexpr (KS > 1) {  // add the K-slice partials of the row tile, fixed order
+    if (ks > 0) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[((w * NBW + nb) * NBB + bb) * 256 + r * 64 + lane] = acc[nb][bb][r];
+    }
+    __syncthreads();
+    if (ks == 0) {
+      for (int k2 = 1; k2 < KS; ++k2) {
+        const int w2 = rt + k2 * RT;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+          for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[nb][bb][r] += red[((w2 * NBW + nb) * NBB + bb) * 256 + r * 64 + lane];
+      }
+    }
+  }
+  const bool active = ks == 0;
+  // D fragment: lane holds rows 4*(lane/16)+r of column lane%16 of each 16x16 tile
+  const int rsub = (lane >> 4) * 4, col = lane & 15;
+
+  if (p.epi == EPI_LOGITS) {
+    if constexpr (KS > 1) __syncthreads();   // the partial tiles in `red` have been read
+    for (int i = threadIdx.x; i < NBB * 16; i += NW * 64) kmax[i] = 0ull;
+    __syncthreads();
+    if (active) {
+#pragma unroll
+      for (int bb = 0; bb < NBB; ++bb) {
+        const int b = bb * 16 + col;
+        unsigned long long best = 0ull;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int n = (tile * NBW + nb) * 16 + rsub + r;
+            if (n < p.N && b < p.B && tile * NBW + nb < NB) {
+              float v = acc[nb][bb][r];
+              if (p.out) p.out[(int64_t)b * p.ldo + n] = v;
+              if (v != v) { raise_err(p.err, ERR_NAN); v = -INFINITY; }
+              const unsigned long long k = argmax_key(v, n);
+              best = k > best ? k : best;
+            }
+          }
+        unsigned long long o = __shfl_xor(best, 16, WAVE);
+        best = o > best ? o : best;
+        o = __shfl_xor(best, 32, WAVE);
+        best = o > best ? o : best;
+        if (lane < 16 && b < p.B) atomicMax(&kmax[b], best);
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < p.B; i += NW * 64) p.amax[(int64_t)blockIdx.x * p.ldp + i] = kmax[i];
+    return;
+  }
+  if (!active) return;
+  if (p.epi == EPI_SWIGLU_SPLIT) {  // row blocks alternate gate, up for the same 16 outputs
+    const int half = p.N >> 1;
+#pragma unroll
+    for (int nb = 0; nb + 1 < NBW; nb += 2)
+#pragma unroll
+      for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = ((tile * NBW + nb) >> 1) * 16 + rsub + r;
+          const int b = bb * 16 + col;
+          if (j < half && b < p.B)
+            store_split<T>(p.yo_hi, p.yo_lo, frag_offset(b, j, half), m_silu(acc[nb][bb][r]) * acc[nb + 1][bb][r]);
+        }
+    return;
+  }
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = (tile * NBW + nb) * 16 + rsub + r;
+        const int b = bb * 16 + col;
+        if (n < p.N && b < p.B && tile * NBW + nb < NB) epi_one<T>(p, n, b, acc[nb][bb][r]);
+      }
+}
+
+struct MShape { int NBW, NBB, KS; };
+// Shape per projection: enough waves in flight for a weight stream of a few MB, K split
+// over the waves of a workgroup so each walks at most ~10 K steps, and several 16-row
+// blocks per wave where N is large (fewer activation re-reads per weight byte).
+// Tuning override for shape sweeps: WD_MGEMV_SHAPE="nbw,ks" (read once; ignored if invalid).
+static bool shape_override(MShape& s) {
+  static int nbw = -1, ks = -1;
+  static bool read = false;
+  if (!read) {
+    read = true;
+    if (const char* e = getenv("WD_MGEMV_SHAPE")) {
+      if (sscanf(e, "%d,%d", &nbw, &ks) != 2) nbw = ks = -1;
+    }
+  }
+  if (nbw < 0) return false;
+  s.NBW = nbw;
+  s.KS = ks;
+  return true;
+}
+
+static MShape mpick(int N, int K, int B, int epi) {
+  MShape s;
+  s.NBB = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
+  const int nblocks = (N + 15) / 16, ksteps = K / 32;
+  if (nblocks >= 1024) {
+    s.NBW = s.NBB == 4 ? 2 : 4;
+    s.KS = (s.NBW == 2 && ksteps >= 32) ? 2 : 1;
+  } else if (nblocks >= 128 || epi == EPI_SWIGLU_SPLIT) {
+    s.NBW = 2;
+    s.KS = ksteps >= 64 ? 8 : 4;
+  } else {
+    s.NBW = 1;
+    s.KS = ksteps >= 96 ? 16 : (ksteps >= 32 ? 8 : 4);
+    if (s.NBB == 4 && s.KS > 8) s.KS = 8;   // 16 waves x 64-wide tiles would spill
+  }
+  if (epi != EPI_LOGITS) {
+    MShape o = s;
+    if (shape_override(o) && !(epi == EPI_SWIGLU_SPLIT && o.NBW % 2)) s = o;
+  }
+  return s;
+}
+static int rows_per_block(const MShape& s) { return s.NBW * (s.KS >= 4 ? 1 : 4 / s.KS); }
+
+int mgemv_blocks(int N, int B) {
+  int most = 1;
+  for (int K : {32, 1024, 2048, 4096, 8192}) {  // the logits launch has K = d; cover any K
+    const MShape s = mpick(N, K, B, EPI_LOGITS);
+    most = std::max(most, ((N + 15) / 16 + rows_per_block(s) - 1) / rows_per_block(s));
+  }
+  return most;
+}
+int mgemv_blocks_k(int N, int K, int B) {
+  const MShape s = mpick(N, K, B, EPI_LOGITS);
+  return ((N + 15) / 16 + rows_per_block(s) - 1) / rows_per_block(s);
+}
+
+constexpr int DEPTH = 3;
+
+template <typename T, int NBB>
+static hipError_t mrun_b(const MGemvParams& p, const MShape& s, hipStream_t st) {
+  const int per = rows_per_block(s);
+  const int grid = ((p.N + 15) / 16 + per - 1) / per;
+  const int threads = 64 * (s.KS >= 4 ? s.KS : 4);
+#define WD_MG(NBW_, KS_) \
+  if (s.NBW == NBW_ && s.KS == KS_) { k_mgemv<T, NBW_, NBB, KS_, DEPTH><<<grid, threads, 0, st>>>(p); return hipGetLastError(); }
+  if constexpr (NBB < 4) { WD_MG(4, 1) }
+  WD_MG(2, 1) WD_MG(2, 2) WD_MG(2, 4) WD_MG(2, 8)
+  WD_MG(1, 4) WD_MG(1, 8)
+  if constexpr (NBB < 4) { WD_MG(1, 16) }
+#undef WD_MG
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t mrun(const MGemvParams& p, hipStream_t st) {
+  const MShape s = mpick(p.N, p.K, p.B, p.epi);
+  if (s.NBB == 1) return mrun_b<T, 1>(p, s, st);
+  if (s.NBB == 2) return mrun_b<T, 2>(p, s, st);
+  return mrun_b<T, 4>(p, s, st);
+}
+
+hipError_t launch_mgemv(const MGemvParams& p, hipStream_t s) {
+  if (p.N <= 0 || p.K <= 0 || (p.K % 32) || p.B <= 0 || p.B > 64 || !p.W || !p.Yhi || !p.Ylo)
+    return hipErrorInvalidValue;
+  switch (p.epi) {
+    case EPI_STORE: case EPI_RESID: if (!p.out) return hipErrorInvalidValue; break;
+    case EPI_GELU_SPLIT: if (!p.yo_hi || !p.yo_lo) return hipErrorInvalidValue; break;
+    case EPI_SWIGLU_SPLIT: if (!p.yo_hi || !p.yo_lo || (p.N % 32)) return hipErrorInvalidValue; break;
+    case EPI_QKV:
+      if (!p.out || p.N != 3 * p.d || !p.pos || !p.Kc || !p.Vc || p.hd <= 0 || p.d != p.H * p.hd)
+        return hipErrorInvalidValue;
+      break;
+    case EPI_LOGITS: if (!p.amax || p.ldp < p.B) return hipErrorInvalidValue; break;
+    default: return hipErrorInvalidValue;
+  }
+  if (p.w_dtype == DT_BF16) return mrun<bf16_t>(p, s);
+  if (p.w_dtype == DT_F16) return mrun<f16_t>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace wd

@@ -2,6 +2,8 @@
 // Qwen3 per-head QK norm + RoPE + cache append, argmax finalisation and the
 // beam-reorder cache gather.  All are tiny next to the weight and cache
 // streams; they are written for coalesced 16-byte accesses where it matters.
+#include <algorithm>
+
 #include "wd_common.h"
 #include "wd_kernels.h"
 
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(256) void k_embed(float* __restrict__ x, const WT* 
                                                const WT* __restrict__ P, const int32_t* tok,
                                                int tok_stride, const int32_t* pos,
                                                const WT* __restrict__ ov, int64_t ov_stride, int d,
-                                               int V, int ctx, unsigned* err) {
+                                               int V, int ctx, unsigned* err, bool E_frag) {
   const int b = blockIdx.x;
   const int p = pos[b];
   const bool bad_p = p < 0 || p >= ctx;
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(256) void k_embed(float* __restrict__ x, const WT* 
       if (ov) {
         v = to_f(ov[(int64_t)b * ov_stride + i]);
       } else {
-        v = to_f(E[(int64_t)t * d + i]);
+        v = to_f(E[E_frag ? frag_offset(t, i, d) : (int64_t)t * d + i]);
         if (P) v += to_f(P[(int64_t)p * d + i]);
       }
     }
@@ -100,51 +102,124 @@ __global__ __launch_bounds__(256) void k_embed(float* __restrict__ x, const WT* 
 
 hipError_t launch_embed(float* x, const void* E, const void* P, int w_dtype, const int32_t* tok,
                         int tok_stride, const int32_t* pos, const void* ov, int64_t ov_stride,
-                        int B, int d, int V, int ctx, unsigned* err, hipStream_t s) {
-  if (B <= 0 || d <= 0 || (!ov && !tok) || !pos) return hipErrorInvalidValue;
+                        int B, int d, int V, int ctx, unsigned* err, bool E_frag, hipStream_t s) {
+  if (B <= 0 || d <= 0 || (!ov && !tok) || !pos || (E_frag && d % 32)) return hipErrorInvalidValue;
   switch (w_dtype) {
-    case DT_F32: k_embed<<<B, 256, 0, s>>>(x, (const float*)E, (const float*)P, tok, tok_stride, pos, (const float*)ov, ov_stride, d, V, ctx, err); break;
-    case DT_F16: k_embed<<<B, 256, 0, s>>>(x, (const f16_t*)E, (const f16_t*)P, tok, tok_stride, pos, (const f16_t*)ov, ov_stride, d, V, ctx, err); break;
-    case DT_BF16: k_embed<<<B, 256, 0, s>>>(x, (const bf16_t*)E, (const bf16_t*)P, tok, tok_stride, pos, (const bf16_t*)ov, ov_stride, d, V, ctx, err); break;
+    case DT_F32: k_embed<<<B, 256, 0, s>>>(x, (const float*)E, (const float*)P, tok, tok_stride, pos, (const float*)ov, ov_stride, d, V, ctx, err, E_frag); break;
+    case DT_F16: k_embed<<<B, 256, 0, s>>>(x, (const f16_t*)E, (const f16_t*)P, tok, tok_stride, pos, (const f16_t*)ov, ov_stride, d, V, ctx, err, E_frag); break;
+    case DT_BF16: k_embed<<<B, 256, 0, s>>>(x, (const bf16_t*)E, (const bf16_t*)P, tok, tok_stride, pos, (const bf16_t*)ov, ov_stride, d, V, ctx, err, E_frag); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------
-// row norms, one block per row; LayerNorm uses the two-pass (mean, then centred
-// variance) form, eps inside the square root.
+// row norms, one block per row, the row read once into registers: LayerNorm takes the
+// mean, then the variance of the centred values (eps inside the square root); RMSNorm
+// the mean square.  Output fp32 row-major, or the split fragment layout for the MFMA GEMM.
 // ------------------------------------------------------------------------------------------
+constexpr int NORM_MAXE = 16;  // d <= 4096
+
+template <typename OT, bool SPLIT>
 __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, float* __restrict__ y,
+                                              OT* __restrict__ yh, OT* __restrict__ yl,
                                               const float* __restrict__ g,
                                               const float* __restrict__ bvec, int d, float eps) {
   __shared__ float red[4];
-  const float* xr = x + (int64_t)blockIdx.x * d;
-  float* yr = y + (int64_t)blockIdx.x * d;
+  const int row = blockIdx.x, t = threadIdx.x;
+  const float* xr = x + (int64_t)row * d;
+  float v[NORM_MAXE], gv[NORM_MAXE], bv[NORM_MAXE];
+#pragma unroll
+  for (int j = 0; j < NORM_MAXE; ++j) {  // all loads issued before any reduction
+    const int i = t + j * 256;
+    v[j] = i < d ? xr[i] : 0.f;
+    gv[j] = i < d ? g[i] : 0.f;
+    bv[j] = (bvec && i < d) ? bvec[i] : 0.f;
+  }
   float mean = 0.f;
   if (bvec) {
-    float s = 0.f;
-    for (int i = threadIdx.x; i < d; i += 256) s += xr[i];
-    mean = block_sum<256>(s, red) / (float)d;
+    float s1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NORM_MAXE; ++j) s1 += v[j];
+    mean = block_sum<256>(s1, red) / (float)d;
   }
   float s2 = 0.f;
-  for (int i = threadIdx.x; i < d; i += 256) {
-    const float c = xr[i] - mean;
+#pragma unroll
+  for (int j = 0; j < NORM_MAXE; ++j) {
+    const int i = t + j * 256;
+    const float c = i < d ? v[j] - mean : 0.f;
     s2 += c * c;
   }
-  const float var = block_sum<256>(s2, red) / (float)d;
-  const float rs = 1.0f / sqrtf(var + eps);
-  for (int i = threadIdx.x; i < d; i += 256) {
-    const float v = (xr[i] - mean) * rs * g[i];
-    yr[i] = bvec ? v + bvec[i] : v;
+  const float rs = 1.0f / sqrtf(block_sum<256>(s2, red) / (float)d + eps);
+#pragma unroll
+  for (int j = 0; j < NORM_MAXE; ++j) {
+    const int i = t + j * 256;
+    if (i < d) {
+      const float o = (v[j] - mean) * rs * gv[j] + bv[j];
+      if constexpr (SPLIT) store_split<OT>(yh, yl, frag_offset(row, i, d), o);
+      else y[(int64_t)row * d + i] = o;
+    }
   }
 }
 
 hipError_t launch_norm(const float* x, float* y, const float* g, const float* b, int B, int d,
                        float eps, hipStream_t s) {
-  if (B <= 0 || d <= 0 || !g) return hipErrorInvalidValue;
-  k_norm<<<B, 256, 0, s>>>(x, y, g, b, d, eps);
+  if (B <= 0 || d <= 0 || d > 256 * NORM_MAXE || !g) return hipErrorInvalidValue;
+  k_norm<float, false><<<B, 256, 0, s>>>(x, y, nullptr, nullptr, g, b, d, eps);
   return hipGetLastError();
+}
+
+hipError_t launch_norm_split(const float* x, void* y_hi, void* y_lo, int act_dtype, const float* g,
+                             const float* b, int B, int d, float eps, hipStream_t s) {
+  if (B <= 0 || d <= 0 || d > 256 * NORM_MAXE || (d % 32) || !g || !y_hi || !y_lo) return hipErrorInvalidValue;
+  if (act_dtype == DT_BF16)
+    k_norm<bf16_t, true><<<B, 256, 0, s>>>(x, nullptr, (bf16_t*)y_hi, (bf16_t*)y_lo, g, b, d, eps);
+  else if (act_dtype == DT_F16)
+    k_norm<f16_t, true><<<B, 256, 0, s>>>(x, nullptr, (f16_t*)y_hi, (f16_t*)y_lo, g, b, d, eps);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// fragment-layout repack: source row r of a [rows, K] matrix lands in fused row
+// (r / 16) * blk_mul * 16 + blk_add * 16 + r % 16 of the destination
+// ------------------------------------------------------------------------------------------
+template <typename S, typename D>
+__global__ void k_pack_frag(const S* __restrict__ src, D* __restrict__ dst, int64_t rows, int64_t K,
+                            int64_t blk_mul, int64_t blk_add) {
+  const int64_t n = rows * K;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / K, k = i - r * K;
+    const int64_t fr = (r >> 4) * blk_mul * 16 + blk_add * 16 + (r & 15);
+    dst[frag_offset(fr, k, K)] = from_f<D>(to_f(src[i]));
+  }
+}
+
+template <typename S>
+static hipError_t pack_to(const S* src, void* dst, int dst_dtype, int64_t rows, int64_t K, int64_t mul,
+                          int64_t add, hipStream_t s) {
+  const int64_t n = rows * K;
+  const int blocks = (int)std::min<int64_t>((n + 255) / 256, 65536);
+  if (n <= 0) return hipSuccess;
+  switch (dst_dtype) {
+    case DT_F16: k_pack_frag<<<blocks, 256, 0, s>>>(src, (f16_t*)dst, rows, K, mul, add); break;
+    case DT_BF16: k_pack_frag<<<blocks, 256, 0, s>>>(src, (bf16_t*)dst, rows, K, mul, add); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_frag(const void* src, int src_dtype, void* dst, int dst_dtype, int64_t rows,
+                            int64_t K, int64_t blk_mul, int64_t blk_add, hipStream_t s) {
+  if (K % 32 || blk_mul < 1 || blk_add < 0) return hipErrorInvalidValue;
+  if (rows % 16 && blk_mul != 1) return hipErrorInvalidValue;
+  switch (src_dtype) {
+    case DT_F32: return pack_to((const float*)src, dst, dst_dtype, rows, K, blk_mul, blk_add, s);
+    case DT_F16: return pack_to((const f16_t*)src, dst, dst_dtype, rows, K, blk_mul, blk_add, s);
+    case DT_BF16: return pack_to((const bf16_t*)src, dst, dst_dtype, rows, K, blk_mul, blk_add, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // ------------------------------------------------------------------------------------------

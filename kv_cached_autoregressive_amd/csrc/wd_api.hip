@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <new>
@@ -43,6 +45,8 @@ struct LayerOff {
 
 struct Plan {
   size_t total = 0;
+  bool mfma = false;        // 16-bit weights: fragment layout + MFMA skinny GEMM
+  size_t yh = 0, yl = 0, oh = 0, ol = 0, hh = 0, hl = 0;   // split activations [B_pad, K]
   std::vector<LayerOff> L;
   size_t embed = 0, pos = 0, lnfg = 0, lnfb = 0;
   size_t self[2] = {0, 0};
@@ -91,10 +95,23 @@ std::string check_config(const wd_config& c) {
 
 // Split of an attention over `rows` cache rows: aim at >= 2048 blocks in total, at
 // least 64 rows (one K/V tile of a few KB) per block, scores within the LDS budget.
-void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits) {
+// Tuning override for sweeps: WD_ATTN_ROWS="self_rows,cross_rows" (0 keeps the policy).
+int attn_rows_override(bool cross) {
+  static int sr = 0, cr = 0;
+  static bool read = false;
+  if (!read) {
+    read = true;
+    if (const char* e = getenv("WD_ATTN_ROWS"))
+      if (sscanf(e, "%d,%d", &sr, &cr) != 2) sr = cr = 0;
+  }
+  return cross ? cr : sr;
+}
+
+void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits, bool cross = false) {
   const int want = std::max(1, (2048 + slabs - 1) / slabs);
   int r = (rows + want - 1) / want;
   r = std::max(r, 64);
+  if (const int o = attn_rows_override(cross)) r = o;
   r = (r + 31) & ~31;
   r = std::min(r, 12288 / std::max(nq, 1));
   r = std::max(r, 1);
@@ -108,6 +125,9 @@ Plan make_plan(const wd_config& c) {
   const size_t d = c.d_model, ff = c.d_ff, hd = c.head_dim, hq = c.n_heads, hkv = c.n_kv_heads;
   const size_t wb = dtype_bytes(c.w_dtype), cb = dtype_bytes(c.cache_dtype), f4 = 4;
   const size_t Bm = c.max_batch;
+  p.mfma = c.w_dtype != DT_F32;
+  // fragment layout pads matrix rows to 16 (only the tied head's vocab rows can be ragged)
+  const size_t V = p.mfma ? ((size_t)c.vocab + 15) / 16 * 16 : (size_t)c.vocab;
   p.L.resize(c.n_layers);
   for (auto& l : p.L) {
     std::memset(&l, 0, sizeof(l));
@@ -125,7 +145,7 @@ Plan make_plan(const wd_config& c) {
       l.n1g = b.take(d * f4); l.n2g = b.take(d * f4); l.qn = b.take(hd * f4); l.kn = b.take(hd * f4);
     }
   }
-  p.embed = b.take((size_t)c.vocab * d * wb);
+  p.embed = b.take(V * d * wb);
   if (c.arch == WD_ARCH_WHISPER) {
     p.pos = b.take((size_t)c.context * d * wb);
     p.lnfb = b.take(d * f4);
@@ -148,7 +168,14 @@ Plan make_plan(const wd_config& c) {
   const int rows_max = std::max(c.context, c.arch == WD_ARCH_WHISPER ? c.max_frames : 0);
   p.max_splits = (rows_max + 63) / 64;
   p.part = b.take(Bm * hq * (size_t)p.max_splits * (hd + 2) * f4);
-  p.amax_parts = wd::gemv_blocks(c.vocab, c.max_batch);
+  if (p.mfma) {
+    const size_t Bp = (Bm + 15) / 16 * 16;
+    const size_t kmax = std::max(d, hq * hd);
+    p.yh = b.take(Bp * kmax * wb); p.yl = b.take(Bp * kmax * wb);
+    p.oh = b.take(Bp * hq * hd * wb); p.ol = b.take(Bp * hq * hd * wb);
+    p.hh = b.take(Bp * ff * wb); p.hl = b.take(Bp * ff * wb);
+  }
+  p.amax_parts = std::max(wd::gemv_blocks(c.vocab, c.max_batch), wd::mgemv_blocks(c.vocab, c.max_batch));
   p.amax = b.take((size_t)p.amax_parts * Bm * 8);
   p.err = b.take(64);
   p.pos_tmp = b.take(Bm * 4);
@@ -216,6 +243,127 @@ int rows_per_set(const wd_config& c, int B) {
   return c.max_batch / c.n_enc;
 }
 
+// The step's layers and head for 16-bit weights: every projection on the MFMA skinny
+// GEMM, activations handed between kernels in the split fragment layout.
+wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, int32_t* argmax, bool head) {
+  const wd_config& g = c->cfg;
+  const Plan& P = c->plan;
+  hipStream_t s = c->stream;
+  const int d = g.d_model, hd = g.head_dim, hq = g.n_heads, hkv = g.n_kv_heads, ff = g.d_ff;
+  const bool whisper = g.arch == WD_ARCH_WHISPER;
+  const int adt = g.w_dtype;  // activation split dtype = weight dtype
+  float* x = c->at<float>(P.x);
+  float* q = c->at<float>(P.q);
+  float* qkv = c->at<float>(P.qkv);
+  float* part = c->at<float>(P.part);
+  unsigned* err = c->at<unsigned>(P.err);
+  void *yh = c->at(P.yh), *yl = c->at(P.yl), *oh = c->at(P.oh), *ol = c->at(P.ol);
+  void *hh = c->at(P.hh), *hl = c->at(P.hl);
+  const int64_t kv_bstride = (int64_t)hkv * g.context * hd;
+  const float qscale = 1.0f / sqrtf((float)hd);
+
+  int s_rows, s_splits;
+  split_for(g.context, B * hkv, hq / hkv, &s_rows, &s_splits);
+  const int qpk = whisper ? rows_per_set(g, B) : 1;
+  int c_rows = 0, c_splits = 1;
+  if (whisper) split_for(c->frames, (B / qpk) * hkv, qpk, &c_rows, &c_splits, true);
+
+  auto proj = [&](const void* W, int N, int K, const void* Yh, const void* Yl, int epi, const float* bias,
+                  float* out, int ldo, float scale) {
+    wd::MGemvParams m{};
+    m.W = W; m.w_dtype = g.w_dtype; m.N = N; m.K = K; m.Yhi = Yh; m.Ylo = Yl; m.B = B; m.epi = epi;
+    m.bias = bias; m.out = out; m.ldo = ldo; m.scale = scale; m.err = err;
+    m.yo_hi = hh; m.yo_lo = hl;
+    return m;
+  };
+
+  for (int l = 0; l < g.n_layers; ++l) {
+    const LayerOff& L = P.L[l];
+    wd::AttnParams ap{};
+    ap.cache_dtype = g.cache_dtype; ap.B = B; ap.Hq = hq; ap.Hkv = hkv; ap.hd = hd; ap.part = part;
+    ap.o_hi = oh; ap.o_lo = ol; ap.o_dtype = adt;
+    if (whisper) {
+      HIPCHK(c, wd::launch_norm_split(x, yh, yl, adt, c->at<float>(L.ln1g), c->at<float>(L.ln1b), B, d, g.norm_eps, s), "ln1");
+      wd::MGemvParams m = proj(c->at(L.wqkv), 3 * d, d, yh, yl, wd::EPI_QKV, c->at<float>(L.bqkv), q, d, qscale);
+      m.d = d; m.H = hq; m.hd = hd; m.ctx = g.context; m.pos = pos;
+      m.Kc = c->self_k(l); m.Vc = c->self_v(l); m.cache_dtype = g.cache_dtype; m.kv_bstride = kv_bstride;
+      HIPCHK(c, wd::launch_mgemv(m, s), "qkv projection");
+    } else {
+      HIPCHK(c, wd::launch_norm_split(x, yh, yl, adt, c->at<float>(L.n1g), nullptr, B, d, g.norm_eps, s), "norm1");
+      const int nqkv = (hq + 2 * hkv) * hd;
+      HIPCHK(c, wd::launch_mgemv(proj(c->at(L.wqkv), nqkv, d, yh, yl, wd::EPI_STORE, nullptr, qkv, nqkv, 1.0f), s),
+             "qkv projection");
+      HIPCHK(c, wd::launch_qk_rope_append(qkv, B, hq, hkv, hd, pos, g.context, c->at<float>(L.qn),
+                                          c->at<float>(L.kn), g.norm_eps, g.rope_base, qscale, q,
+                                          c->self_k(l), c->self_v(l), g.cache_dtype, kv_bstride, s),
+             "qk norm/rope/append");
+    }
+    ap.q = q; ap.q_ld = hq * hd; ap.K = c->self_k(l); ap.V = c->self_v(l);
+    ap.kvb_stride = kv_bstride; ap.rows_cap = g.context; ap.pos = pos; ap.n_rows_fixed = 0;
+    ap.q_per_kvb = 1; ap.split_rows = s_rows; ap.n_splits = s_splits; ap.out = nullptr; ap.out_ld = 0;
+    {
+      const bool on = prof_on(c, PK_SELF_ATTN, l);
+      prof_begin(c, on);
+      HIPCHK(c, wd::launch_attention(ap, s), "self attention");
+      prof_end(c, on);
+    }
+    HIPCHK(c, wd::launch_attention_combine(ap, s), "self attention combine");
+    HIPCHK(c, wd::launch_mgemv(proj(c->at(L.wo), d, hq * hd, oh, ol, wd::EPI_RESID,
+                                    whisper ? c->at<float>(L.bo) : nullptr, x, d, 1.0f), s), "out projection");
+    if (whisper) {
+      HIPCHK(c, wd::launch_norm_split(x, yh, yl, adt, c->at<float>(L.ln2g), c->at<float>(L.ln2b), B, d, g.norm_eps, s), "ln2");
+      HIPCHK(c, wd::launch_mgemv(proj(c->at(L.wcq), d, d, yh, yl, wd::EPI_STORE, c->at<float>(L.bcq), q, d, qscale), s),
+             "cross q projection");
+      wd::AttnParams cp = ap;
+      cp.K = c->cross_k(l); cp.V = c->cross_v(l);
+      cp.kvb_stride = (int64_t)hq * g.max_frames * hd; cp.rows_cap = g.max_frames;
+      cp.pos = nullptr; cp.n_rows_fixed = c->frames; cp.q_per_kvb = qpk;
+      cp.split_rows = c_rows; cp.n_splits = c_splits;
+      {
+        const bool on = prof_on(c, PK_CROSS_ATTN, l);
+        prof_begin(c, on);
+        HIPCHK(c, wd::launch_attention(cp, s), "cross attention");
+        prof_end(c, on);
+      }
+      HIPCHK(c, wd::launch_attention_combine(cp, s), "cross attention combine");
+      HIPCHK(c, wd::launch_mgemv(proj(c->at(L.wco), d, d, oh, ol, wd::EPI_RESID, c->at<float>(L.bco), x, d, 1.0f), s),
+             "cross out projection");
+      HIPCHK(c, wd::launch_norm_split(x, yh, yl, adt, c->at<float>(L.ln3g), c->at<float>(L.ln3b), B, d, g.norm_eps, s), "ln3");
+      {
+        const bool on = prof_on(c, PK_FC1, l);
+        prof_begin(c, on);
+        HIPCHK(c, wd::launch_mgemv(proj(c->at(L.w1), ff, d, yh, yl, wd::EPI_GELU_SPLIT, c->at<float>(L.b1), nullptr, 0, 1.0f), s),
+               "fc1");
+        prof_end(c, on);
+      }
+      HIPCHK(c, wd::launch_mgemv(proj(c->at(L.w2), d, ff, hh, hl, wd::EPI_RESID, c->at<float>(L.b2), x, d, 1.0f), s), "fc2");
+    } else {
+      HIPCHK(c, wd::launch_norm_split(x, yh, yl, adt, c->at<float>(L.n2g), nullptr, B, d, g.norm_eps, s), "norm2");
+      {
+        const bool on = prof_on(c, PK_FC1, l);
+        prof_begin(c, on);
+        HIPCHK(c, wd::launch_mgemv(proj(c->at(L.wgu), 2 * ff, d, yh, yl, wd::EPI_SWIGLU_SPLIT, nullptr, nullptr, 0, 1.0f), s),
+               "gate|up projection");
+        prof_end(c, on);
+      }
+      HIPCHK(c, wd::launch_mgemv(proj(c->at(L.wdn), d, ff, hh, hl, wd::EPI_RESID, nullptr, x, d, 1.0f), s), "down projection");
+    }
+  }
+  if (!head) return WD_OK;
+  HIPCHK(c, wd::launch_norm_split(x, yh, yl, adt, c->at<float>(P.lnfg), whisper ? c->at<float>(P.lnfb) : nullptr, B, d,
+                                  g.norm_eps, s), "final norm");
+  wd::MGemvParams hm = proj(c->at(P.embed), g.vocab, d, yh, yl, wd::EPI_LOGITS, nullptr, logits, g.vocab, 1.0f);
+  hm.amax = c->at<unsigned long long>(P.amax); hm.ldp = g.max_batch;
+  {
+    const bool on = prof_on(c, PK_LOGITS, -1);
+    prof_begin(c, on);
+    HIPCHK(c, wd::launch_mgemv(hm, s), "logits");
+    prof_end(c, on);
+  }
+  HIPCHK(c, wd::launch_argmax_final(hm.amax, wd::mgemv_blocks_k(g.vocab, d, B), g.max_batch, B, argmax, s), "argmax");
+  return WD_OK;
+}
+
 // One decoder step over rows 0..B-1.  tok: ids (stride tok_stride) or null with ov;
 // pos: device positions; ov: embedding override rows (stride ov_stride) or null.
 wd_status run_step(wd_ctx* c, const int32_t* tok, int tok_stride, const int32_t* pos, const void* ov,
@@ -237,14 +385,15 @@ wd_status run_step(wd_ctx* c, const int32_t* tok, int tok_stride, const int32_t*
   const float qscale = 1.0f / sqrtf((float)hd);
 
   HIPCHK(c, wd::launch_embed(x, c->at(P.embed), whisper ? c->at(P.pos) : nullptr, g.w_dtype, tok, tok_stride,
-                             pos, ov, ov_stride, B, d, g.vocab, g.context, err, s), "embed");
+                             pos, ov, ov_stride, B, d, g.vocab, g.context, err, P.mfma, s), "embed");
+  if (P.mfma) return run_layers_mfma(c, pos, B, logits, argmax, head);
 
   // self-attention split policy (positions live on the device, so split by context)
   int s_rows, s_splits;
   split_for(g.context, B * hkv, hq / hkv, &s_rows, &s_splits);
   const int qpk = whisper ? rows_per_set(g, B) : 1;
   int c_rows = 0, c_splits = 1;
-  if (whisper) split_for(c->frames, (B / qpk) * hkv, qpk, &c_rows, &c_splits);
+  if (whisper) split_for(c->frames, (B / qpk) * hkv, qpk, &c_rows, &c_splits, true);
 
   for (int l = 0; l < g.n_layers; ++l) {
     const LayerOff& L = P.L[l];
@@ -492,7 +641,21 @@ wd_status wd_load(const wd_config* cfg, const wd_tensor* weights, int32_t n_weig
     const int64_t d = cfg->d_model, ff = cfg->d_ff, hd = cfg->head_dim, hq = cfg->n_heads, hkv = cfg->n_kv_heads;
     hipError_t e = hipSuccess;
     auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
-    chk(cp("embed", plan.embed, wdt, cfg->vocab, d, 0));
+    // fragment-layout pack into fused row blocks (16-bit weights) or plain row copy (fp32)
+    auto mat = [&](const std::string& nm, size_t dst, int64_t rows, int64_t K, int64_t blk_mul, int64_t blk_add,
+                   int64_t row_add) {
+      if (!plan.mfma) return cp(nm, dst, wdt, rows, K, row_add);
+      const wd_tensor* t = T(nm);
+      return wd::launch_pack_frag(t->data, t->dtype, c->ws + dst, wdt, rows, K, blk_mul, blk_add, s);
+    };
+    if (plan.mfma) chk(zero(plan.embed, ((int64_t)(cfg->vocab + 15) / 16 * 16) * d * dtype_bytes(wdt) / 4));
+    chk(mat("embed", plan.embed, cfg->vocab, d, 1, 0, 0));
+    if (plan.mfma) {
+      const int64_t Bp = (cfg->max_batch + 15) / 16 * 16;
+      for (size_t off : {plan.yh, plan.yl}) chk(zero(off, Bp * std::max(d, hq * hd) * dtype_bytes(wdt) / 4));
+      for (size_t off : {plan.oh, plan.ol}) chk(zero(off, Bp * hq * hd * dtype_bytes(wdt) / 4));
+      for (size_t off : {plan.hh, plan.hl}) chk(zero(off, Bp * ff * dtype_bytes(wdt) / 4));
+    }
     if (cfg->arch == WD_ARCH_WHISPER) {
       chk(cp("pos", plan.pos, wdt, cfg->context, d, 0));
       chk(vcopy("ln_f.g", plan.lnfg, d));
@@ -500,16 +663,16 @@ wd_status wd_load(const wd_config* cfg, const wd_tensor* weights, int32_t n_weig
       for (int i = 0; i < cfg->n_layers && e == hipSuccess; ++i) {
         const std::string p = "dec." + std::to_string(i) + ".";
         const LayerOff& L = plan.L[i];
-        chk(cp(p + "self.q.w", L.wqkv, wdt, d, d, 0));
-        chk(cp(p + "self.k.w", L.wqkv, wdt, d, d, d));
-        chk(cp(p + "self.v.w", L.wqkv, wdt, d, d, 2 * d));
-        chk(cp(p + "self.o.w", L.wo, wdt, d, d, 0));
-        chk(cp(p + "cross.q.w", L.wcq, wdt, d, d, 0));
-        chk(cp(p + "cross.k.w", L.wckv, wdt, d, d, 0));
+        chk(mat(p + "self.q.w", L.wqkv, d, d, 1, 0, 0));
+        chk(mat(p + "self.k.w", L.wqkv, d, d, 1, d / 16, d));
+        chk(mat(p + "self.v.w", L.wqkv, d, d, 1, 2 * d / 16, 2 * d));
+        chk(mat(p + "self.o.w", L.wo, d, d, 1, 0, 0));
+        chk(mat(p + "cross.q.w", L.wcq, d, d, 1, 0, 0));
+        chk(cp(p + "cross.k.w", L.wckv, wdt, d, d, 0));       // row-major: the cross-K/V GEMM reads rows
         chk(cp(p + "cross.v.w", L.wckv, wdt, d, d, d));
-        chk(cp(p + "cross.o.w", L.wco, wdt, d, d, 0));
-        chk(cp(p + "fc1.w", L.w1, wdt, ff, d, 0));
-        chk(cp(p + "fc2.w", L.w2, wdt, d, ff, 0));
+        chk(mat(p + "cross.o.w", L.wco, d, d, 1, 0, 0));
+        chk(mat(p + "fc1.w", L.w1, ff, d, 1, 0, 0));
+        chk(mat(p + "fc2.w", L.w2, d, ff, 1, 0, 0));
         chk(vcopy(p + "self.q.b", L.bqkv, d));
         chk(zero(L.bqkv + d * 4, d));                 // keys: no bias
         chk(vcopy(p + "self.v.b", L.bqkv + 2 * d * 4, d));
@@ -529,13 +692,14 @@ wd_status wd_load(const wd_config* cfg, const wd_tensor* weights, int32_t n_weig
       for (int i = 0; i < cfg->n_layers && e == hipSuccess; ++i) {
         const std::string p = "dec." + std::to_string(i) + ".";
         const LayerOff& L = plan.L[i];
-        chk(cp(p + "self.q.w", L.wqkv, wdt, hq * hd, d, 0));
-        chk(cp(p + "self.k.w", L.wqkv, wdt, hkv * hd, d, hq * hd));
-        chk(cp(p + "self.v.w", L.wqkv, wdt, hkv * hd, d, (hq + hkv) * hd));
-        chk(cp(p + "self.o.w", L.wo, wdt, d, hq * hd, 0));
-        chk(cp(p + "mlp.gate.w", L.wgu, wdt, ff, d, 0));
-        chk(cp(p + "mlp.up.w", L.wgu, wdt, ff, d, ff));
-        chk(cp(p + "mlp.down.w", L.wdn, wdt, d, ff, 0));
+        chk(mat(p + "self.q.w", L.wqkv, hq * hd, d, 1, 0, 0));
+        chk(mat(p + "self.k.w", L.wqkv, hkv * hd, d, 1, hq * hd / 16, hq * hd));
+        chk(mat(p + "self.v.w", L.wqkv, hkv * hd, d, 1, (hq + hkv) * hd / 16, (hq + hkv) * hd));
+        chk(mat(p + "self.o.w", L.wo, d, hq * hd, 1, 0, 0));
+        // gate and up: contiguous halves (fp32 path) or alternating 16-row blocks (MFMA path)
+        chk(mat(p + "mlp.gate.w", L.wgu, ff, d, 2, 0, 0));
+        chk(mat(p + "mlp.up.w", L.wgu, ff, d, 2, 1, ff));
+        chk(mat(p + "mlp.down.w", L.wdn, d, ff, 1, 0, 0));
         chk(vcopy(p + "norm1.g", L.n1g, d));
         chk(vcopy(p + "norm2.g", L.n2g, d));
         chk(vcopy(p + "q_norm.g", L.qn, hd));

@@ -81,6 +81,20 @@ __device__ __forceinline__ void unpack8(const Raw8<float>& r, float (&f)[8]) {
 __device__ __forceinline__ void unpack8(const Raw8<f16_t>& r, float (&f)[8]) { unpack_h8(r.v, f); }
 __device__ __forceinline__ void unpack8(const Raw8<bf16_t>& r, float (&f)[8]) { unpack_b8(r.v, f); }
 
+// fp32 -> (hi, lo) 16-bit pair with hi + lo ~= v to ~16 significant bits
+template <typename T>
+__device__ __forceinline__ void split_hi_lo(float v, T& hi, T& lo) {
+  hi = from_f<T>(v);
+  lo = from_f<T>(v - to_f(hi));
+}
+template <typename T>
+__device__ __forceinline__ void store_split(void* hi_base, void* lo_base, int64_t off, float v) {
+  T h, l;
+  split_hi_lo<T>(v, h, l);
+  reinterpret_cast<T*>(hi_base)[off] = h;
+  reinterpret_cast<T*>(lo_base)[off] = l;
+}
+
 // Butterfly sum / max over the 64 lanes of a wave (every lane gets the result).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

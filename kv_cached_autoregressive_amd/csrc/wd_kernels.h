@@ -23,9 +23,10 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 
 // ---- embedding ---------------------------------------------------------------------------
 // x[b] = ov ? ov[b*ov_stride ..] : E[tok[b*tok_stride]] + (P ? P[pos[b]] : 0); validates ranges.
+// E_frag: E is stored in fragment layout (rows padded to 16) rather than row-major.
 hipError_t launch_embed(float* x, const void* E, const void* P, int w_dtype, const int32_t* tok,
                         int tok_stride, const int32_t* pos, const void* ov, int64_t ov_stride,
-                        int B, int d, int V, int ctx, unsigned* err, hipStream_t s);
+                        int B, int d, int V, int ctx, unsigned* err, bool E_frag, hipStream_t s);
 
 // ---- row norm: LayerNorm (b != nullptr) or RMSNorm (b == nullptr) ----------------------
 hipError_t launch_norm(const float* x, float* y, const float* g, const float* b, int B, int d,
@@ -54,6 +55,44 @@ hipError_t launch_gemv(const GemvParams& p, hipStream_t s);
 hipError_t launch_argmax_final(const unsigned long long* amax, int nparts, int ldp, int B,
                                int32_t* out, hipStream_t s);
 
+// ---- MFMA skinny GEMM (16-bit weights) ------------------------------------------------------
+// Weights are stored in MFMA fragment order ("fragment layout"): for W [N, K] with N padded
+// to 16 and K % 32 == 0, element (n, k) sits at frag_offset(n, k, K).  One 16 x 32 tile is
+// 1 KB contiguous, in the order lane l holds row l%16, columns 8*(l/16)..+7 of the tile.
+// Activations feeding the MFMA GEMM use the same layout over [B_pad, K] and are split
+// into two 16-bit parts, hi = round(y), lo = round(y - hi), so the products keep ~16
+// mantissa bits of the fp32 activation.
+__host__ __device__ inline int64_t frag_offset(int64_t r, int64_t k, int64_t K) {
+  return ((((r >> 4) * (K >> 5) + (k >> 5)) * 64 + ((r & 15) | (((k >> 3) & 3) << 4))) << 3) + (k & 7);
+}
+
+enum Epi2 : int { EPI_GELU_SPLIT = 5, EPI_SWIGLU_SPLIT = 6 };
+
+struct MGemvParams {
+  const void* W; int w_dtype; int N; int K;   // W in fragment layout, rows padded to 16
+  const void* Yhi; const void* Ylo; int B;    // activations [B_pad, K] fragment layout
+  int epi;
+  const float* bias;
+  float* out; int ldo; float scale;           // STORE / RESID / QKV(q) / LOGITS targets
+  int d; int H; int hd; int ctx; const int32_t* pos;   // EPI_QKV (Whisper)
+  void* Kc; void* Vc; int cache_dtype; int64_t kv_bstride;
+  unsigned long long* amax; int ldp;          // EPI_LOGITS partial keys [blocks][ldp]
+  void* yo_hi; void* yo_lo;                   // GELU_SPLIT / SWIGLU_SPLIT output [B_pad, N or N/2]
+  unsigned* err;
+};
+// Number of argmax partials (blocks) a logits launch writes: upper bound over K, and exact for K.
+int mgemv_blocks(int N, int B);
+int mgemv_blocks_k(int N, int K, int B);
+hipError_t launch_mgemv(const MGemvParams& p, hipStream_t s);
+
+// Row norm writing the split fragment layout (MFMA consumers).
+hipError_t launch_norm_split(const float* x, void* y_hi, void* y_lo, int act_dtype, const float* g,
+                             const float* b, int B, int d, float eps, hipStream_t s);
+// Fragment-layout repack of a [rows, K] matrix into fused row blocks:
+// fused row of source row r = (r / 16) * blk_mul * 16 + blk_add * 16 + r % 16.
+hipError_t launch_pack_frag(const void* src, int src_dtype, void* dst, int dst_dtype, int64_t rows,
+                            int64_t K, int64_t blk_mul, int64_t blk_add, hipStream_t s);
+
 // ---- attention over a K/V cache --------------------------------------------------------------
 struct AttnParams {
   const float* q; int q_ld;                   // q [B, q_ld]; head h at h*hd, pre-scaled
@@ -62,7 +101,8 @@ struct AttnParams {
   const int32_t* pos; int n_rows_fixed;       // pos: rows 0..pos[b]; else n_rows_fixed rows
   int B; int Hq; int Hkv; int hd; int q_per_kvb;
   int split_rows; int n_splits;
-  float* out; int out_ld;                     // [B, out_ld] (head h at h*hd)
+  float* out; int out_ld;                     // [B, out_ld] (head h at h*hd), or:
+  void* o_hi; void* o_lo; int o_dtype;        // split fragment layout [B_pad, Hq*hd] if set
   float* part;                                // [B*Hq][n_splits][hd+2] when n_splits > 1
 };
 // main kernel (writes o directly when n_splits == 1, else partials) ...
