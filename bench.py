@@ -14,8 +14,8 @@ algorithmic HBM bytes per window (weights once per step + self-cache rows
 0..pos + cross cache once per encoder set) and their rate against the 8 TB/s
 peak are extra fields.  `roofline` reports the dominant kernel (the
 cross-attention) from HIP events recorded around its launches in one layer
-during the timed region; `cpu_baseline` times the CPU oracle on a bounded sample
-of the same workload.
+over a window run right after the timed ones; `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -156,13 +156,14 @@ def main():
             tok = prompt[p] if p < prompt.shape[0] else amax
             K.wd_step(ctx, tok.data_ptr(), pos_all[p].data_ptr(), B, 0, amax.data_ptr())
 
+    torch.cuda.synchronize()
+    torch.cuda.set_stream(stream)          # everything below is queued on the decoder's stream
     for _ in range(args.warmup):
         window()
     torch.cuda.synchronize()
     if dec.check() != 0:
         raise RuntimeError(dec.last_error())
 
-    K.wd_profile(ctx, K.K_CROSS_ATTN, args.profile_layer)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -178,10 +179,15 @@ def main():
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     xkv_ms = sum(starts[i].elapsed_time(mids[i]) for i in range(args.steps)) / args.steps
-    attn_ms, attn_n = K.wd_profile_read(ctx)
-    K.wd_profile(ctx, -1, -1)
     if dec.check() != 0:
         raise RuntimeError(dec.last_error())
+    # kernel timing: HIP events around every cross-attention launch of one layer, over a
+    # window of the same shape run right after (steps are launched one by one there,
+    # since a captured step replays without per-launch host hooks)
+    K.wd_profile(ctx, K.K_CROSS_ATTN, args.profile_layer)
+    window()
+    attn_ms, attn_n = K.wd_profile_read(ctx)
+    K.wd_profile(ctx, -1, -1)
 
     ms_window = total_ms / args.steps
     dec_ms = ms_window - xkv_ms

@@ -210,7 +210,9 @@ class Decoder:
         self.w = w
         self.cfg = config_from(w)
         self.device = torch.device(device)
-        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        # a stream of our own (default priority): the library captures each step into a
+        # HIP graph, which the legacy null stream does not allow
+        self.stream = stream if stream is not None else torch.cuda.Stream(self.device)
         nbytes = wd_workspace_bytes(self.cfg)
         if nbytes == 0:
             raise WdError(1, "invalid configuration")
@@ -240,8 +242,24 @@ class Decoder:
         except Exception:
             pass
 
+    # ordering against torch's current stream: a call waits for the work queued there
+    # before it, and work queued there after it waits for the call (no-ops when the
+    # caller already runs on self.stream)
+    def _enter(self):
+        import torch
+        cur = torch.cuda.current_stream(self.device)
+        if cur != self.stream:
+            self.stream.wait_stream(cur)
+        return cur
+
+    def _leave(self, cur):
+        if cur != self.stream:
+            cur.wait_stream(self.stream)
+
     def cross_kv(self, enc, frames: Optional[int] = None):
+        cur = self._enter()
         wd_cross_kv(self.ctx, enc.data_ptr(), enc.shape[1] if frames is None else frames)
+        self._leave(cur)
 
     def step(self, tokens, positions, logits=None, argmax=None):
         """tokens, positions: int32 device tensors [B].  Returns (logits, argmax)."""
@@ -249,8 +267,10 @@ class Decoder:
         B = tokens.shape[0]
         if argmax is None:
             argmax = torch.empty(B, dtype=torch.int32, device=self.device)
+        cur = self._enter()
         wd_step(self.ctx, tokens.data_ptr(), positions.data_ptr(), B,
                 logits.data_ptr() if logits is not None else 0, argmax.data_ptr())
+        self._leave(cur)
         return logits, argmax
 
     def prefill(self, tokens, embeds=None, offset: int = 0, logits=None, argmax=None):
@@ -259,12 +279,16 @@ class Decoder:
         if argmax is None:
             argmax = torch.empty(B, dtype=torch.int32, device=self.device)
         A = 0 if embeds is None else embeds.shape[1]
+        cur = self._enter()
         wd_prefill(self.ctx, tokens.data_ptr(), B, T, embeds.data_ptr() if embeds is not None else 0,
                    A, offset, logits.data_ptr() if logits is not None else 0, argmax.data_ptr())
+        self._leave(cur)
         return logits, argmax
 
     def reorder(self, beam_idx, n_rows: int):
+        cur = self._enter()
         wd_reorder(self.ctx, [int(i) for i in beam_idx], n_rows)
+        self._leave(cur)
 
     def check(self) -> int:
         return wd_check(self.ctx)

@@ -17,6 +17,7 @@
 // with the K/V cache append, and tied-head logits with per-block argmax keys.
 #include <algorithm>
 #include <cstdio>
+#include <type_traits>
 #include <cstdlib>
 
 #include "wd_common.h"
@@ -35,6 +36,14 @@ __device__ __forceinline__ mf32x4_t mma(const uint4& a, const uint4& b, const mf
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mf16x8_t, a), __builtin_bit_cast(mf16x8_t, b), c, 0, 0, 0);
 }
 
+typedef uint32_t mv4u __attribute__((ext_vector_type(4)));   // one 16-byte fragment slice
+__device__ __forceinline__ mf32x4_t mma(const mv4u& a, const mv4u& b, const mf32x4_t& c, bf16_t*) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8_t, a), __builtin_bit_cast(mbf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ mf32x4_t mma(const mv4u& a, const mv4u& b, const mf32x4_t& c, f16_t*) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mf16x8_t, a), __builtin_bit_cast(mf16x8_t, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float m_gelu(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
 __device__ __forceinline__ float m_silu(float z) { return z / (1.0f + expf(-z)); }
 
@@ -48,7 +57,7 @@ __device__ __forceinline__ void epi_one(const MGemvParams& p, int n, int b, floa
   const float bias = p.bias ? p.bias[n] : 0.f;
   switch (p.epi) {
     case EPI_STORE: p.out[(int64_t)b * p.ldo + n] = (v + bias) * p.scale; break;
-    case EPI_RESID: p.out[(int64_t)b * p.ldo + n] += v + bias; break;
+    case EPI_RESID: atomicAdd(&p.out[(int64_t)b * p.ldo + n], v + bias); break;  // sole writer: x + v exactly
     case EPI_GELU_SPLIT: store_split<T>(p.yo_hi, p.yo_lo, frag_offset(b, n, p.N), m_gelu(v + bias)); break;
     case EPI_QKV: {
       const int seg = n / p.d, c_all = n - seg * p.d;
@@ -69,6 +78,80 @@ __device__ __forceinline__ void epi_one(const MGemvParams& p, int n, int b, floa
     }
     default: break;
   }
+}
+
+// Epilogue on the accumulator tiles of one wave.  The activations were the MFMA A
+// operand, so tile (nb, bb) holds batch rows bb*16 + 4*(lane/16) + r along the
+// registers and output column (tile*NBW + nb)*16 + lane%16 along the lanes: stores
+// of one register index cover 16 consecutive outputs of 4 rows.  Only `active`
+// waves hold final sums; all threads of the workgroup must call it (the logits
+// path synchronises).  kmax: >= NBB*16 u64 of LDS.
+template <typename T, int NBW, int NBB, int NW>
+__device__ __forceinline__ void mg_epilogue(const MGemvParams& p, mf32x4_t (&acc)[NBW][NBB], bool active, int tile,
+                                            int NB, unsigned long long* kmax) {
+  const int lane = threadIdx.x & 63;
+  const int rsub = (lane >> 4) * 4, col = lane & 15;
+
+  if (p.epi == EPI_LOGITS) {
+    __syncthreads();   // the caller's LDS buffer (aliased by kmax) is no longer read
+    for (int i = threadIdx.x; i < NBB * 16; i += NW * 64) kmax[i] = 0ull;
+    __syncthreads();
+    if (active) {
+#pragma unroll
+      for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int b = bb * 16 + rsub + r;
+          unsigned long long best = 0ull;
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb) {
+            const int n = (tile * NBW + nb) * 16 + col;
+            if (n < p.N && b < p.B && tile * NBW + nb < NB) {
+              float v = acc[nb][bb][r];
+              if (p.out) p.out[(int64_t)b * p.ldo + n] = v;
+              if (v != v) { raise_err(p.err, ERR_NAN); v = -INFINITY; }
+              const unsigned long long k = argmax_key(v, n);
+              best = k > best ? k : best;
+            }
+          }
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) {   // the 16 lanes holding row b
+            const unsigned long long t = __shfl_xor(best, o, WAVE);
+            best = t > best ? t : best;
+          }
+          if (col == 0 && b < p.B) atomicMax(&kmax[b], best);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < p.B; i += NW * 64) p.amax[(int64_t)blockIdx.x * p.ldp + i] = kmax[i];
+    return;
+  }
+  if (!active) return;
+  if (p.epi == EPI_SWIGLU_SPLIT) {  // row blocks alternate gate, up for the same 16 outputs
+    const int half = p.N >> 1;
+#pragma unroll
+    for (int nb = 0; nb + 1 < NBW; nb += 2)
+#pragma unroll
+      for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = ((tile * NBW + nb) >> 1) * 16 + col;
+          const int b = bb * 16 + rsub + r;
+          if (j < half && b < p.B)
+            store_split<T>(p.yo_hi, p.yo_lo, frag_offset(b, j, half), m_silu(acc[nb][bb][r]) * acc[nb + 1][bb][r]);
+        }
+    return;
+  }
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = (tile * NBW + nb) * 16 + col;
+        const int b = bb * 16 + rsub + r;
+        if (n < p.N && b < p.B && tile * NBW + nb < NB) epi_one<T>(p, n, b, acc[nb][bb][r]);
+      }
 }
 
 constexpr int mg_waves(int KS) { return KS >= 4 ? KS : 4; }
@@ -130,8 +213,8 @@ __global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv(MGemvParams p) {
         for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
           for (int bb = 0; bb < NBB; ++bb) {
-            acc[nb][bb] = mma(wr[j][nb], hr[j][bb], acc[nb][bb], (T*)nullptr);
-            acc[nb][bb] = mma(wr[j][nb], lr[j][bb], acc[nb][bb], (T*)nullptr);
+            acc[nb][bb] = mma(hr[j][bb], wr[j][nb], acc[nb][bb], (T*)nullptr);
+            acc[nb][bb] = mma(lr[j][bb], wr[j][nb], acc[nb][bb], (T*)nullptr);
           }
       }
     }
@@ -159,69 +242,220 @@ __global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv(MGemvParams p) {
       }
     }
   }
-  const bool active = ks == 0;
-  // D fragment: lane holds rows 4*(lane/16)+r of column lane%16 of each 16x16 tile
-  const int rsub = (lane >> 4) * 4, col = lane & 15;
+  mg_epilogue<T, NBW, NBB, NW>(p, acc, ks == 0, tile, NB, kmax);
+}
 
-  if (p.epi == EPI_LOGITS) {
-    if constexpr (KS > 1) __syncthreads();   // the partial tiles in `red` have been read
-    for (int i = threadIdx.x; i < NBB * 16; i += NW * 64) kmax[i] = 0ull;
-    __syncthreads();
-    if (active) {
+// Latency-bound variant for the per-layer projections: a wave issues the loads of
+// its whole weight slice (at most MAXS K steps x NBW tiles) before the first MFMA,
+// so the HBM round trip is paid about once per wave instead of once per step; the
+// activation tiles (L2-resident) follow through a 3-deep register ring.
+template <typename T, int NBW, int NBB, int KS, int MAXS>
+__global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv_pf(MGemvParams p) {
+  constexpr int RT = KS >= 4 ? 1 : 4 / KS;
+  constexpr int NW = RT * KS;
+  constexpr int DY = 3;
+  constexpr int RED = KS > 1 ? NW * NBW * NBB * 256 : 0;
+  constexpr int LDSF = RED > NBB * 32 ? RED : NBB * 32;
+  __shared__ __align__(16) float red[LDSF];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rt = w % RT, ks = w / RT;
+  const int tile = blockIdx.x * RT + rt;
+  const int NB = (p.N + 15) >> 4;
+  const int KST = p.K >> 5;
+  const int s0 = (ks * KST) / KS, n = ((ks + 1) * KST) / KS - s0;   // n <= MAXS (host checks)
+  const mv4u* __restrict__ Wv = reinterpret_cast<const mv4u*>(p.W);
+  const mv4u* __restrict__ Yh = reinterpret_cast<const mv4u*>(p.Yhi);
+  const mv4u* __restrict__ Yl = reinterpret_cast<const mv4u*>(p.Ylo);
+
+  mv4u wr[MAXS][NBW];
 #pragma unroll
-      for (int bb = 0; bb < NBB; ++bb) {
-        const int b = bb * 16 + col;
-        unsigned long long best = 0ull;
+  for (int i = 0; i < MAXS; ++i)
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
+    for (int nb = 0; nb < NBW; ++nb)
+      if (i < n) wr[i][nb] = Wv[((int64_t)min(tile * NBW + nb, NB - 1) * KST + s0 + i) * 64 + lane];
+
+  mv4u hr[DY][NBB], lr[DY][NBB];
+  auto loadY = [&](int i, mv4u (&h)[NBB], mv4u (&l)[NBB]) __attribute__((always_inline)) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int n = (tile * NBW + nb) * 16 + rsub + r;
-            if (n < p.N && b < p.B && tile * NBW + nb < NB) {
-              float v = acc[nb][bb][r];
-              if (p.out) p.out[(int64_t)b * p.ldo + n] = v;
-              if (v != v) { raise_err(p.err, ERR_NAN); v = -INFINITY; }
-              const unsigned long long k = argmax_key(v, n);
-              best = k > best ? k : best;
-            }
-          }
-        unsigned long long o = __shfl_xor(best, 16, WAVE);
-        best = o > best ? o : best;
-        o = __shfl_xor(best, 32, WAVE);
-        best = o > best ? o : best;
-        if (lane < 16 && b < p.B) atomicMax(&kmax[b], best);
-      }
+    for (int bb = 0; bb < NBB; ++bb) {
+      const int64_t yi = ((int64_t)bb * KST + s0 + i) * 64 + lane;
+      h[bb] = Yh[yi];
+      l[bb] = Yl[yi];
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < p.B; i += NW * 64) p.amax[(int64_t)blockIdx.x * p.ldp + i] = kmax[i];
-    return;
-  }
-  if (!active) return;
-  if (p.epi == EPI_SWIGLU_SPLIT) {  // row blocks alternate gate, up for the same 16 outputs
-    const int half = p.N >> 1;
+  };
 #pragma unroll
-    for (int nb = 0; nb + 1 < NBW; nb += 2)
-#pragma unroll
-      for (int bb = 0; bb < NBB; ++bb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = ((tile * NBW + nb) >> 1) * 16 + rsub + r;
-          const int b = bb * 16 + col;
-          if (j < half && b < p.B)
-            store_split<T>(p.yo_hi, p.yo_lo, frag_offset(b, j, half), m_silu(acc[nb][bb][r]) * acc[nb + 1][bb][r]);
-        }
-    return;
-  }
+  for (int d = 0; d < DY - 1; ++d)
+    if (d < n) loadY(d, hr[d], lr[d]);
+
+  mf32x4_t acc[NBW][NBB];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-    for (int bb = 0; bb < NBB; ++bb)
+    for (int bb = 0; bb < NBB; ++bb) acc[nb][bb] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = (tile * NBW + nb) * 16 + rsub + r;
-        const int b = bb * 16 + col;
-        if (n < p.N && b < p.B && tile * NBW + nb < NB) epi_one<T>(p, n, b, acc[nb][bb][r]);
+  for (int i = 0; i < MAXS; ++i) {
+    if (i < n) {
+      if (i + DY - 1 < n) loadY(i + DY - 1, hr[(i + DY - 1) % DY], lr[(i + DY - 1) % DY]);
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int bb = 0; bb < NBB; ++bb) {
+          acc[nb][bb] = mma(hr[i % DY][bb], wr[i][nb], acc[nb][bb], (T*)nullptr);
+          acc[nb][bb] = mma(lr[i % DY][bb], wr[i][nb], acc[nb][bb], (T*)nullptr);
+        }
+    }
+  }
+
+  if constexpr (KS > 1) {
+    if (ks > 0) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[((w * NBW + nb) * NBB + bb) * 256 + r * 64 + lane] = acc[nb][bb][r];
+    }
+    __syncthreads();
+    if (ks == 0) {
+      for (int k2 = 1; k2 < KS; ++k2) {
+        const int w2 = rt + k2 * RT;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+          for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[nb][bb][r] += red[((w2 * NBW + nb) * NBB + bb) * 256 + r * 64 + lane];
       }
+    }
+  }
+  mg_epilogue<T, NBW, NBB, NW>(p, acc, ks == 0, tile, NB, reinterpret_cast<unsigned long long*>(red));
+}
+
+// Variant for B > 16: the RT waves of a K group share each K step's activation
+// fragments through LDS (loaded once per group, double-buffered, one barrier per
+// step), so activation traffic from L2 drops by RT; each wave streams only its own
+// weight tiles, DW steps ahead.  KS groups split K inside the workgroup and add
+// their partial tiles through LDS in fixed order.
+template <typename T, int NBW, int NBB, int KS, int RT>
+__global__ __launch_bounds__(64 * KS * RT) void k_mgemv_lds(MGemvParams p) {
+  constexpr int NW = KS * RT;
+  constexpr int FR = 2 * NBB;                 // activation tiles per K step (hi, lo per 16 rows)
+  constexpr int LPT = (FR + RT - 1) / RT;     // tile loads per thread of a group
+  constexpr int DY = 4, DW = 4;               // register lead of activation / weight loads
+  constexpr int YB = KS * 2 * FR * 64;        // mv4u of the double-buffered staging
+  constexpr int RB = (NW * NBW * NBB * 256 + 3) / 4;   // mv4u of the reduction buffer
+  constexpr int LB = YB > RB ? YB : RB;
+  __shared__ mv4u lds[LB > NBB * 8 ? LB : NBB * 8];   // staging, then reduction, then argmax keys
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rt = w % RT, ks = w / RT;
+  const int tg = rt * 64 + lane;              // thread index inside the K group
+  const int NB = (p.N + 15) >> 4;
+  const int KST = p.K >> 5;
+  const int s0 = (ks * KST) / KS, n = ((ks + 1) * KST) / KS - s0;
+  const int iters = (KST + KS - 1) / KS;      // uniform trip count over the workgroup
+  const mv4u* __restrict__ Wv = reinterpret_cast<const mv4u*>(p.W);
+  const mv4u* __restrict__ Yh = reinterpret_cast<const mv4u*>(p.Yhi);
+  const mv4u* __restrict__ Yl = reinterpret_cast<const mv4u*>(p.Ylo);
+  mv4u* ybuf = lds + (size_t)ks * 2 * FR * 64;
+
+  const int blk0 = blockIdx.x * RT * NBW + rt * NBW;
+  int64_t wbase[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) wbase[nb] = (int64_t)min(blk0 + nb, NB - 1) * KST * 64 + lane;
+
+  mf32x4_t acc[NBW][NBB];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int bb = 0; bb < NBB; ++bb) acc[nb][bb] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  mv4u yr[DY][LPT], wr[DW][NBW];
+  auto loadY = [&](int i, mv4u (&dst)[LPT]) __attribute__((always_inline)) {
+    const int st = s0 + i;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int flat = tg + j * RT * 64, f = flat >> 6;
+      if (f < FR) {
+        const int64_t gi = ((int64_t)(f >> 1) * KST + st) * 64 + (flat & 63);
+        const mv4u* src = (f & 1) ? Yl : Yh;
+        dst[j] = src[gi];
+      }
+    }
+  };
+  auto storeY = [&](int slot, const mv4u (&src)[LPT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int flat = tg + j * RT * 64;
+      if ((flat >> 6) < FR) ybuf[(size_t)slot * FR * 64 + flat] = src[j];
+    }
+  };
+  auto loadW = [&](int i, mv4u (&dst)[NBW]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) dst[nb] = Wv[wbase[nb] + (int64_t)(s0 + i) * 64];
+  };
+
+#pragma unroll
+  for (int d = 0; d < DY; ++d)
+    if (d < n) loadY(d, yr[d]);
+#pragma unroll
+  for (int d = 0; d < DW - 1; ++d)
+    if (d < n) loadW(d, wr[d]);
+  if (n > 0) storeY(0, yr[0]);
+
+  // one K step; U is a compile-time constant so every ring index is static
+  auto step = [&](int i, auto U) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;
+    __syncthreads();                        // step i's tiles visible; the other slot is free
+    if (i + 1 < n) storeY((u + 1) & 1, yr[(u + 1) % DY]);
+    if (i + DY < n) loadY(i + DY, yr[u % DY]);
+    if (i + DW - 1 < n) loadW(i + DW - 1, wr[(u + DW - 1) % DW]);
+    if (i < n) {
+      const mv4u* yb = ybuf + (size_t)(u & 1) * FR * 64;
+#pragma unroll
+      for (int bb = 0; bb < NBB; ++bb) {
+        const mv4u h = yb[(2 * bb) * 64 + lane];
+        const mv4u l = yb[(2 * bb + 1) * 64 + lane];
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+          acc[nb][bb] = mma(h, wr[u % DW][nb], acc[nb][bb], (T*)nullptr);
+          acc[nb][bb] = mma(l, wr[u % DW][nb], acc[nb][bb], (T*)nullptr);
+        }
+      }
+    }
+  };
+  for (int i0 = 0; i0 < iters; i0 += 4) {   // trip counts uniform over the workgroup
+    step(i0, std::integral_constant<int, 0>{});
+    if (i0 + 1 < iters) step(i0 + 1, std::integral_constant<int, 1>{});
+    if (i0 + 2 < iters) step(i0 + 2, std::integral_constant<int, 2>{});
+    if (i0 + 3 < iters) step(i0 + 3, std::integral_constant<int, 3>{});
+  }
+
+  float* red = reinterpret_cast<float*>(lds);
+  if constexpr (KS > 1) {
+    __syncthreads();  // staging no longer read
+    if (ks > 0) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[((w * NBW + nb) * NBB + bb) * 256 + r * 64 + lane] = acc[nb][bb][r];
+    }
+    __syncthreads();
+    if (ks == 0) {
+      for (int k2 = 1; k2 < KS; ++k2) {
+        const int w2 = rt + k2 * RT;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+          for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[nb][bb][r] += red[((w2 * NBW + nb) * NBB + bb) * 256 + r * 64 + lane];
+      }
+    }
+  }
+  __syncthreads();  // the buffer is reused for argmax keys
+  mg_epilogue<T, NBW, NBB, NW>(p, acc, ks == 0, blk0 / NBW, NB, reinterpret_cast<unsigned long long*>(lds));
 }
 
 struct MShape { int NBW, NBB, KS; };
@@ -267,17 +501,31 @@ static MShape mpick(int N, int K, int B, int epi) {
 }
 static int rows_per_block(const MShape& s) { return s.NBW * (s.KS >= 4 ? 1 : 4 / s.KS); }
 
-int mgemv_blocks(int N, int B) {
-  int most = 1;
-  for (int K : {32, 1024, 2048, 4096, 8192}) {  // the logits launch has K = d; cover any K
-    const MShape s = mpick(N, K, B, EPI_LOGITS);
-    most = std::max(most, ((N + 15) / 16 + rows_per_block(s) - 1) / rows_per_block(s));
+struct LShape { int NBW, KS, RT; };
+static LShape lpick(int N, int K, int epi);
+static int lds_blocks(const LShape& s, int N);
+// The LDS-shared variant pays off where many waves re-read the same activation
+// tiles: the large-N shapes (the tied head) at B > 16.
+static bool use_lds(int N, int NBB) {
+  static int force = -1;
+  static bool read = false;
+  if (!read) {
+    read = true;
+    if (const char* e = getenv("WD_MGEMV_LDS")) force = atoi(e) > 0 ? 1 : 0;
   }
-  return most;
+  if (force == 1 && getenv("WD_MGEMV_LDS")[0] != '0') return NBB > 1;
+  return NBB > 1 && (N + 15) / 16 >= 1024;
 }
 int mgemv_blocks_k(int N, int K, int B) {
   const MShape s = mpick(N, K, B, EPI_LOGITS);
+  if (use_lds(N, s.NBB)) return lds_blocks(lpick(N, K, EPI_LOGITS), N);
   return ((N + 15) / 16 + rows_per_block(s) - 1) / rows_per_block(s);
+}
+int mgemv_blocks(int N, int B) {
+  int most = 1;
+  for (int K : {32, 1024, 2048, 4096, 8192})  // the logits launch has K = d; cover any K
+    for (int b = 1; b <= B; b += 15) most = std::max(most, mgemv_blocks_k(N, K, std::min(b, B)));
+  return std::max(most, mgemv_blocks_k(N, 32, B));
 }
 
 constexpr int DEPTH = 3;
@@ -297,10 +545,82 @@ static hipError_t mrun_b(const MGemvParams& p, const MShape& s, hipStream_t st) 
   return hipErrorInvalidValue;
 }
 
+// Shapes of the LDS-shared variant (B > 16): NBW rows-blocks per wave, KS K groups,
+// RT waves sharing each group's activation tiles.
+static LShape lpick(int N, int K, int epi) {
+  static int ov[3] = {-1, -1, -1};
+  static bool read = false;
+  if (!read) {
+    read = true;
+    if (const char* e = getenv("WD_MGEMV_LDS"))
+      if (sscanf(e, "%d,%d,%d", &ov[0], &ov[1], &ov[2]) != 3) ov[0] = -1;
+  }
+  const int nblocks = (N + 15) / 16;
+  LShape s;
+  if (nblocks >= 1024) s = {2, 1, 4};
+  else if (nblocks >= 128 || epi == EPI_SWIGLU_SPLIT) s = {2, 4, 2};
+  else s = {1, 8, 2};
+  if (ov[0] > 0 && epi != EPI_LOGITS && !(epi == EPI_SWIGLU_SPLIT && ov[0] % 2)) s = {ov[0], ov[1], ov[2]};
+  (void)K;
+  return s;
+}
+static int lds_blocks(const LShape& s, int N) { return ((N + 15) / 16 + s.RT * s.NBW - 1) / (s.RT * s.NBW); }
+
+template <typename T, int NBB>
+static hipError_t lrun(const MGemvParams& p, const LShape& s, hipStream_t st) {
+  const int grid = lds_blocks(s, p.N);
+#define WD_ML(NBW_, KS_, RT_) \
+  if (s.NBW == NBW_ && s.KS == KS_ && s.RT == RT_) { \
+    k_mgemv_lds<T, NBW_, NBB, KS_, RT_><<<grid, 64 * KS_ * RT_, 0, st>>>(p); return hipGetLastError(); }
+  WD_ML(1, 4, 2) WD_ML(1, 8, 2) WD_ML(1, 2, 4) WD_ML(1, 4, 4)
+  WD_ML(2, 1, 4) WD_ML(2, 2, 4) WD_ML(2, 4, 2) WD_ML(2, 4, 4) WD_ML(2, 2, 2)
+#undef WD_ML
+  return hipErrorInvalidValue;
+}
+
+// Shape of the prefetch variant: NBW tiles per wave, K split into KS waves of at most
+// MAXS = 10 steps each (so a wave's weight slice fits in registers).
+static bool pf_pick(int N, int K, int B, int epi, MShape& s) {
+  static int mode = -1;
+  if (mode < 0) { const char* e = getenv("WD_MGEMV_PF"); mode = e ? atoi(e) : 1; }
+  const int nblocks = (N + 15) / 16, ksteps = K / 32;
+  if (!mode || nblocks >= 1024 || ksteps > 160) return false;
+  s.NBB = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
+  s.NBW = (nblocks >= 128 || epi == EPI_SWIGLU_SPLIT) ? 2 : 1;
+  const int ks = (ksteps + 9) / 10;
+  s.KS = ks <= 1 ? 1 : ks <= 2 ? 2 : ks <= 4 ? 4 : ks <= 8 ? 8 : 16;
+  if (s.KS == 16 && s.NBB * s.NBW >= 2) return false;  // 1024-thread groups: 128 VGPRs
+  return true;
+}
+
+template <typename T, int NBB>
+static hipError_t pfrun(const MGemvParams& p, const MShape& s, hipStream_t st) {
+  const int per = rows_per_block(s);
+  const int grid = ((p.N + 15) / 16 + per - 1) / per;
+  const int threads = 64 * (s.KS >= 4 ? s.KS : 4);
+#define WD_PF(NBW_, KS_) \
+  if (s.NBW == NBW_ && s.KS == KS_) { k_mgemv_pf<T, NBW_, NBB, KS_, 10><<<grid, threads, 0, st>>>(p); return hipGetLastError(); }
+  WD_PF(1, 1) WD_PF(1, 2) WD_PF(1, 4) WD_PF(1, 8) WD_PF(2, 1) WD_PF(2, 2) WD_PF(2, 4) WD_PF(2, 8)
+  if constexpr (NBB == 1) { WD_PF(1, 16) }
+#undef WD_PF
+  return hipErrorInvalidValue;
+}
+
 template <typename T>
 static hipError_t mrun(const MGemvParams& p, hipStream_t st) {
+  MShape pf;
+  if (p.epi != EPI_LOGITS && pf_pick(p.N, p.K, p.B, p.epi, pf)) {
+    if (pf.NBB == 1) return pfrun<T, 1>(p, pf, st);
+    if (pf.NBB == 2) return pfrun<T, 2>(p, pf, st);
+    return pfrun<T, 4>(p, pf, st);
+  }
   const MShape s = mpick(p.N, p.K, p.B, p.epi);
   if (s.NBB == 1) return mrun_b<T, 1>(p, s, st);
+  if (use_lds(p.N, s.NBB)) {
+    const LShape l = lpick(p.N, p.K, p.epi);
+    if (s.NBB == 2) return lrun<T, 2>(p, l, st);
+    return lrun<T, 4>(p, l, st);
+  }
   if (s.NBB == 2) return mrun_b<T, 2>(p, s, st);
   return mrun_b<T, 4>(p, s, st);
 }

@@ -185,6 +185,18 @@ Plan make_plan(const wd_config& c) {
 
 struct ProfPair { hipEvent_t a, b; };
 
+// A captured step: every launch of one wd_step call, replayed with hipGraphLaunch
+// while the call's device pointers, row count, current self cache and frame count
+// stay the same (the positions and tokens are read from device memory at run time).
+struct GraphKey {
+  const void* tok; const void* pos; void* logits; void* argmax; int B, cur, frames;
+  bool operator==(const GraphKey& o) const {
+    return tok == o.tok && pos == o.pos && logits == o.logits && argmax == o.argmax && B == o.B &&
+           cur == o.cur && frames == o.frames;
+  }
+};
+struct GraphEntry { GraphKey key; hipGraphExec_t exec; };
+
 }  // namespace
 
 struct wd_ctx {
@@ -196,6 +208,10 @@ struct wd_ctx {
   bool cross_ready = false;
   int frames = 0;
   std::string err;
+  // captured steps (small cache, oldest evicted first); off when WD_GRAPHS=0, while
+  // profiling, or on the legacy null stream
+  bool use_graphs = true;
+  std::vector<GraphEntry> graphs;
   // measurement
   int prof_kernel = -1, prof_layer = -1;
   std::vector<ProfPair> prof;
@@ -624,6 +640,7 @@ wd_status wd_load(const wd_config* cfg, const wd_tensor* weights, int32_t n_weig
     c->plan = plan;
     c->stream = reinterpret_cast<hipStream_t>(stream);
     c->ws = reinterpret_cast<char*>(workspace);
+    if (const char* g = getenv("WD_GRAPHS")) c->use_graphs = atoi(g) != 0;
     hipStream_t s = c->stream;
     const int wdt = cfg->w_dtype;
     auto T = [&](const std::string& nm) { return byname[nm]; };
@@ -762,7 +779,34 @@ wd_status wd_step(wd_ctx* ctx, const int32_t* tokens, const int32_t* positions, 
     if (!tokens || !positions || !argmax) return fail(ctx, WD_ERR_ARG, "wd_step: tokens, positions, argmax must not be null");
     const wd_status st = check_rows(ctx, B, "wd_step");
     if (st != WD_OK) return st;
-    return run_step(ctx, tokens, 1, positions, nullptr, 0, B, logits, argmax, true);
+    if (!ctx->use_graphs || ctx->prof_kernel >= 0 || ctx->stream == nullptr)
+      return run_step(ctx, tokens, 1, positions, nullptr, 0, B, logits, argmax, true);
+    const GraphKey key{tokens, positions, logits, argmax, B, ctx->cur, ctx->frames};
+    for (auto& e : ctx->graphs)
+      if (e.key == key) {
+        HIPCHK(ctx, hipGraphLaunch(e.exec, ctx->stream), "wd_step: graph launch");
+        return WD_OK;
+      }
+    HIPCHK(ctx, hipStreamBeginCapture(ctx->stream, hipStreamCaptureModeThreadLocal), "wd_step: begin capture");
+    const wd_status r = run_step(ctx, tokens, 1, positions, nullptr, 0, B, logits, argmax, true);
+    hipGraph_t graph = nullptr;
+    const hipError_t ec = hipStreamEndCapture(ctx->stream, &graph);
+    if (r != WD_OK) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return r;
+    }
+    if (ec != hipSuccess) return fail(ctx, WD_ERR_HIP, std::string("wd_step: end capture: ") + hipGetErrorString(ec));
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ei != hipSuccess) return fail(ctx, WD_ERR_HIP, std::string("wd_step: instantiate: ") + hipGetErrorString(ei));
+    if (ctx->graphs.size() >= 8) {
+      (void)hipGraphExecDestroy(ctx->graphs.front().exec);
+      ctx->graphs.erase(ctx->graphs.begin());
+    }
+    ctx->graphs.push_back({key, exec});
+    HIPCHK(ctx, hipGraphLaunch(exec, ctx->stream), "wd_step: graph launch");
+    return WD_OK;
   } catch (...) {
     return fail(ctx, WD_ERR_INTERNAL, "wd_step: internal error");
   }
@@ -845,6 +889,7 @@ const char* wd_last_error(const wd_ctx* ctx) {
 
 void wd_free(wd_ctx* ctx) {
   if (!ctx) return;
+  for (auto& e : ctx->graphs) (void)hipGraphExecDestroy(e.exec);
   for (auto& pr : ctx->prof) {
     (void)hipEventDestroy(pr.a);
     (void)hipEventDestroy(pr.b);
