@@ -156,6 +156,18 @@ __device__ __forceinline__ void mg_epilogue(const MGemvParams& p, mf32x4_t (&acc
 
 constexpr int mg_waves(int KS) { return KS >= 4 ? KS : 4; }
 
+// A wave's steps past its last one (the ring overruns by up to D-1) load the last
+// step again and multiply by zeroed weights: no load sits under a branch, so the
+// compiler's wait counts keep D-1 steps of loads in flight.
+__device__ __forceinline__ uint4 keep_if(const uint4& v, bool live) {
+  const uint32_t m = live ? 0xffffffffu : 0u;
+  return uint4{v.x & m, v.y & m, v.z & m, v.w & m};
+}
+__device__ __forceinline__ mv4u keep_if(const mv4u& v, bool live) {
+  const uint32_t m = live ? 0xffffffffu : 0u;
+  return v & m;
+}
+
 template <typename T, int NBW, int NBB, int KS, int D>
 __global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv(MGemvParams p) {
   constexpr int RT = KS >= 4 ? 1 : 4 / KS;   // row tiles per workgroup (>= 4 waves)
@@ -164,12 +176,13 @@ __global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv(MGemvParams p) {
   constexpr int LDSF = REDF > NBB * 32 ? REDF : NBB * 32;   // argmax keys reuse the buffer
   __shared__ __align__(16) float red[LDSF];
   unsigned long long* kmax = reinterpret_cast<unsigned long long*>(red);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rt = w % RT, ks = w / RT;
   const int tile = blockIdx.x * RT + rt;
   const int NB = (p.N + 15) >> 4;
   const int KST = p.K >> 5;
-  const int s0 = (ks * KST) / KS, s1 = ((ks + 1) * KST) / KS;
+  const int s0 = (ks * KST) / KS, n = ((ks + 1) * KST) / KS - s0;   // n >= 1 (host: KS <= K/32)
   const uint4* __restrict__ Wv = reinterpret_cast<const uint4*>(p.W);
   const uint4* __restrict__ Yh = reinterpret_cast<const uint4*>(p.Yhi);
   const uint4* __restrict__ Yl = reinterpret_cast<const uint4*>(p.Ylo);
@@ -186,8 +199,8 @@ __global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv(MGemvParams p) {
 
   // ring of D k-steps of fragments: loads run D-1 steps ahead of the MFMAs
   uint4 wr[D][NBW], hr[D][NBB], lr[D][NBB];
-  auto load = [&](int slot_unused, int st, uint4 (&wd)[NBW], uint4 (&hd)[NBB], uint4 (&ld)[NBB]) {
-    (void)slot_unused;
+  auto load = [&](int i, uint4 (&wd)[NBW], uint4 (&hd)[NBB], uint4 (&ld)[NBB]) __attribute__((always_inline)) {
+    const int st = s0 + min(i, n - 1);
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) wd[nb] = Wv[wbase[nb] + (int64_t)st * 64];
 #pragma unroll
@@ -198,24 +211,22 @@ __global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv(MGemvParams p) {
     }
   };
 #pragma unroll
-  for (int j = 0; j < D - 1; ++j)
-    if (s0 + j < s1) load(j, s0 + j, wr[j], hr[j], lr[j]);
-  for (int s = s0; s < s1; s += D) {
+  for (int j = 0; j < D - 1; ++j) load(j, wr[j], hr[j], lr[j]);
+  for (int i = 0; i < n; i += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
-      const int ss = s + j;
-      if (ss < s1) {
-        const int pre = ss + D - 1;
-        constexpr int dummy = 0;
-        (void)dummy;
-        if (pre < s1) load((j + D - 1) % D, pre, wr[(j + D - 1) % D], hr[(j + D - 1) % D], lr[(j + D - 1) % D]);
+      constexpr int dummy = 0;
+      (void)dummy;
+      load(i + j + D - 1, wr[(j + D - 1) % D], hr[(j + D - 1) % D], lr[(j + D - 1) % D]);
+      const bool live = i + j < n;
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
+      for (int nb = 0; nb < NBW; ++nb) {
+        const uint4 wv = keep_if(wr[j][nb], live);
 #pragma unroll
-          for (int bb = 0; bb < NBB; ++bb) {
-            acc[nb][bb] = mma(hr[j][bb], wr[j][nb], acc[nb][bb], (T*)nullptr);
-            acc[nb][bb] = mma(lr[j][bb], wr[j][nb], acc[nb][bb], (T*)nullptr);
-          }
+        for (int bb = 0; bb < NBB; ++bb) {
+          acc[nb][bb] = mma(hr[j][bb], wv, acc[nb][bb], (T*)nullptr);
+          acc[nb][bb] = mma(lr[j][bb], wv, acc[nb][bb], (T*)nullptr);
+        }
       }
     }
   }
@@ -246,10 +257,11 @@ __global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv(MGemvParams p) {
 }
 
 // Latency-bound variant for the per-layer projections: a wave issues the loads of
-// its whole weight slice (at most MAXS K steps x NBW tiles) before the first MFMA,
-// so the HBM round trip is paid about once per wave instead of once per step; the
-// activation tiles (L2-resident) follow through a 3-deep register ring.
-template <typename T, int NBW, int NBB, int KS, int MAXS>
+// its whole weight slice (NS K steps x NBW tiles, K = KS * NS * 32 exactly) before
+// the first MFMA, so the HBM round trip is paid about once per wave instead of
+// once per step; the activation tiles (L2-resident) follow through a 3-deep
+// register ring.  Straight-line code: every load stays in flight until its use.
+template <typename T, int NBW, int NBB, int KS, int NS>
 __global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv_pf(MGemvParams p) {
   constexpr int RT = KS >= 4 ? 1 : 4 / KS;
   constexpr int NW = RT * KS;
@@ -257,22 +269,23 @@ __global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv_pf(MGemvParams p) {
   constexpr int RED = KS > 1 ? NW * NBW * NBB * 256 : 0;
   constexpr int LDSF = RED > NBB * 32 ? RED : NBB * 32;
   __shared__ __align__(16) float red[LDSF];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rt = w % RT, ks = w / RT;
   const int tile = blockIdx.x * RT + rt;
   const int NB = (p.N + 15) >> 4;
-  const int KST = p.K >> 5;
-  const int s0 = (ks * KST) / KS, n = ((ks + 1) * KST) / KS - s0;   // n <= MAXS (host checks)
+  constexpr int KST = KS * NS;
+  const int s0 = ks * NS;
   const mv4u* __restrict__ Wv = reinterpret_cast<const mv4u*>(p.W);
   const mv4u* __restrict__ Yh = reinterpret_cast<const mv4u*>(p.Yhi);
   const mv4u* __restrict__ Yl = reinterpret_cast<const mv4u*>(p.Ylo);
 
-  mv4u wr[MAXS][NBW];
+  mv4u wr[NS][NBW];
 #pragma unroll
-  for (int i = 0; i < MAXS; ++i)
+  for (int i = 0; i < NS; ++i)
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb)
-      if (i < n) wr[i][nb] = Wv[((int64_t)min(tile * NBW + nb, NB - 1) * KST + s0 + i) * 64 + lane];
+      wr[i][nb] = Wv[((int64_t)min(tile * NBW + nb, NB - 1) * KST + s0 + i) * 64 + lane];
 
   mv4u hr[DY][NBB], lr[DY][NBB];
   auto loadY = [&](int i, mv4u (&h)[NBB], mv4u (&l)[NBB]) __attribute__((always_inline)) {
@@ -284,8 +297,7 @@ __global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv_pf(MGemvParams p) {
     }
   };
 #pragma unroll
-  for (int d = 0; d < DY - 1; ++d)
-    if (d < n) loadY(d, hr[d], lr[d]);
+  for (int d = 0; d < DY - 1 && d < NS; ++d) loadY(d, hr[d], lr[d]);
 
   mf32x4_t acc[NBW][NBB];
 #pragma unroll
@@ -293,17 +305,15 @@ __global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv_pf(MGemvParams p) {
 #pragma unroll
     for (int bb = 0; bb < NBB; ++bb) acc[nb][bb] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < MAXS; ++i) {
-    if (i < n) {
-      if (i + DY - 1 < n) loadY(i + DY - 1, hr[(i + DY - 1) % DY], lr[(i + DY - 1) % DY]);
+  for (int i = 0; i < NS; ++i) {
+    if (i + DY - 1 < NS) loadY(i + DY - 1, hr[(i + DY - 1) % DY], lr[(i + DY - 1) % DY]);
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
+    for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-        for (int bb = 0; bb < NBB; ++bb) {
-          acc[nb][bb] = mma(hr[i % DY][bb], wr[i][nb], acc[nb][bb], (T*)nullptr);
-          acc[nb][bb] = mma(lr[i % DY][bb], wr[i][nb], acc[nb][bb], (T*)nullptr);
-        }
-    }
+      for (int bb = 0; bb < NBB; ++bb) {
+        acc[nb][bb] = mma(hr[i % DY][bb], wr[i][nb], acc[nb][bb], (T*)nullptr);
+        acc[nb][bb] = mma(lr[i % DY][bb], wr[i][nb], acc[nb][bb], (T*)nullptr);
+      }
   }
 
   if constexpr (KS > 1) {
@@ -346,12 +356,13 @@ __global__ __launch_bounds__(64 * KS * RT) void k_mgemv_lds(MGemvParams p) {
   constexpr int RB = (NW * NBW * NBB * 256 + 3) / 4;   // mv4u of the reduction buffer
   constexpr int LB = YB > RB ? YB : RB;
   __shared__ mv4u lds[LB > NBB * 8 ? LB : NBB * 8];   // staging, then reduction, then argmax keys
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rt = w % RT, ks = w / RT;
   const int tg = rt * 64 + lane;              // thread index inside the K group
   const int NB = (p.N + 15) >> 4;
   const int KST = p.K >> 5;
-  const int s0 = (ks * KST) / KS, n = ((ks + 1) * KST) / KS - s0;
+  const int s0 = (ks * KST) / KS, n = ((ks + 1) * KST) / KS - s0;   // n >= 1 (host: KS <= K/32)
   const int iters = (KST + KS - 1) / KS;      // uniform trip count over the workgroup
   const mv4u* __restrict__ Wv = reinterpret_cast<const mv4u*>(p.W);
   const mv4u* __restrict__ Yh = reinterpret_cast<const mv4u*>(p.Yhi);
@@ -369,65 +380,64 @@ __global__ __launch_bounds__(64 * KS * RT) void k_mgemv_lds(MGemvParams p) {
 #pragma unroll
     for (int bb = 0; bb < NBB; ++bb) acc[nb][bb] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Steps past a group's last one reload its last step (and its MFMAs see zeroed
+  // weights): no global load sits under a branch, so the wait counts stay exact.
   mv4u yr[DY][LPT], wr[DW][NBW];
   auto loadY = [&](int i, mv4u (&dst)[LPT]) __attribute__((always_inline)) {
-    const int st = s0 + i;
+    const int st = s0 + min(i, n - 1);
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
-      const int flat = tg + j * RT * 64, f = flat >> 6;
-      if (f < FR) {
-        const int64_t gi = ((int64_t)(f >> 1) * KST + st) * 64 + (flat & 63);
-        const mv4u* src = (f & 1) ? Yl : Yh;
-        dst[j] = src[gi];
-      }
+      const int flat = tg + j * RT * 64, f = min(flat >> 6, FR - 1);
+      const int64_t gi = ((int64_t)(f >> 1) * KST + st) * 64 + (flat & 63);
+      const mv4u* src = (f & 1) ? Yl : Yh;
+      dst[j] = src[gi];
     }
   };
   auto storeY = [&](int slot, const mv4u (&src)[LPT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
       const int flat = tg + j * RT * 64;
-      if ((flat >> 6) < FR) ybuf[(size_t)slot * FR * 64 + flat] = src[j];
+      if (FR % RT == 0 || (flat >> 6) < FR) ybuf[(size_t)slot * FR * 64 + flat] = src[j];
     }
   };
   auto loadW = [&](int i, mv4u (&dst)[NBW]) __attribute__((always_inline)) {
+    const int st = s0 + min(i, n - 1);
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) dst[nb] = Wv[wbase[nb] + (int64_t)(s0 + i) * 64];
+    for (int nb = 0; nb < NBW; ++nb) dst[nb] = Wv[wbase[nb] + (int64_t)st * 64];
   };
 
 #pragma unroll
-  for (int d = 0; d < DY; ++d)
-    if (d < n) loadY(d, yr[d]);
+  for (int d = 0; d < DY; ++d) loadY(d, yr[d]);
 #pragma unroll
-  for (int d = 0; d < DW - 1; ++d)
-    if (d < n) loadW(d, wr[d]);
-  if (n > 0) storeY(0, yr[0]);
+  for (int d = 0; d < DW - 1; ++d) loadW(d, wr[d]);
+  storeY(0, yr[0]);
 
   // one K step; U is a compile-time constant so every ring index is static
   auto step = [&](int i, auto U) __attribute__((always_inline)) {
     constexpr int u = decltype(U)::value;
     __syncthreads();                        // step i's tiles visible; the other slot is free
-    if (i + 1 < n) storeY((u + 1) & 1, yr[(u + 1) % DY]);
-    if (i + DY < n) loadY(i + DY, yr[u % DY]);
-    if (i + DW - 1 < n) loadW(i + DW - 1, wr[(u + DW - 1) % DW]);
-    if (i < n) {
-      const mv4u* yb = ybuf + (size_t)(u & 1) * FR * 64;
+    storeY((u + 1) & 1, yr[(u + 1) % DY]);
+    loadY(i + DY, yr[u % DY]);
+    loadW(i + DW - 1, wr[(u + DW - 1) % DW]);
+    const bool live = i < n;
+    const mv4u* yb = ybuf + (size_t)(u & 1) * FR * 64;
 #pragma unroll
-      for (int bb = 0; bb < NBB; ++bb) {
-        const mv4u h = yb[(2 * bb) * 64 + lane];
-        const mv4u l = yb[(2 * bb + 1) * 64 + lane];
+    for (int bb = 0; bb < NBB; ++bb) {
+      const mv4u h = yb[(2 * bb) * 64 + lane];
+      const mv4u l = yb[(2 * bb + 1) * 64 + lane];
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-          acc[nb][bb] = mma(h, wr[u % DW][nb], acc[nb][bb], (T*)nullptr);
-          acc[nb][bb] = mma(l, wr[u % DW][nb], acc[nb][bb], (T*)nullptr);
-        }
+      for (int nb = 0; nb < NBW; ++nb) {
+        const mv4u wv = keep_if(wr[u % DW][nb], live);
+        acc[nb][bb] = mma(h, wv, acc[nb][bb], (T*)nullptr);
+        acc[nb][bb] = mma(l, wv, acc[nb][bb], (T*)nullptr);
       }
     }
   };
   for (int i0 = 0; i0 < iters; i0 += 4) {   // trip counts uniform over the workgroup
     step(i0, std::integral_constant<int, 0>{});
-    if (i0 + 1 < iters) step(i0 + 1, std::integral_constant<int, 1>{});
-    if (i0 + 2 < iters) step(i0 + 2, std::integral_constant<int, 2>{});
-    if (i0 + 3 < iters) step(i0 + 3, std::integral_constant<int, 3>{});
+    step(i0 + 1, std::integral_constant<int, 1>{});
+    step(i0 + 2, std::integral_constant<int, 2>{});
+    step(i0 + 3, std::integral_constant<int, 3>{});
   }
 
   float* red = reinterpret_cast<float*>(lds);
@@ -456,6 +466,177 @@ __global__ __launch_bounds__(64 * KS * RT) void k_mgemv_lds(MGemvParams p) {
   }
   __syncthreads();  // the buffer is reused for argmax keys
   mg_epilogue<T, NBW, NBB, NW>(p, acc, ks == 0, blk0 / NBW, NB, reinterpret_cast<unsigned long long*>(lds));
+}
+
+// Split-K variant for B > 16.  At 32..64 rows the activations of a K step (hi + lo, 2-8 KB)
+// outweigh its weight tile, so the kernel is shaped around reading them as rarely as possible:
+// a workgroup of NWV waves owns NWV*NBW 16-row tiles (64..128 outputs) and one of G groups of
+// K steps; per chunk of NSC steps it stages the activations once in LDS (every thread issues
+// its loads up front) and holds the chunk's weight tiles in registers; each wave then runs its
+// MFMAs from LDS.  With G > 1 the K groups write fp32 partials part[g][b][n] that the consumer
+// adds in order (the next norm for a residual, else launch_mgemv_finish); with G == 1 the
+// usual epilogue runs here.
+template <typename T, int NBW, int NBB, int NSC, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_mgemv_sk(MGemvParams p) {
+  constexpr int YT = NBB * 2 * NSC;                      // activation tiles of one chunk
+  constexpr int PER = (YT * 64 + 64 * NWV - 1) / (64 * NWV);
+  __shared__ mv4u ys[YT * 64 > NBB * 8 ? YT * 64 : NBB * 8];   // also the argmax keys
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int NB = (p.N + 15) >> 4;
+  const int KST = p.K >> 5;
+  const int g = blockIdx.y, G = gridDim.y;
+  const int s_lo = (g * KST) / G, s_hi = ((g + 1) * KST) / G;   // >= 1 step (host: G <= KST)
+  const int tile = blockIdx.x * NWV + w;                        // this wave's group of NBW tiles
+  const mv4u* __restrict__ Wv = reinterpret_cast<const mv4u*>(p.W);
+  const mv4u* __restrict__ Yh = reinterpret_cast<const mv4u*>(p.Yhi);
+  const mv4u* __restrict__ Yl = reinterpret_cast<const mv4u*>(p.Ylo);
+  int64_t wbase[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) wbase[nb] = (int64_t)min(tile * NBW + nb, NB - 1) * KST * 64 + lane;
+
+  mf32x4_t acc[NBW][NBB];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int bb = 0; bb < NBB; ++bb) acc[nb][bb] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = s_lo; c0 < s_hi; c0 += NSC) {   // uniform over the workgroup
+    const int nst = min(NSC, s_hi - c0);
+    // the chunk's weight tiles, then its activation tiles (steps past the chunk reload its
+    // last step; their MFMAs see zeroed weights), all issued before the first wait
+    mv4u wr[NSC][NBW];
+#pragma unroll
+    for (int i = 0; i < NSC; ++i)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) wr[i][nb] = Wv[wbase[nb] + (int64_t)(c0 + min(i, nst - 1)) * 64];
+    mv4u tmp[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int flat = threadIdx.x + j * 64 * NWV;
+      const int t = min(flat >> 6, YT - 1);
+      const int bb = t / (2 * NSC), part = (t / NSC) & 1, i = t % NSC;
+      const mv4u* src = part ? Yl : Yh;
+      tmp[j] = src[((int64_t)bb * KST + c0 + min(i, nst - 1)) * 64 + (flat & 63)];
+    }
+    if (c0 != s_lo) __syncthreads();   // the previous chunk's LDS reads are done
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int flat = threadIdx.x + j * 64 * NWV;
+      if ((YT * 64) % (64 * NWV) == 0 || flat < YT * 64) ys[flat] = tmp[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) {
+      const bool live = i < nst;
+#pragma unroll
+      for (int bb = 0; bb < NBB; ++bb) {
+        const mv4u h = ys[((bb * 2 + 0) * NSC + i) * 64 + lane];
+        const mv4u l = ys[((bb * 2 + 1) * NSC + i) * 64 + lane];
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+          const mv4u wv = keep_if(wr[i][nb], live);
+          acc[nb][bb] = mma(h, wv, acc[nb][bb], (T*)nullptr);
+          acc[nb][bb] = mma(l, wv, acc[nb][bb], (T*)nullptr);
+        }
+      }
+    }
+  }
+  if (G == 1) {
+    __syncthreads();   // the staging buffer is reused for argmax keys
+    mg_epilogue<T, NBW, NBB, NWV>(p, acc, true, tile, NB, reinterpret_cast<unsigned long long*>(ys));
+    return;
+  }
+  const int rsub = (lane >> 4) * 4, col = lane & 15;
+  float* P = p.part + (int64_t)g * p.B * p.N;
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = (tile * NBW + nb) * 16 + col, b = bb * 16 + rsub + r;
+        if (n < p.N && b < p.B && tile * NBW + nb < NB) P[(int64_t)b * p.N + n] = acc[nb][bb][r];
+      }
+}
+
+// Sum of the G partials of each output (in order), then the launch's epilogue.
+template <typename T, int GMAX>
+__global__ __launch_bounds__(256) void k_mgemv_finish(MGemvParams p, int G) {
+  const bool swiglu = p.epi == EPI_SWIGLU_SPLIT;
+  const int cols = swiglu ? p.N >> 1 : p.N;
+  const int64_t total = (int64_t)p.B * cols, slab = (int64_t)p.B * p.N;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int b = (int)(e / cols), j = (int)(e - (int64_t)b * cols);
+    if (swiglu) {   // gate and up of output j sit in consecutive 16-row blocks
+      const int ng = (j >> 4) * 32 + (j & 15);
+      const float* P = p.part + (int64_t)b * p.N + ng;
+      const float vg = sum_parts<GMAX>(P, slab, G), vu = sum_parts<GMAX>(P + 16, slab, G);
+      store_split<T>(p.yo_hi, p.yo_lo, frag_offset(b, j, cols), m_silu(vg) * vu);
+    } else {
+      epi_one<T>(p, j, b, sum_parts<GMAX>(p.part + (int64_t)b * p.N + j, slab, G));
+    }
+  }
+}
+
+struct SkShape { int NBW, NBB, G; };
+// Split-K shape: 4 waves per workgroup, NBW = 2 (128 outputs) for the wide or deep
+// projections, and enough K groups for ~240 workgroups with at least 2 K steps each.
+// Tuning overrides: WD_MGEMV_SK=0 disables the variant; WD_MGEMV_SKG=<G> forces G.
+static bool sk_pick(int N, int K, int B, int epi, SkShape& s) {
+  static int mode = -1, forceg = 0;
+  if (mode < 0) {
+    const char* e = getenv("WD_MGEMV_SK");
+    mode = e ? atoi(e) : 1;
+    const char* f = getenv("WD_MGEMV_SKG");
+    forceg = f ? atoi(f) : 0;
+  }
+  if (!mode || B <= 16 || epi == EPI_LOGITS) return false;
+  const int NB = (N + 15) / 16, KST = K / 32;
+  s.NBB = B <= 32 ? 2 : 4;
+  s.NBW = (NB >= 256 || KST >= 128 || epi == EPI_SWIGLU_SPLIT) ? 2 : 1;
+  const int ncg = (NB + 4 * s.NBW - 1) / (4 * s.NBW);
+  int G = forceg > 0 ? forceg : (240 + ncg / 2) / ncg;
+  G = std::max(1, std::min({G, std::max(1, KST / 2), 32}));   // the consumers add at most 32
+  s.G = G;
+  return true;
+}
+int mgemv_groups(int N, int K, int B, int epi) {
+  SkShape s;
+  return sk_pick(N, K, B, epi, s) ? s.G : 1;
+}
+
+template <typename T>
+static hipError_t skrun(const MGemvParams& p, const SkShape& s, hipStream_t st) {
+  const int NB = (p.N + 15) / 16;
+  dim3 grid((NB + 4 * s.NBW - 1) / (4 * s.NBW), s.G);
+  if (s.G > 1 && (!p.part || (int64_t)s.G * p.B * p.N > p.part_cap)) return hipErrorInvalidValue;
+#define WD_SK(NBW_, NBB_)                                                   \
+  if (s.NBW == NBW_ && s.NBB == NBB_) {                                     \
+    k_mgemv_sk<T, NBW_, NBB_, 8, 4><<<grid, 256, 0, st>>>(p);               \
+    return hipGetLastError();                                               \
+  }
+  WD_SK(1, 2) WD_SK(2, 2) WD_SK(1, 4) WD_SK(2, 4)
+#undef WD_SK
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_mgemv_finish(const MGemvParams& p, int G, hipStream_t s) {
+  if (G < 1 || !p.part || p.B <= 0 || p.N <= 0 || (int64_t)G * p.B * p.N > p.part_cap) return hipErrorInvalidValue;
+  if (p.epi == EPI_LOGITS) return hipErrorInvalidValue;
+  if (G > 32) return hipErrorInvalidValue;
+  const int64_t total = (int64_t)p.B * p.N;
+  const int blocks = (int)std::min<int64_t>((total + 255) / 256, 4096);
+#define WD_FIN(T_)                                                                                \
+  if (G <= 4) k_mgemv_finish<T_, 4><<<blocks, 256, 0, s>>>(p, G);                                 \
+  else if (G <= 8) k_mgemv_finish<T_, 8><<<blocks, 256, 0, s>>>(p, G);                            \
+  else if (G <= 16) k_mgemv_finish<T_, 16><<<blocks, 256, 0, s>>>(p, G);                          \
+  else k_mgemv_finish<T_, 32><<<blocks, 256, 0, s>>>(p, G);
+  if (p.w_dtype == DT_BF16) { WD_FIN(bf16_t) }
+  else if (p.w_dtype == DT_F16) { WD_FIN(f16_t) }
+  else return hipErrorInvalidValue;
+#undef WD_FIN
+  return hipGetLastError();
 }
 
 struct MShape { int NBW, NBB, KS; };
@@ -497,6 +678,7 @@ static MShape mpick(int N, int K, int B, int epi) {
     MShape o = s;
     if (shape_override(o) && !(epi == EPI_SWIGLU_SPLIT && o.NBW % 2)) s = o;
   }
+  if (s.KS > ksteps) { s.NBW = 2; s.KS = 1; }   // every wave needs at least one K step
   return s;
 }
 static int rows_per_block(const MShape& s) { return s.NBW * (s.KS >= 4 ? 1 : 4 / s.KS); }
@@ -561,7 +743,7 @@ static LShape lpick(int N, int K, int epi) {
   else if (nblocks >= 128 || epi == EPI_SWIGLU_SPLIT) s = {2, 4, 2};
   else s = {1, 8, 2};
   if (ov[0] > 0 && epi != EPI_LOGITS && !(epi == EPI_SWIGLU_SPLIT && ov[0] % 2)) s = {ov[0], ov[1], ov[2]};
-  (void)K;
+  if (s.KS > K / 32) s = {2, 1, 4};   // every K group needs at least one step
   return s;
 }
 static int lds_blocks(const LShape& s, int N) { return ((N + 15) / 16 + s.RT * s.NBW - 1) / (s.RT * s.NBW); }
@@ -572,46 +754,63 @@ static hipError_t lrun(const MGemvParams& p, const LShape& s, hipStream_t st) {
 #define WD_ML(NBW_, KS_, RT_) \
   if (s.NBW == NBW_ && s.KS == KS_ && s.RT == RT_) { \
     k_mgemv_lds<T, NBW_, NBB, KS_, RT_><<<grid, 64 * KS_ * RT_, 0, st>>>(p); return hipGetLastError(); }
-  WD_ML(1, 4, 2) WD_ML(1, 8, 2) WD_ML(1, 2, 4) WD_ML(1, 4, 4)
+  WD_ML(1, 4, 2) WD_ML(1, 2, 4) WD_ML(1, 4, 4)
+  if constexpr (NBB < 4) { WD_ML(1, 8, 2) }   // 1024 threads x 64-wide tiles would spill
   WD_ML(2, 1, 4) WD_ML(2, 2, 4) WD_ML(2, 4, 2) WD_ML(2, 4, 4) WD_ML(2, 2, 2)
 #undef WD_ML
   return hipErrorInvalidValue;
 }
 
-// Shape of the prefetch variant: NBW tiles per wave, K split into KS waves of at most
-// MAXS = 10 steps each (so a wave's weight slice fits in registers).
-static bool pf_pick(int N, int K, int B, int epi, MShape& s) {
+// Shape of the prefetch variant: NBW tiles per wave and K = KS waves x NS steps
+// exactly, NS <= 12 so a wave's weight slice fits in registers.  Shapes without
+// an exact split (or B in 17..32) take the ring kernel.
+struct PShape { int NBW, NBB, KS, NS; };
+static bool pf_pick(int N, int K, int B, int epi, PShape& s) {
   static int mode = -1;
   if (mode < 0) { const char* e = getenv("WD_MGEMV_PF"); mode = e ? atoi(e) : 1; }
-  const int nblocks = (N + 15) / 16, ksteps = K / 32;
-  if (!mode || nblocks >= 1024 || ksteps > 160) return false;
+  const int nblocks = (N + 15) / 16, kst = K / 32;
+  if (!mode || nblocks >= 1024) return false;
   s.NBB = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
+  if (s.NBB == 2) return false;
   s.NBW = (nblocks >= 128 || epi == EPI_SWIGLU_SPLIT) ? 2 : 1;
-  const int ks = (ksteps + 9) / 10;
-  s.KS = ks <= 1 ? 1 : ks <= 2 ? 2 : ks <= 4 ? 4 : ks <= 8 ? 8 : 16;
-  if (s.KS == 16 && s.NBB * s.NBW >= 2) return false;  // 1024-thread groups: 128 VGPRs
-  return true;
+  static const int split[][3] = {{12, 2, 6},  {16, 2, 8},  {24, 4, 6},   {32, 4, 8},    {40, 4, 10},   {48, 8, 6},
+                                 {64, 8, 8},  {80, 8, 10}, {96, 16, 6}, {128, 16, 8}, {160, 16, 10}, {192, 16, 12}};
+  for (const auto& t : split)
+    if (t[0] == kst) {
+      s.KS = t[1];
+      s.NS = t[2];
+      return !(s.KS == 16 && s.NBB * s.NBW >= 2);   // 1024-thread groups: 128 VGPRs
+    }
+  return false;
 }
 
 template <typename T, int NBB>
-static hipError_t pfrun(const MGemvParams& p, const MShape& s, hipStream_t st) {
-  const int per = rows_per_block(s);
+static hipError_t pfrun(const MGemvParams& p, const PShape& s, hipStream_t st) {
+  const int per = s.NBW * (s.KS >= 4 ? 1 : 4 / s.KS);
   const int grid = ((p.N + 15) / 16 + per - 1) / per;
   const int threads = 64 * (s.KS >= 4 ? s.KS : 4);
-#define WD_PF(NBW_, KS_) \
-  if (s.NBW == NBW_ && s.KS == KS_) { k_mgemv_pf<T, NBW_, NBB, KS_, 10><<<grid, threads, 0, st>>>(p); return hipGetLastError(); }
-  WD_PF(1, 1) WD_PF(1, 2) WD_PF(1, 4) WD_PF(1, 8) WD_PF(2, 1) WD_PF(2, 2) WD_PF(2, 4) WD_PF(2, 8)
-  if constexpr (NBB == 1) { WD_PF(1, 16) }
+#define WD_PF(NBW_, KS_, NS_)                                                              \
+  if (s.NBW == NBW_ && s.KS == KS_ && s.NS == NS_) {                                       \
+    k_mgemv_pf<T, NBW_, NBB, KS_, NS_><<<grid, threads, 0, st>>>(p);                       \
+    return hipGetLastError();                                                              \
+  }
+#define WD_PF_ALL(NBW_) \
+  WD_PF(NBW_, 2, 6) WD_PF(NBW_, 2, 8) WD_PF(NBW_, 4, 6) WD_PF(NBW_, 4, 8) WD_PF(NBW_, 4, 10) \
+  WD_PF(NBW_, 8, 6) WD_PF(NBW_, 8, 8) WD_PF(NBW_, 8, 10)
+  WD_PF_ALL(1) WD_PF_ALL(2)
+  if constexpr (NBB == 1) { WD_PF(1, 16, 6) WD_PF(1, 16, 8) WD_PF(1, 16, 10) WD_PF(1, 16, 12) }
+#undef WD_PF_ALL
 #undef WD_PF
   return hipErrorInvalidValue;
 }
 
 template <typename T>
 static hipError_t mrun(const MGemvParams& p, hipStream_t st) {
-  MShape pf;
+  SkShape sk;
+  if (sk_pick(p.N, p.K, p.B, p.epi, sk)) return skrun<T>(p, sk, st);
+  PShape pf;
   if (p.epi != EPI_LOGITS && pf_pick(p.N, p.K, p.B, p.epi, pf)) {
     if (pf.NBB == 1) return pfrun<T, 1>(p, pf, st);
-    if (pf.NBB == 2) return pfrun<T, 2>(p, pf, st);
     return pfrun<T, 4>(p, pf, st);
   }
   const MShape s = mpick(p.N, p.K, p.B, p.epi);

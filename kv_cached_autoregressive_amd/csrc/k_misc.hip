@@ -120,6 +120,7 @@ hipError_t launch_embed(float* x, const void* E, const void* P, int w_dtype, con
 // ------------------------------------------------------------------------------------------
 constexpr int NORM_MAXE = 16;  // d <= 4096
 
+// One block per row.
 template <typename OT, bool SPLIT>
 __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, float* __restrict__ y,
                                               OT* __restrict__ yh, OT* __restrict__ yl,
@@ -162,6 +163,61 @@ __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, float
   }
 }
 
+// Norm of x + pbias + sum_g part[g][row][:] (the G partial slabs of a split-K residual
+// projection, added in order g = 0..G-1); the new x is written back.  1024 threads per row,
+// at most PE elements each, so each thread has all of its PE * GMAX partial loads in flight.
+template <typename OT, int PE, int GMAX>
+__global__ __launch_bounds__(1024) void k_norm_part(float* __restrict__ x, OT* __restrict__ yh, OT* __restrict__ yl,
+                                                    const float* __restrict__ g, const float* __restrict__ bvec,
+                                                    int d, float eps, const float* __restrict__ part, int G, int B,
+                                                    const float* __restrict__ pbias) {
+  __shared__ float red[16];
+  const int row = blockIdx.x, t = threadIdx.x;
+  float* xr = x + (int64_t)row * d;
+  float v[PE];
+#pragma unroll
+  for (int j = 0; j < PE; ++j) {
+    const int i = min(t + j * 1024, d - 1);
+    v[j] = xr[i] + (pbias ? pbias[i] : 0.f) + sum_parts<GMAX>(part + (int64_t)row * d + i, (int64_t)B * d, G);
+  }
+  float s1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < PE; ++j)
+    if (t + j * 1024 < d) {
+      xr[t + j * 1024] = v[j];
+      s1 += v[j];
+    }
+  float mean = 0.f;
+  if (bvec) mean = block_sum<1024>(s1, red) / (float)d;
+  float s2 = 0.f;
+#pragma unroll
+  for (int j = 0; j < PE; ++j) {
+    const float c = t + j * 1024 < d ? v[j] - mean : 0.f;
+    s2 += c * c;
+  }
+  const float rs = 1.0f / sqrtf(block_sum<1024>(s2, red) / (float)d + eps);
+#pragma unroll
+  for (int j = 0; j < PE; ++j) {
+    const int i = t + j * 1024;
+    if (i < d) store_split<OT>(yh, yl, frag_offset(row, i, d), (v[j] - mean) * rs * g[i] + (bvec ? bvec[i] : 0.f));
+  }
+}
+
+template <typename OT>
+static hipError_t norm_part(float* x, void* yh, void* yl, const float* g, const float* b, int B, int d, float eps,
+                            const float* part, int G, const float* pbias, hipStream_t s) {
+  if (G > 32 || d > 4096) return hipErrorInvalidValue;
+#define WD_NP(PE_, GM_) \
+  k_norm_part<OT, PE_, GM_><<<B, 1024, 0, s>>>(x, (OT*)yh, (OT*)yl, g, b, d, eps, part, G, B, pbias)
+  if (d <= 2048) {
+    if (G <= 8) WD_NP(2, 8); else if (G <= 16) WD_NP(2, 16); else WD_NP(2, 32);
+  } else {
+    if (G <= 8) WD_NP(4, 8); else if (G <= 16) WD_NP(4, 16); else WD_NP(4, 32);
+  }
+#undef WD_NP
+  return hipGetLastError();
+}
+
 hipError_t launch_norm(const float* x, float* y, const float* g, const float* b, int B, int d,
                        float eps, hipStream_t s) {
   if (B <= 0 || d <= 0 || d > 256 * NORM_MAXE || !g) return hipErrorInvalidValue;
@@ -169,9 +225,16 @@ hipError_t launch_norm(const float* x, float* y, const float* g, const float* b,
   return hipGetLastError();
 }
 
-hipError_t launch_norm_split(const float* x, void* y_hi, void* y_lo, int act_dtype, const float* g,
-                             const float* b, int B, int d, float eps, hipStream_t s) {
+hipError_t launch_norm_split(float* x, void* y_hi, void* y_lo, int act_dtype, const float* g,
+                             const float* b, int B, int d, float eps, hipStream_t s,
+                             const float* part, int G, const float* pbias) {
   if (B <= 0 || d <= 0 || d > 256 * NORM_MAXE || (d % 32) || !g || !y_hi || !y_lo) return hipErrorInvalidValue;
+  if (part) {
+    if (G <= 0) return hipErrorInvalidValue;
+    if (act_dtype == DT_BF16) return norm_part<bf16_t>(x, y_hi, y_lo, g, b, B, d, eps, part, G, pbias, s);
+    if (act_dtype == DT_F16) return norm_part<f16_t>(x, y_hi, y_lo, g, b, B, d, eps, part, G, pbias, s);
+    return hipErrorInvalidValue;
+  }
   if (act_dtype == DT_BF16)
     k_norm<bf16_t, true><<<B, 256, 0, s>>>(x, nullptr, (bf16_t*)y_hi, (bf16_t*)y_lo, g, b, d, eps);
   else if (act_dtype == DT_F16)

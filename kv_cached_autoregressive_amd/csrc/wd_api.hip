@@ -54,6 +54,7 @@ struct Plan {
   int n_bufs = 1;
   size_t cross = 0, cross_slab = 0;
   size_t x = 0, y = 0, q = 0, qkv = 0, o = 0, h = 0, part = 0, amax = 0, err = 0, pos_tmp = 0;
+  size_t gpart = 0; int64_t gpart_cap = 0;   // split-K GEMM partials [G][B][N] fp32
   int max_splits = 1, amax_parts = 1;
 };
 
@@ -66,6 +67,10 @@ struct Bump {
     return at;
   }
 };
+
+// Activation rows padded to the MFMA GEMM's row tile (16, 32 or 64 rows): every row a
+// tile reads exists (rows past B stay zero).
+int row_pad(int max_batch) { return max_batch <= 16 ? 16 : max_batch <= 32 ? 32 : 64; }
 
 bool valid_dt(int dt) { return dt == DT_F32 || dt == DT_F16 || dt == DT_BF16; }
 
@@ -169,11 +174,25 @@ Plan make_plan(const wd_config& c) {
   p.max_splits = (rows_max + 63) / 64;
   p.part = b.take(Bm * hq * (size_t)p.max_splits * (hd + 2) * f4);
   if (p.mfma) {
-    const size_t Bp = (Bm + 15) / 16 * 16;
+    const size_t Bp = row_pad(c.max_batch);
     const size_t kmax = std::max(d, hq * hd);
     p.yh = b.take(Bp * kmax * wb); p.yl = b.take(Bp * kmax * wb);
     p.oh = b.take(Bp * hq * hd * wb); p.ol = b.take(Bp * hq * hd * wb);
     p.hh = b.take(Bp * ff * wb); p.hl = b.take(Bp * ff * wb);
+    int64_t cap = 0;
+    auto shape = [&](int N, int K, int epi) {
+      const int G = wd::mgemv_groups(N, K, c.max_batch, epi);
+      if (G > 1) cap = std::max(cap, (int64_t)G * (int64_t)Bm * N);
+    };
+    if (c.arch == WD_ARCH_WHISPER) {
+      shape(3 * d, d, wd::EPI_QKV); shape(d, d, wd::EPI_RESID); shape(d, d, wd::EPI_STORE);
+      shape(ff, d, wd::EPI_GELU_SPLIT); shape(d, ff, wd::EPI_RESID);
+    } else {
+      shape((hq + 2 * hkv) * hd, d, wd::EPI_STORE); shape(d, hq * hd, wd::EPI_RESID);
+      shape(2 * ff, d, wd::EPI_SWIGLU_SPLIT); shape(d, ff, wd::EPI_RESID);
+    }
+    p.gpart_cap = cap;
+    if (cap) p.gpart = b.take((size_t)cap * f4);
   }
   p.amax_parts = std::max(wd::gemv_blocks(c.vocab, c.max_batch), wd::mgemv_blocks(c.vocab, c.max_batch));
   p.amax = b.take((size_t)p.amax_parts * Bm * 8);
@@ -284,14 +303,41 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
   int c_rows = 0, c_splits = 1;
   if (whisper) split_for(c->frames, (B / qpk) * hkv, qpk, &c_rows, &c_splits, true);
 
+  float* gpart = P.gpart_cap ? c->at<float>(P.gpart) : nullptr;
   auto proj = [&](const void* W, int N, int K, const void* Yh, const void* Yl, int epi, const float* bias,
                   float* out, int ldo, float scale) {
     wd::MGemvParams m{};
     m.W = W; m.w_dtype = g.w_dtype; m.N = N; m.K = K; m.Yhi = Yh; m.Ylo = Yl; m.B = B; m.epi = epi;
     m.bias = bias; m.out = out; m.ldo = ldo; m.scale = scale; m.err = err;
     m.yo_hi = hh; m.yo_lo = hl;
+    m.part = gpart; m.part_cap = P.gpart_cap;
     return m;
   };
+  // A split-K residual projection leaves its partials (and bias) to the next norm, which
+  // adds them into x; any other split-K epilogue runs in the finish kernel right away.
+  const float* pend_bias = nullptr;
+  int pend_G = 0;
+  auto gemm = [&](const wd::MGemvParams& m, const char* what) -> wd_status {
+    HIPCHK(c, wd::launch_mgemv(m, s), what);
+    const int G = wd::mgemv_groups(m.N, m.K, m.B, m.epi);
+    if (G > 1) {
+      if (m.epi == wd::EPI_RESID) {
+        pend_bias = m.bias;
+        pend_G = G;
+      } else {
+        HIPCHK(c, wd::launch_mgemv_finish(m, G, s), what);
+      }
+    }
+    return WD_OK;
+  };
+  auto norm = [&](void* oh_, void* ol_, const float* gain, const float* bias, const char* what) -> wd_status {
+    HIPCHK(c, wd::launch_norm_split(x, oh_, ol_, adt, gain, bias, B, d, g.norm_eps, s, pend_G ? gpart : nullptr,
+                                    pend_G, pend_bias), what);
+    pend_G = 0;
+    pend_bias = nullptr;
+    return WD_OK;
+  };
+#define WDCHK(expr) do { const wd_status st_ = (expr); if (st_ != WD_OK) return st_; } while (0)
 
   for (int l = 0; l < g.n_layers; ++l) {
     const LayerOff& L = P.L[l];
@@ -299,16 +345,15 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
     ap.cache_dtype = g.cache_dtype; ap.B = B; ap.Hq = hq; ap.Hkv = hkv; ap.hd = hd; ap.part = part;
     ap.o_hi = oh; ap.o_lo = ol; ap.o_dtype = adt;
     if (whisper) {
-      HIPCHK(c, wd::launch_norm_split(x, yh, yl, adt, c->at<float>(L.ln1g), c->at<float>(L.ln1b), B, d, g.norm_eps, s), "ln1");
+      WDCHK(norm(yh, yl, c->at<float>(L.ln1g), c->at<float>(L.ln1b), "ln1"));
       wd::MGemvParams m = proj(c->at(L.wqkv), 3 * d, d, yh, yl, wd::EPI_QKV, c->at<float>(L.bqkv), q, d, qscale);
       m.d = d; m.H = hq; m.hd = hd; m.ctx = g.context; m.pos = pos;
       m.Kc = c->self_k(l); m.Vc = c->self_v(l); m.cache_dtype = g.cache_dtype; m.kv_bstride = kv_bstride;
-      HIPCHK(c, wd::launch_mgemv(m, s), "qkv projection");
+      WDCHK(gemm(m, "qkv projection"));
     } else {
-      HIPCHK(c, wd::launch_norm_split(x, yh, yl, adt, c->at<float>(L.n1g), nullptr, B, d, g.norm_eps, s), "norm1");
+      WDCHK(norm(yh, yl, c->at<float>(L.n1g), nullptr, "norm1"));
       const int nqkv = (hq + 2 * hkv) * hd;
-      HIPCHK(c, wd::launch_mgemv(proj(c->at(L.wqkv), nqkv, d, yh, yl, wd::EPI_STORE, nullptr, qkv, nqkv, 1.0f), s),
-             "qkv projection");
+      WDCHK(gemm(proj(c->at(L.wqkv), nqkv, d, yh, yl, wd::EPI_STORE, nullptr, qkv, nqkv, 1.0f), "qkv projection"));
       HIPCHK(c, wd::launch_qk_rope_append(qkv, B, hq, hkv, hd, pos, g.context, c->at<float>(L.qn),
                                           c->at<float>(L.kn), g.norm_eps, g.rope_base, qscale, q,
                                           c->self_k(l), c->self_v(l), g.cache_dtype, kv_bstride, s),
@@ -324,12 +369,11 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
       prof_end(c, on);
     }
     HIPCHK(c, wd::launch_attention_combine(ap, s), "self attention combine");
-    HIPCHK(c, wd::launch_mgemv(proj(c->at(L.wo), d, hq * hd, oh, ol, wd::EPI_RESID,
-                                    whisper ? c->at<float>(L.bo) : nullptr, x, d, 1.0f), s), "out projection");
+    WDCHK(gemm(proj(c->at(L.wo), d, hq * hd, oh, ol, wd::EPI_RESID, whisper ? c->at<float>(L.bo) : nullptr, x, d, 1.0f),
+               "out projection"));
     if (whisper) {
-      HIPCHK(c, wd::launch_norm_split(x, yh, yl, adt, c->at<float>(L.ln2g), c->at<float>(L.ln2b), B, d, g.norm_eps, s), "ln2");
-      HIPCHK(c, wd::launch_mgemv(proj(c->at(L.wcq), d, d, yh, yl, wd::EPI_STORE, c->at<float>(L.bcq), q, d, qscale), s),
-             "cross q projection");
+      WDCHK(norm(yh, yl, c->at<float>(L.ln2g), c->at<float>(L.ln2b), "ln2"));
+      WDCHK(gemm(proj(c->at(L.wcq), d, d, yh, yl, wd::EPI_STORE, c->at<float>(L.bcq), q, d, qscale), "cross q projection"));
       wd::AttnParams cp = ap;
       cp.K = c->cross_k(l); cp.V = c->cross_v(l);
       cp.kvb_stride = (int64_t)hq * g.max_frames * hd; cp.rows_cap = g.max_frames;
@@ -342,32 +386,34 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
         prof_end(c, on);
       }
       HIPCHK(c, wd::launch_attention_combine(cp, s), "cross attention combine");
-      HIPCHK(c, wd::launch_mgemv(proj(c->at(L.wco), d, d, oh, ol, wd::EPI_RESID, c->at<float>(L.bco), x, d, 1.0f), s),
-             "cross out projection");
-      HIPCHK(c, wd::launch_norm_split(x, yh, yl, adt, c->at<float>(L.ln3g), c->at<float>(L.ln3b), B, d, g.norm_eps, s), "ln3");
+      WDCHK(gemm(proj(c->at(L.wco), d, d, oh, ol, wd::EPI_RESID, c->at<float>(L.bco), x, d, 1.0f), "cross out projection"));
+      WDCHK(norm(yh, yl, c->at<float>(L.ln3g), c->at<float>(L.ln3b), "ln3"));
       {
         const bool on = prof_on(c, PK_FC1, l);
         prof_begin(c, on);
-        HIPCHK(c, wd::launch_mgemv(proj(c->at(L.w1), ff, d, yh, yl, wd::EPI_GELU_SPLIT, c->at<float>(L.b1), nullptr, 0, 1.0f), s),
-               "fc1");
+        WDCHK(gemm(proj(c->at(L.w1), ff, d, yh, yl, wd::EPI_GELU_SPLIT, c->at<float>(L.b1), nullptr, 0, 1.0f), "fc1"));
         prof_end(c, on);
       }
-      HIPCHK(c, wd::launch_mgemv(proj(c->at(L.w2), d, ff, hh, hl, wd::EPI_RESID, c->at<float>(L.b2), x, d, 1.0f), s), "fc2");
+      WDCHK(gemm(proj(c->at(L.w2), d, ff, hh, hl, wd::EPI_RESID, c->at<float>(L.b2), x, d, 1.0f), "fc2"));
     } else {
-      HIPCHK(c, wd::launch_norm_split(x, yh, yl, adt, c->at<float>(L.n2g), nullptr, B, d, g.norm_eps, s), "norm2");
+      WDCHK(norm(yh, yl, c->at<float>(L.n2g), nullptr, "norm2"));
       {
         const bool on = prof_on(c, PK_FC1, l);
         prof_begin(c, on);
-        HIPCHK(c, wd::launch_mgemv(proj(c->at(L.wgu), 2 * ff, d, yh, yl, wd::EPI_SWIGLU_SPLIT, nullptr, nullptr, 0, 1.0f), s),
-               "gate|up projection");
+        WDCHK(gemm(proj(c->at(L.wgu), 2 * ff, d, yh, yl, wd::EPI_SWIGLU_SPLIT, nullptr, nullptr, 0, 1.0f),
+                   "gate|up projection"));
         prof_end(c, on);
       }
-      HIPCHK(c, wd::launch_mgemv(proj(c->at(L.wdn), d, ff, hh, hl, wd::EPI_RESID, nullptr, x, d, 1.0f), s), "down projection");
+      WDCHK(gemm(proj(c->at(L.wdn), d, ff, hh, hl, wd::EPI_RESID, nullptr, x, d, 1.0f), "down projection"));
     }
   }
-  if (!head) return WD_OK;
-  HIPCHK(c, wd::launch_norm_split(x, yh, yl, adt, c->at<float>(P.lnfg), whisper ? c->at<float>(P.lnfb) : nullptr, B, d,
-                                  g.norm_eps, s), "final norm");
+  // without the head (prefill positions before the last) the pending residual still lands in x
+  if (!head) {
+    if (pend_G) WDCHK(norm(yh, yl, c->at<float>(P.lnfg), whisper ? c->at<float>(P.lnfb) : nullptr, "final residual"));
+    return WD_OK;
+  }
+  WDCHK(norm(yh, yl, c->at<float>(P.lnfg), whisper ? c->at<float>(P.lnfb) : nullptr, "final norm"));
+#undef WDCHK
   wd::MGemvParams hm = proj(c->at(P.embed), g.vocab, d, yh, yl, wd::EPI_LOGITS, nullptr, logits, g.vocab, 1.0f);
   hm.amax = c->at<unsigned long long>(P.amax); hm.ldp = g.max_batch;
   {
@@ -668,7 +714,7 @@ wd_status wd_load(const wd_config* cfg, const wd_tensor* weights, int32_t n_weig
     if (plan.mfma) chk(zero(plan.embed, ((int64_t)(cfg->vocab + 15) / 16 * 16) * d * dtype_bytes(wdt) / 4));
     chk(mat("embed", plan.embed, cfg->vocab, d, 1, 0, 0));
     if (plan.mfma) {
-      const int64_t Bp = (cfg->max_batch + 15) / 16 * 16;
+      const int64_t Bp = row_pad(cfg->max_batch);
       for (size_t off : {plan.yh, plan.yl}) chk(zero(off, Bp * std::max(d, hq * hd) * dtype_bytes(wdt) / 4));
       for (size_t off : {plan.oh, plan.ol}) chk(zero(off, Bp * hq * hd * dtype_bytes(wdt) / 4));
       for (size_t off : {plan.hh, plan.hl}) chk(zero(off, Bp * ff * dtype_bytes(wdt) / 4));

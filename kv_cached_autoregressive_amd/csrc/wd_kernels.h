@@ -79,15 +79,26 @@ struct MGemvParams {
   unsigned long long* amax; int ldp;          // EPI_LOGITS partial keys [blocks][ldp]
   void* yo_hi; void* yo_lo;                   // GELU_SPLIT / SWIGLU_SPLIT output [B_pad, N or N/2]
   unsigned* err;
+  float* part; int64_t part_cap;              // K-group partials [G][B][N] fp32 (split-K launches)
 };
 // Number of argmax partials (blocks) a logits launch writes: upper bound over K, and exact for K.
 int mgemv_blocks(int N, int B);
 int mgemv_blocks_k(int N, int K, int B);
+// K groups a launch of this shape splits into (1: the epilogue runs in the GEMM).  With G > 1
+// the launch writes fp32 partials part[g][b][n] (no bias) and the caller finishes them: a
+// residual add is folded into the next norm (launch_norm_split with part), any other
+// epilogue runs in launch_mgemv_finish.
+int mgemv_groups(int N, int K, int B, int epi);
 hipError_t launch_mgemv(const MGemvParams& p, hipStream_t s);
+// Sum of the G partials of each output in order g = 0..G-1, then the launch's epilogue.
+hipError_t launch_mgemv_finish(const MGemvParams& p, int G, hipStream_t s);
 
 // Row norm writing the split fragment layout (MFMA consumers).
-hipError_t launch_norm_split(const float* x, void* y_hi, void* y_lo, int act_dtype, const float* g,
-                             const float* b, int B, int d, float eps, hipStream_t s);
+// With part != null, first x += pbias + sum_g part[g][b][:] (G partial slabs of a split-K
+// residual projection, added in order g = 0..G-1) and x is written back.
+hipError_t launch_norm_split(float* x, void* y_hi, void* y_lo, int act_dtype, const float* g,
+                             const float* b, int B, int d, float eps, hipStream_t s,
+                             const float* part = nullptr, int G = 0, const float* pbias = nullptr);
 // Fragment-layout repack of a [rows, K] matrix into fused row blocks:
 // fused row of source row r = (r / 16) * blk_mul * 16 + blk_add * 16 + r % 16.
 hipError_t launch_pack_frag(const void* src, int src_dtype, void* dst, int dst_dtype, int64_t rows,

@@ -58,3 +58,12 @@ def test_qwen3_small_dims_context_end():
     w = WL.reduced(WL.by_name("qwen3asr_bf16_b8"), layers=2, d=256, heads=4, kv_heads=2,
                    d_ff=512, vocab=7001, context=48, batch=3, audio_offset=3, audio_rows=9)
     _qwen_parity(w, T=20, steps=28, streams=(0, 1, 2))   # last step at position 47 = context - 1
+
+
+def test_qwen3_split_k_above_16_rows():
+    """20 rows: the q|k|v and gate|up projections finish their split-K partials in the
+    finish kernel (store, SwiGLU), the o and down projections fold theirs into the next
+    norm, including across the prefill's head-less positions."""
+    w = WL.reduced(WL.by_name("qwen3asr_bf16_b8"), layers=2, d=512, heads=4, kv_heads=2, d_ff=1536,
+                   vocab=7001, context=64, batch=20, audio_offset=2, audio_rows=6)
+    _qwen_parity(w, T=16, steps=6, streams=(0, 19))

@@ -110,6 +110,16 @@ def test_large_bf16_b64_reduced_layers():
     _sampled_parity(w, steps=24, streams=(0, 63))
 
 
+@pytest.mark.parametrize("batch", [24, 40])
+def test_split_k_projections_above_16_rows(batch):
+    """Rows 17..64 take the split-K projections (K groups write partials that the next
+    norm or the finish kernel adds): 24 rows use 32-row tiles, 40 rows a partly filled
+    64-row tile; K = 768 and 2048 give uneven K groups."""
+    w = WL.reduced(WL.by_name("whisper_large_bf16_b64"), layers=2, batch=batch, n_enc=batch, d=768, heads=12,
+                   kv_heads=12, d_ff=2048, vocab=9001, frames=300)
+    _sampled_parity(w, steps=6, streams=(0, batch - 1))
+
+
 def test_base_f16_beam5_full():
     """Width-5 beam search over one broadcast encoder set, 128 positions: the
     oracle's beam indices drive both sides' cache reorder; the beam choices made
