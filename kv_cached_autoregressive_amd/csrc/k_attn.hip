@@ -75,14 +75,46 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     return;
   }
 
-  const CT* __restrict__ Kp = reinterpret_cast<const CT*>(p.K) + (int64_t)kvb * p.kvb_stride + (int64_t)g * p.rows_cap * HD;
-  const CT* __restrict__ Vp = reinterpret_cast<const CT*>(p.V) + (int64_t)kvb * p.kvb_stride + (int64_t)g * p.rows_cap * HD;
+  // (no __restrict__: the append below writes a row that the loop then reads)
+  const CT* Kp = reinterpret_cast<const CT*>(p.K) + (int64_t)kvb * p.kvb_stride + (int64_t)g * p.rows_cap * HD;
+  const CT* Vp = reinterpret_cast<const CT*>(p.V) + (int64_t)kvb * p.kvb_stride + (int64_t)g * p.rows_cap * HD;
+  const int64_t qslab = (int64_t)p.B * p.qpart_ld;
+
+  // q (and the appended row) from split-K partials: each value is summed once per block
+  // (one thread per value, its G loads in flight together), q through LDS
+  __shared__ float qs[NQ * HD];
+  if (p.qpart) {
+    for (int i = t; i < nq * HD; i += 256) {
+      const int qi = i / HD, c = i - qi * HD;
+      const int col = qhead(qi) * HD + c;
+      const float* src = p.qpart + (int64_t)qrow(qi) * p.qpart_ld + p.q_off + col;
+      qs[i] = (sum_parts<16>(src, qslab, p.qG) + (p.qbias ? p.qbias[col] : 0.f)) * p.qscale;
+    }
+    if (p.append && p.pos) {   // the appended row lives in this block's split: write it first
+      const int ps = n_rows - 1;
+      if (ps >= r_lo && ps < r_hi && t < 2 * HD) {
+        const int c = t % HD;
+        const bool isv = t >= HD;
+        const float* src = p.qpart + (int64_t)bq0 * p.qpart_ld + (isv ? p.v_off : p.k_off) + g * HD + c;
+        float v = sum_parts<16>(src, qslab, p.qG);
+        if (isv && p.vbias) v += p.vbias[g * HD + c];
+        CT* base = reinterpret_cast<CT*>(const_cast<void*>(isv ? p.V : p.K));
+        base[(int64_t)kvb * p.kvb_stride + ((int64_t)g * p.rows_cap + ps) * HD + c] = from_f<CT>(v);
+      }
+    }
+    __syncthreads();   // q in LDS; the appended row visible to the block's loads below
+  }
 
   float qv[NQ][8];
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
     if (qi < nq) {
-      load8(p.q + (int64_t)qrow(qi) * p.q_ld + qhead(qi) * HD + seg * 8, qv[qi]);
+      if (p.qpart) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qv[qi][j] = qs[qi * HD + seg * 8 + j];
+      } else {
+        load8(p.q + (int64_t)qrow(qi) * p.q_ld + qhead(qi) * HD + seg * 8, qv[qi]);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) qv[qi][j] = 0.f;
@@ -99,14 +131,22 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[qi][j] = 0.f;
   }
-  for (int r = r_lo + rr; r - rr < r_hi; r += RPP * UNR) {   // trip count uniform over the block
-    Raw8<CT> kr[UNR], vr[UNR];
+  // Software pipeline: the K/V rows of the next pass are requested before the current
+  // pass is reduced, so each wave keeps 2 * UNR rows of K and V in flight.  Rows past
+  // the split reload its last row (not counted); no load sits under a branch.
+  Raw8<CT> kr[UNR], vr[UNR];
+  auto fetch = [&](int r0, Raw8<CT> (&kd)[UNR], Raw8<CT> (&vd)[UNR]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int ru = min(r + u * RPP, r_hi - 1);
-      kr[u] = fetch8(Kp + (int64_t)ru * HD + seg * 8);
-      vr[u] = fetch8(Vp + (int64_t)ru * HD + seg * 8);
+      const int ru = min(r0 + u * RPP, r_hi - 1);
+      kd[u] = fetch8(Kp + (int64_t)ru * HD + seg * 8);
+      vd[u] = fetch8(Vp + (int64_t)ru * HD + seg * 8);
     }
+  };
+  fetch(r_lo + rr, kr, vr);
+  for (int r = r_lo + rr; r - rr < r_hi; r += RPP * UNR) {   // trip count uniform over the block
+    Raw8<CT> kn[UNR], vn[UNR];
+    fetch(r + RPP * UNR, kn, vn);
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const bool live = r + u * RPP < r_hi;
@@ -134,6 +174,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
           for (int j = 0; j < 8; ++j) acc[qi][j] = fmaf(e, vf[j], acc[qi][j]);
         }
       }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      kr[u] = kn[u];
+      vr[u] = vn[u];
     }
   }
   // merge the (m, l, acc) of the lanes holding the same segment: within the wave,
@@ -235,7 +280,9 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   if (!p.pos && (p.n_rows_fixed < 0 || p.n_rows_fixed > p.rows_cap)) return hipErrorInvalidValue;
   if ((int64_t)p.split_rows * p.n_splits < (p.pos ? p.rows_cap : p.n_rows_fixed)) return hipErrorInvalidValue;
   if (p.n_splits > 1 && !p.part) return hipErrorInvalidValue;
-  if (!p.q || !p.K || !p.V || (p.q_ld % 4)) return hipErrorInvalidValue;
+  if ((!p.q && !p.qpart) || !p.K || !p.V || (!p.qpart && (p.q_ld % 4))) return hipErrorInvalidValue;
+  if (p.qpart && (p.qG < 1 || p.qG > 16 || p.qpart_ld <= 0)) return hipErrorInvalidValue;
+  if (p.append && (!p.qpart || !p.pos || p.Hq != p.Hkv)) return hipErrorInvalidValue;
   if (p.o_hi ? (!p.o_lo || (p.Hq * p.hd) % 32 || (p.o_dtype != DT_F16 && p.o_dtype != DT_BF16))
              : (!p.out || p.out_ld < p.Hq * p.hd))
     return hipErrorInvalidValue;

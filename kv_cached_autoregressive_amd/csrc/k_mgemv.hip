@@ -579,26 +579,30 @@ __global__ __launch_bounds__(256) void k_mgemv_finish(MGemvParams p, int G) {
   }
 }
 
-struct SkShape { int NBW, NBB, G; };
+struct SkShape { int NBW, NBB, G, NSC; };
 // Split-K shape: 4 waves per workgroup, NBW = 2 (128 outputs) for the wide or deep
-// projections, and enough K groups for ~240 workgroups with at least 2 K steps each.
-// Tuning overrides: WD_MGEMV_SK=0 disables the variant; WD_MGEMV_SKG=<G> forces G.
+// projections; S K steps per group so that ~256 workgroups cover the shape (2 <= S <= 8),
+// G = ceil(K steps / S), and the LDS chunk is 4 or 8 steps (no padded steps for S <= 4).
+// Tuning overrides: WD_MGEMV_SK=0 disables the variant; WD_MGEMV_SKS=<S> forces S.
 static bool sk_pick(int N, int K, int B, int epi, SkShape& s) {
-  static int mode = -1, forceg = 0;
+  static int mode = -1, forces = 0;
   if (mode < 0) {
     const char* e = getenv("WD_MGEMV_SK");
     mode = e ? atoi(e) : 1;
-    const char* f = getenv("WD_MGEMV_SKG");
-    forceg = f ? atoi(f) : 0;
+    const char* f = getenv("WD_MGEMV_SKS");
+    forces = f ? atoi(f) : 0;
   }
   if (!mode || B <= 16 || epi == EPI_LOGITS) return false;
   const int NB = (N + 15) / 16, KST = K / 32;
   s.NBB = B <= 32 ? 2 : 4;
   s.NBW = (NB >= 256 || KST >= 128 || epi == EPI_SWIGLU_SPLIT) ? 2 : 1;
   const int ncg = (NB + 4 * s.NBW - 1) / (4 * s.NBW);
-  int G = forceg > 0 ? forceg : (240 + ncg / 2) / ncg;
-  G = std::max(1, std::min({G, std::max(1, KST / 2), 32}));   // the consumers add at most 32
+  int S = forces > 0 ? forces : (KST * ncg + 255) / 256;
+  S = std::max(2, std::min(S, 8));
+  int G = (KST + S - 1) / S;
+  G = std::max(1, std::min(G, 32));     // the consumers add at most 32 partial slabs
   s.G = G;
+  s.NSC = (KST + G - 1) / G <= 4 ? 4 : 8;
   return true;
 }
 int mgemv_groups(int N, int K, int B, int epi) {
@@ -611,12 +615,13 @@ static hipError_t skrun(const MGemvParams& p, const SkShape& s, hipStream_t st) 
   const int NB = (p.N + 15) / 16;
   dim3 grid((NB + 4 * s.NBW - 1) / (4 * s.NBW), s.G);
   if (s.G > 1 && (!p.part || (int64_t)s.G * p.B * p.N > p.part_cap)) return hipErrorInvalidValue;
-#define WD_SK(NBW_, NBB_)                                                   \
-  if (s.NBW == NBW_ && s.NBB == NBB_) {                                     \
-    k_mgemv_sk<T, NBW_, NBB_, 8, 4><<<grid, 256, 0, st>>>(p);               \
+#define WD_SK(NBW_, NBB_, NSC_)                                             \
+  if (s.NBW == NBW_ && s.NBB == NBB_ && s.NSC == NSC_) {                    \
+    k_mgemv_sk<T, NBW_, NBB_, NSC_, 4><<<grid, 256, 0, st>>>(p);            \
     return hipGetLastError();                                               \
   }
-  WD_SK(1, 2) WD_SK(2, 2) WD_SK(1, 4) WD_SK(2, 4)
+  WD_SK(1, 2, 4) WD_SK(2, 2, 4) WD_SK(1, 4, 4) WD_SK(2, 4, 4)
+  WD_SK(1, 2, 8) WD_SK(2, 2, 8) WD_SK(1, 4, 8) WD_SK(2, 4, 8)
 #undef WD_SK
   return hipErrorInvalidValue;
 }

@@ -291,32 +291,45 @@ hipError_t launch_pack_frag(const void* src, int src_dtype, void* dst, int dst_d
 // (head slot, row): slots [0,Hq) are q heads, [Hq,Hq+Hkv) k heads, the rest v heads.
 // The rotation angle pos * base^(-2i/hd) and its sine/cosine are taken in double.
 // ------------------------------------------------------------------------------------------
-template <typename CT>
+template <typename CT, int GMAX>
 __global__ __launch_bounds__(64) void k_qk_rope_append(const float* __restrict__ qkv, int Hq, int Hkv,
                                                        int hd, const int32_t* pos, int ctx,
                                                        const float* __restrict__ qn,
                                                        const float* __restrict__ kn, float eps,
                                                        float base, float qscale, float* q_out,
-                                                       CT* Kc, CT* Vc, int64_t kv_bstride) {
+                                                       CT* Kc, CT* Vc, int64_t kv_bstride,
+                                                       const float* __restrict__ part, int G, int B) {
   __shared__ float z[256];
   const int slot = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int nslot = Hq + 2 * Hkv;
-  const float* src = qkv + ((int64_t)b * nslot + slot) * hd;
+  const int64_t off = ((int64_t)b * nslot + slot) * hd;
+  float v[4];   // this lane's channels lane + 64 j of the head (hd <= 256)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = min(lane + 64 * j, hd - 1);
+    v[j] = part ? sum_parts<GMAX>(part + off + c, (int64_t)B * nslot * hd, G) : qkv[off + c];
+  }
   const int p = pos[b];
   const bool ok = p >= 0 && p < ctx;
   if (slot >= Hq + Hkv) {  // value head: plain append
     if (!ok) return;
     const int g = slot - Hq - Hkv;
     CT* dst = Vc + (int64_t)b * kv_bstride + ((int64_t)g * ctx + p) * hd;
-    for (int c = lane; c < hd; c += 64) dst[c] = from_f<CT>(src[c]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j < hd) dst[lane + 64 * j] = from_f<CT>(v[j]);
     return;
   }
   const float* gain = slot < Hq ? qn : kn;
   float ss = 0.f;
-  for (int c = lane; c < hd; c += 64) ss += src[c] * src[c];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (lane + 64 * j < hd) ss += v[j] * v[j];
   ss = wave_sum(ss);
   const float rs = 1.0f / sqrtf(ss / (float)hd + eps);
-  for (int c = lane; c < hd; c += 64) z[c] = src[c] * rs * gain[c];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (lane + 64 * j < hd) z[lane + 64 * j] = v[j] * rs * gain[lane + 64 * j];
   __syncthreads();
   const int half = hd / 2;
   const double dpos = ok ? (double)p : 0.0;
@@ -338,16 +351,32 @@ __global__ __launch_bounds__(64) void k_qk_rope_append(const float* __restrict__
   }
 }
 
+template <typename CT>
+static void qk_rope_run(dim3 grid, hipStream_t s, const float* qkv, int Hq, int Hkv, int hd, const int32_t* pos,
+                        int ctx, const float* qn, const float* kn, float eps, float base, float qscale, float* q_out,
+                        void* Kc, void* Vc, int64_t kv_bstride, const float* part, int G, int B) {
+  if (!part || G <= 8)
+    k_qk_rope_append<CT, 8><<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out,
+                                                (CT*)Kc, (CT*)Vc, kv_bstride, part, G, B);
+  else if (G <= 16)
+    k_qk_rope_append<CT, 16><<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out,
+                                                 (CT*)Kc, (CT*)Vc, kv_bstride, part, G, B);
+  else
+    k_qk_rope_append<CT, 32><<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out,
+                                                 (CT*)Kc, (CT*)Vc, kv_bstride, part, G, B);
+}
+
 hipError_t launch_qk_rope_append(const float* qkv, int B, int Hq, int Hkv, int hd, const int32_t* pos,
                                  int ctx, const float* qn, const float* kn, float eps, float base,
                                  float qscale, float* q_out, void* Kc, void* Vc, int cache_dtype,
-                                 int64_t kv_bstride, hipStream_t s) {
+                                 int64_t kv_bstride, hipStream_t s, const float* part, int G) {
   if (B <= 0 || hd > 256 || (hd % 2) || Hq <= 0 || Hkv <= 0) return hipErrorInvalidValue;
+  if (part ? (G < 1 || G > 32) : !qkv) return hipErrorInvalidValue;
   dim3 grid(Hq + 2 * Hkv, B);
   switch (cache_dtype) {
-    case DT_F32: k_qk_rope_append<<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, (float*)Kc, (float*)Vc, kv_bstride); break;
-    case DT_F16: k_qk_rope_append<<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, (f16_t*)Kc, (f16_t*)Vc, kv_bstride); break;
-    case DT_BF16: k_qk_rope_append<<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, (bf16_t*)Kc, (bf16_t*)Vc, kv_bstride); break;
+    case DT_F32: qk_rope_run<float>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, Kc, Vc, kv_bstride, part, G, B); break;
+    case DT_F16: qk_rope_run<f16_t>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, Kc, Vc, kv_bstride, part, G, B); break;
+    case DT_BF16: qk_rope_run<bf16_t>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, Kc, Vc, kv_bstride, part, G, B); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -98,8 +98,8 @@ std::string check_config(const wd_config& c) {
   return "";
 }
 
-// Split of an attention over `rows` cache rows: aim at >= 2048 blocks in total, at
-// least 64 rows (one K/V tile of a few KB) per block, scores within the LDS budget.
+// Split of an attention over `rows` cache rows: aim at >= 2048 blocks in total (or none
+// with >= 512 slabs), at least 64 rows (one K/V tile of a few KB) per block.
 // Tuning override for sweeps: WD_ATTN_ROWS="self_rows,cross_rows" (0 keeps the policy).
 int attn_rows_override(bool cross) {
   static int sr = 0, cr = 0;
@@ -113,7 +113,8 @@ int attn_rows_override(bool cross) {
 }
 
 void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits, bool cross = false) {
-  const int want = std::max(1, (2048 + slabs - 1) / slabs);
+  // with >= 512 slabs every CU already streams two or more: one split, no combine launch
+  const int want = slabs >= 512 ? 1 : std::max(1, (2048 + slabs - 1) / slabs);
   int r = (rows + want - 1) / want;
   r = std::max(r, 64);
   if (const int o = attn_rows_override(cross)) r = o;
@@ -317,14 +318,17 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
   // adds them into x; any other split-K epilogue runs in the finish kernel right away.
   const float* pend_bias = nullptr;
   int pend_G = 0;
-  auto gemm = [&](const wd::MGemvParams& m, const char* what) -> wd_status {
+  // With sums_in_consumer the caller's next kernel reads the partials itself (the attention
+  // prologue, the Qwen3 q/k norm + RoPE); *Gout receives G.
+  auto gemm = [&](const wd::MGemvParams& m, const char* what, int* Gout = nullptr, int gmax = 16) -> wd_status {
     HIPCHK(c, wd::launch_mgemv(m, s), what);
     const int G = wd::mgemv_groups(m.N, m.K, m.B, m.epi);
+    if (Gout) *Gout = G <= gmax ? G : 1;
     if (G > 1) {
       if (m.epi == wd::EPI_RESID) {
         pend_bias = m.bias;
         pend_G = G;
-      } else {
+      } else if (!Gout || G > gmax) {
         HIPCHK(c, wd::launch_mgemv_finish(m, G, s), what);
       }
     }
@@ -349,14 +353,21 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
       wd::MGemvParams m = proj(c->at(L.wqkv), 3 * d, d, yh, yl, wd::EPI_QKV, c->at<float>(L.bqkv), q, d, qscale);
       m.d = d; m.H = hq; m.hd = hd; m.ctx = g.context; m.pos = pos;
       m.Kc = c->self_k(l); m.Vc = c->self_v(l); m.cache_dtype = g.cache_dtype; m.kv_bstride = kv_bstride;
-      WDCHK(gemm(m, "qkv projection"));
+      int G = 1;
+      WDCHK(gemm(m, "qkv projection", &G));
+      if (G > 1) {   // the self-attention sums q and the appended k, v from the partials
+        ap.qpart = gpart; ap.qG = G; ap.qpart_ld = 3 * d; ap.q_off = 0; ap.qbias = m.bias; ap.qscale = qscale;
+        ap.append = true; ap.k_off = d; ap.v_off = 2 * d; ap.vbias = m.bias + 2 * d;
+      }
     } else {
       WDCHK(norm(yh, yl, c->at<float>(L.n1g), nullptr, "norm1"));
       const int nqkv = (hq + 2 * hkv) * hd;
-      WDCHK(gemm(proj(c->at(L.wqkv), nqkv, d, yh, yl, wd::EPI_STORE, nullptr, qkv, nqkv, 1.0f), "qkv projection"));
+      int G = 1;
+      WDCHK(gemm(proj(c->at(L.wqkv), nqkv, d, yh, yl, wd::EPI_STORE, nullptr, qkv, nqkv, 1.0f), "qkv projection", &G, 32));
       HIPCHK(c, wd::launch_qk_rope_append(qkv, B, hq, hkv, hd, pos, g.context, c->at<float>(L.qn),
                                           c->at<float>(L.kn), g.norm_eps, g.rope_base, qscale, q,
-                                          c->self_k(l), c->self_v(l), g.cache_dtype, kv_bstride, s),
+                                          c->self_k(l), c->self_v(l), g.cache_dtype, kv_bstride, s,
+                                          G > 1 ? gpart : nullptr, G),
              "qk norm/rope/append");
     }
     ap.q = q; ap.q_ld = hq * hd; ap.K = c->self_k(l); ap.V = c->self_v(l);
@@ -373,8 +384,14 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
                "out projection"));
     if (whisper) {
       WDCHK(norm(yh, yl, c->at<float>(L.ln2g), c->at<float>(L.ln2b), "ln2"));
-      WDCHK(gemm(proj(c->at(L.wcq), d, d, yh, yl, wd::EPI_STORE, c->at<float>(L.bcq), q, d, qscale), "cross q projection"));
+      int Gq = 1;
+      WDCHK(gemm(proj(c->at(L.wcq), d, d, yh, yl, wd::EPI_STORE, c->at<float>(L.bcq), q, d, qscale), "cross q projection",
+                 &Gq));
       wd::AttnParams cp = ap;
+      cp.append = false; cp.qpart = nullptr;
+      if (Gq > 1) {   // the cross-attention sums q from the partials
+        cp.qpart = gpart; cp.qG = Gq; cp.qpart_ld = d; cp.q_off = 0; cp.qbias = c->at<float>(L.bcq); cp.qscale = qscale;
+      }
       cp.K = c->cross_k(l); cp.V = c->cross_v(l);
       cp.kvb_stride = (int64_t)hq * g.max_frames * hd; cp.rows_cap = g.max_frames;
       cp.pos = nullptr; cp.n_rows_fixed = c->frames; cp.q_per_kvb = qpk;

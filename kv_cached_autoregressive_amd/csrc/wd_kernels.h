@@ -115,6 +115,14 @@ struct AttnParams {
   float* out; int out_ld;                     // [B, out_ld] (head h at h*hd), or:
   void* o_hi; void* o_lo; int o_dtype;        // split fragment layout [B_pad, Hq*hd] if set
   float* part;                                // [B*Hq][n_splits][hd+2] when n_splits > 1
+  // q from the fp32 partials of a split-K projection (then q is ignored):
+  //   q[b][h*hd + c] = (sum_g qpart[g][b][q_off + h*hd + c] + qbias[h*hd + c]) * qscale,
+  // slabs of B rows x qpart_ld columns, g < qG <= 16
+  const float* qpart; int qG; int qpart_ld; int q_off; const float* qbias; float qscale;
+  // self-attention append from the same partials (Whisper q|k|v): the block whose split holds
+  // row pos[b] writes cache row pos[b] of its head, k = sum_g qpart[..k_off..] (no bias) and
+  // v = sum_g qpart[..v_off..] + vbias, rounded to the cache dtype, before reading any row
+  int k_off; int v_off; const float* vbias; bool append;
 };
 // main kernel (writes o directly when n_splits == 1, else partials) ...
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
@@ -122,10 +130,13 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 hipError_t launch_attention_combine(const AttnParams& p, hipStream_t s);
 
 // ---- Qwen3: per-head q/k RMSNorm + NeoX RoPE, K/V append -------------------------------------
+// With part != null the q|k|v row is the in-order sum of G fp32 partial slabs
+// part[g][b][:] ([G][B][(Hq + 2 Hkv) hd]) instead of qkv.
 hipError_t launch_qk_rope_append(const float* qkv, int B, int Hq, int Hkv, int hd,
                                  const int32_t* pos, int ctx, const float* qn, const float* kn,
                                  float eps, float base, float qscale, float* q_out, void* Kc,
-                                 void* Vc, int cache_dtype, int64_t kv_bstride, hipStream_t s);
+                                 void* Vc, int cache_dtype, int64_t kv_bstride, hipStream_t s,
+                                 const float* part = nullptr, int G = 0);
 
 // ---- beam reorder: cache-row gather -----------------------------------------------------------
 struct BeamIdx { int32_t v[64]; };
