@@ -35,11 +35,13 @@ __device__ __forceinline__ void write_o(float* out, int out_ld, void* o_hi, void
   }
 }
 
+// One query per block (NQ == 1) is kept to <= 96 VGPRs: 5 waves per SIMD, so 5 blocks per
+// CU and 1280 blocks (64 rows x 20 heads) resident at once, with no second partial round.
 template <typename CT, int HD, int NQ>
 __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
   constexpr int SEGS = HD / 8;          // lanes per cache row (16 bytes each)
   constexpr int RPP = 256 / SEGS;       // rows per block pass
-  constexpr int UNR = 4;                // rows in flight per lane, for K and for V
+  constexpr int UNR = NQ == 1 ? 3 : 4;  // rows per pass per lane (x2 in flight), for K and for V
   __shared__ float red[4][NQ][HD + 2];
 
   const int s = blockIdx.x, g = blockIdx.y, kvb = blockIdx.z;
@@ -131,9 +133,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[qi][j] = 0.f;
   }
-  // Software pipeline: the K/V rows of the next pass are requested before the current
-  // pass is reduced, so each wave keeps 2 * UNR rows of K and V in flight.  Rows past
-  // the split reload its last row (not counted); no load sits under a branch.
+  // Software pipeline: the K/V rows of the next pass are requested before the current one
+  // is reduced, so a wave never waits on an empty queue; UNR is sized so the single-query
+  // kernel stays at <= 96 VGPRs (5 waves per SIMD, all blocks resident).  Rows past the
+  // split reload its last row (not counted); no load sits under a branch.
   Raw8<CT> kr[UNR], vr[UNR];
   auto fetch = [&](int r0, Raw8<CT> (&kd)[UNR], Raw8<CT> (&vd)[UNR]) __attribute__((always_inline)) {
 #pragma unroll

@@ -468,26 +468,41 @@ __global__ __launch_bounds__(64 * KS * RT) void k_mgemv_lds(MGemvParams p) {
   mg_epilogue<T, NBW, NBB, NW>(p, acc, ks == 0, blk0 / NBW, NB, reinterpret_cast<unsigned long long*>(lds));
 }
 
-// Split-K variant for B > 16.  At 32..64 rows the activations of a K step (hi + lo, 2-8 KB)
+// Split-K variant for B > 16.  At 32..64 rows the activations of a K step (hi + lo, 4-8 KB)
 // outweigh its weight tile, so the kernel is shaped around reading them as rarely as possible:
 // a workgroup of NWV waves owns NWV*NBW 16-row tiles (64..128 outputs) and one of G groups of
-// K steps; per chunk of NSC steps it stages the activations once in LDS (every thread issues
-// its loads up front) and holds the chunk's weight tiles in registers; each wave then runs its
-// MFMAs from LDS.  With G > 1 the K groups write fp32 partials part[g][b][n] that the consumer
-// adds in order (the next norm for a residual, else launch_mgemv_finish); with G == 1 the
-// usual epilogue runs here.
-template <typename T, int NBW, int NBB, int NSC, int NWV>
+// at most S K steps.  Every load of the group is issued up front in step order (the step's
+// activation slice, then its weight tiles), so data arrives step by step; each step's
+// activations go to their own LDS slot as soon as they land (one barrier per step) and the
+// step's MFMAs run while later steps are still in flight.  With G > 1 the K groups write fp32
+// partials part[g][b][n] that the consumer adds in order (the next norm for a residual, the
+// attention prologue for q and the appended K/V row, else launch_mgemv_finish); with G == 1
+// the usual epilogue runs here.
+template <typename T, int NBW, int NBB, int S, int NWV>
 __global__ __launch_bounds__(64 * NWV) void k_mgemv_sk(MGemvParams p) {
-  constexpr int YT = NBB * 2 * NSC;                      // activation tiles of one chunk
-  constexpr int PER = (YT * 64 + 64 * NWV - 1) / (64 * NWV);
-  __shared__ mv4u ys[YT * 64 > NBB * 8 ? YT * 64 : NBB * 8];   // also the argmax keys
+  constexpr int YT = NBB * 2;                              // activation tiles of one step
+  constexpr int PER = (YT * 64 + 64 * NWV - 1) / (64 * NWV);   // staging loads per thread per step
+  __shared__ mv4u ys[S * YT * 64 > NBB * 8 ? S * YT * 64 : NBB * 8];   // also the argmax keys
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int NB = (p.N + 15) >> 4;
   const int KST = p.K >> 5;
-  const int g = blockIdx.y, G = gridDim.y;
-  const int s_lo = (g * KST) / G, s_hi = ((g + 1) * KST) / G;   // >= 1 step (host: G <= KST)
-  const int tile = blockIdx.x * NWV + w;                        // this wave's group of NBW tiles
+  const int G = p.part_G;
+  // Workgroups go to the 8 XCDs round-robin by launch index.  With G a multiple of 8, K
+  // group g runs on XCD g % 8 for every column group, so each XCD's L2 fetches only its own
+  // eighth of the activations; otherwise column groups take G consecutive indices.
+  const int L = blockIdx.x;
+  int g, cg;
+  if (G % 8 == 0) {
+    const int gx = G / 8, xcd = L % 8, q = L / 8;
+    g = xcd + 8 * (q % gx);
+    cg = q / gx;
+  } else {
+    g = L % G;
+    cg = L / G;
+  }
+  const int s_lo = (g * KST) / G, n = ((g + 1) * KST) / G - s_lo;   // 1 <= n <= S (host)
+  const int tile = cg * NWV + w;                                    // this wave's group of NBW tiles
   const mv4u* __restrict__ Wv = reinterpret_cast<const mv4u*>(p.W);
   const mv4u* __restrict__ Yh = reinterpret_cast<const mv4u*>(p.Yhi);
   const mv4u* __restrict__ Yl = reinterpret_cast<const mv4u*>(p.Ylo);
@@ -495,52 +510,48 @@ __global__ __launch_bounds__(64 * NWV) void k_mgemv_sk(MGemvParams p) {
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) wbase[nb] = (int64_t)min(tile * NBW + nb, NB - 1) * KST * 64 + lane;
 
+  // all loads up front, in step order (steps past n reload step n-1; their MFMAs see zero weights)
+  mv4u yr[S][PER], wr[S][NBW];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int st = s_lo + min(i, n - 1);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int flat = min((int)threadIdx.x + j * 64 * NWV, YT * 64 - 1);
+      const int t = flat >> 6;                    // tile: row block t/2, hi or lo by t%2
+      const mv4u* src = (t & 1) ? Yl : Yh;
+      yr[i][j] = src[((int64_t)(t >> 1) * KST + st) * 64 + (flat & 63)];
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) wr[i][nb] = Wv[wbase[nb] + (int64_t)st * 64];
+  }
+
   mf32x4_t acc[NBW][NBB];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
     for (int bb = 0; bb < NBB; ++bb) acc[nb][bb] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int c0 = s_lo; c0 < s_hi; c0 += NSC) {   // uniform over the workgroup
-    const int nst = min(NSC, s_hi - c0);
-    // the chunk's weight tiles, then its activation tiles (steps past the chunk reload its
-    // last step; their MFMAs see zeroed weights), all issued before the first wait
-    mv4u wr[NSC][NBW];
 #pragma unroll
-    for (int i = 0; i < NSC; ++i)
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) wr[i][nb] = Wv[wbase[nb] + (int64_t)(c0 + min(i, nst - 1)) * 64];
-    mv4u tmp[PER];
+  for (int i = 0; i < S; ++i) {
+    mv4u* slot = ys + i * YT * 64;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int flat = threadIdx.x + j * 64 * NWV;
-      const int t = min(flat >> 6, YT - 1);
-      const int bb = t / (2 * NSC), part = (t / NSC) & 1, i = t % NSC;
-      const mv4u* src = part ? Yl : Yh;
-      tmp[j] = src[((int64_t)bb * KST + c0 + min(i, nst - 1)) * 64 + (flat & 63)];
+      if ((YT * 64) % (64 * NWV) == 0 || flat < YT * 64) slot[flat] = yr[i][j];
     }
-    if (c0 != s_lo) __syncthreads();   // the previous chunk's LDS reads are done
+    __syncthreads();   // step i's activation tiles are in LDS
+    const bool live = i < n;
+    mv4u wv[NBW];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int flat = threadIdx.x + j * 64 * NWV;
-      if ((YT * 64) % (64 * NWV) == 0 || flat < YT * 64) ys[flat] = tmp[j];
-    }
-    __syncthreads();
+    for (int nb = 0; nb < NBW; ++nb) wv[nb] = keep_if(wr[i][nb], live);
 #pragma unroll
-    for (int i = 0; i < NSC; ++i) {
-      const bool live = i < nst;
+    for (int part = 0; part < 2; ++part)          // hi then lo: consecutive MFMAs are independent
 #pragma unroll
       for (int bb = 0; bb < NBB; ++bb) {
-        const mv4u h = ys[((bb * 2 + 0) * NSC + i) * 64 + lane];
-        const mv4u l = ys[((bb * 2 + 1) * NSC + i) * 64 + lane];
+        const mv4u y = slot[(bb * 2 + part) * 64 + lane];
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-          const mv4u wv = keep_if(wr[i][nb], live);
-          acc[nb][bb] = mma(h, wv, acc[nb][bb], (T*)nullptr);
-          acc[nb][bb] = mma(l, wv, acc[nb][bb], (T*)nullptr);
-        }
+        for (int nb = 0; nb < NBW; ++nb) acc[nb][bb] = mma(y, wv[nb], acc[nb][bb], (T*)nullptr);
       }
-    }
   }
   if (G == 1) {
     __syncthreads();   // the staging buffer is reused for argmax keys
@@ -555,8 +566,8 @@ __global__ __launch_bounds__(64 * NWV) void k_mgemv_sk(MGemvParams p) {
     for (int bb = 0; bb < NBB; ++bb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int n = (tile * NBW + nb) * 16 + col, b = bb * 16 + rsub + r;
-        if (n < p.N && b < p.B && tile * NBW + nb < NB) P[(int64_t)b * p.N + n] = acc[nb][bb][r];
+        const int nn = (tile * NBW + nb) * 16 + col, b = bb * 16 + rsub + r;   // tile from cg
+        if (nn < p.N && b < p.B && tile * NBW + nb < NB) P[(int64_t)b * p.N + nn] = acc[nb][bb][r];
       }
 }
 
@@ -600,9 +611,12 @@ static bool sk_pick(int N, int K, int B, int epi, SkShape& s) {
   int S = forces > 0 ? forces : (KST * ncg + 255) / 256;
   S = std::max(2, std::min(S, 8));
   int G = (KST + S - 1) / S;
-  G = std::max(1, std::min(G, 32));     // the consumers add at most 32 partial slabs
+  // narrow outputs (N <= 2048): every XCD would fetch all the activations, which weigh as
+  // much as the partials; with G a multiple of 8 each XCD fetches one K eighth of them
+  if (N <= 2048 && KST >= 16 && !forces) G = 8 * ((KST + 63) / 64);
+  if (G > 32) return false;             // the consumers add at most 32 partial slabs
   s.G = G;
-  s.NSC = (KST + G - 1) / G <= 4 ? 4 : 8;
+  s.NSC = (KST + G - 1) / G <= 4 ? 4 : 8;   // steps per group, rounded up to an instance
   return true;
 }
 int mgemv_groups(int N, int K, int B, int epi) {
@@ -611,10 +625,13 @@ int mgemv_groups(int N, int K, int B, int epi) {
 }
 
 template <typename T>
-static hipError_t skrun(const MGemvParams& p, const SkShape& s, hipStream_t st) {
-  const int NB = (p.N + 15) / 16;
-  dim3 grid((NB + 4 * s.NBW - 1) / (4 * s.NBW), s.G);
-  if (s.G > 1 && (!p.part || (int64_t)s.G * p.B * p.N > p.part_cap)) return hipErrorInvalidValue;
+static hipError_t skrun(const MGemvParams& p0, const SkShape& s, hipStream_t st) {
+  const int NB = (p0.N + 15) / 16;
+  const int ncg = (NB + 4 * s.NBW - 1) / (4 * s.NBW);
+  if (s.G > 1 && (!p0.part || (int64_t)s.G * p0.B * p0.N > p0.part_cap)) return hipErrorInvalidValue;
+  MGemvParams p = p0;
+  p.part_G = s.G;
+  const dim3 grid(ncg * s.G);
 #define WD_SK(NBW_, NBB_, NSC_)                                             \
   if (s.NBW == NBW_ && s.NBB == NBB_ && s.NSC == NSC_) {                    \
     k_mgemv_sk<T, NBW_, NBB_, NSC_, 4><<<grid, 256, 0, st>>>(p);            \

@@ -80,6 +80,7 @@ struct MGemvParams {
   void* yo_hi; void* yo_lo;                   // GELU_SPLIT / SWIGLU_SPLIT output [B_pad, N or N/2]
   unsigned* err;
   float* part; int64_t part_cap;              // K-group partials [G][B][N] fp32 (split-K launches)
+  int part_G;                                 // set by the launcher: K groups of this launch
 };
 // Number of argmax partials (blocks) a logits launch writes: upper bound over K, and exact for K.
 int mgemv_blocks(int N, int B);
