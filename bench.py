@@ -37,7 +37,7 @@ HBM_PEAK = 8.0e12
 DEFAULT = "whisper_large_bf16_b64"
 DT_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 ATTN_SRC = os.path.join(ROOT, "kv_cached_autoregressive_amd", "csrc", "k_attn.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cross_attention_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_cross_whisper_large_bf16_b64_traffic.json")
 
 
 def whisper_bytes_per_step(w, pos: int) -> int:
@@ -71,6 +71,46 @@ def traffic_per_launch():
         return int(t["hbm_bytes_per_launch"])
     except Exception:
         return None
+
+
+COPY_PROBE_BYTES = 256 << 20
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str, commands: list) -> dict:
+    """HBM bytes per cross-attention launch from two rocprofv3 --pmc runs of
+    `bench.py --traffic-probe` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).
+    Each counter is scaled by what it reads for the probe's device copy of
+    COPY_PROBE_BYTES (the largest copy dispatch of the run), so the result is in
+    the copy's bytes."""
+    import csv
+
+    def per_kernel(path, counter):
+        attn, copies = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name, v = r["Kernel_Name"], float(r["Counter_Value"])
+            if "k_attn<" in name and ", true>" in name:
+                attn.append(v)
+            elif "copyBuffer" in name:
+                copies.append(v)
+        if not attn or not copies:
+            raise SystemExit(f"{path}: no cross-attention or copy dispatches with {counter}")
+        return sum(attn) / len(attn), max(copies), len(attn)
+
+    fa, fc, n = per_kernel(fetch_csv, "FETCH_SIZE")
+    wa, wc, _ = per_kernel(write_csv, "WRITE_SIZE")
+    ref_kib = COPY_PROBE_BYTES / 1024
+    f_fac, w_fac = fc / ref_kib, wc / ref_kib
+    fetch_b, write_b = fa * 1024 / f_fac, wa * 1024 / w_fac
+    return {"kernel": "k_attn (cross-attention)", "dispatches": n,
+            "fetch_kib_per_dispatch": fa, "write_kib_per_dispatch": wa,
+            "copy_probe_bytes": COPY_PROBE_BYTES, "copy_fetch_kib": fc, "copy_write_kib": wc,
+            "fetch_scale": f_fac, "write_scale": w_fac,
+            "hbm_fetch_bytes_per_launch": int(fetch_b), "hbm_write_bytes_per_launch": int(write_b),
+            "hbm_bytes_per_launch": int(fetch_b + write_b),
+            "kernel_source_sha256": hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest(),
+            "commands": commands}
 
 
 def cpu_baseline(w, budget_s: float):
@@ -111,9 +151,22 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle decode steps")
     ap.add_argument("--profile-layer", type=int, default=0, help="layer whose cross-attention launches are timed")
+    ap.add_argument("--profile-positions", type=int, default=16, help="positions of the kernel-timing run")
+    ap.add_argument("--profile-repeats", type=int, default=8, help="back-to-back launches per timed event pair")
     ap.add_argument("--positions", type=int, default=0,
                     help="profiling aid: decode only the first N positions of each window")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="after the run, one device copy of a known size (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the cross-attention traffic summary under profiles/ from two --pmc runs and exit")
+    ap.add_argument("--commands", nargs="*", default=[], help="the profiler commands, recorded in the summary")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        out = summarize_traffic(*args.summarize_traffic, args.commands)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(out, f, indent=1)
+        print(json.dumps(out))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU: the decoder step is measured on a single MI355X and no "
@@ -148,13 +201,16 @@ def main():
     stream = dec.stream
     ctx = dec.ctx
 
+    def steps(n):
+        for p in range(n):
+            tok = prompt[p] if p < prompt.shape[0] else amax
+            K.wd_step(ctx, tok.data_ptr(), pos_all[p].data_ptr(), B, 0, amax.data_ptr())
+
     def window(ev=None):
         K.wd_cross_kv(ctx, enc.data_ptr(), w.frames)
         if ev is not None:
             ev.record(stream)
-        for p in range(S):
-            tok = prompt[p] if p < prompt.shape[0] else amax
-            K.wd_step(ctx, tok.data_ptr(), pos_all[p].data_ptr(), B, 0, amax.data_ptr())
+        steps(S)
 
     torch.cuda.synchronize()
     torch.cuda.set_stream(stream)          # everything below is queued on the decoder's stream
@@ -181,13 +237,22 @@ def main():
     xkv_ms = sum(starts[i].elapsed_time(mids[i]) for i in range(args.steps)) / args.steps
     if dec.check() != 0:
         raise RuntimeError(dec.last_error())
-    # kernel timing: HIP events around every cross-attention launch of one layer, over a
-    # window of the same shape run right after (steps are launched one by one there,
-    # since a captured step replays without per-launch host hooks)
-    K.wd_profile(ctx, K.K_CROSS_ATTN, args.profile_layer)
-    window()
+    # kernel timing: HIP events on the decoder's stream around the cross-attention of one
+    # layer, issued `repeats` times back to back per step (the launch is idempotent), over
+    # the first positions of a window run right after the timed ones (steps are launched
+    # one by one there, since a captured step replays without per-launch host hooks); the
+    # cross-attention reads all frames at every position, so any positions will do
+    K.wd_profile(ctx, K.K_CROSS_ATTN, args.profile_layer, args.profile_repeats)
+    steps(min(S, args.profile_positions))
     attn_ms, attn_n = K.wd_profile_read(ctx)
-    K.wd_profile(ctx, -1, -1)
+    K.wd_profile(ctx, -1, -1, 1)
+    if args.traffic_probe:
+        src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.zeros_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ms_window = total_ms / args.steps
     dec_ms = ms_window - xkv_ms

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define WD_ABI_VERSION 1
+#define WD_ABI_VERSION 2
 #define WD_MAX_BATCH 64
 
 typedef struct wd_ctx wd_ctx;
@@ -178,13 +178,17 @@ const char* wd_last_error(const wd_ctx* ctx);
 void wd_free(wd_ctx* ctx);
 
 /* --- measurement support ------------------------------------------------
- * Records a pair of HIP events on the context's stream around every launch
+ * Records a pair of HIP events on the context's stream around the launches
  * of kernel class `kernel` in layer `layer` (-1: all layers) during later
- * wd_step / wd_cross_kv calls; wd_profile_read sums their elapsed times
- * (synchronising first).  kernel: 0 cross-attention, 1 self-attention,
- * 2 logits + argmax, 3 cross-K/V GEMM, 4 FFN fc1 projection.
- * wd_profile(ctx, -1, 0) disables recording and clears the totals.        */
-wd_status wd_profile(wd_ctx* ctx, int32_t kernel, int32_t layer);
+ * wd_step / wd_cross_kv calls; each such launch is issued `repeats` times back
+ * to back between its two events (1..64; every class's launch is idempotent,
+ * so results do not change), which spreads the event overhead over the group.
+ * wd_profile_read returns the summed elapsed time and the number of kernel
+ * launches it covers (synchronising first).  kernel: 0 cross-attention,
+ * 1 self-attention, 2 logits + argmax, 3 cross-K/V GEMM, 4 FFN fc1 projection.
+ * wd_profile(ctx, -1, 0, 1) disables recording and clears the totals.
+ * Errors: ARG (unknown class, repeats out of range).                        */
+wd_status wd_profile(wd_ctx* ctx, int32_t kernel, int32_t layer, int32_t repeats);
 wd_status wd_profile_read(wd_ctx* ctx, double* total_ms, int64_t* launches);
 
 /* --- test hook ------------------------------------------------------------

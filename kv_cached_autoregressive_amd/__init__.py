@@ -81,7 +81,7 @@ def lib():
             "wd_check": (i32, [vp]),
             "wd_last_error": (ctypes.c_char_p, [vp]),
             "wd_free": (None, [vp]),
-            "wd_profile": (i32, [vp, i32, i32]),
+            "wd_profile": (i32, [vp, i32, i32, i32]),
             "wd_profile_read": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
             "wd_debug_cache": (i32, [vp, i32, i32, ctypes.POINTER(vp)]),
         }
@@ -160,8 +160,8 @@ def wd_free(ctx):
     lib().wd_free(ctx)
 
 
-def wd_profile(ctx, kernel: int, layer: int = -1):
-    _check(lib().wd_profile(ctx, kernel, layer), ctx)
+def wd_profile(ctx, kernel: int, layer: int = -1, repeats: int = 1):
+    _check(lib().wd_profile(ctx, kernel, layer, repeats), ctx)
 
 
 def wd_profile_read(ctx):

@@ -37,7 +37,9 @@ __device__ __forceinline__ void write_o(float* out, int out_ld, void* o_hi, void
 
 // One query per block (NQ == 1) is kept to <= 96 VGPRs: 5 waves per SIMD, so 5 blocks per
 // CU and 1280 blocks (64 rows x 20 heads) resident at once, with no second partial round.
-template <typename CT, int HD, int NQ>
+// CROSS only separates the two uses into distinct kernels for profiling (the cross
+// attention over the encoder frames has no positions; the self attention reads rows 0..pos).
+template <typename CT, int HD, int NQ, bool CROSS>
 __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
   constexpr int SEGS = HD / 8;          // lanes per cache row (16 bytes each)
   constexpr int RPP = 256 / SEGS;       // rows per block pass
@@ -260,10 +262,13 @@ __global__ __launch_bounds__(HD) void k_attn_combine(const float* __restrict__ p
 template <typename CT, int HD>
 static hipError_t run_hd(const AttnParams& p, int nq, hipStream_t s) {
   dim3 grid(p.n_splits, p.Hkv, p.B / p.q_per_kvb);
-  if (nq <= 1) k_attn<CT, HD, 1><<<grid, 256, 0, s>>>(p);
-  else if (nq <= 2) k_attn<CT, HD, 2><<<grid, 256, 0, s>>>(p);
-  else if (nq <= 4) k_attn<CT, HD, 4><<<grid, 256, 0, s>>>(p);
-  else k_attn<CT, HD, 8><<<grid, 256, 0, s>>>(p);
+#define WD_ATT(C_)                                                          \
+  if (nq <= 1) k_attn<CT, HD, 1, C_><<<grid, 256, 0, s>>>(p);              \
+  else if (nq <= 2) k_attn<CT, HD, 2, C_><<<grid, 256, 0, s>>>(p);         \
+  else if (nq <= 4) k_attn<CT, HD, 4, C_><<<grid, 256, 0, s>>>(p);         \
+  else k_attn<CT, HD, 8, C_><<<grid, 256, 0, s>>>(p);
+  if (p.pos) { WD_ATT(false) } else { WD_ATT(true) }
+#undef WD_ATT
   return hipGetLastError();
 }
 

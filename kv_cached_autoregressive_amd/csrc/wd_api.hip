@@ -203,7 +203,7 @@ Plan make_plan(const wd_config& c) {
   return p;
 }
 
-struct ProfPair { hipEvent_t a, b; };
+struct ProfPair { hipEvent_t a, b; int n; };
 
 // A captured step: every launch of one wd_step call, replayed with hipGraphLaunch
 // while the call's device pointers, row count, current self cache and frame count
@@ -233,7 +233,7 @@ struct wd_ctx {
   bool use_graphs = true;
   std::vector<GraphEntry> graphs;
   // measurement
-  int prof_kernel = -1, prof_layer = -1;
+  int prof_kernel = -1, prof_layer = -1, prof_repeats = 1;
   std::vector<ProfPair> prof;
   size_t prof_used = 0;
 
@@ -270,7 +270,11 @@ void prof_begin(wd_ctx* c, bool on) {
   if (on) (void)hipEventRecord(c->prof[c->prof_used].a, c->stream);
 }
 void prof_end(wd_ctx* c, bool on) {
-  if (on) { (void)hipEventRecord(c->prof[c->prof_used].b, c->stream); ++c->prof_used; }
+  if (on) {
+    (void)hipEventRecord(c->prof[c->prof_used].b, c->stream);
+    c->prof[c->prof_used].n = c->prof_repeats;
+    ++c->prof_used;
+  }
 }
 
 // Rows of one step share encoder sets in groups of q_per_kvb rows.
@@ -376,7 +380,8 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
     {
       const bool on = prof_on(c, PK_SELF_ATTN, l);
       prof_begin(c, on);
-      HIPCHK(c, wd::launch_attention(ap, s), "self attention");
+      for (int r_ = 0; r_ < (on ? c->prof_repeats : 1); ++r_)
+        HIPCHK(c, wd::launch_attention(ap, s), "self attention");
       prof_end(c, on);
     }
     HIPCHK(c, wd::launch_attention_combine(ap, s), "self attention combine");
@@ -399,7 +404,8 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
       {
         const bool on = prof_on(c, PK_CROSS_ATTN, l);
         prof_begin(c, on);
-        HIPCHK(c, wd::launch_attention(cp, s), "cross attention");
+        for (int r_ = 0; r_ < (on ? c->prof_repeats : 1); ++r_)
+          HIPCHK(c, wd::launch_attention(cp, s), "cross attention");
         prof_end(c, on);
       }
       HIPCHK(c, wd::launch_attention_combine(cp, s), "cross attention combine");
@@ -408,7 +414,8 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
       {
         const bool on = prof_on(c, PK_FC1, l);
         prof_begin(c, on);
-        WDCHK(gemm(proj(c->at(L.w1), ff, d, yh, yl, wd::EPI_GELU_SPLIT, c->at<float>(L.b1), nullptr, 0, 1.0f), "fc1"));
+        for (int r_ = 0; r_ < (on ? c->prof_repeats : 1); ++r_)
+          WDCHK(gemm(proj(c->at(L.w1), ff, d, yh, yl, wd::EPI_GELU_SPLIT, c->at<float>(L.b1), nullptr, 0, 1.0f), "fc1"));
         prof_end(c, on);
       }
       WDCHK(gemm(proj(c->at(L.w2), d, ff, hh, hl, wd::EPI_RESID, c->at<float>(L.b2), x, d, 1.0f), "fc2"));
@@ -417,7 +424,8 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
       {
         const bool on = prof_on(c, PK_FC1, l);
         prof_begin(c, on);
-        WDCHK(gemm(proj(c->at(L.wgu), 2 * ff, d, yh, yl, wd::EPI_SWIGLU_SPLIT, nullptr, nullptr, 0, 1.0f),
+        for (int r_ = 0; r_ < (on ? c->prof_repeats : 1); ++r_)
+          WDCHK(gemm(proj(c->at(L.wgu), 2 * ff, d, yh, yl, wd::EPI_SWIGLU_SPLIT, nullptr, nullptr, 0, 1.0f),
                    "gate|up projection"));
         prof_end(c, on);
       }
@@ -436,7 +444,8 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
   {
     const bool on = prof_on(c, PK_LOGITS, -1);
     prof_begin(c, on);
-    HIPCHK(c, wd::launch_mgemv(hm, s), "logits");
+    for (int r_ = 0; r_ < (on ? c->prof_repeats : 1); ++r_)
+      HIPCHK(c, wd::launch_mgemv(hm, s), "logits");
     prof_end(c, on);
   }
   HIPCHK(c, wd::launch_argmax_final(hm.amax, wd::mgemv_blocks_k(g.vocab, d, B), g.max_batch, B, argmax, s), "argmax");
@@ -514,7 +523,8 @@ wd_status run_step(wd_ctx* c, const int32_t* tok, int tok_stride, const int32_t*
     {
       const bool on = prof_on(c, PK_SELF_ATTN, l);
       prof_begin(c, on);
-      HIPCHK(c, wd::launch_attention(ap, s), "self attention");
+      for (int r_ = 0; r_ < (on ? c->prof_repeats : 1); ++r_)
+        HIPCHK(c, wd::launch_attention(ap, s), "self attention");
       prof_end(c, on);
     }
     HIPCHK(c, wd::launch_attention_combine(ap, s), "self attention combine");
@@ -538,7 +548,8 @@ wd_status run_step(wd_ctx* c, const int32_t* tok, int tok_stride, const int32_t*
       {
         const bool on = prof_on(c, PK_CROSS_ATTN, l);
         prof_begin(c, on);
-        HIPCHK(c, wd::launch_attention(cp, s), "cross attention");
+        for (int r_ = 0; r_ < (on ? c->prof_repeats : 1); ++r_)
+          HIPCHK(c, wd::launch_attention(cp, s), "cross attention");
         prof_end(c, on);
       }
       HIPCHK(c, wd::launch_attention_combine(cp, s), "cross attention combine");
@@ -552,7 +563,8 @@ wd_status run_step(wd_ctx* c, const int32_t* tok, int tok_stride, const int32_t*
       {
         const bool on = prof_on(c, PK_FC1, l);
         prof_begin(c, on);
-        HIPCHK(c, wd::launch_gemv(gp, s), "fc1");
+        for (int r_ = 0; r_ < (on ? c->prof_repeats : 1); ++r_)
+          HIPCHK(c, wd::launch_gemv(gp, s), "fc1");
         prof_end(c, on);
       }
       gp.W = c->at(L.w2); gp.N = d; gp.K = ff; gp.Y = h; gp.ldy = ff; gp.epi = wd::EPI_RESID;
@@ -565,7 +577,8 @@ wd_status run_step(wd_ctx* c, const int32_t* tok, int tok_stride, const int32_t*
       {
         const bool on = prof_on(c, PK_FC1, l);
         prof_begin(c, on);
-        HIPCHK(c, wd::launch_gemv(gp, s), "gate|up projection");
+        for (int r_ = 0; r_ < (on ? c->prof_repeats : 1); ++r_)
+          HIPCHK(c, wd::launch_gemv(gp, s), "gate|up projection");
         prof_end(c, on);
       }
       gp.W = c->at(L.wdn); gp.N = d; gp.K = ff; gp.Y = h; gp.ldy = 2 * ff; gp.ymode = wd::Y_SWIGLU;
@@ -584,7 +597,8 @@ wd_status run_step(wd_ctx* c, const int32_t* tok, int tok_stride, const int32_t*
   {
     const bool on = prof_on(c, PK_LOGITS, -1);
     prof_begin(c, on);
-    HIPCHK(c, wd::launch_gemv(hp, s), "logits");
+    for (int r_ = 0; r_ < (on ? c->prof_repeats : 1); ++r_)
+      HIPCHK(c, wd::launch_gemv(hp, s), "logits");
     prof_end(c, on);
   }
   HIPCHK(c, wd::launch_argmax_final(hp.amax, wd::gemv_blocks(g.vocab, B), g.max_batch, B, argmax, s), "argmax");
@@ -960,9 +974,10 @@ void wd_free(wd_ctx* ctx) {
   delete ctx;
 }
 
-wd_status wd_profile(wd_ctx* ctx, int32_t kernel, int32_t layer) {
+wd_status wd_profile(wd_ctx* ctx, int32_t kernel, int32_t layer, int32_t repeats) {
   if (!ctx) return WD_ERR_ARG;
   if (kernel < -1 || kernel > 4) return fail(ctx, WD_ERR_ARG, "wd_profile: unknown kernel class");
+  if (repeats < 1 || repeats > 64) return fail(ctx, WD_ERR_ARG, "wd_profile: repeats must be in [1, 64]");
   if (ctx->prof.empty() && kernel >= 0) {
     ctx->prof.resize(4096);
     for (auto& pr : ctx->prof) {
@@ -972,6 +987,7 @@ wd_status wd_profile(wd_ctx* ctx, int32_t kernel, int32_t layer) {
   }
   ctx->prof_kernel = kernel;
   ctx->prof_layer = layer;
+  ctx->prof_repeats = repeats;
   ctx->prof_used = 0;
   return WD_OK;
 }
@@ -980,13 +996,15 @@ wd_status wd_profile_read(wd_ctx* ctx, double* total_ms, int64_t* launches) {
   if (!ctx || !total_ms || !launches) return WD_ERR_ARG;
   HIPCHK(ctx, hipStreamSynchronize(ctx->stream), "wd_profile_read: sync");
   double t = 0.0;
+  int64_t n = 0;
   for (size_t i = 0; i < ctx->prof_used; ++i) {
     float ms = 0.f;
     HIPCHK(ctx, hipEventElapsedTime(&ms, ctx->prof[i].a, ctx->prof[i].b), "wd_profile_read: elapsed");
     t += ms;
+    n += ctx->prof[i].n;
   }
   *total_ms = t;
-  *launches = (int64_t)ctx->prof_used;
+  *launches = n;
   ctx->prof_used = 0;
   return WD_OK;
 }
