@@ -42,11 +42,20 @@ def _qwen_parity(w, T, steps, streams):
     D = OQ.dims_of(w)
     worst = 0.0
     for b in streams:
+        say(f"  oracle full prefix, row {b}")
         seq = np.concatenate([ids[b], dec_ids[b]])
         ref = OQ.decode_full(D, W, seq, round_cache=True, embeds=audio[b] if A else None, offset=off)
         e, _ = compare_logits(w, np.stack(got[b]), ref[T - 1:], f"row {b}")
         worst = max(worst, e)
     say(f"  worst err {worst:.3e}")
+
+
+@pytest.mark.slow
+def test_qwen3_full_prefill_and_decode_sampled_rows():
+    """The Qwen3-ASR workload at its full size: 28 layers, 8 rows, a 900-token prefill with
+    750 audio rows at offset 10, then 124 decode steps to the context end; rows 0 and 7
+    against the oracle's full-prefix recompute."""
+    _qwen_parity(WL.by_name("qwen3asr_bf16_b8"), T=900, steps=124, streams=(0, 7))
 
 
 def test_qwen3_reduced_layers_full_width():

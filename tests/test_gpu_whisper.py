@@ -94,6 +94,7 @@ def _sampled_parity(w, steps, streams, frames=None):
     D = OW.dims_of(w)
     worst = 0.0
     for b in streams:
+        say(f"  oracle full prefix, row {b}")
         e = b // (w.batch // w.n_enc)
         ref = OW.decode_full(D, W, ids[b], enc[e, :F], round_cache=True)
         err, _ = compare_logits(w, np.stack(got[b]), ref, f"row {b}")
@@ -108,6 +109,19 @@ def test_small_f16_b16_sampled_rows():
 def test_large_bf16_b64_reduced_layers():
     w = WL.reduced(WL.by_name("whisper_large_bf16_b64"), layers=3)
     _sampled_parity(w, steps=24, streams=(0, 63))
+
+
+@pytest.mark.slow
+def test_large_bf16_b64_full_window_sampled_rows():
+    """The large-v3 workload at its full size: 32 layers, 64 rows with their own encoder
+    sets, all 448 positions (teacher-forced ids); rows 0 and 63 against the oracle's
+    full-prefix recompute at every position."""
+    _sampled_parity(WL.by_name("whisper_large_bf16_b64"), steps=448, streams=(0, 63))
+
+
+@pytest.mark.slow
+def test_small_f16_b16_full_window_sampled_rows():
+    _sampled_parity(WL.by_name("whisper_small_f16_b16"), steps=224, streams=(0, 15))
 
 
 @pytest.mark.parametrize("batch", [24, 40])
