@@ -471,20 +471,26 @@ __global__ __launch_bounds__(64 * KS * RT) void k_mgemv_lds(MGemvParams p) {
 // Split-K variant for B > 16.  At 32..64 rows the activations of a K step (hi + lo, 4-8 KB)
 // outweigh its weight tile, so the kernel is shaped around reading them as rarely as possible:
 // a workgroup of NWV waves owns NWV*NBW 16-row tiles (64..128 outputs) and one of G groups of
-// at most S K steps.  Every load of the group is issued up front in step order (the step's
-// activation slice, then its weight tiles), so data arrives step by step; each step's
-// activations go to their own LDS slot as soon as they land (one barrier per step) and the
-// step's MFMAs run while later steps are still in flight.  With G > 1 the K groups write fp32
+// at most S K steps.  Every load of the group is issued up front (a step's activation slice,
+// then its weight tiles); the activations are staged once in LDS behind one barrier (a
+// barrier per step measured slower: its LDS round trips outweigh the overlap), and each
+// wave then runs the MFMAs of all its steps back to back.  With G > 1 the K groups write fp32
 // partials part[g][b][n] that the consumer adds in order (the next norm for a residual, the
 // attention prologue for q and the appended K/V row, else launch_mgemv_finish); with G == 1
 // the usual epilogue runs here.
-template <typename T, int NBW, int NBB, int S, int NWV>
-__global__ __launch_bounds__(64 * NWV) void k_mgemv_sk(MGemvParams p) {
+template <typename T, int NBW, int NBB, int S, int KS>
+__global__ __launch_bounds__(256 * KS) void k_mgemv_sk(MGemvParams p) {
+  // 4 column waves x KS K slices: the KS waves of a column tile take alternate steps of the
+  // group (more waves per CU keep more loads in flight) and add up through LDS at the end
+  constexpr int NWV = 4, NW = NWV * KS;
   constexpr int YT = NBB * 2;                              // activation tiles of one step
-  constexpr int PER = (YT * 64 + 64 * NWV - 1) / (64 * NWV);   // staging loads per thread per step
-  __shared__ mv4u ys[S * YT * 64 > NBB * 8 ? S * YT * 64 : NBB * 8];   // also the argmax keys
+  constexpr int PER = (YT * 64 + 64 * NW - 1) / (64 * NW);  // staging loads per thread per step
+  constexpr int STAGE = S * YT * 64;                       // mv4u of the staging buffer
+  constexpr int RED = KS > 1 ? (NW - NWV) * NBW * NBB * 64 : 0;   // mv4u of the K-slice partials
+  __shared__ mv4u ys[(STAGE > RED ? STAGE : RED) > NBB * 8 ? (STAGE > RED ? STAGE : RED) : NBB * 8];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cw = w % NWV, ks = w / NWV;
   const int NB = (p.N + 15) >> 4;
   const int KST = p.K >> 5;
   const int G = p.part_G;
@@ -502,7 +508,7 @@ __global__ __launch_bounds__(64 * NWV) void k_mgemv_sk(MGemvParams p) {
     cg = L / G;
   }
   const int s_lo = (g * KST) / G, n = ((g + 1) * KST) / G - s_lo;   // 1 <= n <= S (host)
-  const int tile = cg * NWV + w;                                    // this wave's group of NBW tiles
+  const int tile = cg * NWV + cw;                                   // this wave's group of NBW tiles
   const mv4u* __restrict__ Wv = reinterpret_cast<const mv4u*>(p.W);
   const mv4u* __restrict__ Yh = reinterpret_cast<const mv4u*>(p.Yhi);
   const mv4u* __restrict__ Yl = reinterpret_cast<const mv4u*>(p.Ylo);
@@ -510,20 +516,25 @@ __global__ __launch_bounds__(64 * NWV) void k_mgemv_sk(MGemvParams p) {
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) wbase[nb] = (int64_t)min(tile * NBW + nb, NB - 1) * KST * 64 + lane;
 
-  // all loads up front, in step order (steps past n reload step n-1; their MFMAs see zero weights)
-  mv4u yr[S][PER], wr[S][NBW];
+  // all loads up front, in step order (steps past n reload step n-1; their MFMAs see zero
+  // weights); a wave loads the weight tiles of its own steps only
+  constexpr int SW = (S + KS - 1) / KS;                    // steps per K slice
+  mv4u yr[S][PER], wr[SW][NBW];
 #pragma unroll
   for (int i = 0; i < S; ++i) {
     const int st = s_lo + min(i, n - 1);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const int flat = min((int)threadIdx.x + j * 64 * NWV, YT * 64 - 1);
+      const int flat = min((int)threadIdx.x + j * 64 * NW, YT * 64 - 1);
       const int t = flat >> 6;                    // tile: row block t/2, hi or lo by t%2
       const mv4u* src = (t & 1) ? Yl : Yh;
       yr[i][j] = src[((int64_t)(t >> 1) * KST + st) * 64 + (flat & 63)];
     }
+    if (i % KS == 0) {
+      const int mine = s_lo + min(i + ks, n - 1);
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) wr[i][nb] = Wv[wbase[nb] + (int64_t)st * 64];
+      for (int nb = 0; nb < NBW; ++nb) wr[i / KS][nb] = Wv[wbase[nb] + (int64_t)mine * 64];
+    }
   }
 
   mf32x4_t acc[NBW][NBB];
@@ -536,28 +547,58 @@ __global__ __launch_bounds__(64 * NWV) void k_mgemv_sk(MGemvParams p) {
     mv4u* slot = ys + i * YT * 64;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const int flat = threadIdx.x + j * 64 * NWV;
-      if ((YT * 64) % (64 * NWV) == 0 || flat < YT * 64) slot[flat] = yr[i][j];
+      const int flat = threadIdx.x + j * 64 * NW;
+      if ((YT * 64) % (64 * NW) == 0 || flat < YT * 64) slot[flat] = yr[i][j];
     }
-    __syncthreads();   // step i's activation tiles are in LDS
-    const bool live = i < n;
+  }
+  __syncthreads();   // every step's activation tiles are in LDS
+#pragma unroll
+  for (int i0 = 0; i0 < S; i0 += KS) {
+    const int mi = i0 + ks;                       // this K slice's step
+    const bool live = mi < n && mi < S;
     mv4u wv[NBW];
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) wv[nb] = keep_if(wr[i][nb], live);
+    for (int nb = 0; nb < NBW; ++nb) wv[nb] = keep_if(wr[i0 / KS][nb], live);
+    const mv4u* sl = ys + min(mi, S - 1) * YT * 64;
 #pragma unroll
     for (int part = 0; part < 2; ++part)          // hi then lo: consecutive MFMAs are independent
 #pragma unroll
       for (int bb = 0; bb < NBB; ++bb) {
-        const mv4u y = slot[(bb * 2 + part) * 64 + lane];
+        const mv4u y = sl[(bb * 2 + part) * 64 + lane];
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) acc[nb][bb] = mma(y, wv[nb], acc[nb][bb], (T*)nullptr);
       }
   }
+  if constexpr (KS > 1) {   // add the K slices of each column tile, fixed order
+    __syncthreads();        // the staging buffer is reused for the slice partials
+    float* red = reinterpret_cast<float*>(ys);
+    if (ks > 0) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            red[((((ks - 1) * NWV + cw) * NBW + nb) * NBB + bb) * 256 + r * 64 + lane] = acc[nb][bb][r];
+    }
+    __syncthreads();
+    if (ks == 0) {
+      for (int k2 = 1; k2 < KS; ++k2)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+          for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[nb][bb][r] += red[((((k2 - 1) * NWV + cw) * NBW + nb) * NBB + bb) * 256 + r * 64 + lane];
+    }
+  }
   if (G == 1) {
     __syncthreads();   // the staging buffer is reused for argmax keys
-    mg_epilogue<T, NBW, NBB, NWV>(p, acc, true, tile, NB, reinterpret_cast<unsigned long long*>(ys));
+    mg_epilogue<T, NBW, NBB, NW>(p, acc, ks == 0, tile, NB, reinterpret_cast<unsigned long long*>(ys));
     return;
   }
+  if (ks != 0) return;
   const int rsub = (lane >> 4) * 4, col = lane & 15;
   float* P = p.part + (int64_t)g * p.B * p.N;
 #pragma unroll
@@ -566,7 +607,7 @@ __global__ __launch_bounds__(64 * NWV) void k_mgemv_sk(MGemvParams p) {
     for (int bb = 0; bb < NBB; ++bb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int nn = (tile * NBW + nb) * 16 + col, b = bb * 16 + rsub + r;   // tile from cg
+        const int nn = (tile * NBW + nb) * 16 + col, b = bb * 16 + rsub + r;
         if (nn < p.N && b < p.B && tile * NBW + nb < NB) P[(int64_t)b * p.N + nn] = acc[nb][bb][r];
       }
 }
@@ -607,21 +648,35 @@ static bool sk_pick(int N, int K, int B, int epi, SkShape& s) {
   const int NB = (N + 15) / 16, KST = K / 32;
   s.NBB = B <= 32 ? 2 : 4;
   s.NBW = (NB >= 256 || KST >= 128 || epi == EPI_SWIGLU_SPLIT) ? 2 : 1;
-  const int ncg = (NB + 4 * s.NBW - 1) / (4 * s.NBW);
+  int ncg = (NB + 4 * s.NBW - 1) / (4 * s.NBW);
   int S = forces > 0 ? forces : (KST * ncg + 255) / 256;
   S = std::max(2, std::min(S, 8));
   int G = (KST + S - 1) / S;
+  if (ncg * G > 256 && s.NBW == 1 && !forces) {   // past one workgroup per CU: wider column groups
+    s.NBW = 2;
+    ncg = (NB + 7) / 8;
+    S = std::max(2, std::min((KST * ncg + 255) / 256, 8));
+    G = (KST + S - 1) / S;
+  }
   // narrow outputs (N <= 2048): every XCD would fetch all the activations, which weigh as
   // much as the partials; with G a multiple of 8 each XCD fetches one K eighth of them
   if (N <= 2048 && KST >= 16 && !forces) G = 8 * ((KST + 63) / 64);
   if (G > 32) return false;             // the consumers add at most 32 partial slabs
   s.G = G;
-  s.NSC = (KST + G - 1) / G <= 4 ? 4 : 8;   // steps per group, rounded up to an instance
+  s.NSC = std::max(4, (KST + G - 1) / G);   // the longest group's steps (4..8): at most one padded step
   return true;
 }
 int mgemv_groups(int N, int K, int B, int epi) {
   SkShape s;
   return sk_pick(N, K, B, epi, s) ? s.G : 1;
+}
+
+// K slices per column tile inside a split-K workgroup (1: 4 waves, 2: 8 waves).
+// Tuning override: WD_MGEMV_SKK=1|2.
+static int sk_slices() {
+  static int ks = -1;
+  if (ks < 0) { const char* e = getenv("WD_MGEMV_SKK"); ks = e ? atoi(e) : 1; if (ks != 2) ks = 1; }
+  return ks;
 }
 
 template <typename T>
@@ -632,13 +687,16 @@ static hipError_t skrun(const MGemvParams& p0, const SkShape& s, hipStream_t st)
   MGemvParams p = p0;
   p.part_G = s.G;
   const dim3 grid(ncg * s.G);
-#define WD_SK(NBW_, NBB_, NSC_)                                             \
-  if (s.NBW == NBW_ && s.NBB == NBB_ && s.NSC == NSC_) {                    \
-    k_mgemv_sk<T, NBW_, NBB_, NSC_, 4><<<grid, 256, 0, st>>>(p);            \
-    return hipGetLastError();                                               \
+  const int KS = sk_slices();
+#define WD_SK(NBW_, NBB_, NSC_)                                                  \
+  if (s.NBW == NBW_ && s.NBB == NBB_ && s.NSC == NSC_) {                         \
+    if (KS == 2) k_mgemv_sk<T, NBW_, NBB_, NSC_, 2><<<grid, 512, 0, st>>>(p);   \
+    else k_mgemv_sk<T, NBW_, NBB_, NSC_, 1><<<grid, 256, 0, st>>>(p);            \
+    return hipGetLastError();                                                    \
   }
-  WD_SK(1, 2, 4) WD_SK(2, 2, 4) WD_SK(1, 4, 4) WD_SK(2, 4, 4)
-  WD_SK(1, 2, 8) WD_SK(2, 2, 8) WD_SK(1, 4, 8) WD_SK(2, 4, 8)
+#define WD_SK_S(S_) WD_SK(1, 2, S_) WD_SK(2, 2, S_) WD_SK(1, 4, S_) WD_SK(2, 4, S_)
+  WD_SK_S(4) WD_SK_S(5) WD_SK_S(6) WD_SK_S(7) WD_SK_S(8)
+#undef WD_SK_S
 #undef WD_SK
   return hipErrorInvalidValue;
 }
