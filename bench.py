@@ -113,6 +113,129 @@ def summarize_traffic(fetch_csv: str, write_csv: str, commands: list) -> dict:
             "commands": commands}
 
 
+def qwen_bytes_per_step(w, pos: int) -> int:
+    """Algorithmic HBM bytes of one Qwen3 decode step at position `pos`: every weight once
+    (q, k, v, o, gate, up, down, the norms, the tied head), the B embedding rows and the
+    K/V rows 0..pos of every row and layer."""
+    d, ff, L, hd = w.d, w.d_ff, w.layers, w.head_dim
+    wb, cb = DT_BYTES[w.w_dtype], DT_BYTES[w.cache_dtype]
+    qd, kvd = w.heads * hd, w.kv_heads * hd
+    per_layer = (d * qd + 2 * d * kvd + qd * d + 3 * d * ff) * wb + (2 * d + 2 * hd) * 4
+    glob = w.vocab * d * wb + d * 4 + w.batch * d * wb
+    kv = w.batch * L * (pos + 1) * 2 * kvd * cb
+    return L * per_layer + glob + kv
+
+
+def qwen_cpu_baseline(w, budget_s: float):
+    """The Qwen3 oracle on the host cores: one stream's decode steps from position 0 for
+    about `budget_s` seconds (no prefill; bounded sample)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import qwen3 as OQ
+    W = WL.make_weights(w)
+    O = OQ.QwenOracle(OQ.dims_of(w), W, round_cache=True)
+    del W
+    O.reset(1)
+    ids = WL.random_ids(w, 64)[:1]
+    n, t = 0, 0.0
+    while n < ids.shape[1] and (n < 2 or t < budget_s):
+        t0 = time.perf_counter()
+        O.step(ids[:, n], [n])
+        t += time.perf_counter() - t0
+        n += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": n / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 of {w.batch} streams, decode steps at positions 0..{n - 1} (float64 numpy, no prefill)"}
+
+
+def run_qwen(args, w):
+    """Qwen3-ASR: prefill of 900 positions (audio rows spliced in), then the greedy decode
+    steps to the context end, argmax on the device.  value = decode tokens/s; the prefill,
+    which goes through the step kernels position by position, is timed separately."""
+    import torch
+
+    import kv_cached_autoregressive_amd as K
+    dev = torch.device("cuda:0")
+    W = WL.make_weights(w)
+    ids_np, audio_np = WL.make_qwen_prefill(w)
+    dec = K.Decoder(w, W)
+    del W
+    wdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.w_dtype]
+    B, T, S = w.batch, w.prefill_len, w.steps
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np)).to(dev, torch.int32)
+    audio = torch.from_numpy(np.ascontiguousarray(audio_np)).to(dev, wdt)
+    pos_all = (T + torch.arange(S, dtype=torch.int32, device=dev))[:, None].repeat(1, B).contiguous()
+    amax = torch.zeros(B, dtype=torch.int32, device=dev)
+    stream, ctx = dec.stream, dec.ctx
+
+    def prefill():
+        K.wd_prefill(ctx, ids.data_ptr(), B, T, audio.data_ptr(), audio.shape[1], w.audio_offset, 0,
+                     amax.data_ptr())
+
+    def steps(n):
+        for p in range(n):
+            K.wd_step(ctx, amax.data_ptr(), pos_all[p].data_ptr(), B, 0, amax.data_ptr())
+
+    torch.cuda.synchronize()
+    torch.cuda.set_stream(stream)
+    for _ in range(args.warmup):
+        prefill()
+        steps(S)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    pre_ms, dec_ms = 0.0, 0.0
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[3 * i].record(stream)
+        prefill()
+        ev[3 * i + 1].record(stream)
+        steps(S)
+        ev[3 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    for i in range(args.steps):
+        pre_ms += ev[3 * i].elapsed_time(ev[3 * i + 1]) / args.steps
+        dec_ms += ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) / args.steps
+    if dec.check() != 0:
+        raise RuntimeError(dec.last_error())
+    # kernel timing: the gate|up projection of one layer (the largest weight stream of a layer)
+    prefill()
+    K.wd_profile(ctx, K.K_FC1, args.profile_layer, args.profile_repeats)
+    steps(min(S, args.profile_positions))
+    k_ms, k_n = K.wd_profile_read(ctx)
+    K.wd_profile(ctx, -1, -1, 1)
+    gu_bytes = 2 * w.d_ff * w.d * DT_BYTES[w.w_dtype]
+    k_avg = k_ms / 1e3 / max(k_n, 1)
+    bytes_dec = sum(qwen_bytes_per_step(w, T + p) for p in range(S))
+    out = {
+        "metric": "decoder tokens/sec at batch B; achieved HBM GB/s as % of MI355X peak",
+        "value": B * S / (dec_ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": dec_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.w_dtype,
+        "data": "synthetic (seeded random-init weights N(0,0.02), N(0,1) audio rows, uniform ids)",
+        "config": {"workload": w.name, "batch": B, "prefill": T, "positions": S, "layers": w.layers,
+                   "d": w.d, "q_heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
+                   "d_ff": w.d_ff, "vocab": w.vocab, "w_dtype": w.w_dtype, "cache_dtype": w.cache_dtype,
+                   "step": "124 greedy decode steps after the prefill (prefill timed separately)"},
+        "decode_tokens_per_s": B * S / (dec_ms / 1e3),
+        "prefill_ms": pre_ms,
+        "hbm_bytes_decode": bytes_dec,
+        "hbm_gbps_decode": bytes_dec / (dec_ms / 1e3) / 1e9,
+        "hbm_frac_decode": bytes_dec / (dec_ms / 1e3) / HBM_PEAK,
+        "wall_s": wall,
+        "roofline": {"kernel": "gate|up projection (MFMA skinny GEMM, one layer per launch)", "bound": "hbm",
+                     "achieved": gu_bytes / k_avg / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": gu_bytes / k_avg / HBM_PEAK, "traffic": None, "bytes_per_launch": gu_bytes,
+                     "avg_launch_us": k_avg * 1e6, "launches_timed": k_n},
+        "cpu_baseline": None,
+    }
+    del dec
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = qwen_cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(w, budget_s: float):
     """The oracle as it is, on the host cores: one stream of the workload, its
     cross K/V and as many decode steps as fit the time budget."""
@@ -180,12 +303,15 @@ def main():
     w = WL.by_name(args.config)
     if args.positions:
         w = WL.reduced(w, steps=min(args.positions, w.steps))
-    if w.arch != "whisper" or w.mode != "greedy":
-        print(f"bench.py times greedy Whisper-style windows; {w.name} is not one", file=sys.stderr)
-        sys.exit(2)
     K.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if w.arch == "qwen3":
+        run_qwen(args, w)
+        return
+    if w.mode != "greedy":
+        print(f"bench.py times greedy windows; {w.name} is a beam-search workload", file=sys.stderr)
+        sys.exit(2)
 
     W = WL.make_weights(w)
     enc_np = WL.make_encoder_states(w)

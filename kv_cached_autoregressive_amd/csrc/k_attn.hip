@@ -238,23 +238,32 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
   }
 }
 
-template <int HD>
+// Every split's (m, l, o[c]) is loaded before any arithmetic (splits past n_splits reload
+// the last one and get weight 0), so the loads overlap instead of one round trip per split.
+template <int HD, int MAXS>
 __global__ __launch_bounds__(HD) void k_attn_combine(const float* __restrict__ part, int n_splits,
                                                      float* __restrict__ out, int out_ld, int Hq,
                                                      void* o_hi, void* o_lo, int o_dtype) {
   const int bh = blockIdx.x, c = threadIdx.x;
   const int b = bh / Hq, h = bh - (bh / Hq) * Hq;
   const float* pp = part + (int64_t)bh * n_splits * (HD + 2);
+  float m[MAXS], l[MAXS], ov[MAXS];
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    const float* q = pp + min(s, n_splits - 1) * (HD + 2);
+    m[s] = q[HD];
+    l[s] = q[HD + 1];
+    ov[s] = q[c];
+  }
   float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, pp[s * (HD + 2) + HD]);
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) M = s < n_splits ? fmaxf(M, m[s]) : M;
   float L = 0.f, o = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float* q = pp + s * (HD + 2);
-      const float w = expf(q[HD] - M);
-      L += w * q[HD + 1];
-      o += w * q[c];
-    }
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    const float w = (s < n_splits && M != -INFINITY) ? expf(m[s] - M) : 0.f;
+    L += w * l[s];
+    o += w * ov[s];
   }
   write_o(out, out_ld, o_hi, o_lo, o_dtype, Hq, HD, b, h, c, L > 0.f ? o / L : 0.f);
 }
@@ -305,9 +314,19 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
 hipError_t launch_attention_combine(const AttnParams& p, hipStream_t s) {
   if (p.n_splits <= 1) return hipSuccess;
   if (!p.part || (!p.out && !p.o_hi)) return hipErrorInvalidValue;
-  if (p.hd == 64) k_attn_combine<64><<<p.B * p.Hq, 64, 0, s>>>(p.part, p.n_splits, p.out, p.out_ld, p.Hq, p.o_hi, p.o_lo, p.o_dtype);
-  else if (p.hd == 128) k_attn_combine<128><<<p.B * p.Hq, 128, 0, s>>>(p.part, p.n_splits, p.out, p.out_ld, p.Hq, p.o_hi, p.o_lo, p.o_dtype);
-  else return hipErrorInvalidValue;
+  if (p.n_splits > 64) return hipErrorInvalidValue;
+#define WD_CMB(HD_, MS_) \
+  k_attn_combine<HD_, MS_><<<p.B * p.Hq, HD_, 0, s>>>(p.part, p.n_splits, p.out, p.out_ld, p.Hq, p.o_hi, p.o_lo, p.o_dtype)
+  if (p.hd == 64) {
+    if (p.n_splits <= 8) WD_CMB(64, 8); else if (p.n_splits <= 16) WD_CMB(64, 16);
+    else if (p.n_splits <= 32) WD_CMB(64, 32); else WD_CMB(64, 64);
+  } else if (p.hd == 128) {
+    if (p.n_splits <= 8) WD_CMB(128, 8); else if (p.n_splits <= 16) WD_CMB(128, 16);
+    else if (p.n_splits <= 32) WD_CMB(128, 32); else WD_CMB(128, 64);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef WD_CMB
   return hipGetLastError();
 }
 

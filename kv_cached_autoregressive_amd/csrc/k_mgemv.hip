@@ -468,8 +468,9 @@ __global__ __launch_bounds__(64 * KS * RT) void k_mgemv_lds(MGemvParams p) {
   mg_epilogue<T, NBW, NBB, NW>(p, acc, ks == 0, blk0 / NBW, NB, reinterpret_cast<unsigned long long*>(lds));
 }
 
-// Split-K variant for B > 16.  At 32..64 rows the activations of a K step (hi + lo, 4-8 KB)
-// outweigh its weight tile, so the kernel is shaped around reading them as rarely as possible:
+// Split-K skinny GEMM for any B (16-, 32- or 64-row tiles).  At 32..64 rows the activations
+// of a K step (hi + lo, 4-8 KB) outweigh its weight tile, so the kernel is shaped around
+// reading them as rarely as possible, and at every B the K split gives enough workgroups:
 // a workgroup of NWV waves owns NWV*NBW 16-row tiles (64..128 outputs) and one of G groups of
 // at most S K steps.  Every load of the group is issued up front (a step's activation slice,
 // then its weight tiles); the activations are staged once in LDS behind one barrier (a
@@ -644,9 +645,9 @@ static bool sk_pick(int N, int K, int B, int epi, SkShape& s) {
     const char* f = getenv("WD_MGEMV_SKS");
     forces = f ? atoi(f) : 0;
   }
-  if (!mode || B <= 16 || epi == EPI_LOGITS) return false;
+  if (!mode || epi == EPI_LOGITS) return false;
   const int NB = (N + 15) / 16, KST = K / 32;
-  s.NBB = B <= 32 ? 2 : 4;
+  s.NBB = B <= 16 ? 1 : B <= 32 ? 2 : 4;
   s.NBW = (NB >= 256 || KST >= 128 || epi == EPI_SWIGLU_SPLIT) ? 2 : 1;
   int ncg = (NB + 4 * s.NBW - 1) / (4 * s.NBW);
   int S = forces > 0 ? forces : (KST * ncg + 255) / 256;
@@ -694,7 +695,7 @@ static hipError_t skrun(const MGemvParams& p0, const SkShape& s, hipStream_t st)
     else k_mgemv_sk<T, NBW_, NBB_, NSC_, 1><<<grid, 256, 0, st>>>(p);            \
     return hipGetLastError();                                                    \
   }
-#define WD_SK_S(S_) WD_SK(1, 2, S_) WD_SK(2, 2, S_) WD_SK(1, 4, S_) WD_SK(2, 4, S_)
+#define WD_SK_S(S_) WD_SK(1, 1, S_) WD_SK(2, 1, S_) WD_SK(1, 2, S_) WD_SK(2, 2, S_) WD_SK(1, 4, S_) WD_SK(2, 4, S_)
   WD_SK_S(4) WD_SK_S(5) WD_SK_S(6) WD_SK_S(7) WD_SK_S(8)
 #undef WD_SK_S
 #undef WD_SK

@@ -98,8 +98,8 @@ std::string check_config(const wd_config& c) {
   return "";
 }
 
-// Split of an attention over `rows` cache rows: aim at >= 2048 blocks in total (or none
-// with >= 512 slabs), at least 64 rows (one K/V tile of a few KB) per block.
+// Split of an attention over `rows` cache rows: about 1024 blocks in total (or none with
+// >= 512 slabs), at least 64 rows (one K/V tile of a few KB) per block, at most 64 splits.
 // Tuning override for sweeps: WD_ATTN_ROWS="self_rows,cross_rows" (0 keeps the policy).
 int attn_rows_override(bool cross) {
   static int sr = 0, cr = 0;
@@ -113,9 +113,10 @@ int attn_rows_override(bool cross) {
 }
 
 void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits, bool cross = false) {
-  // with >= 512 slabs every CU already streams two or more: one split, no combine launch
-  const int want = slabs >= 512 ? 1 : std::max(1, (2048 + slabs - 1) / slabs);
+  // about 1024 blocks (4 per CU) in total, or one split (no combine launch) with >= 512 slabs
+  const int want = slabs >= 512 ? 1 : std::max(1, (1024 + slabs - 1) / slabs);
   int r = (rows + want - 1) / want;
+  r = std::max(r, (rows + 63) / 64);   // at most 64 splits (the combine's limit)
   r = std::max(r, 64);
   if (const int o = attn_rows_override(cross)) r = o;
   r = (r + 31) & ~31;
