@@ -65,6 +65,39 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------------------------------
+// per-call inputs copied into the context's own buffers, so that a captured step graph reads
+// fixed addresses: tokens (stride tok_stride), positions (or the constant pos_const when
+// pos is null), and optionally B rows of `row_bytes` bytes (source stride src_stride bytes)
+// ------------------------------------------------------------------------------------------
+__global__ void k_stage(const int32_t* __restrict__ tok, int tok_stride, const int32_t* __restrict__ pos,
+                        int pos_const, int32_t* __restrict__ tok_out, int32_t* __restrict__ pos_out, int B,
+                        const uint4* __restrict__ rows, int64_t src_stride16, uint4* __restrict__ rows_out,
+                        int row16) {
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    tok_out[b] = tok[(int64_t)b * tok_stride];
+    pos_out[b] = pos ? pos[b] : pos_const;
+  }
+  if (rows)
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (int64_t)B * row16;
+         i += (int64_t)gridDim.x * blockDim.x) {
+      const int64_t b = i / row16, c = i - b * row16;
+      rows_out[i] = rows[b * src_stride16 + c];
+    }
+}
+
+hipError_t launch_stage(const int32_t* tok, int tok_stride, const int32_t* pos, int pos_const, int32_t* tok_out,
+                        int32_t* pos_out, int B, const void* rows, int64_t src_stride_bytes, void* rows_out,
+                        int64_t row_bytes, hipStream_t s) {
+  if (!tok || !tok_out || !pos_out || B <= 0 || B > 1024) return hipErrorInvalidValue;
+  if (rows && (row_bytes % 16 || src_stride_bytes % 16 || !rows_out)) return hipErrorInvalidValue;
+  const int row16 = rows ? (int)(row_bytes / 16) : 0;
+  const int blocks = rows ? (int)std::min<int64_t>(((int64_t)B * row16 + 255) / 256, 1024) : 1;
+  k_stage<<<blocks, 256, 0, s>>>(tok, tok_stride, pos, pos_const, tok_out, pos_out, B, (const uint4*)rows,
+                                 src_stride_bytes / 16, (uint4*)rows_out, row16);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
 // embedding: token row + learned position row (Whisper) or token row (Qwen3), or an
 // embedding override row (prompt audio splice).  Out-of-range ids/positions raise the
 // device flag and produce a zero row.

@@ -55,6 +55,7 @@ struct Plan {
   size_t cross = 0, cross_slab = 0;
   size_t x = 0, y = 0, q = 0, qkv = 0, o = 0, h = 0, part = 0, amax = 0, err = 0, pos_tmp = 0;
   size_t gpart = 0; int64_t gpart_cap = 0;   // split-K GEMM partials [G][B][N] fp32
+  size_t tok_in = 0, ov_in = 0;              // staged tokens [B] and embedding override rows [B, d]
   int max_splits = 1, amax_parts = 1;
 };
 
@@ -200,6 +201,8 @@ Plan make_plan(const wd_config& c) {
   p.amax = b.take((size_t)p.amax_parts * Bm * 8);
   p.err = b.take(64);
   p.pos_tmp = b.take(Bm * 4);
+  p.tok_in = b.take(Bm * 4);
+  p.ov_in = b.take(Bm * d * wb);
   p.total = (b.off + 255) & ~size_t(255);
   return p;
 }
@@ -210,10 +213,10 @@ struct ProfPair { hipEvent_t a, b; int n; };
 // while the call's device pointers, row count, current self cache and frame count
 // stay the same (the positions and tokens are read from device memory at run time).
 struct GraphKey {
-  const void* tok; const void* pos; void* logits; void* argmax; int B, cur, frames;
+  void* logits; void* argmax; int B, cur, frames, kind;   // kind: 0 step, 1 prefill row, 2 prefill row with override
   bool operator==(const GraphKey& o) const {
-    return tok == o.tok && pos == o.pos && logits == o.logits && argmax == o.argmax && B == o.B &&
-           cur == o.cur && frames == o.frames;
+    return logits == o.logits && argmax == o.argmax && B == o.B && cur == o.cur && frames == o.frames &&
+           kind == o.kind;
   }
 };
 struct GraphEntry { GraphKey key; hipGraphExec_t exec; };
@@ -850,6 +853,46 @@ static wd_status check_rows(wd_ctx* ctx, int32_t B, const char* who) {
   return WD_OK;
 }
 
+// One step over the staged inputs (tokens in tok_in, positions in pos_tmp, override rows in
+// ov_in when `ov`), replayed from a captured graph when the context allows it.  Graphs are
+// keyed by everything a step bakes in: output buffers, B, the current self cache, the frame
+// count and the step kind; the per-call inputs are copied into fixed buffers beforehand.
+static wd_status staged_step(wd_ctx* ctx, int32_t B, float* logits, int32_t* argmax, bool head, bool ov) {
+  const Plan& P = ctx->plan;
+  const int32_t* tok = ctx->at<int32_t>(P.tok_in);
+  const int32_t* pos = ctx->at<int32_t>(P.pos_tmp);
+  const void* ovp = ov ? ctx->at(P.ov_in) : nullptr;
+  const int64_t ovs = (int64_t)ctx->cfg.d_model;
+  if (!ctx->use_graphs || ctx->prof_kernel >= 0 || ctx->stream == nullptr)
+    return run_step(ctx, tok, 1, pos, ovp, ovs, B, logits, argmax, head);
+  const GraphKey key{logits, argmax, B, ctx->cur, ctx->frames, head ? 0 : (ov ? 2 : 1)};
+  for (auto& e : ctx->graphs)
+    if (e.key == key) {
+      HIPCHK(ctx, hipGraphLaunch(e.exec, ctx->stream), "step: graph launch");
+      return WD_OK;
+    }
+  HIPCHK(ctx, hipStreamBeginCapture(ctx->stream, hipStreamCaptureModeThreadLocal), "step: begin capture");
+  const wd_status r = run_step(ctx, tok, 1, pos, ovp, ovs, B, logits, argmax, head);
+  hipGraph_t graph = nullptr;
+  const hipError_t ec = hipStreamEndCapture(ctx->stream, &graph);
+  if (r != WD_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return r;
+  }
+  if (ec != hipSuccess) return fail(ctx, WD_ERR_HIP, std::string("step: end capture: ") + hipGetErrorString(ec));
+  hipGraphExec_t exec = nullptr;
+  const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (ei != hipSuccess) return fail(ctx, WD_ERR_HIP, std::string("step: instantiate: ") + hipGetErrorString(ei));
+  if (ctx->graphs.size() >= 8) {
+    (void)hipGraphExecDestroy(ctx->graphs.front().exec);
+    ctx->graphs.erase(ctx->graphs.begin());
+  }
+  ctx->graphs.push_back({key, exec});
+  HIPCHK(ctx, hipGraphLaunch(exec, ctx->stream), "step: graph launch");
+  return WD_OK;
+}
+
 wd_status wd_step(wd_ctx* ctx, const int32_t* tokens, const int32_t* positions, int32_t B, float* logits,
                   int32_t* argmax) {
   if (!ctx) return WD_ERR_ARG;
@@ -857,34 +900,10 @@ wd_status wd_step(wd_ctx* ctx, const int32_t* tokens, const int32_t* positions, 
     if (!tokens || !positions || !argmax) return fail(ctx, WD_ERR_ARG, "wd_step: tokens, positions, argmax must not be null");
     const wd_status st = check_rows(ctx, B, "wd_step");
     if (st != WD_OK) return st;
-    if (!ctx->use_graphs || ctx->prof_kernel >= 0 || ctx->stream == nullptr)
-      return run_step(ctx, tokens, 1, positions, nullptr, 0, B, logits, argmax, true);
-    const GraphKey key{tokens, positions, logits, argmax, B, ctx->cur, ctx->frames};
-    for (auto& e : ctx->graphs)
-      if (e.key == key) {
-        HIPCHK(ctx, hipGraphLaunch(e.exec, ctx->stream), "wd_step: graph launch");
-        return WD_OK;
-      }
-    HIPCHK(ctx, hipStreamBeginCapture(ctx->stream, hipStreamCaptureModeThreadLocal), "wd_step: begin capture");
-    const wd_status r = run_step(ctx, tokens, 1, positions, nullptr, 0, B, logits, argmax, true);
-    hipGraph_t graph = nullptr;
-    const hipError_t ec = hipStreamEndCapture(ctx->stream, &graph);
-    if (r != WD_OK) {
-      if (graph) (void)hipGraphDestroy(graph);
-      return r;
-    }
-    if (ec != hipSuccess) return fail(ctx, WD_ERR_HIP, std::string("wd_step: end capture: ") + hipGetErrorString(ec));
-    hipGraphExec_t exec = nullptr;
-    const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    (void)hipGraphDestroy(graph);
-    if (ei != hipSuccess) return fail(ctx, WD_ERR_HIP, std::string("wd_step: instantiate: ") + hipGetErrorString(ei));
-    if (ctx->graphs.size() >= 8) {
-      (void)hipGraphExecDestroy(ctx->graphs.front().exec);
-      ctx->graphs.erase(ctx->graphs.begin());
-    }
-    ctx->graphs.push_back({key, exec});
-    HIPCHK(ctx, hipGraphLaunch(exec, ctx->stream), "wd_step: graph launch");
-    return WD_OK;
+    const Plan& P = ctx->plan;
+    HIPCHK(ctx, wd::launch_stage(tokens, 1, positions, 0, ctx->at<int32_t>(P.tok_in), ctx->at<int32_t>(P.pos_tmp), B,
+                                 nullptr, 0, nullptr, 0, ctx->stream), "wd_step: stage inputs");
+    return staged_step(ctx, B, logits, argmax, true, false);
   } catch (...) {
     return fail(ctx, WD_ERR_INTERNAL, "wd_step: internal error");
   }
@@ -901,14 +920,16 @@ wd_status wd_prefill(wd_ctx* ctx, const int32_t* tokens, int32_t B, int32_t T, c
       return fail(ctx, WD_ERR_ARG, "wd_prefill: audio rows must lie inside the prompt");
     const wd_status st = check_rows(ctx, B, "wd_prefill");
     if (st != WD_OK) return st;
-    int32_t* ptmp = ctx->at<int32_t>(ctx->plan.pos_tmp);
+    const Plan& P = ctx->plan;
     const size_t eb = dtype_bytes(g.w_dtype);
+    const int64_t row_bytes = (int64_t)g.d_model * eb;
     for (int t = 0; t < T; ++t) {
-      HIPCHK(ctx, wd::launch_fill_i32(ptmp, t, B, ctx->stream), "prefill positions");
-      const void* ov = nullptr;
-      if (A > 0 && t >= offset && t < offset + A)
-        ov = reinterpret_cast<const char*>(embeds) + (size_t)(t - offset) * g.d_model * eb;
-      const wd_status r = run_step(ctx, tokens + t, T, ptmp, ov, (int64_t)A * g.d_model, B, logits, argmax, t == T - 1);
+      const bool ov = A > 0 && t >= offset && t < offset + A;
+      const void* src = ov ? reinterpret_cast<const char*>(embeds) + (size_t)(t - offset) * row_bytes : nullptr;
+      HIPCHK(ctx, wd::launch_stage(tokens + t, T, nullptr, t, ctx->at<int32_t>(P.tok_in), ctx->at<int32_t>(P.pos_tmp),
+                                   B, src, (int64_t)A * row_bytes, ov ? ctx->at(P.ov_in) : nullptr, row_bytes,
+                                   ctx->stream), "wd_prefill: stage inputs");
+      const wd_status r = staged_step(ctx, B, t == T - 1 ? logits : nullptr, argmax, t == T - 1, ov);
       if (r != WD_OK) return r;
     }
     return WD_OK;

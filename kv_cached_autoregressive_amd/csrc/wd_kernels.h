@@ -20,6 +20,11 @@ hipError_t launch_copy_rows(const void* src, int src_dtype, void* dst, int dst_d
                             hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+// Copies one call's inputs into fixed buffers (tokens with stride, positions or a constant,
+// and optionally B override rows) so that a captured step reads fixed addresses.
+hipError_t launch_stage(const int32_t* tok, int tok_stride, const int32_t* pos, int pos_const, int32_t* tok_out,
+                        int32_t* pos_out, int B, const void* rows, int64_t src_stride_bytes, void* rows_out,
+                        int64_t row_bytes, hipStream_t s);
 
 // ---- embedding ---------------------------------------------------------------------------
 // x[b] = ov ? ov[b*ov_stride ..] : E[tok[b*tok_stride]] + (P ? P[pos[b]] : 0); validates ranges.
