@@ -191,7 +191,81 @@ __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, float
     if (i < d) {
       const float o = (v[j] - mean) * rs * gv[j] + bv[j];
       if constexpr (SPLIT) store_split<OT>(yh, yl, frag_offset(row, i, d), o);
-      else y[(int64_t)row * d + i] = o;
+      else y[(int64_t)row * d + i] = o;   // (fp32 path: two-pass mean and variance)
+    }
+  }
+}
+
+// Row norm for the MFMA path, one 256-thread block per row, 4 consecutive columns per thread
+// and pass (PASS passes of 1024 columns; d % 32 == 0).  With GMAX > 0, first x += pbias +
+// sum_g part[g][row][:] (the G <= GMAX partial slabs of a split-K residual projection,
+// added in order g = 0..G-1, all loads in flight together) and the new x is written back.
+// Mean and mean square come from one block reduction; the output goes to the split
+// fragment layout (4 consecutive k are contiguous there).
+template <typename OT, int PASS, int GMAX>
+__global__ __launch_bounds__(256) void k_norm4(float* __restrict__ x, OT* __restrict__ yh, OT* __restrict__ yl,
+                                               const float* __restrict__ g, const float* __restrict__ bvec, int d,
+                                               float eps, const float* __restrict__ part, int G, int B,
+                                               const float* __restrict__ pbias) {
+  __shared__ float red[2][4];
+  const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  float* xr = x + (int64_t)row * d;
+  float4 v[PASS], gv[PASS], bv[PASS];
+#pragma unroll
+  for (int j = 0; j < PASS; ++j) {   // loads clamped to the last chunk; chunks past d are not used
+    const int c = min(4 * t + 1024 * j, d - 4);
+    float4 a = *reinterpret_cast<const float4*>(xr + c);
+    gv[j] = *reinterpret_cast<const float4*>(g + c);
+    bv[j] = bvec ? *reinterpret_cast<const float4*>(bvec + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (GMAX > 0) {
+      if (pbias) {
+        const float4 pb = *reinterpret_cast<const float4*>(pbias + c);
+        a.x += pb.x; a.y += pb.y; a.z += pb.z; a.w += pb.w;
+      }
+      float4 q[GMAX];
+#pragma unroll
+      for (int k = 0; k < GMAX; ++k)
+        q[k] = *reinterpret_cast<const float4*>(part + ((int64_t)min(k, G - 1) * B + row) * d + c);
+#pragma unroll
+      for (int k = 0; k < GMAX; ++k)
+        if (k < G) { a.x += q[k].x; a.y += q[k].y; a.z += q[k].z; a.w += q[k].w; }
+    }
+    v[j] = a;
+  }
+  float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int j = 0; j < PASS; ++j) {
+    const int c = 4 * t + 1024 * j;
+    if (c < d) {
+      if constexpr (GMAX > 0) *reinterpret_cast<float4*>(xr + c) = v[j];
+      s1 += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+      s2 += (v[j].x * v[j].x + v[j].y * v[j].y) + (v[j].z * v[j].z + v[j].w * v[j].w);
+    }
+  }
+  s1 = wave_sum(s1);
+  s2 = wave_sum(s2);
+  if (lane == 0) { red[0][w] = s1; red[1][w] = s2; }
+  __syncthreads();
+  s1 = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+  s2 = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  const float mean = bvec ? s1 / (float)d : 0.f;                     // LayerNorm, or RMSNorm without bias
+  const float var = fmaxf(s2 / (float)d - mean * mean, 0.f);
+  const float rs = 1.0f / sqrtf(var + eps);
+#pragma unroll
+  for (int j = 0; j < PASS; ++j) {
+    const int c = 4 * t + 1024 * j;
+    if (c < d) {
+      const float o[4] = {(v[j].x - mean) * rs * gv[j].x + bv[j].x, (v[j].y - mean) * rs * gv[j].y + bv[j].y,
+                          (v[j].z - mean) * rs * gv[j].z + bv[j].z, (v[j].w - mean) * rs * gv[j].w + bv[j].w};
+      OT h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split_hi_lo<OT>(o[e], h[e], l[e]);
+      const int64_t off = frag_offset(row, c, d);   // c % 4 == 0: 4 contiguous elements
+      uint2 hp, lp;
+      __builtin_memcpy(&hp, h, 8);
+      __builtin_memcpy(&lp, l, 8);
+      *reinterpret_cast<uint2*>(reinterpret_cast<OT*>(yh) + off) = hp;
+      *reinterpret_cast<uint2*>(reinterpret_cast<OT*>(yl) + off) = lp;
     }
   }
 }
@@ -251,6 +325,21 @@ static hipError_t norm_part(float* x, void* yh, void* yl, const float* g, const 
   return hipGetLastError();
 }
 
+template <typename OT>
+static hipError_t norm4(float* x, void* yh, void* yl, const float* g, const float* b, int B, int d, float eps,
+                        const float* part, int G, const float* pbias, hipStream_t s) {
+  if (d > 4096 || (part && (G < 1 || G > 8))) return hipErrorInvalidValue;
+  const int pass = (d + 1023) / 1024;
+#define WD_N4(P_, GM_) \
+  k_norm4<OT, P_, GM_><<<B, 256, 0, s>>>(x, (OT*)yh, (OT*)yl, g, b, d, eps, part, G, B, pbias)
+#define WD_N4P(P_) \
+  if (!part) WD_N4(P_, 0); else WD_N4(P_, 8);
+  if (pass == 1) { WD_N4P(1) } else if (pass == 2) { WD_N4P(2) } else { WD_N4P(4) }
+#undef WD_N4P
+#undef WD_N4
+  return hipGetLastError();
+}
+
 hipError_t launch_norm(const float* x, float* y, const float* g, const float* b, int B, int d,
                        float eps, hipStream_t s) {
   if (B <= 0 || d <= 0 || d > 256 * NORM_MAXE || !g) return hipErrorInvalidValue;
@@ -261,20 +350,16 @@ hipError_t launch_norm(const float* x, float* y, const float* g, const float* b,
 hipError_t launch_norm_split(float* x, void* y_hi, void* y_lo, int act_dtype, const float* g,
                              const float* b, int B, int d, float eps, hipStream_t s,
                              const float* part, int G, const float* pbias) {
-  if (B <= 0 || d <= 0 || d > 256 * NORM_MAXE || (d % 32) || !g || !y_hi || !y_lo) return hipErrorInvalidValue;
-  if (part) {
-    if (G <= 0) return hipErrorInvalidValue;
-    if (act_dtype == DT_BF16) return norm_part<bf16_t>(x, y_hi, y_lo, g, b, B, d, eps, part, G, pbias, s);
-    if (act_dtype == DT_F16) return norm_part<f16_t>(x, y_hi, y_lo, g, b, B, d, eps, part, G, pbias, s);
-    return hipErrorInvalidValue;
-  }
+  if (B <= 0 || d <= 0 || d > 4096 || (d % 32) || !g || !y_hi || !y_lo) return hipErrorInvalidValue;
+  // up to 8 partial slabs: 256 threads with 16-byte loads; more: 1024 threads (more loads in flight)
+  const bool wide = part && G > 8;
   if (act_dtype == DT_BF16)
-    k_norm<bf16_t, true><<<B, 256, 0, s>>>(x, nullptr, (bf16_t*)y_hi, (bf16_t*)y_lo, g, b, d, eps);
-  else if (act_dtype == DT_F16)
-    k_norm<f16_t, true><<<B, 256, 0, s>>>(x, nullptr, (f16_t*)y_hi, (f16_t*)y_lo, g, b, d, eps);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+    return wide ? norm_part<bf16_t>(x, y_hi, y_lo, g, b, B, d, eps, part, G, pbias, s)
+                : norm4<bf16_t>(x, y_hi, y_lo, g, b, B, d, eps, part, G, pbias, s);
+  if (act_dtype == DT_F16)
+    return wide ? norm_part<f16_t>(x, y_hi, y_lo, g, b, B, d, eps, part, G, pbias, s)
+                : norm4<f16_t>(x, y_hi, y_lo, g, b, B, d, eps, part, G, pbias, s);
+  return hipErrorInvalidValue;
 }
 
 // ------------------------------------------------------------------------------------------
