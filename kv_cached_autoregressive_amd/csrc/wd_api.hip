@@ -99,8 +99,10 @@ std::string check_config(const wd_config& c) {
   return "";
 }
 
-// Split of an attention over `rows` cache rows: about 1024 blocks in total (or none with
-// >= 512 slabs), at least 64 rows (one K/V tile of a few KB) per block, at most 64 splits.
+// Split of an attention over `rows` cache rows: none with >= 128 slabs (a split costs a
+// combine launch, about 4 us, more than the lost overlap: measured at 192 slabs of the
+// whisper-small step), else about 1024 blocks in total, at least 64 rows (one K/V tile of a
+// few KB) per block, at most 64 splits.
 // Tuning override for sweeps: WD_ATTN_ROWS="self_rows,cross_rows" (0 keeps the policy).
 int attn_rows_override(bool cross) {
   static int sr = 0, cr = 0;
@@ -114,8 +116,8 @@ int attn_rows_override(bool cross) {
 }
 
 void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits, bool cross = false) {
-  // about 1024 blocks (4 per CU) in total, or one split (no combine launch) with >= 512 slabs
-  const int want = slabs >= 512 ? 1 : std::max(1, (1024 + slabs - 1) / slabs);
+  // about 1024 blocks (4 per CU) in total, or one split (no combine launch) with >= 128 slabs
+  const int want = slabs >= 128 ? 1 : std::max(1, (1024 + slabs - 1) / slabs);
   int r = (rows + want - 1) / want;
   r = std::max(r, (rows + 63) / 64);   // at most 64 splits (the combine's limit)
   r = std::max(r, 64);
