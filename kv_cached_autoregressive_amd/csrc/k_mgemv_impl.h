@@ -161,6 +161,13 @@ __device__ __forceinline__ void mg_epilogue(const MGemvParams& p, mf32x4_t (&acc
 
 constexpr int mg_waves(int KS) { return KS >= 4 ? KS : 4; }
 
+// Weights are read once per step: nontemporal loads keep them out of the L2's way
+// (measured 3% on the Qwen3 step, 1% on the large-v3 step).
+__device__ __forceinline__ mv4u wload(const mv4u* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint4 wload(const uint4* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const mv4u*>(p)));
+}
+
 // A wave's steps past its last one (the ring overruns by up to D-1) load the last
 // step again and multiply by zeroed weights: no load sits under a branch, so the
 // compiler's wait counts keep D-1 steps of loads in flight.
@@ -207,7 +214,7 @@ __global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv(MGemvParams p) {
   auto load = [&](int i, uint4 (&wd)[NBW], uint4 (&hd)[NBB], uint4 (&ld)[NBB]) __attribute__((always_inline)) {
     const int st = s0 + min(i, n - 1);
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) wd[nb] = Wv[wbase[nb] + (int64_t)st * 64];
+    for (int nb = 0; nb < NBW; ++nb) wd[nb] = wload(Wv + wbase[nb] + (int64_t)st * 64);
 #pragma unroll
     for (int bb = 0; bb < NBB; ++bb) {
       const int64_t yi = ((int64_t)bb * KST + st) * 64 + lane;
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(64 * mg_waves(KS)) void k_mgemv_pf(MGemvParams p) {
   for (int i = 0; i < NS; ++i)
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb)
-      wr[i][nb] = Wv[((int64_t)min(tile * NBW + nb, NB - 1) * KST + s0 + i) * 64 + lane];
+      wr[i][nb] = wload(Wv + ((int64_t)min(tile * NBW + nb, NB - 1) * KST + s0 + i) * 64 + lane);
 
   mv4u hr[DY][NBB], lr[DY][NBB];
   auto loadY = [&](int i, mv4u (&h)[NBB], mv4u (&l)[NBB]) __attribute__((always_inline)) {
@@ -408,7 +415,7 @@ __global__ __launch_bounds__(64 * KS * RT) void k_mgemv_lds(MGemvParams p) {
   auto loadW = [&](int i, mv4u (&dst)[NBW]) __attribute__((always_inline)) {
     const int st = s0 + min(i, n - 1);
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) dst[nb] = Wv[wbase[nb] + (int64_t)st * 64];
+    for (int nb = 0; nb < NBW; ++nb) dst[nb] = wload(Wv + wbase[nb] + (int64_t)st * 64);
   };
 
 #pragma unroll
@@ -539,7 +546,7 @@ __global__ __launch_bounds__(256 * KS) void k_mgemv_sk(MGemvParams p) {
     if (i % KS == 0) {
       const int mine = s_lo + min(i + ks, n - 1);
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) wr[i / KS][nb] = Wv[wbase[nb] + (int64_t)mine * 64];
+      for (int nb = 0; nb < NBW; ++nb) wr[i / KS][nb] = wload(Wv + wbase[nb] + (int64_t)mine * 64);
     }
   }
 

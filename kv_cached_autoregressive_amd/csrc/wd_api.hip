@@ -99,10 +99,13 @@ std::string check_config(const wd_config& c) {
   return "";
 }
 
-// Split of an attention over `rows` cache rows: none with >= 128 slabs (a split costs a
-// combine launch, about 4 us, more than the lost overlap: measured at 192 slabs of the
-// whisper-small step), else about 1024 blocks in total, at least 64 rows (one K/V tile of a
-// few KB) per block, at most 64 splits.
+// Launch shape of an attention over `rows` cache rows of `slabs` K/V slabs (measured on the
+// three batched workloads):
+//  * >= 512 slabs: blocks of 4 waves, one per slab (5 resident per CU at <= 96 VGPRs);
+//  * otherwise blocks of 8 waves and about 256 blocks in total, so a slab is split only
+//    below ~170 slabs (each split costs a combine launch, about 4 us): one split at the
+//    192 slabs of the whisper-small step, 4 splits of 256 rows at the 64 of the Qwen3 step;
+//  * splits of at least 64 rows, at most 64 splits (the combine's limit).
 // Tuning override for sweeps: WD_ATTN_ROWS="self_rows,cross_rows" (0 keeps the policy).
 int attn_rows_override(bool cross) {
   static int sr = 0, cr = 0;
@@ -115,18 +118,19 @@ int attn_rows_override(bool cross) {
   return cross ? cr : sr;
 }
 
-void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits, bool cross = false) {
-  // about 1024 blocks (4 per CU) in total, or one split (no combine launch) with >= 128 slabs
-  const int want = slabs >= 128 ? 1 : std::max(1, (1024 + slabs - 1) / slabs);
+void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits, int* nw, bool cross = false) {
+  const bool wide = slabs < 512;
+  const int want = wide ? std::max(1, (256 + slabs / 2) / slabs) : 1;
   int r = (rows + want - 1) / want;
   r = std::max(r, (rows + 63) / 64);   // at most 64 splits (the combine's limit)
   r = std::max(r, 64);
-  if (const int o = attn_rows_override(cross)) r = o;
+  if (const int o = attn_rows_override(cross)) r = std::max(o, (rows + 63) / 64);
   r = (r + 31) & ~31;
-  r = std::min(r, 12288 / std::max(nq, 1));
+  r = std::min(r, std::max(12288 / std::max(nq, 1), (rows + 63) / 64));
   r = std::max(r, 1);
   *split_rows = r;
   *n_splits = std::max(1, (rows + r - 1) / r);
+  *nw = wide ? 8 : 4;
 }
 
 Plan make_plan(const wd_config& c) {
@@ -308,11 +312,11 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
   const int64_t kv_bstride = (int64_t)hkv * g.context * hd;
   const float qscale = 1.0f / sqrtf((float)hd);
 
-  int s_rows, s_splits;
-  split_for(g.context, B * hkv, hq / hkv, &s_rows, &s_splits);
+  int s_rows, s_splits, s_nw;
+  split_for(g.context, B * hkv, hq / hkv, &s_rows, &s_splits, &s_nw);
   const int qpk = whisper ? rows_per_set(g, B) : 1;
-  int c_rows = 0, c_splits = 1;
-  if (whisper) split_for(c->frames, (B / qpk) * hkv, qpk, &c_rows, &c_splits, true);
+  int c_rows = 0, c_splits = 1, c_nw = 4;
+  if (whisper) split_for(c->frames, (B / qpk) * hkv, qpk, &c_rows, &c_splits, &c_nw, true);
 
   float* gpart = P.gpart_cap ? c->at<float>(P.gpart) : nullptr;
   auto proj = [&](const void* W, int N, int K, const void* Yh, const void* Yl, int epi, const float* bias,
@@ -382,7 +386,7 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
     }
     ap.q = q; ap.q_ld = hq * hd; ap.K = c->self_k(l); ap.V = c->self_v(l);
     ap.kvb_stride = kv_bstride; ap.rows_cap = g.context; ap.pos = pos; ap.n_rows_fixed = 0;
-    ap.q_per_kvb = 1; ap.split_rows = s_rows; ap.n_splits = s_splits; ap.out = nullptr; ap.out_ld = 0;
+    ap.q_per_kvb = 1; ap.split_rows = s_rows; ap.n_splits = s_splits; ap.nw = s_nw; ap.out = nullptr; ap.out_ld = 0;
     {
       const bool on = prof_on(c, PK_SELF_ATTN, l);
       prof_begin(c, on);
@@ -406,7 +410,7 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
       cp.K = c->cross_k(l); cp.V = c->cross_v(l);
       cp.kvb_stride = (int64_t)hq * g.max_frames * hd; cp.rows_cap = g.max_frames;
       cp.pos = nullptr; cp.n_rows_fixed = c->frames; cp.q_per_kvb = qpk;
-      cp.split_rows = c_rows; cp.n_splits = c_splits;
+      cp.split_rows = c_rows; cp.n_splits = c_splits; cp.nw = c_nw;
       {
         const bool on = prof_on(c, PK_CROSS_ATTN, l);
         prof_begin(c, on);
@@ -483,11 +487,11 @@ wd_status run_step(wd_ctx* c, const int32_t* tok, int tok_stride, const int32_t*
   if (P.mfma) return run_layers_mfma(c, pos, B, logits, argmax, head);
 
   // self-attention split policy (positions live on the device, so split by context)
-  int s_rows, s_splits;
-  split_for(g.context, B * hkv, hq / hkv, &s_rows, &s_splits);
+  int s_rows, s_splits, s_nw;
+  split_for(g.context, B * hkv, hq / hkv, &s_rows, &s_splits, &s_nw);
   const int qpk = whisper ? rows_per_set(g, B) : 1;
-  int c_rows = 0, c_splits = 1;
-  if (whisper) split_for(c->frames, (B / qpk) * hkv, qpk, &c_rows, &c_splits, true);
+  int c_rows = 0, c_splits = 1, c_nw = 4;
+  if (whisper) split_for(c->frames, (B / qpk) * hkv, qpk, &c_rows, &c_splits, &c_nw, true);
 
   for (int l = 0; l < g.n_layers; ++l) {
     const LayerOff& L = P.L[l];
@@ -525,7 +529,7 @@ wd_status run_step(wd_ctx* c, const int32_t* tok, int tok_stride, const int32_t*
     // self-attention over rows 0..pos of each row's own cache
     ap.q = q; ap.q_ld = hq * hd; ap.K = c->self_k(l); ap.V = c->self_v(l);
     ap.kvb_stride = kv_bstride; ap.rows_cap = g.context; ap.pos = pos; ap.n_rows_fixed = 0;
-    ap.q_per_kvb = 1; ap.split_rows = s_rows; ap.n_splits = s_splits; ap.out = o; ap.out_ld = hq * hd;
+    ap.q_per_kvb = 1; ap.split_rows = s_rows; ap.n_splits = s_splits; ap.nw = s_nw; ap.out = o; ap.out_ld = hq * hd;
     {
       const bool on = prof_on(c, PK_SELF_ATTN, l);
       prof_begin(c, on);
@@ -550,7 +554,7 @@ wd_status run_step(wd_ctx* c, const int32_t* tok, int tok_stride, const int32_t*
       cp.K = c->cross_k(l); cp.V = c->cross_v(l);
       cp.kvb_stride = (int64_t)hq * g.max_frames * hd; cp.rows_cap = g.max_frames;
       cp.pos = nullptr; cp.n_rows_fixed = c->frames; cp.q_per_kvb = qpk;
-      cp.split_rows = c_rows; cp.n_splits = c_splits;
+      cp.split_rows = c_rows; cp.n_splits = c_splits; cp.nw = c_nw;
       {
         const bool on = prof_on(c, PK_CROSS_ATTN, l);
         prof_begin(c, on);

@@ -118,6 +118,7 @@ struct AttnParams {
   const int32_t* pos; int n_rows_fixed;       // pos: rows 0..pos[b]; else n_rows_fixed rows
   int B; int Hq; int Hkv; int hd; int q_per_kvb;
   int split_rows; int n_splits;
+  int nw;                                     // waves per block: 4 or 8
   float* out; int out_ld;                     // [B, out_ld] (head h at h*hd), or:
   void* o_hi; void* o_lo; int o_dtype;        // split fragment layout [B_pad, Hq*hd] if set
   float* part;                                // [B*Hq][n_splits][hd+2] when n_splits > 1
