@@ -34,6 +34,21 @@ __device__ __forceinline__ Raw8<float> fetch8_nt(const float* p) {
   r.a = __builtin_bit_cast(float4, a); r.b = __builtin_bit_cast(float4, b);
   return r;
 }
+// 8 floats rounded to the cache type, in the register form a fetch produces
+template <typename CT>
+__device__ __forceinline__ Raw8<CT> pack8(const float* f) {
+  Raw8<CT> r;
+  if constexpr (sizeof(CT) == 4) {
+    r.a = make_float4(f[0], f[1], f[2], f[3]);
+    r.b = make_float4(f[4], f[5], f[6], f[7]);
+  } else {
+    CT h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = from_f<CT>(f[e]);
+    __builtin_memcpy(&r.v, h, 16);
+  }
+  return r;
+}
 template <typename T>
 __device__ __forceinline__ Raw8<T> fetch8_nt(const T* p) {
   Raw8<T> r;
@@ -105,10 +120,85 @@ __global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {
   const CT* Vp = reinterpret_cast<const CT*>(p.V) + (int64_t)kvb * p.kvb_stride + (int64_t)g * p.rows_cap * HD;
   const int64_t qslab = (int64_t)p.B * p.qpart_ld;
 
+  // Software pipeline: the K/V rows of the next pass are requested before the current one
+  // is reduced, so a wave never waits on an empty queue; UNR is sized so the single-query
+  // kernel stays at <= 96 VGPRs (5 waves per SIMD, all blocks resident).  Rows past the
+  // split reload its last row (not counted); no load sits under a branch.
+  Raw8<CT> kr[UNR], vr[UNR];
+  auto fetch = [&](int r0, Raw8<CT> (&kd)[UNR], Raw8<CT> (&vd)[UNR]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int ru = min(r0 + u * RPP, r_hi - 1);
+      kd[u] = fetch8_nt(Kp + (int64_t)ru * HD + seg * 8);
+      vd[u] = fetch8_nt(Vp + (int64_t)ru * HD + seg * 8);
+    }
+  };
+  // The first pass is requested before the q prologue below, so its latency overlaps the
+  // partial sums; a row appended by the prologue is patched into it from LDS.
+  fetch(r_lo + rr, kr, vr);
+  __shared__ float apv[2 * HD];   // the appended row (k, then v) before rounding to the cache type
+  const int ps_app = n_rows - 1;
+  const bool appended = p.qpart && p.append && p.pos && ps_app >= r_lo && ps_app < r_hi;
+
   // q (and the appended row) from split-K partials: each value is summed once per block
   // (one thread per value, its G loads in flight together), q through LDS
   __shared__ float qs[NQ * HD];
-  if (p.qpart) {
+  if (p.qpart && p.rope) {
+    // Qwen3: raw q heads and the appended k, v summed into LDS, then per-head RMSNorm and
+    // the NeoX rotation (angles in double, as the standalone q/k kernel takes them)
+    __shared__ float kvs[2 * HD], cs_[HD / 2], sn_[HD / 2], rsq[NQ + 1];
+    const int ps = n_rows - 1;
+    const bool own = p.append && ps >= r_lo && ps < r_hi;
+    for (int i = t; i < nq * HD; i += NT) {
+      const int qi = i / HD, c = i - qi * HD;
+      qs[i] = sum_parts<16>(p.qpart + (int64_t)qrow(qi) * p.qpart_ld + p.q_off + qhead(qi) * HD + c, qslab, p.qG);
+    }
+    if (own)
+      for (int i = t; i < 2 * HD; i += NT) {
+        const int c = i % HD;
+        kvs[i] = sum_parts<16>(p.qpart + (int64_t)bq0 * p.qpart_ld + (i >= HD ? p.v_off : p.k_off) + g * HD + c,
+                               qslab, p.qG);
+      }
+    for (int i = t; i < HD / 2; i += NT) {
+      const double th = (double)ps * pow((double)p.rope_base, -2.0 * (double)i / (double)HD);
+      cs_[i] = (float)cos(th);
+      sn_[i] = (float)sin(th);
+    }
+    __syncthreads();
+    const int nh = nq + (own ? 1 : 0);   // q heads, then the appended k
+    for (int hh = wv; hh < nh; hh += NW) {
+      const float* z = hh < nq ? qs + hh * HD : kvs;
+      float ss = 0.f;
+      for (int c = lane; c < HD; c += 64) ss += z[c] * z[c];
+      ss = wave_sum(ss);
+      if (lane == 0) rsq[hh] = 1.0f / sqrtf(ss / (float)HD + p.eps);
+    }
+    __syncthreads();
+    CT* Kw = reinterpret_cast<CT*>(const_cast<void*>(p.K)) + (int64_t)kvb * p.kvb_stride + ((int64_t)g * p.rows_cap + ps) * HD;
+    CT* Vw = reinterpret_cast<CT*>(const_cast<void*>(p.V)) + (int64_t)kvb * p.kvb_stride + ((int64_t)g * p.rows_cap + ps) * HD;
+    for (int j = t; j < nh * (HD / 2); j += NT) {
+      const int hh = j / (HD / 2), i = j - hh * (HD / 2);
+      float* z = hh < nq ? qs + hh * HD : kvs;
+      const float* gain = hh < nq ? p.qn : p.kn;
+      const float a = z[i] * rsq[hh] * gain[i], b2 = z[i + HD / 2] * rsq[hh] * gain[i + HD / 2];
+      const float r0 = a * cs_[i] - b2 * sn_[i], r1 = b2 * cs_[i] + a * sn_[i];
+      if (hh < nq) {
+        z[i] = r0 * p.qscale;
+        z[i + HD / 2] = r1 * p.qscale;
+      } else {
+        Kw[i] = from_f<CT>(r0);
+        Kw[i + HD / 2] = from_f<CT>(r1);
+        apv[i] = r0;
+        apv[i + HD / 2] = r1;
+      }
+    }
+    if (own)
+      for (int c = t; c < HD; c += NT) {
+        Vw[c] = from_f<CT>(kvs[HD + c]);
+        apv[HD + c] = kvs[HD + c];
+      }
+    __syncthreads();   // q in LDS; the appended row visible to the block's loads below
+  } else if (p.qpart) {
     for (int i = t; i < nq * HD; i += NT) {
       const int qi = i / HD, c = i - qi * HD;
       const int col = qhead(qi) * HD + c;
@@ -125,9 +215,18 @@ __global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {
         if (isv && p.vbias) v += p.vbias[g * HD + c];
         CT* base = reinterpret_cast<CT*>(const_cast<void*>(isv ? p.V : p.K));
         base[(int64_t)kvb * p.kvb_stride + ((int64_t)g * p.rows_cap + ps) * HD + c] = from_f<CT>(v);
+        apv[t] = v;
       }
     }
     __syncthreads();   // q in LDS; the appended row visible to the block's loads below
+  }
+  if (appended) {   // the prefetched first pass predates the append: take that row from LDS
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+      if (min(r_lo + rr + u * RPP, r_hi - 1) == ps_app) {
+        kr[u] = pack8<CT>(apv + seg * 8);
+        vr[u] = pack8<CT>(apv + HD + seg * 8);
+      }
   }
 
   float qv[NQ][8];
@@ -156,20 +255,6 @@ __global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[qi][j] = 0.f;
   }
-  // Software pipeline: the K/V rows of the next pass are requested before the current one
-  // is reduced, so a wave never waits on an empty queue; UNR is sized so the single-query
-  // kernel stays at <= 96 VGPRs (5 waves per SIMD, all blocks resident).  Rows past the
-  // split reload its last row (not counted); no load sits under a branch.
-  Raw8<CT> kr[UNR], vr[UNR];
-  auto fetch = [&](int r0, Raw8<CT> (&kd)[UNR], Raw8<CT> (&vd)[UNR]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int ru = min(r0 + u * RPP, r_hi - 1);
-      kd[u] = fetch8_nt(Kp + (int64_t)ru * HD + seg * 8);
-      vd[u] = fetch8_nt(Vp + (int64_t)ru * HD + seg * 8);
-    }
-  };
-  fetch(r_lo + rr, kr, vr);
   for (int r = r_lo + rr; r - rr < r_hi; r += RPP * UNR) {   // trip count uniform over the block
     Raw8<CT> kn[UNR], vn[UNR];
     fetch(r + RPP * UNR, kn, vn);
@@ -323,7 +408,9 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   if (p.n_splits > 1 && !p.part) return hipErrorInvalidValue;
   if ((!p.q && !p.qpart) || !p.K || !p.V || (!p.qpart && (p.q_ld % 4))) return hipErrorInvalidValue;
   if (p.qpart && (p.qG < 1 || p.qG > 16 || p.qpart_ld <= 0)) return hipErrorInvalidValue;
-  if (p.append && (!p.qpart || !p.pos || p.Hq != p.Hkv)) return hipErrorInvalidValue;
+  if (p.append && (!p.qpart || !p.pos || (p.Hq != p.Hkv && !p.rope))) return hipErrorInvalidValue;
+  if (p.rope && (!p.qpart || !p.pos || !p.qn || !p.kn || !(p.eps > 0.f) || !(p.rope_base > 0.f)))
+    return hipErrorInvalidValue;
   if (p.o_hi ? (!p.o_lo || (p.Hq * p.hd) % 32 || (p.o_dtype != DT_F16 && p.o_dtype != DT_BF16))
              : (!p.out || p.out_ld < p.Hq * p.hd))
     return hipErrorInvalidValue;

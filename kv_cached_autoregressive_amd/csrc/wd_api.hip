@@ -378,11 +378,17 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
       const int nqkv = (hq + 2 * hkv) * hd;
       int G = 1;
       WDCHK(gemm(proj(c->at(L.wqkv), nqkv, d, yh, yl, wd::EPI_STORE, nullptr, qkv, nqkv, 1.0f), "qkv projection", &G, 32));
-      HIPCHK(c, wd::launch_qk_rope_append(qkv, B, hq, hkv, hd, pos, g.context, c->at<float>(L.qn),
-                                          c->at<float>(L.kn), g.norm_eps, g.rope_base, qscale, q,
-                                          c->self_k(l), c->self_v(l), g.cache_dtype, kv_bstride, s,
-                                          G > 1 ? gpart : nullptr, G),
-             "qk norm/rope/append");
+      if (G <= 16) {   // the attention prologue takes q/k norm, RoPE and the K/V append
+        ap.qpart = G > 1 ? gpart : qkv; ap.qG = G; ap.qpart_ld = nqkv; ap.q_off = 0; ap.qbias = nullptr;
+        ap.qscale = qscale; ap.append = true; ap.k_off = hq * hd; ap.v_off = (hq + hkv) * hd; ap.vbias = nullptr;
+        ap.rope = true; ap.qn = c->at<float>(L.qn); ap.kn = c->at<float>(L.kn); ap.eps = g.norm_eps;
+        ap.rope_base = g.rope_base;
+      } else {
+        HIPCHK(c, wd::launch_qk_rope_append(qkv, B, hq, hkv, hd, pos, g.context, c->at<float>(L.qn),
+                                            c->at<float>(L.kn), g.norm_eps, g.rope_base, qscale, q,
+                                            c->self_k(l), c->self_v(l), g.cache_dtype, kv_bstride, s, gpart, G),
+               "qk norm/rope/append");
+      }
     }
     ap.q = q; ap.q_ld = hq * hd; ap.K = c->self_k(l); ap.V = c->self_v(l);
     ap.kvb_stride = kv_bstride; ap.rows_cap = g.context; ap.pos = pos; ap.n_rows_fixed = 0;

@@ -130,6 +130,10 @@ struct AttnParams {
   // row pos[b] writes cache row pos[b] of its head, k = sum_g qpart[..k_off..] (no bias) and
   // v = sum_g qpart[..v_off..] + vbias, rounded to the cache dtype, before reading any row
   int k_off; int v_off; const float* vbias; bool append;
+  // Qwen3 (rope): q and the appended k first go through the per-head RMSNorm (gains qn / kn
+  // [hd], eps) and the NeoX rotation by pos * rope_base^(-2i/hd) of the pairs (i, i + hd/2);
+  // v is appended as summed.  GQA allowed.
+  bool rope; const float* qn; const float* kn; float eps; float rope_base;
 };
 // main kernel (writes o directly when n_splits == 1, else partials) ...
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
