@@ -653,22 +653,25 @@ hipError_t mrun_f16(const MGemvParams& p, hipStream_t st);
 // G = ceil(K steps / S), and the LDS chunk is 4 or 8 steps (no padded steps for S <= 4).
 // Tuning overrides: WD_MGEMV_SK=0 disables the variant; WD_MGEMV_SKS=<S> forces S.
 static bool sk_pick(int N, int K, int B, int epi, SkShape& s) {
-  static int mode = -1, forces = 0;
+  static int mode = -1, forces = 0, forcew = 0;
   if (mode < 0) {
     const char* e = getenv("WD_MGEMV_SK");
     mode = e ? atoi(e) : 1;
     const char* f = getenv("WD_MGEMV_SKS");
     forces = f ? atoi(f) : 0;
+    const char* w = getenv("WD_MGEMV_SKW");
+    forcew = w ? atoi(w) : 0;
   }
   if (!mode || epi == EPI_LOGITS) return false;
   const int NB = (N + 15) / 16, KST = K / 32;
   s.NBB = B <= 16 ? 1 : B <= 32 ? 2 : 4;
   s.NBW = (NB >= 256 || KST >= 128 || epi == EPI_SWIGLU_SPLIT) ? 2 : 1;
+  if ((forcew == 1 && epi != EPI_SWIGLU_SPLIT) || forcew == 2) s.NBW = forcew;
   int ncg = (NB + 4 * s.NBW - 1) / (4 * s.NBW);
   int S = forces > 0 ? forces : (KST * ncg + 255) / 256;
   S = std::max(2, std::min(S, 8));
   int G = (KST + S - 1) / S;
-  if (ncg * G > 256 && s.NBW == 1 && !forces) {   // past one workgroup per CU: wider column groups
+  if (ncg * G > 256 && s.NBW == 1 && !forces && !forcew) {   // past one workgroup per CU: wider column groups
     s.NBW = 2;
     ncg = (NB + 7) / 8;
     S = std::max(2, std::min((KST * ncg + 255) / 256, 8));
