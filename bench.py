@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -74,6 +75,8 @@ def traffic_per_launch():
 
 
 COPY_PROBE_BYTES = 256 << 20
+# the cross-attention instantiation: k_attn<cache type, head dim, queries, CROSS = true, waves>
+CROSS_ATTN_NAME = re.compile(r"k_attn<[^<>]*?,\s*true\s*,")
 
 
 def summarize_traffic(fetch_csv: str, write_csv: str, commands: list) -> dict:
@@ -90,7 +93,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, commands: list) -> dict:
             if r["Counter_Name"] != counter:
                 continue
             name, v = r["Kernel_Name"], float(r["Counter_Value"])
-            if "k_attn<" in name and ", true>" in name:
+            if CROSS_ATTN_NAME.search(name):
                 attn.append(v)
             elif "copyBuffer" in name:
                 copies.append(v)
