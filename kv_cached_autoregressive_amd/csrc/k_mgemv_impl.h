@@ -666,7 +666,8 @@ static bool sk_pick(int N, int K, int B, int epi, SkShape& s) {
   const int NB = (N + 15) / 16, KST = K / 32;
   s.NBB = B <= 16 ? 1 : B <= 32 ? 2 : 4;
   s.NBW = (NB >= 256 || KST >= 128 || epi == EPI_SWIGLU_SPLIT) ? 2 : 1;
-  if ((forcew == 1 && epi != EPI_SWIGLU_SPLIT) || forcew == 2) s.NBW = forcew;
+  // (SwiGLU's in-kernel epilogue needs gate and up in one wave: NBW = 1 only with K groups)
+  if ((forcew == 1 && (epi != EPI_SWIGLU_SPLIT || KST > 8)) || forcew == 2) s.NBW = forcew;
   int ncg = (NB + 4 * s.NBW - 1) / (4 * s.NBW);
   int S = forces > 0 ? forces : (KST * ncg + 255) / 256;
   S = std::max(2, std::min(S, 8));
