@@ -37,7 +37,16 @@ import workloads as WL  # noqa: E402
 HBM_PEAK = 8.0e12
 DEFAULT = "whisper_large_bf16_b64"
 DT_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
-ATTN_SRC = os.path.join(ROOT, "kv_cached_autoregressive_amd", "csrc", "k_attn.hip")
+# the cross-attention kernel's source: its file and the headers it includes
+ATTN_SRC = [os.path.join(ROOT, "kv_cached_autoregressive_amd", "csrc", f)
+            for f in ("k_attn.hip", "wd_common.h", "wd_kernels.h")]
+
+
+def attn_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ATTN_SRC:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_cross_whisper_large_bf16_b64_traffic.json")
 
 
@@ -66,8 +75,7 @@ def traffic_per_launch():
     summary, or None when absent or taken on a different kernel source."""
     try:
         t = json.load(open(TRAFFIC_FILE))
-        sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-        if t.get("kernel_source_sha256") != sha:
+        if t.get("kernel_source_sha256") != attn_source_sha():
             return None
         return int(t["hbm_bytes_per_launch"])
     except Exception:
@@ -112,7 +120,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, commands: list) -> dict:
             "fetch_scale": f_fac, "write_scale": w_fac,
             "hbm_fetch_bytes_per_launch": int(fetch_b), "hbm_write_bytes_per_launch": int(write_b),
             "hbm_bytes_per_launch": int(fetch_b + write_b),
-            "kernel_source_sha256": hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest(),
+            "kernel_source_sha256": attn_source_sha(),
             "commands": commands}
 
 

@@ -9,6 +9,8 @@
 
 namespace wd {
 
+typedef float nt4f __attribute__((ext_vector_type(4)));
+
 // ------------------------------------------------------------------------------------------
 // repack: row copy with dtype conversion and a row remap (fused q|k|v, gate|up blocks)
 // ------------------------------------------------------------------------------------------
@@ -225,7 +227,8 @@ __global__ __launch_bounds__(256) void k_norm4(float* __restrict__ x, OT* __rest
       float4 q[GMAX];
 #pragma unroll
       for (int k = 0; k < GMAX; ++k)
-        q[k] = *reinterpret_cast<const float4*>(part + ((int64_t)min(k, G - 1) * B + row) * d + c);
+        q[k] = __builtin_bit_cast(float4, __builtin_nontemporal_load(   // read once (see sum_parts)
+            reinterpret_cast<const nt4f*>(part + ((int64_t)min(k, G - 1) * B + row) * d + c)));
 #pragma unroll
       for (int k = 0; k < GMAX; ++k)
         if (k < G) { a.x += q[k].x; a.y += q[k].y; a.z += q[k].z; a.w += q[k].w; }

@@ -148,12 +148,14 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
 
 // Sum over k < G of p[k * stride], added in order k = 0..G-1.  Every load is issued
 // before the first add (G <= GMAX; indices past G-1 reload the last slab and are not
-// added), so the G loads overlap instead of paying one memory round trip each.
+// added), so the G loads overlap instead of paying one memory round trip each.  Partial
+// slabs are read once: nontemporal loads keep them out of the L2 (3.4% on the large-v3
+// step, within noise at 8-16 rows).
 template <int GMAX>
 __device__ __forceinline__ float sum_parts(const float* __restrict__ p, int64_t stride, int G) {
   float v[GMAX];
 #pragma unroll
-  for (int k = 0; k < GMAX; ++k) v[k] = p[(int64_t)min(k, G - 1) * stride];
+  for (int k = 0; k < GMAX; ++k) v[k] = __builtin_nontemporal_load(p + (int64_t)min(k, G - 1) * stride);
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < GMAX; ++k) s += k < G ? v[k] : 0.f;
