@@ -673,10 +673,23 @@ static bool sk_pick(int N, int K, int B, int epi, SkShape& s) {
   s.NBW = (NB >= 256 || KST >= 128 || epi == EPI_SWIGLU_SPLIT) ? 2 : 1;
   // (SwiGLU's in-kernel epilogue needs gate and up in one wave: NBW = 1 only with K groups)
   if ((forcew == 1 && (epi != EPI_SWIGLU_SPLIT || KST > 8)) || forcew == 2) s.NBW = forcew;
+  // up to 16 rows and at least 8 MB of 16-bit weights: 16-column tiles and K groups of up to
+  // 16 steps (half the partial slabs of 8-step groups; measured 14.4 -> 13.3 us on the Qwen3
+  // gate|up, 4.7% on its step)
+  const bool narrow = s.NBB == 1 && !forcew && (epi != EPI_SWIGLU_SPLIT || KST > 16) &&
+                      (int64_t)KST * ((NB + 3) / 4) >= 8 * 256;
+  if (narrow) s.NBW = 1;
   int ncg = (NB + 4 * s.NBW - 1) / (4 * s.NBW);
   int S = forces > 0 ? forces : (KST * ncg + 255) / 256;
-  S = std::max(2, std::min(S, 8));
+  S = std::max(2, std::min(S, (narrow || forces > 8) && s.NBB == 1 ? 16 : 8));
   int G = (KST + S - 1) / S;
+  if (narrow) {
+    if (G > 32) return false;
+    s.G = G;
+    s.NSC = std::max(4, (KST + G - 1) / G);
+    if (s.NSC > 8) s.NSC = 16;   // instantiated: 4..8 and 16 (steps past a group's end are padding)
+    return true;
+  }
   if (ncg * G > 256 && s.NBW == 1 && !forces && !forcew) {   // past one workgroup per CU: wider column groups
     s.NBW = 2;
     ncg = (NB + 7) / 8;
@@ -689,6 +702,7 @@ static bool sk_pick(int N, int K, int B, int epi, SkShape& s) {
   if (G > 32) return false;             // the consumers add at most 32 partial slabs
   s.G = G;
   s.NSC = std::max(4, (KST + G - 1) / G);   // the longest group's steps (4..8): at most one padded step
+  if (s.NSC > 8) s.NSC = 16;
   return true;
 }
 #ifdef WD_MG_MAIN
@@ -722,7 +736,7 @@ static hipError_t skrun(const MGemvParams& p0, const SkShape& s, hipStream_t st)
     return hipGetLastError();                                                    \
   }
 #define WD_SK_S(S_) WD_SK(1, 1, S_) WD_SK(2, 1, S_) WD_SK(1, 2, S_) WD_SK(2, 2, S_) WD_SK(1, 4, S_) WD_SK(2, 4, S_)
-  WD_SK_S(4) WD_SK_S(5) WD_SK_S(6) WD_SK_S(7) WD_SK_S(8)
+  WD_SK_S(4) WD_SK_S(5) WD_SK_S(6) WD_SK_S(7) WD_SK_S(8) WD_SK(1, 1, 16) WD_SK(2, 1, 16)
 #undef WD_SK_S
 #undef WD_SK
   return hipErrorInvalidValue;
