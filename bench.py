@@ -161,8 +161,9 @@ def qwen_cpu_baseline(w, budget_s: float):
 
 def run_qwen(args, w):
     """Qwen3-ASR: prefill of 900 positions (audio rows spliced in), then the greedy decode
-    steps to the context end, argmax on the device.  value = decode tokens/s; the prefill,
-    which goes through the step kernels position by position, is timed separately."""
+    steps to the context end, argmax on the device.  value = decode tokens/s; the prefill
+    (batched: chunks of positions through dense MFMA GEMMs and a causal prefill attention)
+    is timed separately."""
     import torch
 
     import kv_cached_autoregressive_amd as K

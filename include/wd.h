@@ -161,6 +161,9 @@ wd_status wd_reorder(wd_ctx* ctx, const int32_t* beam_idx, int32_t B, int32_t n_
  * in w_dtype or NULL: rows offset..offset+A-1 take these embeddings instead of
  * the token embeddings (decoder.h "Audio injection").  Fills cache rows
  * 0..T-1 and returns the logits (nullable) and argmax of the last position.
+ * Qwen3 with 16-bit weights runs the prompt in chunks of positions through dense
+ * GEMMs and a causal prefill attention (decoder.h `PrefillBuildBatched`); Whisper
+ * runs one decode step per position.
  * Errors: ARG (T outside [1, context], offset/A outside [0, T]), STATE. */
 wd_status wd_prefill(wd_ctx* ctx, const int32_t* tokens, int32_t B, int32_t T,
                      const void* embeds, int32_t A, int32_t offset,

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwd.so")
-SOURCES = ["k_mgemv_bf16.hip", "k_mgemv_f16.hip", "k_attn.hip",
+SOURCES = ["k_mgemv_bf16.hip", "k_mgemv_f16.hip", "k_attn.hip", "k_prefill.hip",
            "k_misc.hip", "k_gemv.hip", "k_mgemv.hip", "k_gemm.hip", "wd_api.hip"]
 ARCH = "gfx950"
 # Packed fp32 ALU ops stay off: the compiler must not form them from scalar code.

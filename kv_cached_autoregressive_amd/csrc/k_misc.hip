@@ -419,7 +419,7 @@ __global__ __launch_bounds__(64) void k_qk_rope_append(const float* __restrict__
                                                        const float* __restrict__ kn, float eps,
                                                        float base, float qscale, float* q_out,
                                                        CT* Kc, CT* Vc, int64_t kv_bstride,
-                                                       const float* __restrict__ part, int G, int B) {
+                                                       const float* __restrict__ part, int G, int B, int rps) {
   __shared__ float z[256];
   const int slot = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int nslot = Hq + 2 * Hkv;
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(64) void k_qk_rope_append(const float* __restrict__
   if (slot >= Hq + Hkv) {  // value head: plain append
     if (!ok) return;
     const int g = slot - Hq - Hkv;
-    CT* dst = Vc + (int64_t)b * kv_bstride + ((int64_t)g * ctx + p) * hd;
+    CT* dst = Vc + (int64_t)(b / rps) * kv_bstride + ((int64_t)g * ctx + p) * hd;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (lane + 64 * j < hd) dst[lane + 64 * j] = from_f<CT>(v[j]);
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(64) void k_qk_rope_append(const float* __restrict__
       qo[i + half] = r1 * qscale;
     } else if (ok) {
       const int g = slot - Hq;
-      CT* dst = Kc + (int64_t)b * kv_bstride + ((int64_t)g * ctx + p) * hd;
+      CT* dst = Kc + (int64_t)(b / rps) * kv_bstride + ((int64_t)g * ctx + p) * hd;
       dst[i] = from_f<CT>(r0);
       dst[i + half] = from_f<CT>(r1);
     }
@@ -475,29 +475,29 @@ __global__ __launch_bounds__(64) void k_qk_rope_append(const float* __restrict__
 template <typename CT>
 static void qk_rope_run(dim3 grid, hipStream_t s, const float* qkv, int Hq, int Hkv, int hd, const int32_t* pos,
                         int ctx, const float* qn, const float* kn, float eps, float base, float qscale, float* q_out,
-                        void* Kc, void* Vc, int64_t kv_bstride, const float* part, int G, int B) {
+                        void* Kc, void* Vc, int64_t kv_bstride, const float* part, int G, int B, int rps) {
   if (!part || G <= 8)
     k_qk_rope_append<CT, 8><<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out,
-                                                (CT*)Kc, (CT*)Vc, kv_bstride, part, G, B);
+                                                (CT*)Kc, (CT*)Vc, kv_bstride, part, G, B, rps);
   else if (G <= 16)
     k_qk_rope_append<CT, 16><<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out,
-                                                 (CT*)Kc, (CT*)Vc, kv_bstride, part, G, B);
+                                                 (CT*)Kc, (CT*)Vc, kv_bstride, part, G, B, rps);
   else
     k_qk_rope_append<CT, 32><<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out,
-                                                 (CT*)Kc, (CT*)Vc, kv_bstride, part, G, B);
+                                                 (CT*)Kc, (CT*)Vc, kv_bstride, part, G, B, rps);
 }
 
 hipError_t launch_qk_rope_append(const float* qkv, int B, int Hq, int Hkv, int hd, const int32_t* pos,
                                  int ctx, const float* qn, const float* kn, float eps, float base,
                                  float qscale, float* q_out, void* Kc, void* Vc, int cache_dtype,
-                                 int64_t kv_bstride, hipStream_t s, const float* part, int G) {
-  if (B <= 0 || hd > 256 || (hd % 2) || Hq <= 0 || Hkv <= 0) return hipErrorInvalidValue;
+                                 int64_t kv_bstride, hipStream_t s, const float* part, int G, int rps) {
+  if (B <= 0 || hd > 256 || (hd % 2) || Hq <= 0 || Hkv <= 0 || rps < 1) return hipErrorInvalidValue;
   if (part ? (G < 1 || G > 32) : !qkv) return hipErrorInvalidValue;
   dim3 grid(Hq + 2 * Hkv, B);
   switch (cache_dtype) {
-    case DT_F32: qk_rope_run<float>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, Kc, Vc, kv_bstride, part, G, B); break;
-    case DT_F16: qk_rope_run<f16_t>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, Kc, Vc, kv_bstride, part, G, B); break;
-    case DT_BF16: qk_rope_run<bf16_t>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, Kc, Vc, kv_bstride, part, G, B); break;
+    case DT_F32: qk_rope_run<float>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, Kc, Vc, kv_bstride, part, G, B, rps); break;
+    case DT_F16: qk_rope_run<f16_t>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, Kc, Vc, kv_bstride, part, G, B, rps); break;
+    case DT_BF16: qk_rope_run<bf16_t>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, Kc, Vc, kv_bstride, part, G, B, rps); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -57,6 +57,9 @@ struct Plan {
   size_t gpart = 0; int64_t gpart_cap = 0;   // split-K GEMM partials [G][B][N] fp32
   size_t tok_in = 0, ov_in = 0;              // staged tokens [B] and embedding override rows [B, d]
   int max_splits = 1, amax_parts = 1;
+  // batched Qwen3 prefill: chunks of PF_CHUNK positions for all rows (pf_rows = rows of a chunk)
+  int pf_rows = 0;
+  size_t pf_x = 0, pf_pos = 0, pf_ah = 0, pf_al = 0, pf_hh = 0, pf_hl = 0, pf_qkv = 0, pf_q = 0;
 };
 
 struct Bump {
@@ -133,6 +136,10 @@ void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits, int*
   *nw = wide ? 8 : 4;
 }
 
+// Positions per chunk of the batched prefill: its rows (streams x positions) feed dense MFMA
+// GEMMs; 128 positions of 8 streams make 1024-row products.
+constexpr int PF_CHUNK = 128;
+
 Plan make_plan(const wd_config& c) {
   Plan p;
   Bump b;
@@ -208,6 +215,16 @@ Plan make_plan(const wd_config& c) {
   p.err = b.take(64);
   p.pos_tmp = b.take(Bm * 4);
   p.tok_in = b.take(Bm * 4);
+  if (c.arch == WD_ARCH_QWEN3 && p.mfma) {
+    const size_t R = ((size_t)Bm * PF_CHUNK + 127) / 128 * 128, nqkv = (hq + 2 * hkv) * hd;
+    p.pf_rows = (int)R;
+    p.pf_x = b.take(R * d * f4);
+    p.pf_pos = b.take(R * 4);
+    p.pf_ah = b.take(R * std::max(d, hq * hd) * wb); p.pf_al = b.take(R * std::max(d, hq * hd) * wb);
+    p.pf_hh = b.take(R * ff * wb); p.pf_hl = b.take(R * ff * wb);
+    p.pf_qkv = b.take(R * nqkv * f4);
+    p.pf_q = b.take(R * hq * hd * f4);
+  }
   p.ov_in = b.take(Bm * d * wb);
   p.total = (b.off + 255) & ~size_t(255);
   return p;
@@ -921,6 +938,99 @@ wd_status wd_step(wd_ctx* ctx, const int32_t* tokens, const int32_t* positions, 
   }
 }
 
+namespace {
+
+// Final norm, tied-head logits and argmax of the B rows in x (16-bit weights).
+wd_status run_head_mfma(wd_ctx* c, int B, float* logits, int32_t* argmax) {
+  const wd_config& g = c->cfg;
+  const Plan& P = c->plan;
+  hipStream_t s = c->stream;
+  const bool whisper = g.arch == WD_ARCH_WHISPER;
+  HIPCHK(c, wd::launch_norm_split(c->at<float>(P.x), c->at(P.yh), c->at(P.yl), g.w_dtype, c->at<float>(P.lnfg),
+                                  whisper ? c->at<float>(P.lnfb) : nullptr, B, g.d_model, g.norm_eps, s),
+         "final norm");
+  wd::MGemvParams hm{};
+  hm.W = c->at(P.embed); hm.w_dtype = g.w_dtype; hm.N = g.vocab; hm.K = g.d_model;
+  hm.Yhi = c->at(P.yh); hm.Ylo = c->at(P.yl); hm.B = B; hm.epi = wd::EPI_LOGITS;
+  hm.out = logits; hm.ldo = g.vocab; hm.scale = 1.0f; hm.err = c->at<unsigned>(P.err);
+  hm.amax = c->at<unsigned long long>(P.amax); hm.ldp = g.max_batch;
+  HIPCHK(c, wd::launch_mgemv(hm, s), "logits");
+  HIPCHK(c, wd::launch_argmax_final(hm.amax, wd::mgemv_blocks_k(g.vocab, g.d_model, B), g.max_batch, B, argmax, s),
+         "argmax");
+  return WD_OK;
+}
+
+// Batched Qwen3 prefill: the prompt in chunks of PF_CHUNK positions for all B rows, each
+// layer as dense GEMMs over the chunk's rows, the per-head q/k norm + RoPE + append of the
+// decode step, and a causal prefill attention over the cache; then the head on the last
+// position of every row.  Runs eagerly (no graph): a few launches per layer and chunk.
+wd_status prefill_batched(wd_ctx* c, const int32_t* tokens, int B, int T, const void* embeds, int A, int offset,
+                          float* logits, int32_t* argmax) {
+  const wd_config& g = c->cfg;
+  const Plan& P = c->plan;
+  hipStream_t s = c->stream;
+  const int d = g.d_model, hd = g.head_dim, hq = g.n_heads, hkv = g.n_kv_heads, ff = g.d_ff;
+  const int nqkv = (hq + 2 * hkv) * hd, C = PF_CHUNK, R = B * C;
+  const int adt = g.w_dtype;
+  const float qscale = 1.0f / sqrtf((float)hd);
+  const int64_t kv_bstride = (int64_t)hkv * g.context * hd;
+  float* x = c->at<float>(P.pf_x);
+  int32_t* pos = c->at<int32_t>(P.pf_pos);
+  void *ah = c->at(P.pf_ah), *al = c->at(P.pf_al), *hh = c->at(P.pf_hh), *hl = c->at(P.pf_hl);
+  unsigned* err = c->at<unsigned>(P.err);
+  auto gemm = [&](const void* W, int N, int K, const void* Ahi, const void* Alo, int epi, float* out, int ldo,
+                  const char* what) -> wd_status {
+    wd::FgParams f{};
+    f.W = W; f.w_dtype = g.w_dtype; f.N = N; f.K = K; f.Ahi = Ahi; f.Alo = Alo; f.R = R; f.epi = epi;
+    f.out = out; f.ldo = ldo; f.Ohi = hh; f.Olo = hl;
+    HIPCHK(c, wd::launch_fgemm(f, s), what);
+    return WD_OK;
+  };
+#define WDCHK(expr) do { const wd_status st_ = (expr); if (st_ != WD_OK) return st_; } while (0)
+  for (int t0 = 0; t0 < T; t0 += C) {
+    const int Cn = std::min(C, T - t0);
+    HIPCHK(c, wd::launch_pf_embed(x, pos, c->at(P.embed), g.w_dtype, tokens, T, embeds, A, offset, t0, B, C, Cn, d,
+                                  g.vocab, err, s), "prefill: embed");
+    for (int l = 0; l < g.n_layers; ++l) {
+      const LayerOff& L = P.L[l];
+      HIPCHK(c, wd::launch_norm_split(x, ah, al, adt, c->at<float>(L.n1g), nullptr, R, d, g.norm_eps, s), "prefill: norm1");
+      WDCHK(gemm(c->at(L.wqkv), nqkv, d, ah, al, wd::FG_STORE, c->at<float>(P.pf_qkv), nqkv, "prefill: qkv"));
+      HIPCHK(c, wd::launch_qk_rope_append(c->at<float>(P.pf_qkv), R, hq, hkv, hd, pos, g.context, c->at<float>(L.qn),
+                                          c->at<float>(L.kn), g.norm_eps, g.rope_base, qscale, c->at<float>(P.pf_q),
+                                          c->self_k(l), c->self_v(l), g.cache_dtype, kv_bstride, s, nullptr, 0, C),
+             "prefill: qk norm/rope/append");
+      wd::PfAttnParams pa{};
+      pa.q = c->at<float>(P.pf_q); pa.K = c->self_k(l); pa.V = c->self_v(l); pa.cache_dtype = g.cache_dtype;
+      pa.kv_bstride = kv_bstride; pa.ctx = g.context; pa.B = B; pa.C = C; pa.Cn = Cn; pa.t0 = t0;
+      pa.Hq = hq; pa.Hkv = hkv; pa.hd = hd; pa.o_hi = ah; pa.o_lo = al; pa.o_dtype = adt;
+      HIPCHK(c, wd::launch_pf_attn(pa, s), "prefill: attention");
+      WDCHK(gemm(c->at(L.wo), d, hq * hd, ah, al, wd::FG_RESID, x, d, "prefill: out projection"));
+      HIPCHK(c, wd::launch_norm_split(x, ah, al, adt, c->at<float>(L.n2g), nullptr, R, d, g.norm_eps, s), "prefill: norm2");
+      WDCHK(gemm(c->at(L.wgu), 2 * ff, d, ah, al, wd::FG_SWIGLU, nullptr, 0, "prefill: gate|up"));
+      WDCHK(gemm(c->at(L.wdn), d, ff, hh, hl, wd::FG_RESID, x, d, "prefill: down projection"));
+    }
+    if (t0 + Cn == T) {   // the last position of every row -> the step's x, then the head
+      HIPCHK(c, hipMemcpy2DAsync(c->at<float>(P.x), (size_t)d * 4, x + (size_t)(Cn - 1) * d, (size_t)C * d * 4,
+                                 (size_t)d * 4, B, hipMemcpyDeviceToDevice, s), "prefill: last rows");
+      WDCHK(run_head_mfma(c, B, logits, argmax));
+    }
+  }
+#undef WDCHK
+  return WD_OK;
+}
+
+// Batched prefill unless WD_PF_BATCHED=0 (then every position runs as a decode step).
+bool prefill_batched_on(const wd_ctx* c) {
+  static int mode = -1;
+  if (mode < 0) {
+    const char* e = getenv("WD_PF_BATCHED");
+    mode = e ? atoi(e) : 1;
+  }
+  return mode != 0 && c->plan.pf_rows > 0;
+}
+
+}  // namespace
+
 wd_status wd_prefill(wd_ctx* ctx, const int32_t* tokens, int32_t B, int32_t T, const void* embeds, int32_t A,
                      int32_t offset, float* logits, int32_t* argmax) {
   if (!ctx) return WD_ERR_ARG;
@@ -933,6 +1043,7 @@ wd_status wd_prefill(wd_ctx* ctx, const int32_t* tokens, int32_t B, int32_t T, c
     const wd_status st = check_rows(ctx, B, "wd_prefill");
     if (st != WD_OK) return st;
     const Plan& P = ctx->plan;
+    if (prefill_batched_on(ctx)) return prefill_batched(ctx, tokens, B, T, embeds, A, offset, logits, argmax);
     const size_t eb = dtype_bytes(g.w_dtype);
     const int64_t row_bytes = (int64_t)g.d_model * eb;
     for (int t = 0; t < T; ++t) {

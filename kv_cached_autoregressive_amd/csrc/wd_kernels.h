@@ -142,12 +142,38 @@ hipError_t launch_attention_combine(const AttnParams& p, hipStream_t s);
 
 // ---- Qwen3: per-head q/k RMSNorm + NeoX RoPE, K/V append -------------------------------------
 // With part != null the q|k|v row is the in-order sum of G fp32 partial slabs
-// part[g][b][:] ([G][B][(Hq + 2 Hkv) hd]) instead of qkv.
+// part[g][b][:] ([G][B][(Hq + 2 Hkv) hd]) instead of qkv.  Row b appends to the cache of
+// stream b / rows_per_stream at position pos[b] (rows_per_stream > 1: prefill chunks).
 hipError_t launch_qk_rope_append(const float* qkv, int B, int Hq, int Hkv, int hd,
                                  const int32_t* pos, int ctx, const float* qn, const float* kn,
                                  float eps, float base, float qscale, float* q_out, void* Kc,
                                  void* Vc, int cache_dtype, int64_t kv_bstride, hipStream_t s,
-                                 const float* part = nullptr, int G = 0);
+                                 const float* part = nullptr, int G = 0, int rows_per_stream = 1);
+
+// ---- batched prefill (Qwen3) --------------------------------------------------------------------
+// Chunk rows r = b * C + j (stream b, position t0 + j, j < Cn): x[r] = the audio row or the
+// token's embedding (E in fragment layout), pos[r] = t0 + j (-1 and a zero row for j >= Cn).
+hipError_t launch_pf_embed(float* x, int32_t* pos, const void* E, int w_dtype, const int32_t* tokens, int T,
+                           const void* emb, int A, int offset, int t0, int B, int C, int Cn, int d, int V,
+                           unsigned* err, hipStream_t s);
+// Dense GEMM over fragment-layout operands: C[R, N] = (Ahi + Alo)[R, K] . W[N, K]^T.
+enum FgEpi : int { FG_STORE = 0, FG_RESID = 1, FG_SWIGLU = 2 };
+struct FgParams {
+  const void* W; int w_dtype; int N; int K;   // W fragment layout (N % 128 == 0)
+  const void* Ahi; const void* Alo; int R;    // A fragment layout [R rounded up to 128, K]
+  int epi;
+  float* out; int ldo;                        // STORE: out = C; RESID: out += C (fp32 [R, ldo])
+  void* Ohi; void* Olo;                       // SWIGLU: silu(gate) * up, fragment layout [R_pad, N/2]
+};
+hipError_t launch_fgemm(const FgParams& p, hipStream_t s);
+// Causal attention of a chunk's rows over cache rows 0..t of their stream (GQA).
+struct PfAttnParams {
+  const float* q;                             // [B*C, Hq*hd] scaled, normed, rotated
+  const void* K; const void* V; int cache_dtype; int64_t kv_bstride; int ctx;   // [B][Hkv][ctx][hd]
+  int B; int C; int Cn; int t0; int Hq; int Hkv; int hd;
+  void* o_hi; void* o_lo; int o_dtype;        // split fragment layout [B*C rounded up, Hq*hd]
+};
+hipError_t launch_pf_attn(const PfAttnParams& p, hipStream_t s);
 
 // ---- beam reorder: cache-row gather -----------------------------------------------------------
 struct BeamIdx { int32_t v[64]; };
