@@ -78,45 +78,49 @@ hipError_t launch_pf_embed(float* x, int32_t* pos, const void* E, int w_dtype, c
 // ---- dense GEMM over fragment-layout operands -------------------------------------------------
 // C[r][n] = sum_k (Ahi + Alo)[r][k] W[n][k]: A is the split activation [Rp, K] and W the
 // repacked weight [N, K], both in fragment order, so every MFMA operand is one contiguous
-// 1 KB tile read with 16-byte lane loads.  Block tile 128 rows x 128 columns, four waves of
-// 64 x 64 (4 x 4 MFMA tiles), operands one K step ahead of the MFMAs.
-template <typename T, int EPI>
+// 1 KB tile read with 16-byte lane loads; operands run one K step ahead of the MFMAs.
+// WC = 4: block 128 x 128 (waves 2 x 2 of 4 x 4 tiles); WC = 2: block 64 x 128 (waves 1 x 4
+// of 4 x 2 tiles), twice the blocks for narrow outputs.
+template <typename T, int EPI, int WC>
 __global__ __launch_bounds__(256) void k_fgemm(FgParams p) {
+  constexpr int WR = 4;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int rt0 = blockIdx.x * 8 + (w & 1) * 4;    // first 16-row tile of this wave
-  const int ct0 = blockIdx.y * 8 + (w >> 1) * 4;   // first 16-column tile
+  const int rt0 = WC == 4 ? blockIdx.x * 8 + (w & 1) * 4 : blockIdx.x * 4;   // first 16-row tile of this wave
+  const int ct0 = WC == 4 ? blockIdx.y * 8 + (w >> 1) * 4 : blockIdx.y * 8 + w * 2;   // first 16-column tile
   const int KST = p.K >> 5;
   const pv4u* __restrict__ Ah = reinterpret_cast<const pv4u*>(p.Ahi);
   const pv4u* __restrict__ Al = reinterpret_cast<const pv4u*>(p.Alo);
   const pv4u* __restrict__ Wt = reinterpret_cast<const pv4u*>(p.W);
-  pf32x4_t acc[4][4];
+  pf32x4_t acc[WR][WC];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WR; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = pf32x4_t{0.f, 0.f, 0.f, 0.f};
-  pv4u ah[4], al[4], wf[4];
-  auto load = [&](int s, pv4u (&h)[4], pv4u (&l)[4], pv4u (&f)[4]) __attribute__((always_inline)) {
+    for (int j = 0; j < WC; ++j) acc[i][j] = pf32x4_t{0.f, 0.f, 0.f, 0.f};
+  pv4u ah[WR], al[WR], wf[WC];
+  auto load = [&](int s, pv4u (&h)[WR], pv4u (&l)[WR], pv4u (&f)[WC]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < WR; ++i) {
       h[i] = Ah[((int64_t)(rt0 + i) * KST + s) * 64 + lane];
       l[i] = Al[((int64_t)(rt0 + i) * KST + s) * 64 + lane];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f[j] = Wt[((int64_t)(ct0 + j) * KST + s) * 64 + lane];
+    for (int j = 0; j < WC; ++j) f[j] = Wt[((int64_t)(ct0 + j) * KST + s) * 64 + lane];
   };
   load(0, ah, al, wf);
   for (int s = 0; s < KST; ++s) {
-    pv4u nh[4], nl[4], nf[4];
+    pv4u nh[WR], nl[WR], nf[WC];
     load(min(s + 1, KST - 1), nh, nl, nf);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WR; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < WC; ++j) {
         acc[i][j] = pmma(ah[i], wf[j], acc[i][j], (T*)nullptr);
         acc[i][j] = pmma(al[i], wf[j], acc[i][j], (T*)nullptr);
       }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { ah[i] = nh[i]; al[i] = nl[i]; wf[i] = nf[i]; }
+    for (int i = 0; i < WR; ++i) { ah[i] = nh[i]; al[i] = nl[i]; }
+#pragma unroll
+    for (int j = 0; j < WC; ++j) wf[j] = nf[j];
   }
   // tile (i, j): lane holds rows (rt0+i)*16 + 4*(lane/16) + e of column (ct0+j)*16 + lane%16
   const int rsub = (lane >> 4) * 4, col = lane & 15;
@@ -124,9 +128,9 @@ __global__ __launch_bounds__(256) void k_fgemm(FgParams p) {
     // weight row blocks alternate gate, up for the same 16 outputs: tiles (0,1), (2,3)
     const int half = p.N >> 1;
 #pragma unroll
-    for (int j = 0; j < 4; j += 2)
+    for (int j = 0; j < WC; j += 2)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < WR; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = (rt0 + i) * 16 + rsub + e, jj = ((ct0 + j) >> 1) * 16 + col;
@@ -137,9 +141,9 @@ __global__ __launch_bounds__(256) void k_fgemm(FgParams p) {
         }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WR; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < WC; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = (rt0 + i) * 16 + rsub + e, n = (ct0 + j) * 16 + col;
@@ -155,13 +159,18 @@ __global__ __launch_bounds__(256) void k_fgemm(FgParams p) {
 hipError_t launch_fgemm(const FgParams& p, hipStream_t s) {
   if (p.R <= 0 || p.N <= 0 || p.N % 128 || p.K <= 0 || p.K % 32 || !p.W || !p.Ahi || !p.Alo) return hipErrorInvalidValue;
   if (p.epi == FG_SWIGLU ? (!p.Ohi || !p.Olo || p.N % 256) : (!p.out || p.ldo < p.N)) return hipErrorInvalidValue;
-  const dim3 grid((p.R + 127) / 128, p.N / 128);
-#define WD_FG(T_)                                                                     \
-  switch (p.epi) {                                                                    \
-    case FG_STORE: k_fgemm<T_, FG_STORE><<<grid, 256, 0, s>>>(p); break;              \
-    case FG_RESID: k_fgemm<T_, FG_RESID><<<grid, 256, 0, s>>>(p); break;              \
-    case FG_SWIGLU: k_fgemm<T_, FG_SWIGLU><<<grid, 256, 0, s>>>(p); break;            \
-    default: return hipErrorInvalidValue;                                             \
+  // 128-row blocks unless they leave CUs idle (then 64-row blocks; A is padded to 128 rows)
+  const bool wide = (int64_t)((p.R + 127) / 128) * (p.N / 128) >= 256;
+  const dim3 grid(wide ? (p.R + 127) / 128 : (p.R + 63) / 64, p.N / 128);
+#define WD_FG(T_)                                                                                        \
+  switch (p.epi) {                                                                                       \
+    case FG_STORE: if (wide) k_fgemm<T_, FG_STORE, 4><<<grid, 256, 0, s>>>(p);                           \
+                   else k_fgemm<T_, FG_STORE, 2><<<grid, 256, 0, s>>>(p); break;                         \
+    case FG_RESID: if (wide) k_fgemm<T_, FG_RESID, 4><<<grid, 256, 0, s>>>(p);                           \
+                   else k_fgemm<T_, FG_RESID, 2><<<grid, 256, 0, s>>>(p); break;                         \
+    case FG_SWIGLU: if (wide) k_fgemm<T_, FG_SWIGLU, 4><<<grid, 256, 0, s>>>(p);                         \
+                    else k_fgemm<T_, FG_SWIGLU, 2><<<grid, 256, 0, s>>>(p); break;                       \
+    default: return hipErrorInvalidValue;                                                                \
   }
   if (p.w_dtype == DT_BF16) { WD_FG(bf16_t) }
   else if (p.w_dtype == DT_F16) { WD_FG(f16_t) }
@@ -182,7 +191,7 @@ constexpr int PQ = 64, PK = 32;
 template <typename CT, typename OT, int HD>
 __global__ __launch_bounds__(256) void k_pf_attn(PfAttnParams p) {
   constexpr int HH = HD / 2;   // channels per thread
-  __shared__ __align__(16) CT Ks[PK * HD];
+  __shared__ __align__(16) CT Ks[PK * HD];   // cache type (fp32 tiles measured slower: twice the LDS bytes)
   __shared__ __align__(16) CT Vs[PK * HD];
   const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = p.Hq / p.Hkv;
