@@ -53,6 +53,7 @@ struct Plan {
   size_t self_slab = 0;   // bytes of one K (or V) block of one layer
   int n_bufs = 1;
   size_t cross = 0, cross_slab = 0;
+  size_t xfrag = 0;          // encoder states in fragment order (cross-K/V GEMM operand, 16-bit)
   size_t x = 0, y = 0, q = 0, qkv = 0, o = 0, h = 0, part = 0, amax = 0, err = 0, pos_tmp = 0;
   size_t gpart = 0; int64_t gpart_cap = 0;   // split-K GEMM partials [G][B][N] fp32
   size_t tok_in = 0, ov_in = 0;              // staged tokens [B] and embedding override rows [B, d]
@@ -93,6 +94,7 @@ std::string check_config(const wd_config& c) {
   if (c.arch == WD_ARCH_WHISPER) {
     if (c.n_kv_heads != c.n_heads || c.n_heads * c.head_dim != c.d_model) return "whisper: heads * head_dim must equal d_model";
     if (c.max_frames <= 0) return "whisper: max_frames must be positive";
+    if (c.w_dtype != DT_F32 && c.d_model % 128) return "whisper: 16-bit weights need d_model % 128 == 0 (cross K/V GEMM tiles)";
     if (c.n_enc <= 0 || c.max_batch % c.n_enc) return "whisper: n_enc must divide max_batch";
     if (c.max_batch / c.n_enc > 8) return "whisper: at most 8 rows per encoder set";
   } else {
@@ -178,6 +180,7 @@ Plan make_plan(const wd_config& c) {
   if (c.arch == WD_ARCH_WHISPER) {
     p.cross_slab = (size_t)c.n_enc * hq * (size_t)c.max_frames * hd * cb;
     p.cross = b.take(2 * p.cross_slab * c.n_layers);
+    if (p.mfma) p.xfrag = b.take(((size_t)c.n_enc * c.max_frames + 127) / 128 * 128 * d * wb);   // X in fragment order
   }
   const size_t wide = std::max({d, 2 * ff, (hq + 2 * hkv) * hd});
   p.x = b.take(Bm * d * f4);
@@ -795,8 +798,8 @@ wd_status wd_load(const wd_config* cfg, const wd_tensor* weights, int32_t n_weig
         chk(mat(p + "self.v.w", L.wqkv, d, d, 1, 2 * d / 16, 2 * d));
         chk(mat(p + "self.o.w", L.wo, d, d, 1, 0, 0));
         chk(mat(p + "cross.q.w", L.wcq, d, d, 1, 0, 0));
-        chk(cp(p + "cross.k.w", L.wckv, wdt, d, d, 0));       // row-major: the cross-K/V GEMM reads rows
-        chk(cp(p + "cross.v.w", L.wckv, wdt, d, d, d));
+        chk(mat(p + "cross.k.w", L.wckv, d, d, 1, 0, 0));       // fused [Wk; Wv] (fragment order for 16-bit)
+        chk(mat(p + "cross.v.w", L.wckv, d, d, 1, d / 16, d));
         chk(mat(p + "cross.o.w", L.wco, d, d, 1, 0, 0));
         chk(mat(p + "fc1.w", L.w1, ff, d, 1, 0, 0));
         chk(mat(p + "fc2.w", L.w2, d, ff, 1, 0, 0));
@@ -853,11 +856,17 @@ wd_status wd_cross_kv(wd_ctx* ctx, const void* enc, int32_t frames) {
     if (g.arch != WD_ARCH_WHISPER) return fail(ctx, WD_ERR_STATE, "wd_cross_kv: no cross-attention in this arch");
     if (!enc) return fail(ctx, WD_ERR_ARG, "wd_cross_kv: enc must not be null");
     if (frames < 1 || frames > g.max_frames) return fail(ctx, WD_ERR_ARG, "wd_cross_kv: frames outside [1, max_frames]");
+    const void* X = enc;
+    if (ctx->plan.mfma) {   // X feeds every layer: repack it into fragment order once
+      HIPCHK(ctx, wd::launch_pack_rows(enc, g.w_dtype, ctx->at(ctx->plan.xfrag), (int64_t)g.n_enc * frames, g.d_model,
+                                       ctx->stream), "cross K/V: pack encoder states");
+      X = ctx->at(ctx->plan.xfrag);
+    }
     for (int l = 0; l < g.n_layers; ++l) {
       const LayerOff& L = ctx->plan.L[l];
       const bool on = prof_on(ctx, PK_XKV_GEMM, l);
       prof_begin(ctx, on);
-      HIPCHK(ctx, wd::launch_cross_kv_gemm(enc, ctx->at(L.wckv), ctx->at<float>(L.bckv), g.w_dtype,
+      HIPCHK(ctx, wd::launch_cross_kv_gemm(X, ctx->at(L.wckv), ctx->at<float>(L.bckv), g.w_dtype,
                                            g.n_enc * frames, g.d_model, frames, g.max_frames, g.n_heads,
                                            g.head_dim, ctx->cross_k(l), ctx->cross_v(l), g.cache_dtype,
                                            ctx->stream), "cross K/V projection");

@@ -183,9 +183,13 @@ hipError_t launch_reorder(const void* src, void* dst, int elt_bytes, const BeamI
 
 // ---- cross K/V projection (dense GEMM) with cache scatter ------------------------------------
 // C[m, n] = sum_k X[m,k] W[n,k] (+ bias[n]); m = e*frames + f; n < d -> K cache, else V cache;
-// caches [n_enc][H][max_frames][hd] in cache_dtype.
+// caches [n_enc][H][max_frames][hd] in cache_dtype.  fp32: X and W row-major.  16-bit: X in
+// fragment order (launch_pack_rows, rows padded to a multiple of 128), W in fragment order,
+// hd == 64, d % 128 == 0, 16-bit caches.
 hipError_t launch_cross_kv_gemm(const void* X, const void* W, const float* bias, int w_dtype,
                                 int M, int d, int frames, int max_frames, int H, int hd,
                                 void* Kc, void* Vc, int cache_dtype, hipStream_t s);
+// Row-major [M, d] 16-bit rows -> fragment order (the cross-K/V GEMM's X operand).
+hipError_t launch_pack_rows(const void* X, int w_dtype, void* Xf, int64_t M, int d, hipStream_t s);
 
 }  // namespace wd
