@@ -145,24 +145,33 @@ __global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {
   __shared__ float qs[NQ * HD];
   if (p.qpart && p.rope) {
     // Qwen3: raw q heads and the appended k, v summed into LDS, then per-head RMSNorm and
-    // the NeoX rotation (angles in double, as the standalone q/k kernel takes them)
+    // the NeoX rotation (cos and sin of the position's angles from the table)
     __shared__ float kvs[2 * HD], cs_[HD / 2], sn_[HD / 2], rsq[NQ + 1];
     const int ps = n_rows - 1;
     const bool own = p.append && ps >= r_lo && ps < r_hi;
-    for (int i = t; i < nq * HD; i += NT) {
-      const int qi = i / HD, c = i - qi * HD;
-      qs[i] = sum_parts<16>(p.qpart + (int64_t)qrow(qi) * p.qpart_ld + p.q_off + qhead(qi) * HD + c, qslab, p.qG);
+    // the rotation of row ps, requested by the block's last HD/2 threads ahead of the sums
+    const int ti = t - (NT - HD / 2);
+    float rc = 0.f, rsn = 0.f;
+    if (ti >= 0) {
+      rc = p.rope_cs[(int64_t)ps * (HD / 2) + ti];
+      rsn = p.rope_cs[((int64_t)p.rows_cap + ps) * (HD / 2) + ti];
     }
-    if (own)
-      for (int i = t; i < 2 * HD; i += NT) {
-        const int c = i % HD;
-        kvs[i] = sum_parts<16>(p.qpart + (int64_t)bq0 * p.qpart_ld + (i >= HD ? p.v_off : p.k_off) + g * HD + c,
+    // q values, then the appended k and v, spread over the threads (one round trip when
+    // nq * HD + 2 HD <= NT)
+    const int nqv = nq * HD;
+    for (int i = t; i < nqv + (own ? 2 * HD : 0); i += NT) {
+      if (i < nqv) {
+        const int qi = i / HD, c = i - qi * HD;
+        qs[i] = sum_parts<16>(p.qpart + (int64_t)qrow(qi) * p.qpart_ld + p.q_off + qhead(qi) * HD + c, qslab, p.qG);
+      } else {
+        const int j = i - nqv, c = j % HD;
+        kvs[j] = sum_parts<16>(p.qpart + (int64_t)bq0 * p.qpart_ld + (j >= HD ? p.v_off : p.k_off) + g * HD + c,
                                qslab, p.qG);
       }
-    for (int i = t; i < HD / 2; i += NT) {
-      const double th = (double)ps * pow((double)p.rope_base, -2.0 * (double)i / (double)HD);
-      cs_[i] = (float)cos(th);
-      sn_[i] = (float)sin(th);
+    }
+    if (ti >= 0) {
+      cs_[ti] = rc;
+      sn_[ti] = rsn;
     }
     __syncthreads();
     const int nh = nq + (own ? 1 : 0);   // q heads, then the appended k
@@ -199,23 +208,24 @@ __global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {
       }
     __syncthreads();   // q in LDS; the appended row visible to the block's loads below
   } else if (p.qpart) {
-    for (int i = t; i < nq * HD; i += NT) {
-      const int qi = i / HD, c = i - qi * HD;
-      const int col = qhead(qi) * HD + c;
-      const float* src = p.qpart + (int64_t)qrow(qi) * p.qpart_ld + p.q_off + col;
-      qs[i] = (sum_parts<16>(src, qslab, p.qG) + (p.qbias ? p.qbias[col] : 0.f)) * p.qscale;
-    }
-    if (p.append && p.pos) {   // the appended row lives in this block's split: write it first
-      const int ps = n_rows - 1;
-      if (ps >= r_lo && ps < r_hi && t < 2 * HD) {
-        const int c = t % HD;
-        const bool isv = t >= HD;
+    // q values, then (when the appended row lives in this block's split) its k and v, spread
+    // over the threads; the row is written before any row is read
+    const int nqv = nq * HD;
+    for (int i = t; i < nqv + (appended ? 2 * HD : 0); i += NT) {
+      if (i < nqv) {
+        const int qi = i / HD, c = i - qi * HD;
+        const int col = qhead(qi) * HD + c;
+        const float* src = p.qpart + (int64_t)qrow(qi) * p.qpart_ld + p.q_off + col;
+        qs[i] = (sum_parts<16>(src, qslab, p.qG) + (p.qbias ? p.qbias[col] : 0.f)) * p.qscale;
+      } else {
+        const int j = i - nqv, c = j % HD;
+        const bool isv = j >= HD;
         const float* src = p.qpart + (int64_t)bq0 * p.qpart_ld + (isv ? p.v_off : p.k_off) + g * HD + c;
         float v = sum_parts<16>(src, qslab, p.qG);
         if (isv && p.vbias) v += p.vbias[g * HD + c];
         CT* base = reinterpret_cast<CT*>(const_cast<void*>(isv ? p.V : p.K));
-        base[(int64_t)kvb * p.kvb_stride + ((int64_t)g * p.rows_cap + ps) * HD + c] = from_f<CT>(v);
-        apv[t] = v;
+        base[(int64_t)kvb * p.kvb_stride + ((int64_t)g * p.rows_cap + ps_app) * HD + c] = from_f<CT>(v);
+        apv[j] = v;
       }
     }
     __syncthreads();   // q in LDS; the appended row visible to the block's loads below
@@ -409,7 +419,7 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   if ((!p.q && !p.qpart) || !p.K || !p.V || (!p.qpart && (p.q_ld % 4))) return hipErrorInvalidValue;
   if (p.qpart && (p.qG < 1 || p.qG > 16 || p.qpart_ld <= 0)) return hipErrorInvalidValue;
   if (p.append && (!p.qpart || !p.pos || (p.Hq != p.Hkv && !p.rope))) return hipErrorInvalidValue;
-  if (p.rope && (!p.qpart || !p.pos || !p.qn || !p.kn || !(p.eps > 0.f) || !(p.rope_base > 0.f)))
+  if (p.rope && (!p.qpart || !p.pos || !p.qn || !p.kn || !(p.eps > 0.f) || !p.rope_cs))
     return hipErrorInvalidValue;
   if (p.o_hi ? (!p.o_lo || (p.Hq * p.hd) % 32 || (p.o_dtype != DT_F16 && p.o_dtype != DT_BF16))
              : (!p.out || p.out_ld < p.Hq * p.hd))

@@ -417,7 +417,7 @@ __global__ __launch_bounds__(64) void k_qk_rope_append(const float* __restrict__
                                                        int hd, const int32_t* pos, int ctx,
                                                        const float* __restrict__ qn,
                                                        const float* __restrict__ kn, float eps,
-                                                       float base, float qscale, float* q_out,
+                                                       const float* __restrict__ rope_cs, float qscale, float* q_out,
                                                        CT* Kc, CT* Vc, int64_t kv_bstride,
                                                        const float* __restrict__ part, int G, int B, int rps) {
   __shared__ float z[256];
@@ -453,10 +453,10 @@ __global__ __launch_bounds__(64) void k_qk_rope_append(const float* __restrict__
     if (lane + 64 * j < hd) z[lane + 64 * j] = v[j] * rs * gain[lane + 64 * j];
   __syncthreads();
   const int half = hd / 2;
-  const double dpos = ok ? (double)p : 0.0;
+  const float* cs_row = rope_cs + (int64_t)(ok ? p : 0) * half;
+  const float* sn_row = cs_row + (int64_t)ctx * half;
   for (int i = lane; i < half; i += 64) {
-    const double th = dpos * pow((double)base, -2.0 * (double)i / (double)hd);
-    const float cs = (float)cos(th), sn = (float)sin(th);
+    const float cs = cs_row[i], sn = sn_row[i];
     const float a = z[i], bb = z[i + half];
     const float r0 = a * cs - bb * sn, r1 = bb * cs + a * sn;
     if (slot < Hq) {
@@ -474,32 +474,50 @@ __global__ __launch_bounds__(64) void k_qk_rope_append(const float* __restrict__
 
 template <typename CT>
 static void qk_rope_run(dim3 grid, hipStream_t s, const float* qkv, int Hq, int Hkv, int hd, const int32_t* pos,
-                        int ctx, const float* qn, const float* kn, float eps, float base, float qscale, float* q_out,
+                        int ctx, const float* qn, const float* kn, float eps, const float* rope_cs, float qscale, float* q_out,
                         void* Kc, void* Vc, int64_t kv_bstride, const float* part, int G, int B, int rps) {
   if (!part || G <= 8)
-    k_qk_rope_append<CT, 8><<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out,
+    k_qk_rope_append<CT, 8><<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, rope_cs, qscale, q_out,
                                                 (CT*)Kc, (CT*)Vc, kv_bstride, part, G, B, rps);
   else if (G <= 16)
-    k_qk_rope_append<CT, 16><<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out,
+    k_qk_rope_append<CT, 16><<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, rope_cs, qscale, q_out,
                                                  (CT*)Kc, (CT*)Vc, kv_bstride, part, G, B, rps);
   else
-    k_qk_rope_append<CT, 32><<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out,
+    k_qk_rope_append<CT, 32><<<grid, 64, 0, s>>>(qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, rope_cs, qscale, q_out,
                                                  (CT*)Kc, (CT*)Vc, kv_bstride, part, G, B, rps);
 }
 
 hipError_t launch_qk_rope_append(const float* qkv, int B, int Hq, int Hkv, int hd, const int32_t* pos,
-                                 int ctx, const float* qn, const float* kn, float eps, float base,
+                                 int ctx, const float* qn, const float* kn, float eps, const float* rope_cs,
                                  float qscale, float* q_out, void* Kc, void* Vc, int cache_dtype,
                                  int64_t kv_bstride, hipStream_t s, const float* part, int G, int rps) {
-  if (B <= 0 || hd > 256 || (hd % 2) || Hq <= 0 || Hkv <= 0 || rps < 1) return hipErrorInvalidValue;
+  if (B <= 0 || hd > 256 || (hd % 2) || Hq <= 0 || Hkv <= 0 || rps < 1 || !rope_cs) return hipErrorInvalidValue;
   if (part ? (G < 1 || G > 32) : !qkv) return hipErrorInvalidValue;
   dim3 grid(Hq + 2 * Hkv, B);
   switch (cache_dtype) {
-    case DT_F32: qk_rope_run<float>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, Kc, Vc, kv_bstride, part, G, B, rps); break;
-    case DT_F16: qk_rope_run<f16_t>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, Kc, Vc, kv_bstride, part, G, B, rps); break;
-    case DT_BF16: qk_rope_run<bf16_t>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, base, qscale, q_out, Kc, Vc, kv_bstride, part, G, B, rps); break;
+    case DT_F32: qk_rope_run<float>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, rope_cs, qscale, q_out, Kc, Vc, kv_bstride, part, G, B, rps); break;
+    case DT_F16: qk_rope_run<f16_t>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, rope_cs, qscale, q_out, Kc, Vc, kv_bstride, part, G, B, rps); break;
+    case DT_BF16: qk_rope_run<bf16_t>(grid, s, qkv, Hq, Hkv, hd, pos, ctx, qn, kn, eps, rope_cs, qscale, q_out, Kc, Vc, kv_bstride, part, G, B, rps); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_rope_table(float* __restrict__ cs, int ctx, int hd, float base) {
+  const int half = hd / 2;
+  const int64_t n = (int64_t)ctx * half;
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < n; j += (int64_t)gridDim.x * 256) {
+    const int p = (int)(j / half), i = (int)(j - (int64_t)p * half);
+    const double th = (double)p * pow((double)base, -2.0 * (double)i / (double)hd);
+    cs[j] = (float)cos(th);
+    cs[n + j] = (float)sin(th);
+  }
+}
+
+hipError_t launch_rope_table(float* cs, int ctx, int hd, float base, hipStream_t s) {
+  if (!cs || ctx <= 0 || hd <= 0 || hd % 2 || !(base > 0.f)) return hipErrorInvalidValue;
+  const int blocks = (int)std::min<int64_t>(((int64_t)ctx * (hd / 2) + 255) / 256, 4096);
+  k_rope_table<<<blocks, 256, 0, s>>>(cs, ctx, hd, base);
   return hipGetLastError();
 }
 

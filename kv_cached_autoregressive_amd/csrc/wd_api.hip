@@ -55,6 +55,7 @@ struct Plan {
   size_t cross = 0, cross_slab = 0;
   size_t xfrag = 0;          // encoder states in fragment order (cross-K/V GEMM operand, 16-bit)
   size_t x = 0, y = 0, q = 0, qkv = 0, o = 0, h = 0, part = 0, amax = 0, err = 0, pos_tmp = 0;
+  size_t rope = 0;           // Qwen3: cos [context][hd/2], then sin [context][hd/2]
   size_t gpart = 0; int64_t gpart_cap = 0;   // split-K GEMM partials [G][B][N] fp32
   size_t tok_in = 0, ov_in = 0;              // staged tokens [B] and embedding override rows [B, d]
   int max_splits = 1, amax_parts = 1;
@@ -111,16 +112,18 @@ std::string check_config(const wd_config& c) {
 //    below ~170 slabs (each split costs a combine launch, about 4 us): one split at the
 //    192 slabs of the whisper-small step, 4 splits of 256 rows at the 64 of the Qwen3 step;
 //  * splits of at least 64 rows, at most 64 splits (the combine's limit).
-// Tuning override for sweeps: WD_ATTN_ROWS="self_rows,cross_rows" (0 keeps the policy).
-int attn_rows_override(bool cross) {
-  static int sr = 0, cr = 0;
+// Tuning override for sweeps: WD_ATTN_ROWS="self_rows,cross_rows[,waves]" (0 keeps the
+// policy; waves 4 or 8 per block).
+int attn_rows_override(int which) {   // 0 self rows, 1 cross rows, 2 waves
+  static int v[3] = {0, 0, 0};
   static bool read = false;
   if (!read) {
     read = true;
     if (const char* e = getenv("WD_ATTN_ROWS"))
-      if (sscanf(e, "%d,%d", &sr, &cr) != 2) sr = cr = 0;
+      if (sscanf(e, "%d,%d,%d", &v[0], &v[1], &v[2]) < 2) v[0] = v[1] = v[2] = 0;
+    if (v[2] != 4 && v[2] != 8) v[2] = 0;
   }
-  return cross ? cr : sr;
+  return v[which];
 }
 
 void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits, int* nw, bool cross = false) {
@@ -129,13 +132,14 @@ void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits, int*
   int r = (rows + want - 1) / want;
   r = std::max(r, (rows + 63) / 64);   // at most 64 splits (the combine's limit)
   r = std::max(r, 64);
-  if (const int o = attn_rows_override(cross)) r = std::max(o, (rows + 63) / 64);
+  if (const int o = attn_rows_override(cross ? 1 : 0)) r = std::max(o, (rows + 63) / 64);
   r = (r + 31) & ~31;
   r = std::min(r, std::max(12288 / std::max(nq, 1), (rows + 63) / 64));
   r = std::max(r, 1);
   *split_rows = r;
   *n_splits = std::max(1, (rows + r - 1) / r);
   *nw = wide ? 8 : 4;
+  if (const int o = attn_rows_override(2)) *nw = o;
 }
 
 // Positions per chunk of the batched prefill: its rows (streams x positions) feed dense MFMA
@@ -218,6 +222,7 @@ Plan make_plan(const wd_config& c) {
   p.err = b.take(64);
   p.pos_tmp = b.take(Bm * 4);
   p.tok_in = b.take(Bm * 4);
+  if (c.arch == WD_ARCH_QWEN3) p.rope = b.take((size_t)c.context * hd * f4);
   if (c.arch == WD_ARCH_QWEN3 && p.mfma) {
     const size_t R = ((size_t)Bm * PF_CHUNK + 127) / 128 * 128, nqkv = (hq + 2 * hkv) * hd;
     p.pf_rows = (int)R;
@@ -402,10 +407,10 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
         ap.qpart = G > 1 ? gpart : qkv; ap.qG = G; ap.qpart_ld = nqkv; ap.q_off = 0; ap.qbias = nullptr;
         ap.qscale = qscale; ap.append = true; ap.k_off = hq * hd; ap.v_off = (hq + hkv) * hd; ap.vbias = nullptr;
         ap.rope = true; ap.qn = c->at<float>(L.qn); ap.kn = c->at<float>(L.kn); ap.eps = g.norm_eps;
-        ap.rope_base = g.rope_base;
+        ap.rope_cs = c->at<float>(P.rope);
       } else {
         HIPCHK(c, wd::launch_qk_rope_append(qkv, B, hq, hkv, hd, pos, g.context, c->at<float>(L.qn),
-                                            c->at<float>(L.kn), g.norm_eps, g.rope_base, qscale, q,
+                                            c->at<float>(L.kn), g.norm_eps, c->at<float>(P.rope), qscale, q,
                                             c->self_k(l), c->self_v(l), g.cache_dtype, kv_bstride, s, gpart, G),
                "qk norm/rope/append");
       }
@@ -548,7 +553,7 @@ wd_status run_step(wd_ctx* c, const int32_t* tok, int tok_stride, const int32_t*
       gp.epi = wd::EPI_STORE; gp.bias = nullptr; gp.out = qkv; gp.ldo = nqkv;
       HIPCHK(c, wd::launch_gemv(gp, s), "qkv projection");
       HIPCHK(c, wd::launch_qk_rope_append(qkv, B, hq, hkv, hd, pos, g.context, c->at<float>(L.qn),
-                                          c->at<float>(L.kn), g.norm_eps, g.rope_base, qscale, q,
+                                          c->at<float>(L.kn), g.norm_eps, c->at<float>(P.rope), qscale, q,
                                           c->self_k(l), c->self_v(l), g.cache_dtype, kv_bstride, s),
              "qk norm/rope/append");
     }
@@ -819,6 +824,7 @@ wd_status wd_load(const wd_config* cfg, const wd_tensor* weights, int32_t n_weig
       }
     } else {
       chk(vcopy("norm_f.g", plan.lnfg, d));
+      chk(wd::launch_rope_table(reinterpret_cast<float*>(c->ws + plan.rope), cfg->context, (int)hd, cfg->rope_base, s));
       for (int i = 0; i < cfg->n_layers && e == hipSuccess; ++i) {
         const std::string p = "dec." + std::to_string(i) + ".";
         const LayerOff& L = plan.L[i];
@@ -1005,7 +1011,7 @@ wd_status prefill_batched(wd_ctx* c, const int32_t* tokens, int B, int T, const 
       HIPCHK(c, wd::launch_norm_split(x, ah, al, adt, c->at<float>(L.n1g), nullptr, R, d, g.norm_eps, s), "prefill: norm1");
       WDCHK(gemm(c->at(L.wqkv), nqkv, d, ah, al, wd::FG_STORE, c->at<float>(P.pf_qkv), nqkv, "prefill: qkv"));
       HIPCHK(c, wd::launch_qk_rope_append(c->at<float>(P.pf_qkv), R, hq, hkv, hd, pos, g.context, c->at<float>(L.qn),
-                                          c->at<float>(L.kn), g.norm_eps, g.rope_base, qscale, c->at<float>(P.pf_q),
+                                          c->at<float>(L.kn), g.norm_eps, c->at<float>(P.rope), qscale, c->at<float>(P.pf_q),
                                           c->self_k(l), c->self_v(l), g.cache_dtype, kv_bstride, s, nullptr, 0, C),
              "prefill: qk norm/rope/append");
       wd::PfAttnParams pa{};

@@ -131,9 +131,10 @@ struct AttnParams {
   // v = sum_g qpart[..v_off..] + vbias, rounded to the cache dtype, before reading any row
   int k_off; int v_off; const float* vbias; bool append;
   // Qwen3 (rope): q and the appended k first go through the per-head RMSNorm (gains qn / kn
-  // [hd], eps) and the NeoX rotation by pos * rope_base^(-2i/hd) of the pairs (i, i + hd/2);
-  // v is appended as summed.  GQA allowed.
-  bool rope; const float* qn; const float* kn; float eps; float rope_base;
+  // [hd], eps) and the NeoX rotation of the pairs (i, i + hd/2) by the angle pos * base^(-2i/hd),
+  // its cos and sin read from rope_cs (launch_rope_table, rows_cap positions); v is appended as
+  // summed.  GQA allowed.
+  bool rope; const float* qn; const float* kn; float eps; const float* rope_cs;
 };
 // main kernel (writes o directly when n_splits == 1, else partials) ...
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
@@ -144,11 +145,16 @@ hipError_t launch_attention_combine(const AttnParams& p, hipStream_t s);
 // With part != null the q|k|v row is the in-order sum of G fp32 partial slabs
 // part[g][b][:] ([G][B][(Hq + 2 Hkv) hd]) instead of qkv.  Row b appends to the cache of
 // stream b / rows_per_stream at position pos[b] (rows_per_stream > 1: prefill chunks).
+// The rotation angles come from rope_cs (launch_rope_table over ctx positions).
 hipError_t launch_qk_rope_append(const float* qkv, int B, int Hq, int Hkv, int hd,
                                  const int32_t* pos, int ctx, const float* qn, const float* kn,
-                                 float eps, float base, float qscale, float* q_out, void* Kc,
+                                 float eps, const float* rope_cs, float qscale, float* q_out, void* Kc,
                                  void* Vc, int cache_dtype, int64_t kv_bstride, hipStream_t s,
                                  const float* part = nullptr, int G = 0, int rows_per_stream = 1);
+
+// NeoX RoPE table: cs[p][i] = cos(p * base^(-2i/hd)), then sn[p][i] = sin(...) at cs + ctx * hd/2,
+// for p < ctx, i < hd/2 (angles in double, rounded to float).
+hipError_t launch_rope_table(float* cs, int ctx, int hd, float base, hipStream_t s);
 
 // ---- batched prefill (Qwen3) --------------------------------------------------------------------
 // Chunk rows r = b * C + j (stream b, position t0 + j, j < Cn): x[r] = the audio row or the
