@@ -10,8 +10,9 @@
 // add, RMSNorm, gate|up with the SwiGLU epilogue, and down with the residual add.
 //
 // This file: the chunk's embedding rows, the dense GEMM over fragment-layout operands, and
-// the causal prefill attention.
+// the causal prefill attention (flash attention on the matrix cores).
 #include <algorithm>
+#include <type_traits>
 
 #include "wd_common.h"
 #include "wd_kernels.h"
@@ -180,99 +181,183 @@ hipError_t launch_fgemm(const FgParams& p, hipStream_t s) {
 }
 
 // ---- causal prefill attention ------------------------------------------------------------------
-// One block per (tile of PQ positions, kv head g, stream b): its PQ * G queries (G query heads
-// per kv head, GQA) attend over cache rows 0..t of their own position t.  Two threads per
-// query, each with half of the head's channels; K and V come through LDS in tiles of PK rows
-// (every lane of a wave reads the same key row: broadcast), and each query keeps an online
-// softmax state.  q is the scaled, normed and rotated query [R, Hq*hd] fp32; the output o goes
-// to the split fragment layout [Rp, Hq*hd] of the out projection.
-constexpr int PQ = 64, PK = 32;
+// Flash attention on the matrix cores.  A block takes 64 queries of one kv head g and stream b,
+// enumerated (position j, query head g*G + i) as q = j*G + i; wave w holds 16 of them.  Cache
+// rows stream through LDS in tiles of 32 keys: K as stored ([key][hd], rows padded), V
+// transposed ([hd][key]).  Per tile a wave computes S^T = K Q^T (16 keys x 16 queries per MFMA
+// tile, q split into hi + lo in the cache type), so a lane holds 4 keys of one query; the online
+// softmax state of that query lives in the lane; P^T (split hi + lo) is the B operand of
+// O^T += V^T P^T as it stands, with the A operand read from the transposed V tile in the same
+// key order.  Causal: key k counts for the query at position t when k <= t.  q is the scaled,
+// normed and rotated query [R, Hq*hd] fp32; o goes to the split fragment layout [Rp, Hq*hd].
+constexpr int PA_KT = 32;    // keys per tile
+constexpr int PA_QB = 64;    // queries per block (4 waves x 16)
+
+template <typename CT>
+__device__ __forceinline__ uint32_t pa_bits(CT v) {
+  if constexpr (sizeof(CT) == 2 && std::is_same<CT, bf16_t>::value) return v.x;
+  else return (uint32_t)__builtin_bit_cast(uint16_t, v);
+}
+template <typename CT>
+__device__ __forceinline__ uint32_t pa_pack2(float a, float b, uint32_t& lo) {
+  CT ha, la, hb, lb;
+  split_hi_lo<CT>(a, ha, la);
+  split_hi_lo<CT>(b, hb, lb);
+  lo = pa_bits(la) | (pa_bits(lb) << 16);
+  return pa_bits(ha) | (pa_bits(hb) << 16);
+}
 
 template <typename CT, typename OT, int HD>
 __global__ __launch_bounds__(256) void k_pf_attn(PfAttnParams p) {
-  constexpr int HH = HD / 2;   // channels per thread
-  __shared__ __align__(16) CT Ks[PK * HD];   // cache type (fp32 tiles measured slower: twice the LDS bytes)
-  __shared__ __align__(16) CT Vs[PK * HD];
-  const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  constexpr int KLD = HD + 8;                 // K tile row stride (elements): conflict-free 16 B reads
+  constexpr int VLD = PA_KT + 4;              // transposed V tile row stride
+  constexpr int NCH = PA_KT * HD / 8;         // 16-byte chunks per tile (K or V)
+  constexpr int CPT = NCH / 256;              // chunks per thread
+  constexpr int KS = HD / 32;                 // MFMA k-steps over the head dim
+  constexpr int HT = HD / 16;                 // output channel tiles
+  __shared__ __align__(16) CT Ks[PA_KT * KLD];
+  __shared__ __align__(16) CT Vt[HD * VLD];
+  const int g = blockIdx.y, b = blockIdx.z;
   const int G = p.Hq / p.Hkv;
-  const int t = threadIdx.x, qi = t >> 1, half = t & 1;
-  const int nq = PQ * G;                       // queries of the block (<= 128)
-  const int jq = qi / G, hq = g * G + qi % G;  // position within the chunk, query head
-  const bool active = qi < nq && tile * PQ + jq < p.Cn;
-  const int jrow = min(tile * PQ + jq, p.Cn - 1);
-  const int r = b * p.C + jrow;
-  const int tpos = p.t0 + jrow;                // absolute position of this query
-  // the block's last position bounds the rows it streams
-  const int jlast = min(tile * PQ + PQ, p.Cn) - 1;
-  const int rows = p.t0 + jlast + 1;
-  float q[HH], o[HH];
-  const float* qr = p.q + (int64_t)r * p.Hq * HD + hq * HD + half * HH;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+
+  // this lane's query (column col of the wave's 16)
+  const int qidx = blockIdx.x * PA_QB + wv * 16 + col;
+  const int jq = qidx / G, hq = g * G + (qidx - jq * G);
+  const bool active = jq < p.Cn;
+  const int jc = min(jq, p.Cn - 1);
+  const int tq = p.t0 + jc;
+  const int r = b * p.C + jc;
+  // key ranges: the block's (staged) and the wave's (computed)
+  const int rows_blk = p.t0 + min(p.Cn - 1, (blockIdx.x * PA_QB + PA_QB - 1) / G) + 1;
+  const int rows_w = p.t0 + min(p.Cn - 1, (blockIdx.x * PA_QB + wv * 16 + 15) / G) + 1;
+
+  // q^T as the B operand: lane (col, grp) holds channels 32 ks + 8 grp .. +8 of its query
+  pv4u qh[KS], ql[KS];
+  {
+    const float* qr = p.q + (int64_t)r * p.Hq * HD + hq * HD + 8 * grp;
 #pragma unroll
-  for (int c = 0; c < HH; c += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(qr + c);
-    q[c] = v.x; q[c + 1] = v.y; q[c + 2] = v.z; q[c + 3] = v.w;
+    for (int ks = 0; ks < KS; ++ks) {
+      const float4 u0 = *reinterpret_cast<const float4*>(qr + 32 * ks);
+      const float4 u1 = *reinterpret_cast<const float4*>(qr + 32 * ks + 4);
+      uint32_t l0, l1, l2, l3;
+      qh[ks][0] = pa_pack2<CT>(u0.x, u0.y, l0); qh[ks][1] = pa_pack2<CT>(u0.z, u0.w, l1);
+      qh[ks][2] = pa_pack2<CT>(u1.x, u1.y, l2); qh[ks][3] = pa_pack2<CT>(u1.z, u1.w, l3);
+      ql[ks][0] = l0; ql[ks][1] = l1; ql[ks][2] = l2; ql[ks][3] = l3;
+    }
   }
+  pf32x4_t acc[HT];
 #pragma unroll
-  for (int c = 0; c < HH; ++c) o[c] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  for (int h = 0; h < HT; ++h) acc[h] = pf32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+
   const CT* Kb = reinterpret_cast<const CT*>(p.K) + (int64_t)b * p.kv_bstride + (int64_t)g * p.ctx * HD;
   const CT* Vb = reinterpret_cast<const CT*>(p.V) + (int64_t)b * p.kv_bstride + (int64_t)g * p.ctx * HD;
-  constexpr int CH = 16 / sizeof(CT);          // elements per 16-byte chunk
-  constexpr int NCH = PK * HD / CH;            // chunks per tile
-  for (int k0 = 0; k0 < rows; k0 += PK) {
+  uint4 kst[CPT], vst[CPT];
+  auto fetch = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int i = t + 256 * u;
+      const int kr = min(k0 + i / (HD / 8), rows_blk - 1), c0 = (i % (HD / 8)) * 8;
+      kst[u] = *reinterpret_cast<const uint4*>(Kb + (int64_t)kr * HD + c0);
+      vst[u] = *reinterpret_cast<const uint4*>(Vb + (int64_t)kr * HD + c0);
+    }
+  };
+  fetch(0);
+  for (int k0 = 0; k0 < rows_blk; k0 += PA_KT) {
     __syncthreads();   // the previous tile is no longer read
-    for (int i = t; i < NCH; i += 256) {
-      const int kr = min(k0 + (i * CH) / HD, rows - 1), kc = (i * CH) % HD;
-      *reinterpret_cast<uint4*>(Ks + i * CH) = *reinterpret_cast<const uint4*>(Kb + (int64_t)kr * HD + kc);
-      *reinterpret_cast<uint4*>(Vs + i * CH) = *reinterpret_cast<const uint4*>(Vb + (int64_t)kr * HD + kc);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int i = t + 256 * u;
+      const int kk = i / (HD / 8), c0 = (i % (HD / 8)) * 8;
+      *reinterpret_cast<uint4*>(Ks + kk * KLD + c0) = kst[u];
+      const CT* ve = reinterpret_cast<const CT*>(&vst[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[(c0 + e) * VLD + kk] = ve[e];
     }
     __syncthreads();
-    const int kn = min(PK, rows - k0);
-    for (int kk = 0; kk < kn; ++kk) {
-      const CT* kr = Ks + kk * HD + half * HH;
-      float sc = 0.f;
+    if (k0 + PA_KT < rows_blk) fetch(k0 + PA_KT);   // next tile in flight during the math
+    if (k0 < rows_w) {
+      // S^T: two 16-key tiles; lane holds keys k0 + 16 kt + 4 grp + e of its query
+      pf32x4_t sc[2];
 #pragma unroll
-      for (int c = 0; c < HH; ++c) sc = fmaf(q[c], to_f(kr[c]), sc);
-      sc += __shfl_xor(sc, 1, WAVE);
-      if (k0 + kk <= tpos) {   // causal: rows 0..t of this query's position
-        if (sc > m) {
-          const float f = expf(m - sc);
-          l *= f;
+      for (int kt = 0; kt < 2; ++kt) {
+        sc[kt] = pf32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int c = 0; c < HH; ++c) o[c] *= f;
-          m = sc;
+        for (int ks = 0; ks < KS; ++ks) {
+          const pv4u a = *reinterpret_cast<const pv4u*>(Ks + (kt * 16 + col) * KLD + 32 * ks + 8 * grp);
+          sc[kt] = pmma(a, qh[ks], sc[kt], (CT*)nullptr);
+          sc[kt] = pmma(a, ql[ks], sc[kt], (CT*)nullptr);
         }
-        const float e = expf(sc - m);
-        l += e;
-        const CT* vr = Vs + kk * HD + half * HH;
+      }
+      float sv[8];
+      float mx = -INFINITY;
 #pragma unroll
-        for (int c = 0; c < HH; ++c) o[c] = fmaf(e, to_f(vr[c]), o[c]);
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = k0 + kt * 16 + 4 * grp + e;
+          sv[kt * 4 + e] = key <= tq ? sc[kt][e] : -INFINITY;
+          mx = fmaxf(mx, sv[kt * 4 + e]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+      const float mn = fmaxf(m, mx);          // finite: key 0 counts for every query
+      const float f = expf(m - mn);
+      m = mn;
+      lsum *= f;
+#pragma unroll
+      for (int h = 0; h < HT; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[h][e] *= f;
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = expf(sv[i] - mn);
+        lsum += pv[i];
+      }
+      pv4u ph, pl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t lo;
+        ph[i] = pa_pack2<CT>(pv[2 * i], pv[2 * i + 1], lo);
+        pl[i] = lo;
+      }
+      // O^T += V^T P^T; A operand: channel row col of tile h, keys 4 grp .. +4 and 16 + 4 grp .. +4
+#pragma unroll
+      for (int h = 0; h < HT; ++h) {
+        const CT* vr = Vt + (h * 16 + col) * VLD + 4 * grp;
+        const uint2 v0 = *reinterpret_cast<const uint2*>(vr);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16);
+        const pv4u a = pv4u{v0.x, v0.y, v1.x, v1.y};
+        acc[h] = pmma(a, ph, acc[h], (CT*)nullptr);
+        acc[h] = pmma(a, pl, acc[h], (CT*)nullptr);
       }
     }
   }
+  lsum += __shfl_xor(lsum, 16, WAVE);
+  lsum += __shfl_xor(lsum, 32, WAVE);
   if (!active) return;
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  const float inv = 1.0f / lsum;
   const int K = p.Hq * HD;
 #pragma unroll
-  for (int c = 0; c < HH; c += 8) {
-    float v[8];
+  for (int h = 0; h < HT; ++h) {
+    OT h4[4], l4[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = o[c + e] * inv;
-    OT h8[8], l8[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) split_hi_lo<OT>(v[e], h8[e], l8[e]);
-    const int64_t off = frag_offset(r, hq * HD + half * HH + c, K);   // 8 contiguous elements
-    __builtin_memcpy(reinterpret_cast<OT*>(p.o_hi) + off, h8, 16);
-    __builtin_memcpy(reinterpret_cast<OT*>(p.o_lo) + off, l8, 16);
+    for (int e = 0; e < 4; ++e) split_hi_lo<OT>(acc[h][e] * inv, h4[e], l4[e]);
+    const int64_t off = frag_offset(r, hq * HD + h * 16 + 4 * grp, K);   // 4 contiguous channels
+    __builtin_memcpy(reinterpret_cast<OT*>(p.o_hi) + off, h4, 8);
+    __builtin_memcpy(reinterpret_cast<OT*>(p.o_lo) + off, l4, 8);
   }
 }
 
 hipError_t launch_pf_attn(const PfAttnParams& p, hipStream_t s) {
   const int G = p.Hkv > 0 ? p.Hq / p.Hkv : 0;
-  if (p.B <= 0 || p.C <= 0 || p.Cn <= 0 || p.Cn > p.C || G <= 0 || p.Hq % p.Hkv || PQ * G > 128 ||
+  if (p.B <= 0 || p.C <= 0 || p.Cn <= 0 || p.Cn > p.C || G <= 0 || p.Hq % p.Hkv ||
       p.t0 < 0 || p.t0 + p.Cn > p.ctx || !p.q || !p.K || !p.V || !p.o_hi || !p.o_lo)
     return hipErrorInvalidValue;
-  const dim3 grid((p.Cn + PQ - 1) / PQ, p.Hkv, p.B);
+  const dim3 grid((p.Cn * G + PA_QB - 1) / PA_QB, p.Hkv, p.B);
 #define WD_PFA(CT_, HD_)                                                                        \
   if (p.o_dtype == DT_BF16) k_pf_attn<CT_, bf16_t, HD_><<<grid, 256, 0, s>>>(p);               \
   else if (p.o_dtype == DT_F16) k_pf_attn<CT_, f16_t, HD_><<<grid, 256, 0, s>>>(p);            \

@@ -76,3 +76,12 @@ def test_qwen3_split_k_above_16_rows():
     w = WL.reduced(WL.by_name("qwen3asr_bf16_b8"), layers=2, d=512, heads=4, kv_heads=2, d_ff=1536,
                    vocab=7001, context=64, batch=20, audio_offset=2, audio_rows=6)
     _qwen_parity(w, T=16, steps=6, streams=(0, 19))
+
+
+def test_qwen3_prefill_two_chunks_hd64_bf16_cache_gqa4():
+    """Head dim 64, a bf16 cache and 4 query heads per kv head (the prefill attention's
+    other instantiation), over two prefill chunks of 128 and 22 positions."""
+    w = WL.reduced(WL.by_name("qwen3asr_bf16_b8"), layers=2, d=256, heads=8, kv_heads=2, head_dim=64,
+                   cache_dtype="bf16", d_ff=512, vocab=7001, context=160, batch=2, audio_offset=5,
+                   audio_rows=60)
+    _qwen_parity(w, T=150, steps=4, streams=(0, 1))
