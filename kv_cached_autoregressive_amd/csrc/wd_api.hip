@@ -59,8 +59,8 @@ struct Plan {
   size_t gpart = 0; int64_t gpart_cap = 0;   // split-K GEMM partials [G][B][N] fp32
   size_t tok_in = 0, ov_in = 0;              // staged tokens [B] and embedding override rows [B, d]
   int max_splits = 1, amax_parts = 1;
-  // batched Qwen3 prefill: chunks of PF_CHUNK positions for all rows (pf_rows = rows of a chunk)
-  int pf_rows = 0;
+  // batched Qwen3 prefill: chunks of pf_pos_chunk positions for all rows (pf_rows = rows of a chunk)
+  int pf_rows = 0, pf_pos_chunk = 0;
   size_t pf_x = 0, pf_pos = 0, pf_ah = 0, pf_al = 0, pf_hh = 0, pf_hl = 0, pf_qkv = 0, pf_q = 0;
 };
 
@@ -142,9 +142,23 @@ void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits, int*
   if (const int o = attn_rows_override(2)) *nw = o;
 }
 
-// Positions per chunk of the batched prefill: its rows (streams x positions) feed dense MFMA
-// GEMMs; 128 positions of 8 streams make 1024-row products.
-constexpr int PF_CHUNK = 128;
+// Rows per chunk of the batched prefill (streams x positions): they feed dense MFMA GEMMs;
+// 4096 rows (512 positions of 8 streams) make 512 output tiles of 128 x 128 at N = 2048.
+// Measured on the 900-position, 8-stream prefill: 103 ms at 128 positions per chunk, 72 at
+// 256, 62 at 512, 67-68 at 768 and 1024.
+constexpr int PF_ROWS = 4096, PF_MAX_POS = 512;
+int pf_positions(int max_batch) {
+  return std::max(16, std::min(PF_MAX_POS, PF_ROWS / max_batch / 16 * 16));
+}
+// positions per chunk: the plan's, or fewer with WD_PF_CHUNK (sweeps)
+int pf_chunk(int plan_positions) {
+  static int v = -1;
+  if (v < 0) {
+    v = 0;
+    if (const char* e = getenv("WD_PF_CHUNK")) v = atoi(e) / 16 * 16;
+  }
+  return v >= 16 && v <= plan_positions ? v : plan_positions;
+}
 
 Plan make_plan(const wd_config& c) {
   Plan p;
@@ -224,7 +238,8 @@ Plan make_plan(const wd_config& c) {
   p.tok_in = b.take(Bm * 4);
   if (c.arch == WD_ARCH_QWEN3) p.rope = b.take((size_t)c.context * hd * f4);
   if (c.arch == WD_ARCH_QWEN3 && p.mfma) {
-    const size_t R = ((size_t)Bm * PF_CHUNK + 127) / 128 * 128, nqkv = (hq + 2 * hkv) * hd;
+    p.pf_pos_chunk = pf_positions((int)Bm);
+    const size_t R = ((size_t)Bm * p.pf_pos_chunk + 127) / 128 * 128, nqkv = (hq + 2 * hkv) * hd;
     p.pf_rows = (int)R;
     p.pf_x = b.take(R * d * f4);
     p.pf_pos = b.take(R * 4);
@@ -975,7 +990,7 @@ wd_status run_head_mfma(wd_ctx* c, int B, float* logits, int32_t* argmax) {
   return WD_OK;
 }
 
-// Batched Qwen3 prefill: the prompt in chunks of PF_CHUNK positions for all B rows, each
+// Batched Qwen3 prefill: the prompt in chunks of up to pf_pos_chunk positions for all B rows, each
 // layer as dense GEMMs over the chunk's rows, the per-head q/k norm + RoPE + append of the
 // decode step, and a causal prefill attention over the cache; then the head on the last
 // position of every row.  Runs eagerly (no graph): a few launches per layer and chunk.
@@ -985,7 +1000,7 @@ wd_status prefill_batched(wd_ctx* c, const int32_t* tokens, int B, int T, const 
   const Plan& P = c->plan;
   hipStream_t s = c->stream;
   const int d = g.d_model, hd = g.head_dim, hq = g.n_heads, hkv = g.n_kv_heads, ff = g.d_ff;
-  const int nqkv = (hq + 2 * hkv) * hd, C = PF_CHUNK, R = B * C;
+  const int nqkv = (hq + 2 * hkv) * hd, CH = pf_chunk(P.pf_pos_chunk);
   const int adt = g.w_dtype;
   const float qscale = 1.0f / sqrtf((float)hd);
   const int64_t kv_bstride = (int64_t)hkv * g.context * hd;
@@ -993,17 +1008,20 @@ wd_status prefill_batched(wd_ctx* c, const int32_t* tokens, int B, int T, const 
   int32_t* pos = c->at<int32_t>(P.pf_pos);
   void *ah = c->at(P.pf_ah), *al = c->at(P.pf_al), *hh = c->at(P.pf_hh), *hl = c->at(P.pf_hl);
   unsigned* err = c->at<unsigned>(P.err);
+  int R_ = 0;   // rows of the current chunk
   auto gemm = [&](const void* W, int N, int K, const void* Ahi, const void* Alo, int epi, float* out, int ldo,
                   const char* what) -> wd_status {
     wd::FgParams f{};
-    f.W = W; f.w_dtype = g.w_dtype; f.N = N; f.K = K; f.Ahi = Ahi; f.Alo = Alo; f.R = R; f.epi = epi;
+    f.W = W; f.w_dtype = g.w_dtype; f.N = N; f.K = K; f.Ahi = Ahi; f.Alo = Alo; f.R = R_; f.epi = epi;
     f.out = out; f.ldo = ldo; f.Ohi = hh; f.Olo = hl;
     HIPCHK(c, wd::launch_fgemm(f, s), what);
     return WD_OK;
   };
 #define WDCHK(expr) do { const wd_status st_ = (expr); if (st_ != WD_OK) return st_; } while (0)
-  for (int t0 = 0; t0 < T; t0 += C) {
-    const int Cn = std::min(C, T - t0);
+  for (int t0 = 0; t0 < T; t0 += CH) {
+    // a chunk's rows are b * C + j: the last, shorter chunk takes only the rows it has
+    const int Cn = std::min(CH, T - t0), C = Cn, R = B * C;
+    R_ = R;
     HIPCHK(c, wd::launch_pf_embed(x, pos, c->at(P.embed), g.w_dtype, tokens, T, embeds, A, offset, t0, B, C, Cn, d,
                                   g.vocab, err, s), "prefill: embed");
     for (int l = 0; l < g.n_layers; ++l) {

@@ -80,8 +80,8 @@ def test_qwen3_split_k_above_16_rows():
 
 def test_qwen3_prefill_two_chunks_hd64_bf16_cache_gqa4():
     """Head dim 64, a bf16 cache and 4 query heads per kv head (the prefill attention's
-    other instantiation), over two prefill chunks of 128 and 22 positions."""
+    other instantiation), over two prefill chunks of 512 and 88 positions."""
     w = WL.reduced(WL.by_name("qwen3asr_bf16_b8"), layers=2, d=256, heads=8, kv_heads=2, head_dim=64,
-                   cache_dtype="bf16", d_ff=512, vocab=7001, context=160, batch=2, audio_offset=5,
-                   audio_rows=60)
-    _qwen_parity(w, T=150, steps=4, streams=(0, 1))
+                   cache_dtype="bf16", d_ff=512, vocab=7001, context=640, batch=2, audio_offset=5,
+                   audio_rows=300)
+    _qwen_parity(w, T=600, steps=4, streams=(0, 1))
