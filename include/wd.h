@@ -66,16 +66,20 @@ typedef enum { WD_ARCH_WHISPER = 0, WD_ARCH_QWEN3 = 1 } wd_arch;
 
 /* Model and run-size description.
  *   arch        WD_ARCH_WHISPER or WD_ARCH_QWEN3
- *   d_model     residual width d (multiple of 8)
+ *   d_model     residual width d (multiple of 32; Whisper: n_heads * head_dim,
+ *               and a multiple of 128 with 16-bit weights, the cross K/V GEMM's
+ *               column tile)
  *   n_heads     query heads; head_dim = 64 or 128
- *   n_kv_heads  key/value heads (== n_heads for Whisper; divides n_heads)
+ *   n_kv_heads  key/value heads (== n_heads for Whisper; divides n_heads, at
+ *               most 8 query heads per kv head)
  *   n_layers, d_ff (multiple of 8), vocab, context (self-cache rows)
  *   max_frames  cross-cache rows per encoder set (Whisper; 0 for Qwen3)
  *   max_batch   rows per step, 1..WD_MAX_BATCH
  *   n_enc       distinct encoder-state sets (Whisper): max_batch (one per
  *               stream) or 1 (one set broadcast to all rows, as for beams;
  *               this also reserves a second self cache for wd_reorder).
- *               Row b reads set b / (max_batch / n_enc).  0 for Qwen3.
+ *               Row b reads set b / (max_batch / n_enc), at most 8 rows per
+ *               set.  0 for Qwen3.
  *   w_dtype     storage of the weight matrices and encoder states
  *   cache_dtype storage of the self and cross K/V caches
  *   norm_eps    LayerNorm / RMSNorm epsilon; rope_base (Qwen3 only)        */
