@@ -11,6 +11,7 @@
 // contiguous 1 KB tile.  The fp32 mode uses a plain LDS-tiled VALU kernel over
 // row-major operands.
 #include <algorithm>
+#include <cstdlib>
 
 #include "wd_common.h"
 #include "wd_kernels.h"
@@ -138,6 +139,99 @@ __global__ __launch_bounds__(256) void k_xkv_frag(const T* __restrict__ Xf, cons
   }
 }
 
+// Block tile 256 rows of X x 128 output columns; eight waves as 4 x 2, each 64 x 64 (4 x 4 MFMA
+// tiles).  Per 32-deep K step the block's 16 + 8 operand tiles (1 KB each, fragment order) are
+// staged once through LDS (double-buffered, next step's loads in flight) and every wave reads
+// its 4 + 4 tiles from there, so each fragment leaves L2 once per block instead of once per
+// wave.  Same XCD panel order and epilogue as k_xkv_frag, the 256 rows in two halves.
+template <typename T, typename CT>
+__global__ __launch_bounds__(512) void k_xkv_lds(const T* __restrict__ Xf, const T* __restrict__ Wf, int K,
+                                                 XkvOut o, int n_mt, int n_nt) {
+  constexpr int RT = 16, CTL = 8, NTL = RT + CTL;   // tiles per block and K step
+  constexpr int CLD = 128 + 8;
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  __shared__ __align__(16) v4u stage[2][NTL * 64];            // 2 x 24 KB
+  static_assert(sizeof(stage) >= 128 * CLD * sizeof(CT), "epilogue tile fits the staging buffers");
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int L = blockIdx.x, xcd = L % 8, j = L / 8;
+  const int mt = xcd + 8 * (j / n_nt), nt = j - (j / n_nt) * n_nt;
+  if (mt >= n_mt) return;
+  const int wm = wv & 3, wn = wv >> 2;
+  const int KST = K >> 5, lr = lane & 15, lq = lane >> 4;
+  const v4u* __restrict__ A = reinterpret_cast<const v4u*>(Xf) + (int64_t)mt * RT * KST * 64;
+  const v4u* __restrict__ B = reinterpret_cast<const v4u*>(Wf) + (int64_t)nt * CTL * KST * 64;
+  v4u g[3];
+  auto gload = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int q = t + 512 * u, tl = q >> 6, w = q & 63;
+      g[u] = tl < RT ? A[((int64_t)tl * KST + st) * 64 + w] : B[((int64_t)(tl - RT) * KST + st) * 64 + w];
+    }
+  };
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn) acc[i][jn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  gload(0);
+#pragma unroll
+  for (int u = 0; u < 3; ++u) stage[0][t + 512 * u] = g[u];
+  __syncthreads();
+  for (int st = 0; st < KST; ++st) {
+    const int cur = st & 1;
+    const bool more = st + 1 < KST;
+    if (more) gload(st + 1);
+    v4u a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = stage[cur][(wm * 4 + i) * 64 + lane];
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn) b[jn] = stage[cur][(RT + wn * 4 + jn) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn)
+        acc[i][jn] = mfma16x16x32(__builtin_bit_cast(uint4, a[i]), __builtin_bit_cast(uint4, b[jn]), acc[i][jn], (T*)nullptr);
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < 3; ++u) stage[cur ^ 1][t + 512 * u] = g[u];
+    }
+    __syncthreads();
+  }
+  // epilogue through LDS (the staging buffers, free after the loop's last barrier), 128 rows
+  // at a time: waves 0, 1 (rows 0..127) then waves 2, 3 of each column half
+  CT* Cs = reinterpret_cast<CT*>(&stage[0][0]);
+  const int n0 = nt * 128;
+  const bool isv = n0 >= o.d;
+  const int h0 = (isv ? n0 - o.d : n0) / o.hd;   // first head of the tile (128 / hd heads)
+  constexpr int CH = 16 / sizeof(CT), RC = 128 / CH;
+  CT* base = reinterpret_cast<CT*>(isv ? o.Vc : o.Kc);
+  for (int half = 0; half < 2; ++half) {
+    if ((wm >> 1) == half) {
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) {
+        const float bias = o.bias[n0 + wn * 64 + jn * 16 + lr];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            Cs[((wm & 1) * 64 + i * 16 + lq * 4 + e) * CLD + wn * 64 + jn * 16 + lr] = from_f<CT>(acc[i][jn][e] + bias);
+      }
+    }
+    __syncthreads();
+    for (int q = t; q < 128 * RC; q += 512) {
+      const int r = q / RC, c = (q - r * RC) * CH;
+      const int hh = c / o.hd, ch = c - hh * o.hd;
+      const int m = mt * 256 + half * 128 + r;
+      if (m < o.M) {
+        const int e = m / o.frames, f = m - e * o.frames;
+        CT* dst = base + (((int64_t)e * o.H + h0 + hh) * o.max_frames + f) * o.hd + ch;
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(Cs + r * CLD + c);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // fp32: 64x64 block tile, 4x4 per thread, K tiles of 16 through LDS.
 template <typename CT>
 __global__ __launch_bounds__(256) void k_xkv_f32(const float* __restrict__ X, const float* __restrict__ W, int K, XkvOut o) {
@@ -189,9 +283,28 @@ hipError_t launch_cross_kv_gemm(const void* X, const void* W, const float* bias,
     }
     return hipGetLastError();
   }
-  // 16-bit: X already in fragment order (launch_pack_rows, rows padded to 128), W in fragment
+  // 16-bit: X already in fragment order (launch_pack_rows, rows padded to 256), W in fragment
   // order; 128 / hd heads per 128-column tile
   if ((hd != 64 && hd != 128) || d % 128 || (cache_dtype != DT_F16 && cache_dtype != DT_BF16)) return hipErrorInvalidValue;
+  // 256-row blocks with LDS-shared operands once they fill the chip twice over (large-v3: 7500
+  // blocks, 902 -> 704 us per layer; whisper-small 1128, 84.6 -> 81.0 us), else 128-row blocks
+  // (whisper-base, one encoder set: 48 blocks of 256 rows took 17.4 us against 13.5 us).
+  // Tuning override: WD_XKV_LDS=0|1.
+  static int force = -2;
+  if (force == -2) { const char* e = getenv("WD_XKV_LDS"); force = e ? (atoi(e) != 0) : -1; }
+  const bool lds = force >= 0 ? force == 1 : (int64_t)((M + 255) / 256) * (2 * d / 128) >= 512;
+  if (lds) {
+    const int n_mt = (M + 255) / 256, n_nt = 2 * d / 128;
+    const dim3 grid(8 * ((n_mt + 7) / 8) * n_nt);
+#define WD_XKV(T_)                                                                                          \
+  if (cache_dtype == DT_F16) k_xkv_lds<T_, f16_t><<<grid, 512, 0, s>>>((const T_*)X, (const T_*)W, d, o, n_mt, n_nt); \
+  else k_xkv_lds<T_, bf16_t><<<grid, 512, 0, s>>>((const T_*)X, (const T_*)W, d, o, n_mt, n_nt);
+    if (w_dtype == DT_F16) { WD_XKV(f16_t) }
+    else if (w_dtype == DT_BF16) { WD_XKV(bf16_t) }
+    else return hipErrorInvalidValue;
+#undef WD_XKV
+    return hipGetLastError();
+  }
   const int n_mt = (M + 127) / 128, n_nt = 2 * d / 128;
   const dim3 grid(8 * ((n_mt + 7) / 8) * n_nt);
 #define WD_XKV(T_)                                                                                          \

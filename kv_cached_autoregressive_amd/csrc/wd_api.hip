@@ -198,7 +198,7 @@ Plan make_plan(const wd_config& c) {
   if (c.arch == WD_ARCH_WHISPER) {
     p.cross_slab = (size_t)c.n_enc * hq * (size_t)c.max_frames * hd * cb;
     p.cross = b.take(2 * p.cross_slab * c.n_layers);
-    if (p.mfma) p.xfrag = b.take(((size_t)c.n_enc * c.max_frames + 127) / 128 * 128 * d * wb);   // X in fragment order
+    if (p.mfma) p.xfrag = b.take(((size_t)c.n_enc * c.max_frames + 255) / 256 * 256 * d * wb);   // X in fragment order
   }
   const size_t wide = std::max({d, 2 * ff, (hq + 2 * hkv) * hd});
   p.x = b.take(Bm * d * f4);

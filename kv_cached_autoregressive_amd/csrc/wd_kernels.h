@@ -190,7 +190,7 @@ hipError_t launch_reorder(const void* src, void* dst, int elt_bytes, const BeamI
 // ---- cross K/V projection (dense GEMM) with cache scatter ------------------------------------
 // C[m, n] = sum_k X[m,k] W[n,k] (+ bias[n]); m = e*frames + f; n < d -> K cache, else V cache;
 // caches [n_enc][H][max_frames][hd] in cache_dtype.  fp32: X and W row-major.  16-bit: X in
-// fragment order (launch_pack_rows, rows padded to a multiple of 128), W in fragment order,
+// fragment order (launch_pack_rows, rows padded to a multiple of 256), W in fragment order,
 // hd == 64, d % 128 == 0, 16-bit caches.
 hipError_t launch_cross_kv_gemm(const void* X, const void* W, const float* bias, int w_dtype,
                                 int M, int d, int frames, int max_frames, int H, int hd,

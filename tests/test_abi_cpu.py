@@ -39,8 +39,8 @@ def test_workspace_bytes_plan():
     # beams reserve a second self cache
     wb = WL.by_name("whisper_base_f16_beam5")
     one = WL.reduced(wb, n_enc=5)
-    # (and one encoder-state operand copy per window, rows rounded up to 128)
-    r128 = lambda n: (n + 127) // 128 * 128
+    # (and one encoder-state operand copy per window, rows rounded up to 256)
+    r128 = lambda n: (n + 255) // 256 * 256
     assert K.wd_workspace_bytes(K.config_from(wb)) - K.wd_workspace_bytes(K.config_from(one)) == \
         wb.layers * 2 * wb.batch * wb.context * wb.d * 2 - wb.layers * 2 * 4 * wb.frames * wb.d * 2 \
         - (r128(5 * wb.frames) - r128(wb.frames)) * wb.d * 2
