@@ -52,16 +52,20 @@ def _cmp(g, r, dtype, what, max_frac):
     return frac
 
 
-@pytest.mark.parametrize("w_dtype,cache_dtype,batch", [("bf16", "bf16", 3), ("f16", "f16", 3), ("f32", "f32", 3),
-                                                       ("bf16", "f16", 3), ("f32", "bf16", 3),
-                                                       ("bf16", "bf16", 24), ("f16", "f16", 40)])
-def test_cross_and_self_caches_match_oracle(w_dtype, cache_dtype, batch):
+@pytest.mark.parametrize("w_dtype,cache_dtype,batch,frames",
+                         [("bf16", "bf16", 3, 333), ("f16", "f16", 3, 333), ("f32", "f32", 3, 333),
+                          ("bf16", "f16", 3, 333), ("f32", "bf16", 3, 333),
+                          ("bf16", "bf16", 24, 333), ("f16", "f16", 40, 333),
+                          ("bf16", "bf16", 64, 1500), ("f16", "f16", 48, 1500)])
+def test_cross_and_self_caches_match_oracle(w_dtype, cache_dtype, batch, frames):
     """Above 16 rows the q|k|v projection is split over K groups and the self-attention
-    kernel appends the k, v row from the partials: the rows must round the same way."""
+    kernel appends the k, v row from the partials: the rows must round the same way.
+    The 1500-frame cases give the cross K/V GEMM its 256-row, LDS-staged blocks (at
+    least 512 of them; 72000 rows leave a partial last block)."""
     need_gpu()
     w = WL.reduced(WL.by_name("whisper_large_bf16_b64"), layers=2, batch=batch, n_enc=batch, d=384, heads=6,
                    kv_heads=6, d_ff=768, vocab=3001, w_dtype=w_dtype, cache_dtype=cache_dtype,
-                   frames=333)
+                   frames=frames)
     say(f"[caches] {w.describe()}")
     W = WL.make_weights(w)
     enc = WL.make_encoder_states(w)
