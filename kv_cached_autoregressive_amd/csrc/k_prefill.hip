@@ -12,6 +12,7 @@
 // This file: the chunk's embedding rows, the dense GEMM over fragment-layout operands, and
 // the causal prefill attention (flash attention on the matrix cores).
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "wd_common.h"
@@ -82,6 +83,44 @@ hipError_t launch_pf_embed(float* x, int32_t* pos, const void* E, int w_dtype, c
 // 1 KB tile read with 16-byte lane loads; operands run one K step ahead of the MFMAs.
 // WC = 4: block 128 x 128 (waves 2 x 2 of 4 x 4 tiles); WC = 2: block 64 x 128 (waves 1 x 4
 // of 4 x 2 tiles), twice the blocks for narrow outputs.
+// Epilogue of the dense GEMM: wave tiles (i, j) at 16-row tile rt0 + i, 16-column tile ct0 + j.
+template <typename T, int EPI, int WR, int WC>
+__device__ __forceinline__ void fg_epilogue(const FgParams& p, const pf32x4_t (&acc)[WR][WC], int rt0, int ct0,
+                                            int lane) {
+  // tile (i, j): lane holds rows (rt0+i)*16 + 4*(lane/16) + e of column (ct0+j)*16 + lane%16
+  const int rsub = (lane >> 4) * 4, col = lane & 15;
+  if constexpr (EPI == FG_SWIGLU) {
+    // weight row blocks alternate gate, up for the same 16 outputs: tiles (0,1), (2,3)
+    const int half = p.N >> 1;
+#pragma unroll
+    for (int j = 0; j < WC; j += 2)
+#pragma unroll
+      for (int i = 0; i < WR; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = (rt0 + i) * 16 + rsub + e, jj = ((ct0 + j) >> 1) * 16 + col;
+          if (r < p.R) {
+            const float g = acc[i][j][e], u = acc[i][j + 1][e];
+            store_split<T>(p.Ohi, p.Olo, frag_offset(r, jj, half), g / (1.0f + expf(-g)) * u);
+          }
+        }
+  } else {
+#pragma unroll
+    for (int i = 0; i < WR; ++i)
+#pragma unroll
+      for (int j = 0; j < WC; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = (rt0 + i) * 16 + rsub + e, n = (ct0 + j) * 16 + col;
+          if (r < p.R) {
+            float* o = p.out + (int64_t)r * p.ldo + n;
+            if constexpr (EPI == FG_RESID) *o += acc[i][j][e];
+            else *o = acc[i][j][e];
+          }
+        }
+  }
+}
+
 template <typename T, int EPI, int WC>
 __global__ __launch_bounds__(256) void k_fgemm(FgParams p) {
   constexpr int WR = 4;
@@ -123,38 +162,68 @@ __global__ __launch_bounds__(256) void k_fgemm(FgParams p) {
 #pragma unroll
     for (int j = 0; j < WC; ++j) wf[j] = nf[j];
   }
-  // tile (i, j): lane holds rows (rt0+i)*16 + 4*(lane/16) + e of column (ct0+j)*16 + lane%16
-  const int rsub = (lane >> 4) * 4, col = lane & 15;
-  if constexpr (EPI == FG_SWIGLU) {
-    // weight row blocks alternate gate, up for the same 16 outputs: tiles (0,1), (2,3)
-    const int half = p.N >> 1;
+  fg_epilogue<T, EPI, WR, WC>(p, acc, rt0, ct0, lane);
+}
+
+// 128 x 128 blocks (waves 2 x 2 of 4 x 4 tiles) with the block's operand tiles of a K step
+// (8 Ahi + 8 Alo + 8 W, 1 KB each) staged once through LDS, double-buffered with the next
+// step's loads in flight: each fragment leaves L2 once per block instead of once per wave.
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void k_fgemm_lds(FgParams p) {
+  constexpr int WR = 4, WC = 4, NTL = 24;
+  __shared__ __align__(16) pv4u stage[2][NTL * 64];   // 2 x 24 KB
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  const int rt0 = blockIdx.x * 8 + wm * 4, ct0 = blockIdx.y * 8 + wn * 4;
+  const int KST = p.K >> 5;
+  const pv4u* __restrict__ Ah = reinterpret_cast<const pv4u*>(p.Ahi) + (int64_t)blockIdx.x * 8 * KST * 64;
+  const pv4u* __restrict__ Al = reinterpret_cast<const pv4u*>(p.Alo) + (int64_t)blockIdx.x * 8 * KST * 64;
+  const pv4u* __restrict__ Wt = reinterpret_cast<const pv4u*>(p.W) + (int64_t)blockIdx.y * 8 * KST * 64;
+  pv4u g[6];
+  auto gload = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < WC; j += 2)
+    for (int u = 0; u < 6; ++u) {
+      // u = 0, 1: Ahi tiles; 2, 3: Alo; 4, 5: W (tile (u & 1) * 4 + wave, lane x)
+      const int tl = (u & 1) * 4 + (t >> 6), x = t & 63;
+      const int64_t off = ((int64_t)tl * KST + st) * 64 + x;
+      g[u] = u < 2 ? Ah[off] : u < 4 ? Al[off] : Wt[off];
+    }
+  };
+  pf32x4_t acc[WR][WC];
 #pragma unroll
-      for (int i = 0; i < WR; ++i)
+  for (int i = 0; i < WR; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = (rt0 + i) * 16 + rsub + e, jj = ((ct0 + j) >> 1) * 16 + col;
-          if (r < p.R) {
-            const float g = acc[i][j][e], u = acc[i][j + 1][e];
-            store_split<T>(p.Ohi, p.Olo, frag_offset(r, jj, half), g / (1.0f + expf(-g)) * u);
-          }
-        }
-  } else {
+    for (int j = 0; j < WC; ++j) acc[i][j] = pf32x4_t{0.f, 0.f, 0.f, 0.f};
+  gload(0);
+#pragma unroll
+  for (int u = 0; u < 6; ++u) stage[0][t + 256 * u] = g[u];
+  __syncthreads();
+  for (int st = 0; st < KST; ++st) {
+    const int cur = st & 1;
+    const bool more = st + 1 < KST;
+    if (more) gload(st + 1);
+    pv4u ah[WR], al[WR], wf[WC];
+#pragma unroll
+    for (int i = 0; i < WR; ++i) {
+      ah[i] = stage[cur][(wm * 4 + i) * 64 + lane];
+      al[i] = stage[cur][(8 + wm * 4 + i) * 64 + lane];
+    }
+#pragma unroll
+    for (int j = 0; j < WC; ++j) wf[j] = stage[cur][(16 + wn * 4 + j) * 64 + lane];
 #pragma unroll
     for (int i = 0; i < WR; ++i)
 #pragma unroll
-      for (int j = 0; j < WC; ++j)
+      for (int j = 0; j < WC; ++j) {
+        acc[i][j] = pmma(ah[i], wf[j], acc[i][j], (T*)nullptr);
+        acc[i][j] = pmma(al[i], wf[j], acc[i][j], (T*)nullptr);
+      }
+    if (more) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = (rt0 + i) * 16 + rsub + e, n = (ct0 + j) * 16 + col;
-          if (r < p.R) {
-            float* o = p.out + (int64_t)r * p.ldo + n;
-            if constexpr (EPI == FG_RESID) *o += acc[i][j][e];
-            else *o = acc[i][j][e];
-          }
-        }
+      for (int u = 0; u < 6; ++u) stage[cur ^ 1][t + 256 * u] = g[u];
+    }
+    __syncthreads();
   }
+  fg_epilogue<T, EPI, WR, WC>(p, acc, rt0, ct0, lane);
 }
 
 hipError_t launch_fgemm(const FgParams& p, hipStream_t s) {
@@ -163,20 +232,25 @@ hipError_t launch_fgemm(const FgParams& p, hipStream_t s) {
   // 128-row blocks unless they leave CUs idle (then 64-row blocks; A is padded to 128 rows)
   const bool wide = (int64_t)((p.R + 127) / 128) * (p.N / 128) >= 256;
   const dim3 grid(wide ? (p.R + 127) / 128 : (p.R + 63) / 64, p.N / 128);
+  // 128-row blocks: operands staged through LDS unless WD_FGEMM_LDS=0 (tuning override)
+  static int lds = -1;
+  if (lds < 0) { const char* e = getenv("WD_FGEMM_LDS"); lds = e ? atoi(e) != 0 : 1; }
+#define WD_FG1(T_, E_)                                                                                   \
+  if (wide && lds) k_fgemm_lds<T_, E_><<<grid, 256, 0, s>>>(p);                                          \
+  else if (wide) k_fgemm<T_, E_, 4><<<grid, 256, 0, s>>>(p);                                             \
+  else k_fgemm<T_, E_, 2><<<grid, 256, 0, s>>>(p);
 #define WD_FG(T_)                                                                                        \
   switch (p.epi) {                                                                                       \
-    case FG_STORE: if (wide) k_fgemm<T_, FG_STORE, 4><<<grid, 256, 0, s>>>(p);                           \
-                   else k_fgemm<T_, FG_STORE, 2><<<grid, 256, 0, s>>>(p); break;                         \
-    case FG_RESID: if (wide) k_fgemm<T_, FG_RESID, 4><<<grid, 256, 0, s>>>(p);                           \
-                   else k_fgemm<T_, FG_RESID, 2><<<grid, 256, 0, s>>>(p); break;                         \
-    case FG_SWIGLU: if (wide) k_fgemm<T_, FG_SWIGLU, 4><<<grid, 256, 0, s>>>(p);                         \
-                    else k_fgemm<T_, FG_SWIGLU, 2><<<grid, 256, 0, s>>>(p); break;                       \
+    case FG_STORE: WD_FG1(T_, FG_STORE) break;                                                           \
+    case FG_RESID: WD_FG1(T_, FG_RESID) break;                                                           \
+    case FG_SWIGLU: WD_FG1(T_, FG_SWIGLU) break;                                                         \
     default: return hipErrorInvalidValue;                                                                \
   }
   if (p.w_dtype == DT_BF16) { WD_FG(bf16_t) }
   else if (p.w_dtype == DT_F16) { WD_FG(f16_t) }
   else return hipErrorInvalidValue;
 #undef WD_FG
+#undef WD_FG1
   return hipGetLastError();
 }
 
