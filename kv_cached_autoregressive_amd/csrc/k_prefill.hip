@@ -282,7 +282,7 @@ __device__ __forceinline__ uint32_t pa_pack2(float a, float b, uint32_t& lo) {
 }
 
 template <typename CT, typename OT, int HD>
-__global__ __launch_bounds__(256) void k_pf_attn(PfAttnParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) void k_pf_attn(PfAttnParams p) {
   constexpr int KLD = HD + 8;                 // K tile row stride (elements): conflict-free 16 B reads
   constexpr int VLD = PA_KT + 4;              // transposed V tile row stride
   constexpr int NCH = PA_KT * HD / 8;         // 16-byte chunks per tile (K or V)
@@ -346,9 +346,12 @@ __global__ __launch_bounds__(256) void k_pf_attn(PfAttnParams p) {
       const int i = t + 256 * u;
       const int kk = i / (HD / 8), c0 = (i % (HD / 8)) * 8;
       *reinterpret_cast<uint4*>(Ks + kk * KLD + c0) = kst[u];
-      const CT* ve = reinterpret_cast<const CT*>(&vst[u]);
+      // 16-bit halves of the chunk's words, taken with shifts (no address of a register array)
+      unsigned short* vt = reinterpret_cast<unsigned short*>(Vt);
+      const uint32_t wds[4] = {vst[u].x, vst[u].y, vst[u].z, vst[u].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[(c0 + e) * VLD + kk] = ve[e];
+      for (int e = 0; e < 8; ++e)
+        vt[(c0 + e) * VLD + kk] = (unsigned short)((e & 1) ? (wds[e >> 1] >> 16) : (wds[e >> 1] & 0xFFFFu));
     }
     __syncthreads();
     if (k0 + PA_KT < rows_blk) fetch(k0 + PA_KT);   // next tile in flight during the math
@@ -417,12 +420,16 @@ __global__ __launch_bounds__(256) void k_pf_attn(PfAttnParams p) {
   const int K = p.Hq * HD;
 #pragma unroll
   for (int h = 0; h < HT; ++h) {
-    OT h4[4], l4[4];
+    uint32_t hw[2], lw[2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) split_hi_lo<OT>(acc[h][e] * inv, h4[e], l4[e]);
+    for (int e = 0; e < 4; e += 2) {
+      uint32_t lo;
+      hw[e >> 1] = pa_pack2<OT>(acc[h][e] * inv, acc[h][e + 1] * inv, lo);
+      lw[e >> 1] = lo;
+    }
     const int64_t off = frag_offset(r, hq * HD + h * 16 + 4 * grp, K);   // 4 contiguous channels
-    __builtin_memcpy(reinterpret_cast<OT*>(p.o_hi) + off, h4, 8);
-    __builtin_memcpy(reinterpret_cast<OT*>(p.o_lo) + off, l4, 8);
+    *reinterpret_cast<uint2*>(reinterpret_cast<OT*>(p.o_hi) + off) = uint2{hw[0], hw[1]};
+    *reinterpret_cast<uint2*>(reinterpret_cast<OT*>(p.o_lo) + off) = uint2{lw[0], lw[1]};
   }
 }
 
