@@ -85,3 +85,11 @@ def test_qwen3_prefill_two_chunks_hd64_bf16_cache_gqa4():
                    cache_dtype="bf16", d_ff=512, vocab=7001, context=640, batch=2, audio_offset=5,
                    audio_rows=300)
     _qwen_parity(w, T=600, steps=4, streams=(0, 1))
+
+
+def test_qwen3_prefill_mha_odd_rows():
+    """One query head per kv head (no GQA) and 3 streams of 70 positions: the prefill
+    attention's query tiles mix positions across a partial last block."""
+    w = WL.reduced(WL.by_name("qwen3asr_bf16_b8"), layers=2, d=256, heads=4, kv_heads=4, d_ff=512, vocab=7001,
+                   context=96, batch=3, audio_offset=4, audio_rows=30)
+    _qwen_parity(w, T=70, steps=3, streams=(0, 2))
