@@ -146,15 +146,19 @@ __global__ __launch_bounds__(256) void k_xkv_frag(const T* __restrict__ Xf, cons
 // wave.  Same XCD panel order and epilogue as k_xkv_frag, the 256 rows in two halves.
 template <typename T, typename CT>
 __global__ __launch_bounds__(512) void k_xkv_lds(const T* __restrict__ Xf, const T* __restrict__ Wf, int K,
-                                                 XkvOut o, int n_mt, int n_nt) {
+                                                 XkvOut o, int n_mt, int n_nt, int pg) {
   constexpr int RT = 16, CTL = 8, NTL = RT + CTL;   // tiles per block and K step
   constexpr int CLD = 128 + 8;
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
   __shared__ __align__(16) v4u stage[2][NTL * 64];            // 2 x 24 KB
   static_assert(sizeof(stage) >= 128 * CLD * sizeof(CT), "epilogue tile fits the staging buffers");
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  // workgroup L runs on XCD L % 8; that XCD's j-th workgroup takes, within a group of pg of
+  // its row panels, column tile j / pg of panel j % pg: the group's X panels stay in the XCD's
+  // L2 while the W column tiles sweep past them, each W tile used pg times in a row
   const int L = blockIdx.x, xcd = L % 8, j = L / 8;
-  const int mt = xcd + 8 * (j / n_nt), nt = j - (j / n_nt) * n_nt;
+  const int grp = j / (pg * n_nt), w_in = j - grp * pg * n_nt;
+  const int nt = w_in / pg, mt = xcd + 8 * (grp * pg + (w_in - nt * pg));
   if (mt >= n_mt) return;
   const int wm = wv & 3, wn = wv >> 2;
   const int KST = K >> 5, lr = lane & 15, lq = lane >> 4;
@@ -294,11 +298,14 @@ hipError_t launch_cross_kv_gemm(const void* X, const void* W, const float* bias,
   if (force == -2) { const char* e = getenv("WD_XKV_LDS"); force = e ? (atoi(e) != 0) : -1; }
   const bool lds = force >= 0 ? force == 1 : (int64_t)((M + 255) / 256) * (2 * d / 128) >= 512;
   if (lds) {
+    static int pg = -1;   // row panels per L2 group (tuning override WD_XKV_PG)
+    if (pg < 0) { const char* e = getenv("WD_XKV_PG"); pg = e ? std::max(1, std::min(16, atoi(e))) : 4; }
     const int n_mt = (M + 255) / 256, n_nt = 2 * d / 128;
-    const dim3 grid(8 * ((n_mt + 7) / 8) * n_nt);
+    const int per_xcd = ((n_mt + 7) / 8 + pg - 1) / pg * pg;   // panels per XCD, whole groups
+    const dim3 grid(8 * per_xcd * n_nt);
 #define WD_XKV(T_)                                                                                          \
-  if (cache_dtype == DT_F16) k_xkv_lds<T_, f16_t><<<grid, 512, 0, s>>>((const T_*)X, (const T_*)W, d, o, n_mt, n_nt); \
-  else k_xkv_lds<T_, bf16_t><<<grid, 512, 0, s>>>((const T_*)X, (const T_*)W, d, o, n_mt, n_nt);
+  if (cache_dtype == DT_F16) k_xkv_lds<T_, f16_t><<<grid, 512, 0, s>>>((const T_*)X, (const T_*)W, d, o, n_mt, n_nt, pg); \
+  else k_xkv_lds<T_, bf16_t><<<grid, 512, 0, s>>>((const T_*)X, (const T_*)W, d, o, n_mt, n_nt, pg);
     if (w_dtype == DT_F16) { WD_XKV(f16_t) }
     else if (w_dtype == DT_BF16) { WD_XKV(bf16_t) }
     else return hipErrorInvalidValue;
