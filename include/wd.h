@@ -160,6 +160,18 @@ wd_status wd_step(wd_ctx* ctx, const int32_t* tokens, const int32_t* positions, 
  * Errors: ARG (index outside [0,B), n_rows outside [0,context]), STATE. */
 wd_status wd_reorder(wd_ctx* ctx, const int32_t* beam_idx, int32_t B, int32_t n_rows);
 
+/* Beam candidates on the device, so a beam search need not copy [B, vocab] logits to the
+ * host: for each row b < B of `logits` (dev fp32 [B, vocab], as written by wd_step), the W
+ * largest logits in descending order (equal values: lower token id first; a NaN counts as
+ * -inf) into top_val / top_id (dev [B, W], fp32 / int32), and lse[b] (dev fp32) =
+ * log(sum_v exp(logits[b][v])), so log_softmax(v) = logit(v) - lse[b].  Every candidate a
+ * width-W beam step keeps (score S_b + log_softmax of row b; mlx-bun `WhisperKvCache.rearrange`
+ * consumes the resulting indices) is among the W of its row, so the caller merges W x W
+ * candidates instead of B x vocab.  1 <= W <= min(8, vocab).  Asynchronous on the context's
+ * stream.  Errors: ARG (null, B or W out of range), HIP. */
+wd_status wd_topk(wd_ctx* ctx, const float* logits, int32_t B, int32_t W, float* top_val,
+                  int32_t* top_id, float* lse);
+
 /* Prompt prefill for rows 0..B-1 at positions 0..T-1 (Nest entry `prefill`;
  * decoder.h `PrefillBuild`).  tokens dev int32 [B, T]; embeds dev [B, A, d]
  * in w_dtype or NULL: rows offset..offset+A-1 take these embeddings instead of

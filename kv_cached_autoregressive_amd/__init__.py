@@ -19,7 +19,7 @@ from typing import Dict, Iterable, Optional, Sequence
 __all__ = [
     "WdError", "WdConfig", "WdTensor", "lib", "lib_path", "declared_functions",
     "wd_abi_version", "wd_workspace_bytes", "wd_load", "wd_cross_kv", "wd_step", "wd_reorder",
-    "wd_prefill", "wd_check", "wd_last_error", "wd_free", "wd_profile", "wd_profile_read",
+    "wd_topk", "wd_prefill", "wd_check", "wd_last_error", "wd_free", "wd_profile", "wd_profile_read",
     "wd_debug_cache",
     "config_from", "Decoder", "DTYPES", "STATUS",
 ]
@@ -77,6 +77,7 @@ def lib():
             "wd_cross_kv": (i32, [vp, vp, i32]),
             "wd_step": (i32, [vp, vp, vp, i32, vp, vp]),
             "wd_reorder": (i32, [vp, ctypes.POINTER(i32), i32, i32]),
+            "wd_topk": (i32, [vp, vp, i32, i32, vp, vp, vp]),
             "wd_prefill": (i32, [vp, vp, i32, i32, vp, i32, i32, vp, vp]),
             "wd_check": (i32, [vp]),
             "wd_last_error": (ctypes.c_char_p, [vp]),
@@ -137,6 +138,11 @@ def wd_reorder(ctx, beam_idx: Iterable[int], n_rows: int):
     idx = list(beam_idx)
     arr = (ctypes.c_int32 * max(1, len(idx)))(*idx)
     _check(lib().wd_reorder(ctx, arr, len(idx), n_rows), ctx)
+
+
+def wd_topk(ctx, logits: int, B: int, W: int, top_val: int, top_id: int, lse: int):
+    _check(lib().wd_topk(ctx, ctypes.c_void_p(logits), B, W, ctypes.c_void_p(top_val), ctypes.c_void_p(top_id),
+                         ctypes.c_void_p(lse)), ctx)
 
 
 def wd_prefill(ctx, tokens: int, B: int, T: int, embeds: int, A: int, offset: int, logits: int,
@@ -289,6 +295,20 @@ class Decoder:
         cur = self._enter()
         wd_reorder(self.ctx, [int(i) for i in beam_idx], n_rows)
         self._leave(cur)
+
+    def topk(self, logits, W: int):
+        """logits: fp32 device tensor [B, vocab].  Returns device tensors (top values [B, W],
+        top ids [B, W] int32, lse [B])."""
+        import torch
+        B = logits.shape[0]
+        assert logits.dtype == torch.float32 and logits.is_contiguous() and logits.shape[1] == self.w.vocab
+        vals = torch.empty(B, W, dtype=torch.float32, device=self.device)
+        ids = torch.empty(B, W, dtype=torch.int32, device=self.device)
+        lse = torch.empty(B, dtype=torch.float32, device=self.device)
+        cur = self._enter()
+        wd_topk(self.ctx, logits.data_ptr(), B, W, vals.data_ptr(), ids.data_ptr(), lse.data_ptr())
+        self._leave(cur)
+        return vals, ids, lse
 
     def check(self) -> int:
         return wd_check(self.ctx)

@@ -3,6 +3,7 @@
 // beam-reorder cache gather.  All are tiny next to the weight and cache
 // streams; they are written for coalesced 16-byte accesses where it matters.
 #include <algorithm>
+#include <climits>
 
 #include "wd_common.h"
 #include "wd_kernels.h"
@@ -550,6 +551,111 @@ hipError_t launch_argmax_final(const unsigned long long* amax, int nparts, int l
                                int32_t* out, hipStream_t s) {
   if (B <= 0 || nparts <= 0 || ldp < B) return hipErrorInvalidValue;
   k_argmax_final<<<B, 256, 0, s>>>(amax, nparts, ldp, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// beam candidates: per row the W largest logits (ties: lower id first; NaN counts as -inf) and
+// the row's log-sum-exp, so log_softmax(v) = logit(v) - lse.  One block of 512 threads per
+// row: each thread keeps its own top W and (max, sum exp) over a strided slice, then the
+// block merges the lists pairwise in LDS and reduces (max, sum exp).  (Register lists are
+// indexed with compile-time indices only, so they stay in registers.)
+// ------------------------------------------------------------------------------------------
+constexpr int TK_MAX = 8, TK_NT = 512;
+
+__device__ __forceinline__ bool tk_better(float a, int ia, float b, int ib) {
+  return a > b || (a == b && ia < ib);
+}
+
+__global__ __launch_bounds__(TK_NT) void k_topk_lse(const float* __restrict__ logits, int V, int64_t ld, int W,
+                                                     float* __restrict__ top_val, int32_t* __restrict__ top_id,
+                                                     float* __restrict__ lse) {
+  __shared__ float sv[TK_NT * TK_MAX];
+  __shared__ int si[TK_NT * TK_MAX];
+  __shared__ float sm[TK_NT / 64], ss[TK_NT / 64];
+  const int b = blockIdx.x, t = threadIdx.x;
+  const float* row = logits + (int64_t)b * ld;
+  float v[TK_MAX];
+  int id[TK_MAX];
+#pragma unroll
+  for (int k = 0; k < TK_MAX; ++k) { v[k] = -INFINITY; id[k] = INT_MAX; }
+  float m = -INFINITY, sum = 0.f;
+  for (int i = t; i < V; i += TK_NT) {
+    float x = row[i];
+    if (x != x) x = -INFINITY;   // NaN
+    if (x != -INFINITY) {
+      if (x > m) { sum = sum * expf(m - x) + 1.f; m = x; }
+      else sum += expf(x - m);
+    }
+    float lv = v[0];
+    int li = id[0];
+#pragma unroll
+    for (int k = 1; k < TK_MAX; ++k)
+      if (k == W - 1) { lv = v[k]; li = id[k]; }
+    if (tk_better(x, i, lv, li)) {   // insert, keeping the list sorted (shift the worse ones down)
+      bool placed = false;
+#pragma unroll
+      for (int k = TK_MAX - 1; k >= 1; --k) {
+        if (k < W && !placed) {
+          if (tk_better(x, i, v[k - 1], id[k - 1])) { v[k] = v[k - 1]; id[k] = id[k - 1]; }
+          else { v[k] = x; id[k] = i; placed = true; }
+        }
+      }
+      if (!placed) { v[0] = x; id[0] = i; }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < TK_MAX; ++k)
+    if (k < W) { sv[t * TK_MAX + k] = v[k]; si[t * TK_MAX + k] = id[k]; }
+  // (max, sum exp): within the wave, then across the 16 waves
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, WAVE), s2 = __shfl_xor(sum, o, WAVE);
+    const float mn = fmaxf(m, m2);
+    sum = (m == -INFINITY ? 0.f : sum * expf(m - mn)) + (m2 == -INFINITY ? 0.f : s2 * expf(m2 - mn));
+    m = mn;
+  }
+  if ((t & 63) == 0) { sm[t >> 6] = m; ss[t >> 6] = sum; }
+  __syncthreads();
+  // pairwise merges of the sorted lists: list t takes the best W of lists t and t + stride
+  for (int stride = TK_NT / 2; stride > 0; stride >>= 1) {
+    if (t < stride) {
+      const float* av = sv + t * TK_MAX; const int* ai = si + t * TK_MAX;
+      const float* bv = sv + (t + stride) * TK_MAX; const int* bi = si + (t + stride) * TK_MAX;
+      float ov[TK_MAX]; int oi[TK_MAX];
+      int x = 0, y = 0;   // x + y = k <= W - 1: both stay inside their lists
+#pragma unroll
+      for (int k = 0; k < TK_MAX; ++k) {
+        if (k < W) {
+          if (tk_better(av[x], ai[x], bv[y], bi[y])) { ov[k] = av[x]; oi[k] = ai[x]; ++x; }
+          else { ov[k] = bv[y]; oi[k] = bi[y]; ++y; }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < TK_MAX; ++k)
+        if (k < W) { sv[t * TK_MAX + k] = ov[k]; si[t * TK_MAX + k] = oi[k]; }
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    float M = -INFINITY;
+    for (int w = 0; w < TK_NT / 64; ++w) M = fmaxf(M, sm[w]);
+    float S = 0.f;
+    for (int w = 0; w < TK_NT / 64; ++w)
+      if (sm[w] != -INFINITY) S += ss[w] * expf(sm[w] - M);
+    lse[b] = M == -INFINITY ? -INFINITY : M + logf(S);
+    for (int k = 0; k < W; ++k) {
+      top_val[(int64_t)b * W + k] = sv[k];
+      top_id[(int64_t)b * W + k] = si[k];
+    }
+  }
+}
+
+hipError_t launch_topk_lse(const float* logits, int B, int V, int64_t ld, int W, float* top_val, int32_t* top_id,
+                           float* lse, hipStream_t s) {
+  if (!logits || !top_val || !top_id || !lse || B <= 0 || V <= 0 || ld < V || W < 1 || W > TK_MAX || W > V)
+    return hipErrorInvalidValue;
+  k_topk_lse<<<B, TK_NT, 0, s>>>(logits, V, ld, W, top_val, top_id, lse);
   return hipGetLastError();
 }
 

@@ -1121,6 +1121,22 @@ wd_status wd_reorder(wd_ctx* ctx, const int32_t* beam_idx, int32_t B, int32_t n_
   }
 }
 
+wd_status wd_topk(wd_ctx* ctx, const float* logits, int32_t B, int32_t W, float* top_val, int32_t* top_id,
+                  float* lse) {
+  if (!ctx) return WD_ERR_ARG;
+  try {
+    const wd_config& g = ctx->cfg;
+    if (!logits || !top_val || !top_id || !lse) return fail(ctx, WD_ERR_ARG, "wd_topk: null pointer");
+    if (B < 1 || B > g.max_batch) return fail(ctx, WD_ERR_ARG, "wd_topk: B outside [1, max_batch]");
+    if (W < 1 || W > 8 || W > g.vocab) return fail(ctx, WD_ERR_ARG, "wd_topk: W outside [1, min(8, vocab)]");
+    HIPCHK(ctx, wd::launch_topk_lse(logits, B, g.vocab, g.vocab, W, top_val, top_id, lse, ctx->stream),
+           "beam candidates");
+    return WD_OK;
+  } catch (...) {
+    return fail(ctx, WD_ERR_INTERNAL, "wd_topk: internal error");
+  }
+}
+
 wd_status wd_check(wd_ctx* ctx) {
   if (!ctx) return WD_ERR_ARG;
   HIPCHK(ctx, hipStreamSynchronize(ctx->stream), "wd_check: stream sync");

@@ -134,6 +134,58 @@ def test_split_k_projections_above_16_rows(batch):
     _sampled_parity(w, steps=6, streams=(0, batch - 1))
 
 
+def _merge_candidates(scores, vals, ids, lse, V, first):
+    """Width-W beam step from per-row device candidates: scores S_b + (logit - lse_b) of the
+    W x W candidates, the W best kept, ties to the lower flat index b * V + v."""
+    W = vals.shape[0]
+    rows = 1 if first else W
+    cand = np.asarray(scores, np.float64)[:rows, None] + (vals[:rows].astype(np.float64) -
+                                                          lse[:rows, None].astype(np.float64))
+    flat = (np.arange(rows)[:, None] * V + ids[:rows]).reshape(-1)
+    c = cand.reshape(-1)
+    keep = np.lexsort((flat, -c))[:W]
+    return (flat[keep] // V).astype(np.int32), (flat[keep] % V).astype(np.int32)
+
+
+def _topk_definition(lg, W):
+    """Per row: ids of the W largest values, equal values lower id first, NaN as -inf; and
+    log(sum exp) over the non-NaN values, in float64."""
+    x = np.where(np.isnan(lg), -np.inf, lg.astype(np.float64))
+    ids = np.stack([np.lexsort((np.arange(x.shape[1]), -x[b]))[:W] for b in range(x.shape[0])])
+    m = x.max(1, keepdims=True)
+    lse = m[:, 0] + np.log(np.exp(x - m).sum(1))
+    return ids, lse
+
+
+def test_topk_candidates_ties_and_nan():
+    """wd_topk against its definition on seeded logits over the full 51865-id vocabulary,
+    with exact ties (lowest id first), a row of equal values and NaNs (never picked, left out
+    of the log-sum-exp)."""
+    need_gpu()
+    w = WL.reduced(WL.by_name("whisper_small_f16_b16"), layers=1, d=256, heads=4, kv_heads=4, d_ff=512)
+    G = GpuRun(w, WL.make_weights(w))
+    rng = np.random.default_rng(123)
+    lg = (rng.standard_normal((w.batch, w.vocab)) * 3).astype(np.float32)
+    lg[0, [5, 17, 40000]] = 20.0
+    lg[1, :] = 1.0
+    lg[2, [3, 99]] = np.nan
+    lg[2, 4] = 30.0
+    lg[3, [50, 100, 200, w.vocab - 1]] = np.float32(7.5)
+    dev = torch.from_numpy(lg).cuda()
+    for W in (1, 5, 8):
+        vals, ids, lse = G.dec.topk(dev, W)
+        ids_r, lse_r = _topk_definition(lg, W)
+        np.testing.assert_array_equal(ids.cpu().numpy(), ids_r, err_msg=f"W={W}")
+        ref_vals = np.take_along_axis(np.where(np.isnan(lg), -np.inf, lg), ids_r, 1)
+        np.testing.assert_array_equal(vals.cpu().numpy(), ref_vals, err_msg=f"W={W}")
+        np.testing.assert_allclose(lse.cpu().numpy(), lse_r, rtol=0, atol=1e-4, err_msg=f"W={W}")
+    for bad in (0, 9):
+        with pytest.raises(G.K.WdError):
+            G.dec.topk(dev, bad)
+    assert G.check() == 0
+    G.close()
+
+
 def test_base_f16_beam5_full():
     """Width-5 beam search over one broadcast encoder set, 128 positions: the
     oracle's beam indices drive both sides' cache reorder; the beam choices made
@@ -153,7 +205,7 @@ def test_base_f16_beam5_full():
     scores = np.zeros(w.batch)
     toks = prompt[:, 0]
     beam_idx = None
-    decided, worst = 0, 0.0
+    decided, merged, worst = 0, 0, 0.0
     for p in range(w.steps):
         if p < prompt.shape[1]:
             toks = prompt[:, p]
@@ -167,16 +219,24 @@ def test_base_f16_beam5_full():
         if p >= prompt.shape[1] - 1:
             first = p == prompt.shape[1] - 1
             bi, tk, sc, gaps = OB.select(scores, ref, first)
-            gbi, gtk, _, _ = OB.select(scores, lg.astype(np.float64), first)
+            gbi, gtk, _, ggaps = OB.select(scores, lg.astype(np.float64), first)
             if np.all(gaps > 1e-2):
                 np.testing.assert_array_equal(gbi, bi, err_msg=f"beam indices at pos {p}")
                 np.testing.assert_array_equal(gtk, tk, err_msg=f"beam tokens at pos {p}")
                 decided += 1
+            # the same choice from the device candidates (wd_topk: W per row + lse), merged here
+            vals, ids, lse = G.dec.topk(G.logits[:w.batch], w.batch)
+            tbi, ttk = _merge_candidates(scores, vals.cpu().numpy(), ids.cpu().numpy(), lse.cpu().numpy(),
+                                         w.vocab, first)
+            if np.all(ggaps > 1e-4):
+                np.testing.assert_array_equal(tbi, gbi, err_msg=f"device-candidate beams at pos {p}")
+                np.testing.assert_array_equal(ttk, gtk, err_msg=f"device-candidate tokens at pos {p}")
+                merged += 1
             beam_idx, toks, scores = bi, tk, sc
     assert G.check() == 0
     G.close()
-    say(f"  worst err {worst:.3e}; beam decisions compared {decided}")
-    assert decided > 0
+    say(f"  worst err {worst:.3e}; beam decisions compared {decided}, from device candidates {merged}")
+    assert decided > 0 and merged > 0
 
 
 def test_reorder_identity_and_inverse_restore_cache():
