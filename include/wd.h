@@ -136,6 +136,16 @@ wd_status wd_load(const wd_config* cfg, const wd_tensor* weights, int32_t n_weig
  * 1 <= frames <= max_frames.  Errors: ARG, STATE (Qwen3 context). */
 wd_status wd_cross_kv(wd_ctx* ctx, const void* enc, int32_t frames);
 
+/* Whisper, a window whose encoder sets have different lengths (batches of audio of
+ * different durations, continuous batching): as wd_cross_kv over enc (dev [n_enc, F, d] in
+ * w_dtype, F = the largest frames[e]), where set e has frames[e] valid rows (frames: host
+ * int32 [n_enc], each in [1, max_frames]) and its rows f >= frames[e] are padding: their
+ * K/V are computed but the cross-attention of the rows of set e reads rows 0..frames[e]-1
+ * only.  Each row then matches a window of its set alone (Nest `listen` accepts states
+ * shorter than 1500 frames).  A later wd_cross_kv returns to one length for all sets.
+ * Errors: ARG (null, a frame count out of range), STATE (Qwen3 context), HIP. */
+wd_status wd_cross_kv_ragged(wd_ctx* ctx, const void* enc, const int32_t* frames);
+
 /* One decoder step for rows 0..B-1 (1 <= B <= max_batch).
  *   tokens    dev int32 [B]   token id per row (may alias `argmax` for
  *                             on-device greedy decoding)

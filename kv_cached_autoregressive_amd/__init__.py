@@ -18,7 +18,7 @@ from typing import Dict, Iterable, Optional, Sequence
 
 __all__ = [
     "WdError", "WdConfig", "WdTensor", "lib", "lib_path", "declared_functions",
-    "wd_abi_version", "wd_workspace_bytes", "wd_load", "wd_cross_kv", "wd_step", "wd_reorder",
+    "wd_abi_version", "wd_workspace_bytes", "wd_load", "wd_cross_kv", "wd_cross_kv_ragged", "wd_step", "wd_reorder",
     "wd_topk", "wd_prefill", "wd_check", "wd_last_error", "wd_free", "wd_profile", "wd_profile_read",
     "wd_debug_cache",
     "config_from", "Decoder", "DTYPES", "STATUS",
@@ -75,6 +75,7 @@ def lib():
             "wd_load": (i32, [ctypes.POINTER(WdConfig), ctypes.POINTER(WdTensor), i32, vp, sz, vp,
                               ctypes.POINTER(vp)]),
             "wd_cross_kv": (i32, [vp, vp, i32]),
+            "wd_cross_kv_ragged": (i32, [vp, vp, ctypes.POINTER(i32)]),
             "wd_step": (i32, [vp, vp, vp, i32, vp, vp]),
             "wd_reorder": (i32, [vp, ctypes.POINTER(i32), i32, i32]),
             "wd_topk": (i32, [vp, vp, i32, i32, vp, vp, vp]),
@@ -127,6 +128,12 @@ def wd_load(cfg: WdConfig, tensors: Sequence[WdTensor], workspace: int, ws_bytes
 
 def wd_cross_kv(ctx, enc: int, frames: int):
     _check(lib().wd_cross_kv(ctx, ctypes.c_void_p(enc), frames), ctx)
+
+
+def wd_cross_kv_ragged(ctx, enc: int, frames: Iterable[int]):
+    f = [int(x) for x in frames]
+    arr = (ctypes.c_int32 * max(1, len(f)))(*f)
+    _check(lib().wd_cross_kv_ragged(ctx, ctypes.c_void_p(enc), arr), ctx)
 
 
 def wd_step(ctx, tokens: int, positions: int, B: int, logits: int, argmax: int):
@@ -265,6 +272,13 @@ class Decoder:
     def cross_kv(self, enc, frames: Optional[int] = None):
         cur = self._enter()
         wd_cross_kv(self.ctx, enc.data_ptr(), enc.shape[1] if frames is None else frames)
+        self._leave(cur)
+
+    def cross_kv_ragged(self, enc, frames: Sequence[int]):
+        """enc: device tensor [n_enc, max(frames), d]; set e has frames[e] valid rows."""
+        assert enc.shape[0] == self.w.n_enc and enc.shape[1] == max(frames) and len(frames) == self.w.n_enc
+        cur = self._enter()
+        wd_cross_kv_ragged(self.ctx, enc.data_ptr(), frames)
         self._leave(cur)
 
     def step(self, tokens, positions, logits=None, argmax=None):

@@ -93,6 +93,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {
   if (p.pos) {
     const int ps = p.pos[bq0];
     n_rows = (ps < 0 || ps >= p.rows_cap) ? 0 : ps + 1;
+  } else if (p.rows_kvb) {   // ragged KV sets: this set's own length
+    n_rows = min(max(p.rows_kvb[kvb], 0), p.n_rows_fixed);
   }
   const int r_lo = s * p.split_rows;
   const int r_hi = min(r_lo + p.split_rows, n_rows);

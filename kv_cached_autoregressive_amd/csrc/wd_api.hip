@@ -54,6 +54,7 @@ struct Plan {
   int n_bufs = 1;
   size_t cross = 0, cross_slab = 0;
   size_t xfrag = 0;          // encoder states in fragment order (cross-K/V GEMM operand, 16-bit)
+  size_t frames_dev = 0;     // per encoder set frame counts [n_enc] int32 (ragged windows)
   size_t x = 0, y = 0, q = 0, qkv = 0, o = 0, h = 0, part = 0, amax = 0, err = 0, pos_tmp = 0;
   size_t rope = 0;           // Qwen3: cos [context][hd/2], then sin [context][hd/2]
   size_t gpart = 0; int64_t gpart_cap = 0;   // split-K GEMM partials [G][B][N] fp32
@@ -199,6 +200,7 @@ Plan make_plan(const wd_config& c) {
     p.cross_slab = (size_t)c.n_enc * hq * (size_t)c.max_frames * hd * cb;
     p.cross = b.take(2 * p.cross_slab * c.n_layers);
     if (p.mfma) p.xfrag = b.take(((size_t)c.n_enc * c.max_frames + 255) / 256 * 256 * d * wb);   // X in fragment order
+    p.frames_dev = b.take((size_t)c.n_enc * 4);
   }
   const size_t wide = std::max({d, 2 * ff, (hq + 2 * hkv) * hd});
   p.x = b.take(Bm * d * f4);
@@ -260,9 +262,10 @@ struct ProfPair { hipEvent_t a, b; int n; };
 // stay the same (the positions and tokens are read from device memory at run time).
 struct GraphKey {
   void* logits; void* argmax; int B, cur, frames, kind;   // kind: 0 step, 1 prefill row, 2 prefill row with override
+  bool ragged;                                              // per-set frame counts (wd_cross_kv_ragged)
   bool operator==(const GraphKey& o) const {
     return logits == o.logits && argmax == o.argmax && B == o.B && cur == o.cur && frames == o.frames &&
-           kind == o.kind;
+           kind == o.kind && ragged == o.ragged;
   }
 };
 struct GraphEntry { GraphKey key; hipGraphExec_t exec; };
@@ -276,7 +279,9 @@ struct wd_ctx {
   char* ws = nullptr;
   int cur = 0;               // current self-cache buffer
   bool cross_ready = false;
-  int frames = 0;
+  int frames = 0;            // frames of the current window (the longest set when ragged)
+  bool ragged = false;       // per-set frame counts in plan.frames_dev
+  std::vector<int32_t> frames_host;   // staging of the last ragged window's counts
   std::string err;
   // captured steps (small cache, oldest evicted first); off when WD_GRAPHS=0, while
   // profiling, or on the legacy null stream
@@ -456,6 +461,7 @@ wd_status run_layers_mfma(wd_ctx* c, const int32_t* pos, int B, float* logits, i
       cp.K = c->cross_k(l); cp.V = c->cross_v(l);
       cp.kvb_stride = (int64_t)hq * g.max_frames * hd; cp.rows_cap = g.max_frames;
       cp.pos = nullptr; cp.n_rows_fixed = c->frames; cp.q_per_kvb = qpk;
+      cp.rows_kvb = c->ragged ? c->at<int32_t>(P.frames_dev) : nullptr;
       cp.split_rows = c_rows; cp.n_splits = c_splits; cp.nw = c_nw;
       {
         const bool on = prof_on(c, PK_CROSS_ATTN, l);
@@ -600,6 +606,7 @@ wd_status run_step(wd_ctx* c, const int32_t* tok, int tok_stride, const int32_t*
       cp.K = c->cross_k(l); cp.V = c->cross_v(l);
       cp.kvb_stride = (int64_t)hq * g.max_frames * hd; cp.rows_cap = g.max_frames;
       cp.pos = nullptr; cp.n_rows_fixed = c->frames; cp.q_per_kvb = qpk;
+      cp.rows_kvb = c->ragged ? c->at<int32_t>(P.frames_dev) : nullptr;
       cp.split_rows = c_rows; cp.n_splits = c_splits; cp.nw = c_nw;
       {
         const bool on = prof_on(c, PK_CROSS_ATTN, l);
@@ -870,6 +877,30 @@ wd_status wd_load(const wd_config* cfg, const wd_tensor* weights, int32_t n_weig
   }
 }
 
+// Every layer's cross K/V from the encoder states [n_enc, frames, d] (one window).
+wd_status cross_kv_impl(wd_ctx* ctx, const void* enc, int32_t frames, const char* who) {
+  const wd_config& g = ctx->cfg;
+  const void* X = enc;
+  if (ctx->plan.mfma) {   // X feeds every layer: repack it into fragment order once
+    HIPCHK(ctx, wd::launch_pack_rows(enc, g.w_dtype, ctx->at(ctx->plan.xfrag), (int64_t)g.n_enc * frames, g.d_model,
+                                     ctx->stream), who);
+    X = ctx->at(ctx->plan.xfrag);
+  }
+  for (int l = 0; l < g.n_layers; ++l) {
+    const LayerOff& L = ctx->plan.L[l];
+    const bool on = prof_on(ctx, PK_XKV_GEMM, l);
+    prof_begin(ctx, on);
+    HIPCHK(ctx, wd::launch_cross_kv_gemm(X, ctx->at(L.wckv), ctx->at<float>(L.bckv), g.w_dtype,
+                                         g.n_enc * frames, g.d_model, frames, g.max_frames, g.n_heads,
+                                         g.head_dim, ctx->cross_k(l), ctx->cross_v(l), g.cache_dtype,
+                                         ctx->stream), who);
+    prof_end(ctx, on);
+  }
+  ctx->cross_ready = true;
+  ctx->frames = frames;
+  return WD_OK;
+}
+
 wd_status wd_cross_kv(wd_ctx* ctx, const void* enc, int32_t frames) {
   if (!ctx) return WD_ERR_ARG;
   try {
@@ -877,27 +908,34 @@ wd_status wd_cross_kv(wd_ctx* ctx, const void* enc, int32_t frames) {
     if (g.arch != WD_ARCH_WHISPER) return fail(ctx, WD_ERR_STATE, "wd_cross_kv: no cross-attention in this arch");
     if (!enc) return fail(ctx, WD_ERR_ARG, "wd_cross_kv: enc must not be null");
     if (frames < 1 || frames > g.max_frames) return fail(ctx, WD_ERR_ARG, "wd_cross_kv: frames outside [1, max_frames]");
-    const void* X = enc;
-    if (ctx->plan.mfma) {   // X feeds every layer: repack it into fragment order once
-      HIPCHK(ctx, wd::launch_pack_rows(enc, g.w_dtype, ctx->at(ctx->plan.xfrag), (int64_t)g.n_enc * frames, g.d_model,
-                                       ctx->stream), "cross K/V: pack encoder states");
-      X = ctx->at(ctx->plan.xfrag);
-    }
-    for (int l = 0; l < g.n_layers; ++l) {
-      const LayerOff& L = ctx->plan.L[l];
-      const bool on = prof_on(ctx, PK_XKV_GEMM, l);
-      prof_begin(ctx, on);
-      HIPCHK(ctx, wd::launch_cross_kv_gemm(X, ctx->at(L.wckv), ctx->at<float>(L.bckv), g.w_dtype,
-                                           g.n_enc * frames, g.d_model, frames, g.max_frames, g.n_heads,
-                                           g.head_dim, ctx->cross_k(l), ctx->cross_v(l), g.cache_dtype,
-                                           ctx->stream), "cross K/V projection");
-      prof_end(ctx, on);
-    }
-    ctx->cross_ready = true;
-    ctx->frames = frames;
-    return WD_OK;
+    const wd_status st = cross_kv_impl(ctx, enc, frames, "cross K/V projection");
+    if (st == WD_OK) ctx->ragged = false;
+    return st;
   } catch (...) {
     return fail(ctx, WD_ERR_INTERNAL, "wd_cross_kv: internal error");
+  }
+}
+
+wd_status wd_cross_kv_ragged(wd_ctx* ctx, const void* enc, const int32_t* frames) {
+  if (!ctx) return WD_ERR_ARG;
+  try {
+    const wd_config& g = ctx->cfg;
+    if (g.arch != WD_ARCH_WHISPER) return fail(ctx, WD_ERR_STATE, "wd_cross_kv_ragged: no cross-attention in this arch");
+    if (!enc || !frames) return fail(ctx, WD_ERR_ARG, "wd_cross_kv_ragged: null pointer");
+    int F = 0;
+    for (int e = 0; e < g.n_enc; ++e) {
+      if (frames[e] < 1 || frames[e] > g.max_frames)
+        return fail(ctx, WD_ERR_ARG, "wd_cross_kv_ragged: a set's frames outside [1, max_frames]");
+      F = std::max(F, (int)frames[e]);
+    }
+    ctx->frames_host.assign(frames, frames + g.n_enc);
+    HIPCHK(ctx, hipMemcpyAsync(ctx->at(ctx->plan.frames_dev), ctx->frames_host.data(), (size_t)g.n_enc * 4,
+                               hipMemcpyHostToDevice, ctx->stream), "wd_cross_kv_ragged: frame counts");
+    const wd_status st = cross_kv_impl(ctx, enc, F, "cross K/V projection (ragged)");
+    if (st == WD_OK) ctx->ragged = true;
+    return st;
+  } catch (...) {
+    return fail(ctx, WD_ERR_INTERNAL, "wd_cross_kv_ragged: internal error");
   }
 }
 
@@ -924,7 +962,7 @@ static wd_status staged_step(wd_ctx* ctx, int32_t B, float* logits, int32_t* arg
   const int64_t ovs = (int64_t)ctx->cfg.d_model;
   if (!ctx->use_graphs || ctx->prof_kernel >= 0 || ctx->stream == nullptr)
     return run_step(ctx, tok, 1, pos, ovp, ovs, B, logits, argmax, head);
-  const GraphKey key{logits, argmax, B, ctx->cur, ctx->frames, head ? 0 : (ov ? 2 : 1)};
+  const GraphKey key{logits, argmax, B, ctx->cur, ctx->frames, head ? 0 : (ov ? 2 : 1), ctx->ragged};
   for (auto& e : ctx->graphs)
     if (e.key == key) {
       HIPCHK(ctx, hipGraphLaunch(e.exec, ctx->stream), "step: graph launch");

@@ -121,6 +121,7 @@ struct AttnParams {
   const void* K; const void* V; int cache_dtype;
   int64_t kvb_stride; int rows_cap;           // cache [n_kvb][Hkv][rows_cap][hd]
   const int32_t* pos; int n_rows_fixed;       // pos: rows 0..pos[b]; else n_rows_fixed rows
+  const int32_t* rows_kvb;                    // (no pos) rows of each KV set, at most n_rows_fixed
   int B; int Hq; int Hkv; int hd; int q_per_kvb;
   int split_rows; int n_splits;
   int nw;                                     // waves per block: 4 or 8

@@ -76,14 +76,28 @@ class WhisperOracle:
         self.enc_of = None
 
     # -- cross K/V, once per window ---------------------------------------------------
-    def cross_kv(self, enc: np.ndarray):
-        """enc [n_enc, F, d] -> per layer Kc, Vc [n_enc, F, d] (cache dtype)."""
-        enc = np.asarray(enc, F64)
+    def cross_kv(self, enc):
+        """enc [n_enc, F, d] -> per layer Kc, Vc [n_enc, F, d] (cache dtype).
+
+        ``enc`` may also be a sequence of per-set arrays [F_e, d] of different lengths
+        (a window whose sets come from audio of different durations): set e's rows then
+        attend over its own F_e frames, exactly as a window of that set alone (Nest model
+        page: ``listen`` accepts states shorter than the full 1500 frames)."""
+        if isinstance(enc, np.ndarray) and enc.ndim == 3:
+            sets = None
+            enc = np.asarray(enc, F64)
+        else:
+            sets = [np.asarray(e, F64) for e in enc]
         self.Kc, self.Vc = [], []
         for l in range(self.D.layers):
             p = f"dec.{l}.cross."
-            self.Kc.append(self.rc(enc @ self.W[p + "k.w"].T))
-            self.Vc.append(self.rc(enc @ self.W[p + "v.w"].T + self.W[p + "v.b"]))
+            wk, wv, bv = self.W[p + "k.w"].T, self.W[p + "v.w"].T, self.W[p + "v.b"]
+            if sets is None:
+                self.Kc.append(self.rc(enc @ wk))
+                self.Vc.append(self.rc(enc @ wv + bv))
+            else:
+                self.Kc.append([self.rc(e @ wk) for e in sets])
+                self.Vc.append([self.rc(e @ wv + bv) for e in sets])
 
     def reset(self, B: int, enc_of: Optional[Sequence[int]] = None):
         """Empty self caches for B rows.  Unwritten rows hold NaN, so any read of a

@@ -10,7 +10,7 @@ from oracle import beams as OB
 from oracle import whisper as OW
 from oracle.numerics import argmax_lowest
 
-from .gpu_helpers import GpuRun, compare_logits, need_gpu, say
+from .gpu_helpers import GpuRun, compare_logits, need_gpu, say, to_dev, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -132,6 +132,75 @@ def test_split_k_projections_above_16_rows(batch):
     w = WL.reduced(WL.by_name("whisper_large_bf16_b64"), layers=2, batch=batch, n_enc=batch, d=768, heads=12,
                    kv_heads=12, d_ff=2048, vocab=9001, frames=300)
     _sampled_parity(w, steps=6, streams=(0, batch - 1))
+
+
+def test_ragged_window_sets_of_different_lengths():
+    """wd_cross_kv_ragged: encoder sets of 1500, 777, 1 and 1024 frames in one window, the
+    padding rows filled with large values that must never be read; every row's logits
+    against the oracle's window of its own set, over greedy steps."""
+    need_gpu()
+    w = WL.reduced(WL.by_name("whisper_large_bf16_b64"), layers=2, batch=4, n_enc=4, d=256,
+                   heads=4, kv_heads=4, d_ff=1024, vocab=5003)
+    say(f"[whisper ragged] {w.describe()}")
+    W = WL.make_weights(w)
+    enc = WL.make_encoder_states(w)
+    lens = [1500, 777, 1, 1024]
+    padded = enc.copy()
+    for e, n in enumerate(lens):
+        padded[e, n:] = 50.0
+    O = OW.WhisperOracle(OW.dims_of(w), W)
+    O.cross_kv([enc[e, :lens[e]] for e in range(w.n_enc)])
+    O.reset(w.batch, enc_of=np.arange(w.batch))
+    G = GpuRun(w, W)
+    G.dec.cross_kv_ragged(to_dev(np.ascontiguousarray(padded), torch_dtype(w.w_dtype)), lens)
+    prompt = WL.make_prompt(w)
+    toks = prompt[:, 0]
+    worst = 0.0
+    for p in range(8):
+        toks = prompt[:, p] if p < prompt.shape[1] else toks
+        ref = O.step(toks, np.full(w.batch, p))
+        lg, _ = G.step(toks, p)
+        e, _ = compare_logits(w, lg, ref, f"pos {p}")
+        worst = max(worst, e)
+        toks = argmax_lowest(ref)
+    assert G.check() == 0
+    # a later uniform window returns every set to the full length
+    G.cross(enc)
+    O.cross_kv(enc)
+    ref = O.step(toks, np.full(w.batch, 8))
+    lg, _ = G.step(toks, 8)
+    compare_logits(w, lg, ref, "uniform window after a ragged one")
+    G.close()
+    say(f"  worst err {worst:.3e}")
+
+
+def test_rows_at_different_positions():
+    """Rows of one step at different positions: row b starts 3b steps late (repeating its
+    position-0 token until then), so the rows' cache lengths differ in every step."""
+    need_gpu()
+    w = WL.reduced(WL.by_name("whisper_small_f16_b16"), layers=2, batch=4, n_enc=4, d=256, heads=4,
+                   kv_heads=4, d_ff=512, vocab=3001, frames=300)
+    say(f"[whisper positions] {w.describe()}")
+    W = WL.make_weights(w)
+    enc = WL.make_encoder_states(w)
+    O = OW.WhisperOracle(OW.dims_of(w), W)
+    O.cross_kv(enc)
+    O.reset(w.batch, enc_of=np.arange(w.batch))
+    G = GpuRun(w, W)
+    G.cross(enc)
+    ids = WL.random_ids(w, 24)
+    delays = 3 * np.arange(w.batch)
+    worst = 0.0
+    for st in range(24):
+        pos = np.maximum(0, st - delays).astype(np.int32)
+        toks = ids[np.arange(w.batch), pos]
+        ref = O.step(toks, pos)
+        lg, _ = G.step(toks, pos)
+        e, _ = compare_logits(w, lg, ref, f"step {st} positions {pos}")
+        worst = max(worst, e)
+    assert G.check() == 0
+    G.close()
+    say(f"  worst err {worst:.3e}")
 
 
 def _merge_candidates(scores, vals, ids, lse, V, first):

@@ -179,6 +179,24 @@ def test_batch_rows_are_independent():
         np.testing.assert_allclose(allb[b], alone, rtol=0, atol=1e-12 * np.abs(alone).max())
 
 
+def test_ragged_window_rows_equal_their_set_alone():
+    """Sets of different lengths in one window: every row equals a full-prefix
+    recompute (brute force) over its own set's frames only."""
+    w, W, enc, toks = _setup(11)
+    lens = [w.frames, 3, 1]
+    o = OW.WhisperOracle(OW.dims_of(w), W)
+    o.cross_kv([enc[e, :lens[e]] for e in range(w.n_enc)])
+    o.reset(w.batch, enc_of=np.arange(w.batch) % w.n_enc)
+    got = np.stack([o.step(toks[:, p], np.full(w.batch, p)) for p in range(w.steps)], 1)
+    for b in range(w.batch):
+        e = b % w.n_enc
+        ref = OW.decode_full(OW.dims_of(w), W, toks[b], enc[e, :lens[e]], round_cache=True)
+        np.testing.assert_allclose(got[b], ref, rtol=0, atol=1e-9 * np.abs(ref).max())
+    # and a set cut to fewer frames really changes its rows
+    full = _run_cached(w, W, enc, toks)
+    assert np.abs(full[1] - got[1]).max() > 1e-3 and np.abs(full[2] - got[2]).max() > 1e-3
+
+
 def test_cross_kv_once_equals_recompute_and_rounds_to_cache_dtype():
     w, W, enc, toks = _setup(7, cache_dtype="f16")
     o = OW.WhisperOracle(OW.dims_of(w), W)
