@@ -556,106 +556,169 @@ hipError_t launch_argmax_final(const unsigned long long* amax, int nparts, int l
 
 // ------------------------------------------------------------------------------------------
 // beam candidates: per row the W largest logits (ties: lower id first; NaN counts as -inf) and
-// the row's log-sum-exp, so log_softmax(v) = logit(v) - lse.  One block of 512 threads per
-// row: each thread keeps its own top W and (max, sum exp) over a strided slice, then the
-// block merges the lists pairwise in LDS and reduces (max, sum exp).  (Register lists are
-// indexed with compile-time indices only, so they stay in registers.)
+// the row's log-sum-exp, so log_softmax(v) = logit(v) - lse.  Pass 1: TK_P blocks per row, each
+// over a contiguous part of the row; every thread keeps its own top W and (max, sum exp), the
+// block merges the lists pairwise in LDS and writes one partial list and (max, sum exp).  Pass
+// 2: one wave per row merges the TK_P partial lists and sums.  (Register lists are indexed
+// with compile-time indices only, so they stay in registers.)
 // ------------------------------------------------------------------------------------------
-constexpr int TK_MAX = 8, TK_NT = 512;
+constexpr int TK_MAX = 8, TK_NT = 256, TK_P = 32, TK_EPT = 8;   // TK_EPT: loads per thread per pass
 
 __device__ __forceinline__ bool tk_better(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
 }
 
-__global__ __launch_bounds__(TK_NT) void k_topk_lse(const float* __restrict__ logits, int V, int64_t ld, int W,
-                                                     float* __restrict__ top_val, int32_t* __restrict__ top_id,
-                                                     float* __restrict__ lse) {
-  __shared__ float sv[TK_NT * TK_MAX];
-  __shared__ int si[TK_NT * TK_MAX];
+// insert (x, i) into the sorted list (v, id) of length W (<= TK_MAX) if it belongs there
+__device__ __forceinline__ void tk_insert(float (&v)[TK_MAX], int (&id)[TK_MAX], int W, float x, int i) {
+  float lv = v[0];
+  int li = id[0];
+#pragma unroll
+  for (int k = 1; k < TK_MAX; ++k)
+    if (k == W - 1) { lv = v[k]; li = id[k]; }
+  if (!tk_better(x, i, lv, li)) return;
+  bool placed = false;
+#pragma unroll
+  for (int k = TK_MAX - 1; k >= 1; --k) {
+    if (k < W && !placed) {
+      if (tk_better(x, i, v[k - 1], id[k - 1])) { v[k] = v[k - 1]; id[k] = id[k - 1]; }
+      else { v[k] = x; id[k] = i; placed = true; }
+    }
+  }
+  if (!placed) { v[0] = x; id[0] = i; }
+}
+
+// (max, sum exp) pairs: merge b into a
+__device__ __forceinline__ void tk_lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  s = (m == -INFINITY ? 0.f : s * expf(m - mn)) + (m2 == -INFINITY ? 0.f : s2 * expf(m2 - mn));
+  m = mn;
+}
+
+// The wave's best W entries over its lanes' sorted lists, in order: W rounds of a butterfly
+// search for the best list head (ties: lower id, then lower lane); the winning lane moves on.
+// Round k's entry goes to out_v[k] / out_i[k] from lane 0 (out_* may be LDS or global).
+__device__ __forceinline__ void tk_wave_merge(const float (&v)[TK_MAX], const int (&id)[TK_MAX], int W,
+                                              float* out_v, int* out_i) {
+  const int t = threadIdx.x & 63;
+  int h = 0;   // this lane's next unconsumed entry
+  for (int k = 0; k < W; ++k) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int j = 0; j < TK_MAX; ++j)
+      if (j == h) { bv = v[j]; bi = id[j]; }
+    int bl = t;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, WAVE);
+      const int oi = __shfl_xor(bi, o, WAVE), ol = __shfl_xor(bl, o, WAVE);
+      if (tk_better(ov, oi, bv, bi) || (ov == bv && oi == bi && ol < bl)) { bv = ov; bi = oi; bl = ol; }
+    }
+    if (t == bl) ++h;
+    if (t == 0) { out_v[k] = bv; out_i[k] = bi; }
+  }
+}
+
+__global__ __launch_bounds__(TK_NT) void k_topk_part(const float* __restrict__ logits, int V, int64_t ld, int W,
+                                                      int chunk, float* __restrict__ pv, int* __restrict__ pi,
+                                                      float* __restrict__ pm, float* __restrict__ ps) {
+  __shared__ float sv[TK_NT / 64][TK_MAX];
+  __shared__ int si[TK_NT / 64][TK_MAX];
   __shared__ float sm[TK_NT / 64], ss[TK_NT / 64];
-  const int b = blockIdx.x, t = threadIdx.x;
+  const int part = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const float* row = logits + (int64_t)b * ld;
+  const int i0 = part * chunk, i1 = min(V, i0 + chunk);
   float v[TK_MAX];
   int id[TK_MAX];
 #pragma unroll
   for (int k = 0; k < TK_MAX; ++k) { v[k] = -INFINITY; id[k] = INT_MAX; }
   float m = -INFINITY, sum = 0.f;
-  for (int i = t; i < V; i += TK_NT) {
-    float x = row[i];
-    if (x != x) x = -INFINITY;   // NaN
-    if (x != -INFINITY) {
-      if (x > m) { sum = sum * expf(m - x) + 1.f; m = x; }
-      else sum += expf(x - m);
+  for (int base = i0; base < i1; base += TK_NT * TK_EPT) {
+    float xs[TK_EPT];   // every load of the pass in flight before any is used
+#pragma unroll
+    for (int u = 0; u < TK_EPT; ++u) {
+      const int i = base + t + u * TK_NT;
+      xs[u] = row[min(i, i1 - 1)];
     }
-    float lv = v[0];
-    int li = id[0];
 #pragma unroll
-    for (int k = 1; k < TK_MAX; ++k)
-      if (k == W - 1) { lv = v[k]; li = id[k]; }
-    if (tk_better(x, i, lv, li)) {   // insert, keeping the list sorted (shift the worse ones down)
-      bool placed = false;
-#pragma unroll
-      for (int k = TK_MAX - 1; k >= 1; --k) {
-        if (k < W && !placed) {
-          if (tk_better(x, i, v[k - 1], id[k - 1])) { v[k] = v[k - 1]; id[k] = id[k - 1]; }
-          else { v[k] = x; id[k] = i; placed = true; }
+    for (int u = 0; u < TK_EPT; ++u) {
+      const int i = base + t + u * TK_NT;
+      if (i < i1) {
+        float x = xs[u];
+        if (x != x) x = -INFINITY;   // NaN
+        if (x != -INFINITY) {
+          if (x > m) { sum = sum * expf(m - x) + 1.f; m = x; }
+          else sum += expf(x - m);
         }
+        tk_insert(v, id, W, x, i);
       }
-      if (!placed) { v[0] = x; id[0] = i; }
     }
   }
+  // each wave's best W into LDS, then wave 0 merges the waves' lists
+  tk_wave_merge(v, id, W, sv[t >> 6], si[t >> 6]);
 #pragma unroll
-  for (int k = 0; k < TK_MAX; ++k)
-    if (k < W) { sv[t * TK_MAX + k] = v[k]; si[t * TK_MAX + k] = id[k]; }
-  // (max, sum exp): within the wave, then across the 16 waves
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o, WAVE), s2 = __shfl_xor(sum, o, WAVE);
-    const float mn = fmaxf(m, m2);
-    sum = (m == -INFINITY ? 0.f : sum * expf(m - mn)) + (m2 == -INFINITY ? 0.f : s2 * expf(m2 - mn));
-    m = mn;
-  }
+  for (int o = 32; o > 0; o >>= 1) tk_lse_merge(m, sum, __shfl_xor(m, o, WAVE), __shfl_xor(sum, o, WAVE));
   if ((t & 63) == 0) { sm[t >> 6] = m; ss[t >> 6] = sum; }
   __syncthreads();
-  // pairwise merges of the sorted lists: list t takes the best W of lists t and t + stride
-  for (int stride = TK_NT / 2; stride > 0; stride >>= 1) {
-    if (t < stride) {
-      const float* av = sv + t * TK_MAX; const int* ai = si + t * TK_MAX;
-      const float* bv = sv + (t + stride) * TK_MAX; const int* bi = si + (t + stride) * TK_MAX;
-      float ov[TK_MAX]; int oi[TK_MAX];
-      int x = 0, y = 0;   // x + y = k <= W - 1: both stay inside their lists
+  if (t >= 64) return;
 #pragma unroll
-      for (int k = 0; k < TK_MAX; ++k) {
-        if (k < W) {
-          if (tk_better(av[x], ai[x], bv[y], bi[y])) { ov[k] = av[x]; oi[k] = ai[x]; ++x; }
-          else { ov[k] = bv[y]; oi[k] = bi[y]; ++y; }
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < TK_MAX; ++k)
-        if (k < W) { sv[t * TK_MAX + k] = ov[k]; si[t * TK_MAX + k] = oi[k]; }
-    }
-    __syncthreads();
+  for (int k = 0; k < TK_MAX; ++k) {
+    const bool in = t < TK_NT / 64 && k < W;
+    v[k] = in ? sv[min(t, TK_NT / 64 - 1)][k] : -INFINITY;
+    id[k] = in ? si[min(t, TK_NT / 64 - 1)][k] : INT_MAX;
   }
+  const int64_t o = ((int64_t)b * gridDim.x + part);
+  tk_wave_merge(v, id, W, pv + o * TK_MAX, pi + o * TK_MAX);
   if (t == 0) {
-    float M = -INFINITY;
-    for (int w = 0; w < TK_NT / 64; ++w) M = fmaxf(M, sm[w]);
-    float S = 0.f;
-    for (int w = 0; w < TK_NT / 64; ++w)
-      if (sm[w] != -INFINITY) S += ss[w] * expf(sm[w] - M);
-    lse[b] = M == -INFINITY ? -INFINITY : M + logf(S);
-    for (int k = 0; k < W; ++k) {
-      top_val[(int64_t)b * W + k] = sv[k];
-      top_id[(int64_t)b * W + k] = si[k];
-    }
+    float M = sm[0], S = ss[0];
+    for (int w = 1; w < TK_NT / 64; ++w) tk_lse_merge(M, S, sm[w], ss[w]);
+    pm[o] = M;
+    ps[o] = S;
   }
 }
 
+__global__ __launch_bounds__(64) void k_topk_final(const float* __restrict__ pv, const int* __restrict__ pi,
+                                                    const float* __restrict__ pm, const float* __restrict__ ps,
+                                                    int P, int W, float* __restrict__ top_val,
+                                                    int32_t* __restrict__ top_id, float* __restrict__ lse) {
+  const int b = blockIdx.x, t = threadIdx.x;
+  float v[TK_MAX];
+  int id[TK_MAX];
+#pragma unroll
+  for (int k = 0; k < TK_MAX; ++k) { v[k] = -INFINITY; id[k] = INT_MAX; }
+  float m = -INFINITY, s = 0.f;
+  for (int q = t; q < P; q += 64) {   // lane t: the lists of parts t, t + 64, ...
+    const int64_t o = (int64_t)b * P + q;
+#pragma unroll
+    for (int k = 0; k < TK_MAX; ++k)
+      if (k < W) tk_insert(v, id, W, pv[o * TK_MAX + k], pi[o * TK_MAX + k]);
+    tk_lse_merge(m, s, pm[o], ps[o]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tk_lse_merge(m, s, __shfl_xor(m, o, WAVE), __shfl_xor(s, o, WAVE));
+  tk_wave_merge(v, id, W, top_val + (int64_t)b * W, top_id + (int64_t)b * W);
+  if (t == 0) lse[b] = m == -INFINITY ? -INFINITY : m + logf(s);
+}
+
+int topk_parts(int V) { return std::max(1, std::min(TK_P, (V + 4 * TK_NT - 1) / (4 * TK_NT))); }
+
+size_t topk_scratch_bytes(int B, int V) {
+  const size_t P = topk_parts(V);
+  return (size_t)B * P * (TK_MAX * 8 + 8);
+}
+
 hipError_t launch_topk_lse(const float* logits, int B, int V, int64_t ld, int W, float* top_val, int32_t* top_id,
-                           float* lse, hipStream_t s) {
-  if (!logits || !top_val || !top_id || !lse || B <= 0 || V <= 0 || ld < V || W < 1 || W > TK_MAX || W > V)
+                           float* lse, void* scratch, hipStream_t s) {
+  if (!logits || !top_val || !top_id || !lse || !scratch || B <= 0 || V <= 0 || ld < V || W < 1 || W > TK_MAX ||
+      W > V)
     return hipErrorInvalidValue;
-  k_topk_lse<<<B, TK_NT, 0, s>>>(logits, V, ld, W, top_val, top_id, lse);
+  const int P = topk_parts(V), chunk = (V + P - 1) / P;
+  float* pv = reinterpret_cast<float*>(scratch);
+  int* pi = reinterpret_cast<int*>(pv + (size_t)B * P * TK_MAX);
+  float* pm = reinterpret_cast<float*>(pi + (size_t)B * P * TK_MAX);
+  float* ps = pm + (size_t)B * P;
+  k_topk_part<<<dim3(P, B), TK_NT, 0, s>>>(logits, V, ld, W, chunk, pv, pi, pm, ps);
+  k_topk_final<<<B, 64, 0, s>>>(pv, pi, pm, ps, P, W, top_val, top_id, lse);
   return hipGetLastError();
 }
 

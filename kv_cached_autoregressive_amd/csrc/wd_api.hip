@@ -57,6 +57,7 @@ struct Plan {
   size_t frames_dev = 0;     // per encoder set frame counts [n_enc] int32 (ragged windows)
   size_t x = 0, y = 0, q = 0, qkv = 0, o = 0, h = 0, part = 0, amax = 0, err = 0, pos_tmp = 0;
   size_t rope = 0;           // Qwen3: cos [context][hd/2], then sin [context][hd/2]
+  size_t topk = 0;           // wd_topk partial lists
   size_t gpart = 0; int64_t gpart_cap = 0;   // split-K GEMM partials [G][B][N] fp32
   size_t tok_in = 0, ov_in = 0;              // staged tokens [B] and embedding override rows [B, d]
   int max_splits = 1, amax_parts = 1;
@@ -235,6 +236,7 @@ Plan make_plan(const wd_config& c) {
   }
   p.amax_parts = std::max(wd::gemv_blocks(c.vocab, c.max_batch), wd::mgemv_blocks(c.vocab, c.max_batch));
   p.amax = b.take((size_t)p.amax_parts * Bm * 8);
+  p.topk = b.take(wd::topk_scratch_bytes((int)Bm, c.vocab));   // beam-candidate partial lists
   p.err = b.take(64);
   p.pos_tmp = b.take(Bm * 4);
   p.tok_in = b.take(Bm * 4);
@@ -1167,8 +1169,8 @@ wd_status wd_topk(wd_ctx* ctx, const float* logits, int32_t B, int32_t W, float*
     if (!logits || !top_val || !top_id || !lse) return fail(ctx, WD_ERR_ARG, "wd_topk: null pointer");
     if (B < 1 || B > g.max_batch) return fail(ctx, WD_ERR_ARG, "wd_topk: B outside [1, max_batch]");
     if (W < 1 || W > 8 || W > g.vocab) return fail(ctx, WD_ERR_ARG, "wd_topk: W outside [1, min(8, vocab)]");
-    HIPCHK(ctx, wd::launch_topk_lse(logits, B, g.vocab, g.vocab, W, top_val, top_id, lse, ctx->stream),
-           "beam candidates");
+    HIPCHK(ctx, wd::launch_topk_lse(logits, B, g.vocab, g.vocab, W, top_val, top_id, lse, ctx->at(ctx->plan.topk),
+                                    ctx->stream), "beam candidates");
     return WD_OK;
   } catch (...) {
     return fail(ctx, WD_ERR_INTERNAL, "wd_topk: internal error");

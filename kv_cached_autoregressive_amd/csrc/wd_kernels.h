@@ -61,9 +61,10 @@ hipError_t launch_argmax_final(const unsigned long long* amax, int nparts, int l
                                int32_t* out, hipStream_t s);
 // Per row b < B of logits [B, ld]: the W (<= 8) largest of the first V values, descending
 // (ties: lower index first; NaN as -inf), into top_val / top_id [B, W], and lse[b] =
-// log(sum_v exp(logits[b][v])).
+// log(sum_v exp(logits[b][v])).  scratch: topk_scratch_bytes(B, V) bytes of device memory.
+size_t topk_scratch_bytes(int B, int V);
 hipError_t launch_topk_lse(const float* logits, int B, int V, int64_t ld, int W, float* top_val, int32_t* top_id,
-                           float* lse, hipStream_t s);
+                           float* lse, void* scratch, hipStream_t s);
 
 // ---- MFMA skinny GEMM (16-bit weights) ------------------------------------------------------
 // Weights are stored in MFMA fragment order ("fragment layout"): for W [N, K] with N padded
