@@ -107,6 +107,8 @@ def test_null_context_calls_return_arg():
     L = K.lib()
     assert L.wd_step(None, None, None, 1, None, None) == 1
     assert L.wd_cross_kv(None, None, 1) == 1
+    assert L.wd_cross_kv_ragged(None, None, None) == 1
+    assert L.wd_topk(None, None, 1, 1, None, None, None) == 1
     assert L.wd_reorder(None, None, 1, 1) == 1
     assert L.wd_prefill(None, None, 1, 1, None, 0, 0, None, None) == 1
     assert L.wd_check(None) == 1
