@@ -594,28 +594,41 @@ __device__ __forceinline__ void tk_lse_merge(float& m, float& s, float m2, float
   m = mn;
 }
 
+// Order-preserving 64-bit key of (value, id): larger key = larger value, then lower id (-0 is
+// taken as +0, as the value comparison takes them equal).
+__device__ __forceinline__ unsigned long long tk_key(float v, int id) {
+  const uint32_t b = __float_as_uint(v == 0.f ? 0.f : v);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)o << 32) | (uint32_t)(0x7FFFFFFF - id);
+}
+
 // The wave's best W entries over its lanes' sorted lists, in order: W rounds of a butterfly
-// search for the best list head (ties: lower id, then lower lane); the winning lane moves on.
-// Round k's entry goes to out_v[k] / out_i[k] from lane 0 (out_* may be LDS or global).
+// maximum of the lanes' head keys; the lane whose head won moves on (equal keys are only the
+// empty (-inf, INT_MAX) entries, past which every list stays empty).  Round k's entry goes to
+// out_v[k] / out_i[k] from lane 0 (out_* may be LDS or global).
 __device__ __forceinline__ void tk_wave_merge(const float (&v)[TK_MAX], const int (&id)[TK_MAX], int W,
                                               float* out_v, int* out_i) {
   const int t = threadIdx.x & 63;
   int h = 0;   // this lane's next unconsumed entry
   for (int k = 0; k < W; ++k) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
+    float hv = -INFINITY;
+    int hi = INT_MAX;
 #pragma unroll
     for (int j = 0; j < TK_MAX; ++j)
-      if (j == h) { bv = v[j]; bi = id[j]; }
-    int bl = t;
+      if (j == h) { hv = v[j]; hi = id[j]; }
+    const unsigned long long mine = tk_key(hv, hi);
+    unsigned long long best = mine;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, WAVE);
-      const int oi = __shfl_xor(bi, o, WAVE), ol = __shfl_xor(bl, o, WAVE);
-      if (tk_better(ov, oi, bv, bi) || (ov == bv && oi == bi && ol < bl)) { bv = ov; bi = oi; bl = ol; }
+      const unsigned long long other = __shfl_xor(best, o, WAVE);
+      best = other > best ? other : best;
     }
-    if (t == bl) ++h;
-    if (t == 0) { out_v[k] = bv; out_i[k] = bi; }
+    if (mine == best) ++h;
+    if (t == 0) {
+      const uint32_t ob = (uint32_t)(best >> 32);
+      out_v[k] = __uint_as_float((ob & 0x80000000u) ? (ob & 0x7FFFFFFFu) : ~ob);
+      out_i[k] = 0x7FFFFFFF - (int)(uint32_t)(best & 0xFFFFFFFFu);
+    }
   }
 }
 
