@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define WD_ABI_VERSION 2
+#define WD_ABI_VERSION 3
 #define WD_MAX_BATCH 64
 
 typedef struct wd_ctx wd_ctx;

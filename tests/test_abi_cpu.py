@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
             "wd_free", "wd_workspace_bytes", "wd_last_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert K.wd_abi_version() == 2
+    assert K.wd_abi_version() == 3
 
 
 def test_workspace_bytes_plan():
