@@ -146,6 +146,32 @@ wd_status wd_cross_kv(wd_ctx* ctx, const void* enc, int32_t frames);
  * Errors: ARG (null, a frame count out of range), STATE (Qwen3 context), HIP. */
 wd_status wd_cross_kv_ragged(wd_ctx* ctx, const void* enc, const int32_t* frames);
 
+/* Audio encoder of a Whisper context (16-bit weights): the step before wd_cross_kv.  It shares
+ * d_model, n_heads, head_dim, w_dtype and norm_eps with the decoder and has its own n_layers,
+ * d_ff (a multiple of 128) and n_mels.  `frames` mel frames become P = (frames - 1) / 2 + 1
+ * states (P <= max_frames): Nest model page, "The convolutional stem" and lib.linnet
+ * `encoded`; mlx-bun whisper.ts `encode`:
+ *   x = GELU(conv1(mel) + b1)   (kernel 3, stride 1, padding 1, over the mel channels)
+ *   x = GELU(conv2(x) + b2) + pos   (kernel 3, stride 2, padding 1; pos the stored table)
+ *   per layer: x += attn(LN1(x)) over all P states (no mask, no key bias);
+ *              x += W2 GELU(W1 LN2(x) + b1) + b2
+ *   out = LN_post(x), in w_dtype.
+ * Tensors (i = layer): enc.conv1.w [d, n_mels, 3], enc.conv1.b, enc.conv2.w [d, d, 3],
+ * enc.conv2.b, enc.pos [P, d], enc.i.ln1.g/.b, enc.i.attn.q.w/.b, enc.i.attn.k.w,
+ * enc.i.attn.v.w/.b, enc.i.attn.o.w/.b, enc.i.ln2.g/.b, enc.i.fc1.w/.b, enc.i.fc2.w/.b,
+ * enc.ln_post.g/.b (matrices in w_dtype).  The repacked weights and the encoder's buffers live
+ * in a second caller-owned workspace of wd_encoder_workspace_bytes(...) bytes (0: invalid).
+ * max_sets bounds the encoder sets per wd_encode call.  Errors: ARG, OOM, HIP. */
+size_t wd_encoder_workspace_bytes(const wd_ctx* ctx, int32_t n_mels, int32_t frames, int32_t n_layers,
+                                  int32_t d_ff, int32_t max_sets);
+wd_status wd_load_encoder(wd_ctx* ctx, int32_t n_mels, int32_t frames, int32_t n_layers, int32_t d_ff,
+                          int32_t max_sets, const wd_tensor* weights, int32_t n_weights, void* workspace,
+                          size_t ws_bytes);
+/* Encoder states of n_sets windows: mel dev [n_sets, frames, n_mels] (positions first) in
+ * w_dtype -> enc dev [n_sets, P, d] in w_dtype, ready for wd_cross_kv(ctx, enc, P).
+ * Asynchronous on the context's stream.  Errors: ARG, STATE (no encoder loaded), HIP. */
+wd_status wd_encode(wd_ctx* ctx, const void* mel, int32_t n_sets, void* enc);
+
 /* One decoder step for rows 0..B-1 (1 <= B <= max_batch).
  *   tokens    dev int32 [B]   token id per row (may alias `argmax` for
  *                             on-device greedy decoding)

@@ -19,7 +19,7 @@ from typing import Dict, Iterable, Optional, Sequence
 __all__ = [
     "WdError", "WdConfig", "WdTensor", "lib", "lib_path", "declared_functions",
     "wd_abi_version", "wd_workspace_bytes", "wd_load", "wd_cross_kv", "wd_cross_kv_ragged", "wd_step", "wd_reorder",
-    "wd_topk", "wd_prefill", "wd_check", "wd_last_error", "wd_free", "wd_profile", "wd_profile_read",
+    "wd_topk", "wd_prefill", "wd_encoder_workspace_bytes", "wd_load_encoder", "wd_encode", "wd_check", "wd_last_error", "wd_free", "wd_profile", "wd_profile_read",
     "wd_debug_cache",
     "config_from", "Decoder", "DTYPES", "STATUS",
 ]
@@ -79,6 +79,9 @@ def lib():
             "wd_step": (i32, [vp, vp, vp, i32, vp, vp]),
             "wd_reorder": (i32, [vp, ctypes.POINTER(i32), i32, i32]),
             "wd_topk": (i32, [vp, vp, i32, i32, vp, vp, vp]),
+            "wd_encoder_workspace_bytes": (sz, [vp, i32, i32, i32, i32, i32]),
+            "wd_load_encoder": (i32, [vp, i32, i32, i32, i32, i32, ctypes.POINTER(WdTensor), i32, vp, sz]),
+            "wd_encode": (i32, [vp, vp, i32, vp]),
             "wd_prefill": (i32, [vp, vp, i32, i32, vp, i32, i32, vp, vp]),
             "wd_check": (i32, [vp]),
             "wd_last_error": (ctypes.c_char_p, [vp]),
@@ -150,6 +153,21 @@ def wd_reorder(ctx, beam_idx: Iterable[int], n_rows: int):
 def wd_topk(ctx, logits: int, B: int, W: int, top_val: int, top_id: int, lse: int):
     _check(lib().wd_topk(ctx, ctypes.c_void_p(logits), B, W, ctypes.c_void_p(top_val), ctypes.c_void_p(top_id),
                          ctypes.c_void_p(lse)), ctx)
+
+
+def wd_encoder_workspace_bytes(ctx, n_mels: int, frames: int, n_layers: int, d_ff: int, max_sets: int) -> int:
+    return lib().wd_encoder_workspace_bytes(ctx, n_mels, frames, n_layers, d_ff, max_sets)
+
+
+def wd_load_encoder(ctx, n_mels: int, frames: int, n_layers: int, d_ff: int, max_sets: int,
+                    tensors: Sequence[WdTensor], workspace: int, ws_bytes: int):
+    arr = (WdTensor * max(1, len(tensors)))(*tensors)
+    _check(lib().wd_load_encoder(ctx, n_mels, frames, n_layers, d_ff, max_sets, arr if tensors else None,
+                                 len(tensors), ctypes.c_void_p(workspace), ws_bytes), ctx)
+
+
+def wd_encode(ctx, mel: int, n_sets: int, enc: int):
+    _check(lib().wd_encode(ctx, ctypes.c_void_p(mel), n_sets, ctypes.c_void_p(enc)), ctx)
 
 
 def wd_prefill(ctx, tokens: int, B: int, T: int, embeds: int, A: int, offset: int, logits: int,
@@ -243,6 +261,42 @@ class Decoder:
         self.ctx = wd_load(self.cfg, descs, self.ws_ptr, nbytes, self.stream.cuda_stream)
         self.stream.synchronize()
         del up
+
+    def load_encoder(self, weights: Dict[str, object], n_mels: int, frames: int, n_layers: int, d_ff: int,
+                     max_sets: int):
+        """Loads the audio encoder (canonical ``enc.*`` names) into a second workspace."""
+        import numpy as np
+        import torch
+        nbytes = wd_encoder_workspace_bytes(self.ctx, n_mels, frames, n_layers, d_ff, max_sets)
+        if nbytes == 0:
+            raise WdError(1, "invalid encoder configuration")
+        self.enc_workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        ptr = (self.enc_workspace.data_ptr() + 255) & ~255
+        wdt = _torch_dtype(self.w.w_dtype)
+        up, descs = [], []
+        with torch.cuda.stream(self.stream):
+            for name, arr in weights.items():
+                t = arr if isinstance(arr, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(arr))
+                t = t.to(device=self.device, dtype=wdt).contiguous()
+                up.append(t)
+                descs.append(WdTensor(name.encode(), t.data_ptr(), t.numel(), DTYPES[self.w.w_dtype]))
+        wd_load_encoder(self.ctx, n_mels, frames, n_layers, d_ff, max_sets, descs, ptr, nbytes)
+        self.stream.synchronize()
+        del up
+        self.enc_frames = frames
+
+    def encode(self, mel, out=None):
+        """mel: device tensor [n_sets, frames, n_mels] in w_dtype.  Returns [n_sets, P, d]."""
+        import torch
+        n, frames = mel.shape[0], mel.shape[1]
+        assert frames == self.enc_frames and mel.is_contiguous()
+        P = (frames - 1) // 2 + 1
+        if out is None:
+            out = torch.empty(n, P, self.w.d, dtype=mel.dtype, device=self.device)
+        cur = self._enter()
+        wd_encode(self.ctx, mel.data_ptr(), n, out.data_ptr())
+        self._leave(cur)
+        return out
 
     def close(self):
         if getattr(self, "ctx", None):

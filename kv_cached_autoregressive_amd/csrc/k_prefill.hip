@@ -106,18 +106,29 @@ __device__ __forceinline__ void fg_epilogue(const FgParams& p, const pf32x4_t (&
         }
   } else {
 #pragma unroll
-    for (int i = 0; i < WR; ++i)
+    for (int j = 0; j < WC; ++j) {
+      const int n = (ct0 + j) * 16 + col;
+      const float bn = p.bias ? p.bias[n] : 0.f;
 #pragma unroll
-      for (int j = 0; j < WC; ++j)
+      for (int i = 0; i < WR; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = (rt0 + i) * 16 + rsub + e, n = (ct0 + j) * 16 + col;
+          const int r = (rt0 + i) * 16 + rsub + e;
           if (r < p.R) {
-            float* o = p.out + (int64_t)r * p.ldo + n;
-            if constexpr (EPI == FG_RESID) *o += acc[i][j][e];
-            else *o = acc[i][j][e];
+            const float c = acc[i][j][e] + bn;
+            if constexpr (EPI == FG_GELU_SPLIT) {
+              store_split<T>(p.Ohi, p.Olo, frag_offset(r, n, p.N), 0.5f * c * (1.0f + erff(c * 0.70710678118654752f)));
+            } else {
+              float* o = p.out + (int64_t)r * p.ldo + n;
+              if constexpr (EPI == FG_RESID) *o += c;
+              else if constexpr (EPI == FG_GELU)
+                *o = 0.5f * c * (1.0f + erff(c * 0.70710678118654752f)) +
+                     (p.pos ? p.pos[(int64_t)(r % p.pos_rows) * p.N + n] : 0.f);
+              else *o = c;
+            }
           }
         }
+    }
   }
 }
 
@@ -228,7 +239,10 @@ __global__ __launch_bounds__(256) void k_fgemm_lds(FgParams p) {
 
 hipError_t launch_fgemm(const FgParams& p, hipStream_t s) {
   if (p.R <= 0 || p.N <= 0 || p.N % 128 || p.K <= 0 || p.K % 32 || !p.W || !p.Ahi || !p.Alo) return hipErrorInvalidValue;
-  if (p.epi == FG_SWIGLU ? (!p.Ohi || !p.Olo || p.N % 256) : (!p.out || p.ldo < p.N)) return hipErrorInvalidValue;
+  if (p.epi == FG_SWIGLU ? (!p.Ohi || !p.Olo || p.N % 256)
+      : p.epi == FG_GELU_SPLIT ? (!p.Ohi || !p.Olo)
+      : (!p.out || p.ldo < p.N || (p.epi == FG_GELU && p.pos && p.pos_rows <= 0)))
+    return hipErrorInvalidValue;
   // 128-row blocks unless they leave CUs idle (then 64-row blocks; A is padded to 128 rows)
   const bool wide = (int64_t)((p.R + 127) / 128) * (p.N / 128) >= 256;
   const dim3 grid(wide ? (p.R + 127) / 128 : (p.R + 63) / 64, p.N / 128);
@@ -244,6 +258,8 @@ hipError_t launch_fgemm(const FgParams& p, hipStream_t s) {
     case FG_STORE: WD_FG1(T_, FG_STORE) break;                                                           \
     case FG_RESID: WD_FG1(T_, FG_RESID) break;                                                           \
     case FG_SWIGLU: WD_FG1(T_, FG_SWIGLU) break;                                                         \
+    case FG_GELU: WD_FG1(T_, FG_GELU) break;                                                             \
+    case FG_GELU_SPLIT: WD_FG1(T_, FG_GELU_SPLIT) break;                                                 \
     default: return hipErrorInvalidValue;                                                                \
   }
   if (p.w_dtype == DT_BF16) { WD_FG(bf16_t) }
@@ -304,8 +320,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
   const int tq = p.t0 + jc;
   const int r = b * p.C + jc;
   // key ranges: the block's (staged) and the wave's (computed)
-  const int rows_blk = p.t0 + min(p.Cn - 1, (blockIdx.x * PA_QB + PA_QB - 1) / G) + 1;
-  const int rows_w = p.t0 + min(p.Cn - 1, (blockIdx.x * PA_QB + wv * 16 + 15) / G) + 1;
+  const int rows_blk = p.full ? p.t0 + p.Cn : p.t0 + min(p.Cn - 1, (blockIdx.x * PA_QB + PA_QB - 1) / G) + 1;
+  const int rows_w = p.full ? rows_blk : p.t0 + min(p.Cn - 1, (blockIdx.x * PA_QB + wv * 16 + 15) / G) + 1;
+  const int tmax = p.full ? rows_blk - 1 : tq;   // the last key this lane's query sees
 
   // q^T as the B operand: lane (col, grp) holds channels 32 ks + 8 grp .. +8 of its query
   pv4u qh[KS], ql[KS];
@@ -375,7 +392,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = k0 + kt * 16 + 4 * grp + e;
-          sv[kt * 4 + e] = key <= tq ? sc[kt][e] : -INFINITY;
+          sv[kt * 4 + e] = key <= tmax ? sc[kt][e] : -INFINITY;
           mx = fmaxf(mx, sv[kt * 4 + e]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
@@ -449,6 +466,117 @@ hipError_t launch_pf_attn(const PfAttnParams& p, hipStream_t s) {
   else if (p.hd == 64 && p.cache_dtype == DT_BF16) { WD_PFA(bf16_t, 64) }
   else return hipErrorInvalidValue;
 #undef WD_PFA
+  return hipGetLastError();
+}
+
+// ---- audio encoder glue ------------------------------------------------------------------------
+template <typename S, typename T>
+__global__ __launch_bounds__(256) void k_conv_windows(const S* __restrict__ x, int nb, int L, int C, int stride,
+                                                      int Lout, int Kp, T* __restrict__ a_hi, T* __restrict__ a_lo) {
+  const int64_t n = (int64_t)nb * Lout * Kp;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / Kp;
+    const int kk = (int)(i - r * Kp);
+    const int b = (int)(r / Lout), o = (int)(r - (int64_t)b * Lout);
+    float v = 0.f;
+    if (kk < 3 * C) {
+      const int c = kk / 3, k = kk - c * 3, t = o * stride + k - 1;
+      if (t >= 0 && t < L) v = to_f(x[((int64_t)b * L + t) * C + c]);
+    }
+    store_split<T>(a_hi, a_lo, frag_offset(r, kk, Kp), v);
+  }
+}
+
+hipError_t launch_conv_windows(const void* x, int x_dtype, int nb, int L, int C, int stride, int Lout, int Kp,
+                               void* a_hi, void* a_lo, int a_dtype, hipStream_t s) {
+  if (!x || !a_hi || !a_lo || nb <= 0 || L <= 0 || C <= 0 || Lout <= 0 || Kp % 32 || Kp < 3 * C ||
+      (stride != 1 && stride != 2))
+    return hipErrorInvalidValue;
+  const int blocks = (int)std::min<int64_t>(((int64_t)nb * Lout * Kp + 255) / 256, 65536);
+#define WD_CW(S_, T_) k_conv_windows<S_, T_><<<blocks, 256, 0, s>>>((const S_*)x, nb, L, C, stride, Lout, Kp, (T_*)a_hi, (T_*)a_lo)
+#define WD_CW_S(T_)                                      \
+  if (x_dtype == DT_F32) WD_CW(float, T_);               \
+  else if (x_dtype == DT_F16) WD_CW(f16_t, T_);          \
+  else if (x_dtype == DT_BF16) WD_CW(bf16_t, T_);        \
+  else return hipErrorInvalidValue;
+  if (a_dtype == DT_BF16) { WD_CW_S(bf16_t) }
+  else if (a_dtype == DT_F16) { WD_CW_S(f16_t) }
+  else return hipErrorInvalidValue;
+#undef WD_CW_S
+#undef WD_CW
+  return hipGetLastError();
+}
+
+template <typename S, typename T>
+__global__ __launch_bounds__(256) void k_pack_pad(const S* __restrict__ src, int64_t rows, int Ks, T* __restrict__ dst,
+                                                  int Kp) {
+  const int64_t n = rows * Kp;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / Kp;
+    const int k = (int)(i - r * Kp);
+    dst[frag_offset(r, k, Kp)] = from_f<T>(k < Ks ? to_f(src[r * Ks + k]) : 0.f);
+  }
+}
+
+hipError_t launch_pack_pad(const void* src, int src_dtype, int64_t rows, int Ks, void* dst, int dst_dtype, int Kp,
+                           hipStream_t s) {
+  if (!src || !dst || rows <= 0 || Ks <= 0 || Kp < Ks || Kp % 32 || rows % 16) return hipErrorInvalidValue;
+  const int blocks = (int)std::min<int64_t>((rows * Kp + 255) / 256, 65536);
+#define WD_PP(S_, T_) k_pack_pad<S_, T_><<<blocks, 256, 0, s>>>((const S_*)src, rows, Ks, (T_*)dst, Kp)
+#define WD_PP_S(T_)                                      \
+  if (src_dtype == DT_F32) WD_PP(float, T_);             \
+  else if (src_dtype == DT_F16) WD_PP(f16_t, T_);        \
+  else if (src_dtype == DT_BF16) WD_PP(bf16_t, T_);      \
+  else return hipErrorInvalidValue;
+  if (dst_dtype == DT_BF16) { WD_PP_S(bf16_t) }
+  else if (dst_dtype == DT_F16) { WD_PP_S(f16_t) }
+  else return hipErrorInvalidValue;
+#undef WD_PP_S
+#undef WD_PP
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_enc_qkv(const float* __restrict__ qkv, const float* __restrict__ bq,
+                                                 const float* __restrict__ bv, int nb, int P, int H, int hd,
+                                                 float qscale, float* __restrict__ q, T* __restrict__ K,
+                                                 T* __restrict__ V) {
+  const int d = H * hd;
+  const int64_t n = (int64_t)nb * P * d;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / d;
+    const int c = (int)(i - r * d);
+    const int b = (int)(r / P), pp = (int)(r - (int64_t)b * P), h = c / hd, ch = c - h * hd;
+    const float* row = qkv + r * 3 * d;
+    q[i] = (row[c] + (bq ? bq[c] : 0.f)) * qscale;
+    const int64_t kv = (((int64_t)b * H + h) * P + pp) * hd + ch;
+    K[kv] = from_f<T>(row[d + c]);
+    V[kv] = from_f<T>(row[2 * d + c] + (bv ? bv[c] : 0.f));
+  }
+}
+
+hipError_t launch_enc_qkv(const float* qkv, const float* bq, const float* bv, int nb, int P, int H, int hd,
+                          float qscale, float* q, void* K, void* V, int kv_dtype, hipStream_t s) {
+  if (!qkv || !q || !K || !V || nb <= 0 || P <= 0 || H <= 0 || hd <= 0) return hipErrorInvalidValue;
+  const int blocks = (int)std::min<int64_t>(((int64_t)nb * P * H * hd + 255) / 256, 65536);
+  if (kv_dtype == DT_BF16) k_enc_qkv<bf16_t><<<blocks, 256, 0, s>>>(qkv, bq, bv, nb, P, H, hd, qscale, q, (bf16_t*)K, (bf16_t*)V);
+  else if (kv_dtype == DT_F16) k_enc_qkv<f16_t><<<blocks, 256, 0, s>>>(qkv, bq, bv, nb, P, H, hd, qscale, q, (f16_t*)K, (f16_t*)V);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_cast(const float* __restrict__ x, T* __restrict__ y, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) y[i] = from_f<T>(x[i]);
+}
+
+hipError_t launch_cast(const float* x, void* y, int y_dtype, int64_t n, hipStream_t s) {
+  if (!x || !y || n <= 0) return hipErrorInvalidValue;
+  const int blocks = (int)std::min<int64_t>((n + 255) / 256, 65536);
+  if (y_dtype == DT_BF16) k_cast<bf16_t><<<blocks, 256, 0, s>>>(x, (bf16_t*)y, n);
+  else if (y_dtype == DT_F16) k_cast<f16_t><<<blocks, 256, 0, s>>>(x, (f16_t*)y, n);
+  else if (y_dtype == DT_F32) k_cast<float><<<blocks, 256, 0, s>>>(x, (float*)y, n);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -257,6 +257,61 @@ Plan make_plan(const wd_config& c) {
   return p;
 }
 
+// Audio encoder (optional, Whisper): weights and buffers in a second caller-owned workspace.
+struct EncLayer { size_t ln1g, ln1b, wqkv, bq, bv, wo, bo, ln2g, ln2b, w1, b1, w2, b2; };
+struct EncPlan {
+  int mels = 0, frames = 0, P = 0, layers = 0, dff = 0, max_sets = 0, kp1 = 0;
+  size_t conv1w = 0, conv1b = 0, conv2w = 0, conv2b = 0, pos = 0, lnpg = 0, lnpb = 0;
+  std::vector<EncLayer> L;
+  // buffers: rows of the stem's first convolution (sets x frames) and of the layers (sets x P),
+  // both rounded up to the GEMM's 128-row tiles
+  size_t x1 = 0, x = 0, ah = 0, al = 0, hh = 0, hl = 0, qkv = 0, q = 0, K = 0, V = 0;
+  size_t total = 0;
+};
+
+EncPlan make_enc_plan(const wd_config& c, int mels, int frames, int layers, int dff, int max_sets) {
+  EncPlan p;
+  Bump b;
+  const size_t d = c.d_model, wb = dtype_bytes(c.w_dtype), f4 = 4;
+  p.mels = mels; p.frames = frames; p.layers = layers; p.dff = dff; p.max_sets = max_sets;
+  p.P = (frames - 1) / 2 + 1;
+  p.kp1 = (3 * mels + 31) / 32 * 32;
+  p.conv1w = b.take(d * p.kp1 * wb); p.conv1b = b.take(d * f4);
+  p.conv2w = b.take(d * 3 * d * wb); p.conv2b = b.take(d * f4);
+  p.pos = b.take((size_t)p.P * d * f4);
+  p.lnpg = b.take(d * f4); p.lnpb = b.take(d * f4);
+  for (int l = 0; l < layers; ++l) {
+    EncLayer e{};
+    e.ln1g = b.take(d * f4); e.ln1b = b.take(d * f4); e.ln2g = b.take(d * f4); e.ln2b = b.take(d * f4);
+    e.wqkv = b.take(3 * d * d * wb); e.bq = b.take(d * f4); e.bv = b.take(d * f4);
+    e.wo = b.take(d * d * wb); e.bo = b.take(d * f4);
+    e.w1 = b.take((size_t)dff * d * wb); e.b1 = b.take((size_t)dff * f4);
+    e.w2 = b.take(d * dff * wb); e.b2 = b.take(d * f4);
+    p.L.push_back(e);
+  }
+  const size_t r1 = ((size_t)max_sets * frames + 127) / 128 * 128, r = ((size_t)max_sets * p.P + 127) / 128 * 128;
+  const size_t ka = std::max({(size_t)p.kp1 * r1, 3 * d * r, d * r});   // widest split A operand
+  p.x1 = b.take(r1 * d * f4);
+  p.x = b.take(r * d * f4);
+  p.ah = b.take(ka * wb); p.al = b.take(ka * wb);
+  p.hh = b.take(r * dff * wb); p.hl = b.take(r * dff * wb);
+  p.qkv = b.take(r * 3 * d * f4);
+  p.q = b.take(r * d * f4);
+  p.K = b.take((size_t)max_sets * p.P * d * wb); p.V = b.take((size_t)max_sets * p.P * d * wb);
+  p.total = (b.off + 255) & ~size_t(255);
+  return p;
+}
+
+std::string check_enc(const wd_config& c, int mels, int frames, int layers, int dff, int max_sets) {
+  if (c.arch != WD_ARCH_WHISPER) return "the audio encoder belongs to a whisper context";
+  if (c.w_dtype == DT_F32) return "the audio encoder runs with 16-bit weights";
+  if (mels < 1 || frames < 1 || layers < 1 || max_sets < 1) return "n_mels, frames, n_layers, max_sets must be positive";
+  if (dff <= 0 || dff % 128) return "the encoder d_ff must be a positive multiple of 128";
+  if (c.d_model % 128) return "d_model must be a multiple of 128";
+  if ((frames - 1) / 2 + 1 > c.max_frames) return "(frames - 1) / 2 + 1 exceeds max_frames";
+  return "";
+}
+
 struct ProfPair { hipEvent_t a, b; int n; };
 
 // A captured step: every launch of one wd_step call, replayed with hipGraphLaunch
@@ -284,6 +339,8 @@ struct wd_ctx {
   int frames = 0;            // frames of the current window (the longest set when ragged)
   bool ragged = false;       // per-set frame counts in plan.frames_dev
   std::vector<int32_t> frames_host;   // staging of the last ragged window's counts
+  EncPlan* enc = nullptr;    // the audio encoder, once wd_load_encoder ran
+  char* enc_ws = nullptr;
   std::string err;
   // captured steps (small cache, oldest evicted first); off when WD_GRAPHS=0, while
   // profiling, or on the legacy null stream
@@ -1161,6 +1218,166 @@ wd_status wd_reorder(wd_ctx* ctx, const int32_t* beam_idx, int32_t B, int32_t n_
   }
 }
 
+size_t wd_encoder_workspace_bytes(const wd_ctx* ctx, int32_t n_mels, int32_t frames, int32_t n_layers,
+                                   int32_t d_ff, int32_t max_sets) {
+  if (!ctx || !check_enc(ctx->cfg, n_mels, frames, n_layers, d_ff, max_sets).empty()) return 0;
+  return make_enc_plan(ctx->cfg, n_mels, frames, n_layers, d_ff, max_sets).total;
+}
+
+wd_status wd_load_encoder(wd_ctx* ctx, int32_t n_mels, int32_t frames, int32_t n_layers, int32_t d_ff,
+                          int32_t max_sets, const wd_tensor* weights, int32_t n_weights, void* workspace,
+                          size_t ws_bytes) {
+  if (!ctx) return WD_ERR_ARG;
+  try {
+    const wd_config& g = ctx->cfg;
+    const std::string why = check_enc(g, n_mels, frames, n_layers, d_ff, max_sets);
+    if (!why.empty()) return fail(ctx, WD_ERR_ARG, "wd_load_encoder: " + why);
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255))
+      return fail(ctx, WD_ERR_ARG, "wd_load_encoder: workspace must be a 256-byte aligned device pointer");
+    if (n_weights < 0 || (n_weights > 0 && !weights)) return fail(ctx, WD_ERR_ARG, "wd_load_encoder: bad weight list");
+    EncPlan plan = make_enc_plan(g, n_mels, frames, n_layers, d_ff, max_sets);
+    if (ws_bytes < plan.total)
+      return fail(ctx, WD_ERR_OOM, "wd_load_encoder: workspace of " + std::to_string(ws_bytes) + " bytes, need " +
+                                       std::to_string(plan.total));
+    const int64_t d = g.d_model, P = plan.P;
+    struct Need { std::string name; int64_t numel; bool matrix; };
+    std::vector<Need> need = {{"enc.conv1.w", d * n_mels * 3, true}, {"enc.conv1.b", d, false},
+                              {"enc.conv2.w", d * d * 3, true}, {"enc.conv2.b", d, false},
+                              {"enc.pos", P * d, false}, {"enc.ln_post.g", d, false}, {"enc.ln_post.b", d, false}};
+    for (int l = 0; l < n_layers; ++l) {
+      const std::string p = "enc." + std::to_string(l) + ".";
+      for (const char* v : {"ln1.g", "ln1.b", "ln2.g", "ln2.b", "attn.q.b", "attn.v.b", "attn.o.b", "fc2.b"})
+        need.push_back({p + v, d, false});
+      for (const char* m : {"attn.q.w", "attn.k.w", "attn.v.w", "attn.o.w"}) need.push_back({p + m, d * d, true});
+      need.push_back({p + "fc1.w", (int64_t)d_ff * d, true});
+      need.push_back({p + "fc1.b", d_ff, false});
+      need.push_back({p + "fc2.w", d * d_ff, true});
+    }
+    std::map<std::string, const wd_tensor*> byname;
+    for (int i = 0; i < n_weights; ++i) {
+      const wd_tensor& t = weights[i];
+      if (!t.name) return fail(ctx, WD_ERR_ARG, "wd_load_encoder: tensor with null name");
+      const std::string nm(t.name);
+      if (nm.size() >= 4 && nm.compare(nm.size() - 4, 4, ".k.b") == 0)
+        return fail(ctx, WD_ERR_ARG, "wd_load_encoder: '" + nm + "': the key projections carry no bias");
+      if (byname.count(nm)) return fail(ctx, WD_ERR_ARG, "wd_load_encoder: duplicate tensor '" + nm + "'");
+      byname[nm] = &t;
+    }
+    if (byname.size() != need.size()) return fail(ctx, WD_ERR_ARG, "wd_load_encoder: unexpected tensor count");
+    for (const auto& n : need) {
+      auto it = byname.find(n.name);
+      if (it == byname.end()) return fail(ctx, WD_ERR_ARG, "wd_load_encoder: missing tensor '" + n.name + "'");
+      const wd_tensor& t = *it->second;
+      if (!t.data || t.numel != n.numel || !valid_dt(t.dtype) || (n.matrix && t.dtype != g.w_dtype))
+        return fail(ctx, WD_ERR_ARG, "wd_load_encoder: '" + n.name + "' has a bad pointer, size or dtype");
+    }
+    char* ws = reinterpret_cast<char*>(workspace);
+    hipStream_t s = ctx->stream;
+    const int wdt = g.w_dtype;
+    hipError_t e = hipSuccess;
+    auto chk = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+    auto T = [&](const std::string& nm) { return byname[nm]; };
+    auto vec = [&](const std::string& nm, size_t dst, int64_t n) {
+      const wd_tensor* t = T(nm);
+      chk(wd::launch_copy_rows(t->data, t->dtype, ws + dst, DT_F32, 1, n, 1, 0, s));
+    };
+    auto mat = [&](const std::string& nm, size_t dst, int64_t rows, int64_t K, int64_t blk_add) {
+      const wd_tensor* t = T(nm);
+      chk(wd::launch_pack_frag(t->data, t->dtype, ws + dst, wdt, rows, K, 1, blk_add, s));
+    };
+    // the stem's kernels [d, C, 3] flattened as (c, tap), columns padded to whole K steps
+    chk(wd::launch_pack_pad(T("enc.conv1.w")->data, wdt, d, 3 * n_mels, ws + plan.conv1w, wdt, plan.kp1, s));
+    chk(wd::launch_pack_pad(T("enc.conv2.w")->data, wdt, d, 3 * (int)d, ws + plan.conv2w, wdt, 3 * (int)d, s));
+    vec("enc.conv1.b", plan.conv1b, d); vec("enc.conv2.b", plan.conv2b, d);
+    vec("enc.pos", plan.pos, P * d);
+    vec("enc.ln_post.g", plan.lnpg, d); vec("enc.ln_post.b", plan.lnpb, d);
+    for (int l = 0; l < n_layers; ++l) {
+      const std::string p = "enc." + std::to_string(l) + ".";
+      const EncLayer& L = plan.L[l];
+      vec(p + "ln1.g", L.ln1g, d); vec(p + "ln1.b", L.ln1b, d); vec(p + "ln2.g", L.ln2g, d); vec(p + "ln2.b", L.ln2b, d);
+      mat(p + "attn.q.w", L.wqkv, d, d, 0);
+      mat(p + "attn.k.w", L.wqkv, d, d, d / 16);
+      mat(p + "attn.v.w", L.wqkv, d, d, 2 * d / 16);
+      vec(p + "attn.q.b", L.bq, d); vec(p + "attn.v.b", L.bv, d);
+      mat(p + "attn.o.w", L.wo, d, d, 0); vec(p + "attn.o.b", L.bo, d);
+      mat(p + "fc1.w", L.w1, d_ff, d, 0); vec(p + "fc1.b", L.b1, d_ff);
+      mat(p + "fc2.w", L.w2, d, d_ff, 0); vec(p + "fc2.b", L.b2, d);
+    }
+    HIPCHK(ctx, e, "wd_load_encoder: weight repack");
+    delete ctx->enc;
+    ctx->enc = new EncPlan(plan);
+    ctx->enc_ws = ws;
+    return WD_OK;
+  } catch (...) {
+    return fail(ctx, WD_ERR_INTERNAL, "wd_load_encoder: internal error");
+  }
+}
+
+wd_status wd_encode(wd_ctx* ctx, const void* mel, int32_t n_sets, void* enc) {
+  if (!ctx) return WD_ERR_ARG;
+  try {
+    const wd_config& g = ctx->cfg;
+    const EncPlan* E = ctx->enc;
+    if (!E) return fail(ctx, WD_ERR_STATE, "wd_encode: no encoder loaded (wd_load_encoder)");
+    if (!mel || !enc) return fail(ctx, WD_ERR_ARG, "wd_encode: null pointer");
+    if (n_sets < 1 || n_sets > E->max_sets) return fail(ctx, WD_ERR_ARG, "wd_encode: n_sets outside [1, max_sets]");
+    char* ws = ctx->enc_ws;
+    auto at = [&](size_t off) { return reinterpret_cast<void*>(ws + off); };
+    auto atf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+    hipStream_t s = ctx->stream;
+    const int d = g.d_model, H = g.n_heads, hd = g.head_dim, wdt = g.w_dtype, P = E->P;
+    const int R1 = n_sets * E->frames, R = n_sets * P;
+    auto gemm = [&](const void* W, int N, int K, const void* Ahi, const void* Alo, int rows, int epi, float* out,
+                    const float* bias, const float* pos, void* Ohi, void* Olo, const char* what) -> wd_status {
+      wd::FgParams f{};
+      f.W = W; f.w_dtype = wdt; f.N = N; f.K = K; f.Ahi = Ahi; f.Alo = Alo; f.R = rows; f.epi = epi;
+      f.out = out; f.ldo = N; f.Ohi = Ohi; f.Olo = Olo; f.bias = bias; f.pos = pos; f.pos_rows = P;
+      HIPCHK(ctx, wd::launch_fgemm(f, s), what);
+      return WD_OK;
+    };
+#define WDCHK(expr) do { const wd_status st_ = (expr); if (st_ != WD_OK) return st_; } while (0)
+    // stem: GELU(conv1(mel) + b1), GELU(conv2(.) + b2) + positions
+    HIPCHK(ctx, wd::launch_conv_windows(mel, wdt, n_sets, E->frames, E->mels, 1, E->frames, E->kp1, at(E->ah),
+                                        at(E->al), wdt, s), "wd_encode: conv1 windows");
+    WDCHK(gemm(at(E->conv1w), d, E->kp1, at(E->ah), at(E->al), R1, wd::FG_GELU, atf(E->x1), atf(E->conv1b), nullptr,
+               nullptr, nullptr, "wd_encode: conv1"));
+    HIPCHK(ctx, wd::launch_conv_windows(atf(E->x1), DT_F32, n_sets, E->frames, d, 2, P, 3 * d, at(E->ah), at(E->al),
+                                        wdt, s), "wd_encode: conv2 windows");
+    WDCHK(gemm(at(E->conv2w), d, 3 * d, at(E->ah), at(E->al), R, wd::FG_GELU, atf(E->x), atf(E->conv2b), atf(E->pos),
+               nullptr, nullptr, "wd_encode: conv2"));
+    const float qscale = 1.0f / sqrtf((float)hd);
+    for (int l = 0; l < E->layers; ++l) {
+      const EncLayer& L = E->L[l];
+      HIPCHK(ctx, wd::launch_norm_split(atf(E->x), at(E->ah), at(E->al), wdt, atf(L.ln1g), atf(L.ln1b), R, d,
+                                        g.norm_eps, s), "wd_encode: ln1");
+      WDCHK(gemm(at(L.wqkv), 3 * d, d, at(E->ah), at(E->al), R, wd::FG_STORE, atf(E->qkv), nullptr, nullptr,
+                 nullptr, nullptr, "wd_encode: q|k|v"));
+      HIPCHK(ctx, wd::launch_enc_qkv(atf(E->qkv), atf(L.bq), atf(L.bv), n_sets, P, H, hd, qscale, atf(E->q),
+                                     at(E->K), at(E->V), wdt, s), "wd_encode: q, K, V");
+      wd::PfAttnParams pa{};
+      pa.q = atf(E->q); pa.K = at(E->K); pa.V = at(E->V); pa.cache_dtype = wdt;
+      pa.kv_bstride = (int64_t)H * P * hd; pa.ctx = P; pa.B = n_sets; pa.C = P; pa.Cn = P; pa.t0 = 0;
+      pa.Hq = H; pa.Hkv = H; pa.hd = hd; pa.o_hi = at(E->ah); pa.o_lo = at(E->al); pa.o_dtype = wdt; pa.full = true;
+      HIPCHK(ctx, wd::launch_pf_attn(pa, s), "wd_encode: attention");
+      WDCHK(gemm(at(L.wo), d, d, at(E->ah), at(E->al), R, wd::FG_RESID, atf(E->x), atf(L.bo), nullptr, nullptr,
+                 nullptr, "wd_encode: out projection"));
+      HIPCHK(ctx, wd::launch_norm_split(atf(E->x), at(E->ah), at(E->al), wdt, atf(L.ln2g), atf(L.ln2b), R, d,
+                                        g.norm_eps, s), "wd_encode: ln2");
+      WDCHK(gemm(at(L.w1), E->dff, d, at(E->ah), at(E->al), R, wd::FG_GELU_SPLIT, nullptr, atf(L.b1), nullptr,
+                 at(E->hh), at(E->hl), "wd_encode: fc1"));
+      WDCHK(gemm(at(L.w2), d, E->dff, at(E->hh), at(E->hl), R, wd::FG_RESID, atf(E->x), atf(L.b2), nullptr, nullptr,
+                 nullptr, "wd_encode: fc2"));
+    }
+#undef WDCHK
+    HIPCHK(ctx, wd::launch_norm(atf(E->x), atf(E->qkv), atf(E->lnpg), atf(E->lnpb), R, d, g.norm_eps, s),
+           "wd_encode: final norm");
+    HIPCHK(ctx, wd::launch_cast(atf(E->qkv), enc, wdt, (int64_t)R * d, s), "wd_encode: output");
+    return WD_OK;
+  } catch (...) {
+    return fail(ctx, WD_ERR_INTERNAL, "wd_encode: internal error");
+  }
+}
+
 wd_status wd_topk(wd_ctx* ctx, const float* logits, int32_t B, int32_t W, float* top_val, int32_t* top_id,
                   float* lse) {
   if (!ctx) return WD_ERR_ARG;
@@ -1201,6 +1418,7 @@ const char* wd_last_error(const wd_ctx* ctx) {
 void wd_free(wd_ctx* ctx) {
   if (!ctx) return;
   for (auto& e : ctx->graphs) (void)hipGraphExecDestroy(e.exec);
+  delete ctx->enc;
   for (auto& pr : ctx->prof) {
     (void)hipEventDestroy(pr.a);
     (void)hipEventDestroy(pr.b);

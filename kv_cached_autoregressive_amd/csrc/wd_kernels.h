@@ -170,13 +170,17 @@ hipError_t launch_pf_embed(float* x, int32_t* pos, const void* E, int w_dtype, c
                            const void* emb, int A, int offset, int t0, int B, int C, int Cn, int d, int V,
                            unsigned* err, hipStream_t s);
 // Dense GEMM over fragment-layout operands: C[R, N] = (Ahi + Alo)[R, K] . W[N, K]^T.
-enum FgEpi : int { FG_STORE = 0, FG_RESID = 1, FG_SWIGLU = 2 };
+enum FgEpi : int { FG_STORE = 0, FG_RESID = 1, FG_SWIGLU = 2, FG_GELU = 3, FG_GELU_SPLIT = 4 };
 struct FgParams {
   const void* W; int w_dtype; int N; int K;   // W fragment layout (N % 128 == 0)
   const void* Ahi; const void* Alo; int R;    // A fragment layout [R rounded up to 128, K]
   int epi;
   float* out; int ldo;                        // STORE: out = C; RESID: out += C (fp32 [R, ldo])
+                                              // GELU: out = GELU(C) + pos[r % pos_rows] (pos optional)
   void* Ohi; void* Olo;                       // SWIGLU: silu(gate) * up, fragment layout [R_pad, N/2]
+                                              // GELU_SPLIT: GELU(C), fragment layout [R_pad, N]
+  const float* bias;                          // optional [N], added to C first (STORE, RESID, GELU*)
+  const float* pos; int pos_rows;             // GELU: optional [pos_rows, N] added after the GELU
 };
 hipError_t launch_fgemm(const FgParams& p, hipStream_t s);
 // Causal attention of a chunk's rows over cache rows 0..t of their stream (GQA).
@@ -185,8 +189,25 @@ struct PfAttnParams {
   const void* K; const void* V; int cache_dtype; int64_t kv_bstride; int ctx;   // [B][Hkv][ctx][hd]
   int B; int C; int Cn; int t0; int Hq; int Hkv; int hd;
   void* o_hi; void* o_lo; int o_dtype;        // split fragment layout [B*C rounded up, Hq*hd]
+  bool full;                                  // every query attends to all rows 0..t0+Cn-1 (no mask)
 };
 hipError_t launch_pf_attn(const PfAttnParams& p, hipStream_t s);
+
+// ---- audio encoder (stem and layer glue) ------------------------------------------------------
+// Windows of a kernel-3, pad-1 convolution as the split A operand of the dense GEMM: row
+// r = b * Lout + o, column c * 3 + k = x[b][o * stride + k - 1][c] (0 outside [0, L)), columns
+// >= 3 C zero; x [nb, L, C] in x_dtype (f32, f16 or bf16); A fragment layout [rows, Kp].
+hipError_t launch_conv_windows(const void* x, int x_dtype, int nb, int L, int C, int stride, int Lout, int Kp,
+                               void* a_hi, void* a_lo, int a_dtype, hipStream_t s);
+// Row-major [rows, Ks] (any wd dtype) -> fragment layout [rows, Kp] (Kp >= Ks, columns >= Ks zero).
+hipError_t launch_pack_pad(const void* src, int src_dtype, int64_t rows, int Ks, void* dst, int dst_dtype, int Kp,
+                           hipStream_t s);
+// q|k|v rows [nb * P, 3 d] fp32 -> q [nb * P, d] fp32 ((q + bq) * qscale), K and V [nb][H][P][hd]
+// in kv_dtype (K as is, V + bv).
+hipError_t launch_enc_qkv(const float* qkv, const float* bq, const float* bv, int nb, int P, int H, int hd,
+                          float qscale, float* q, void* K, void* V, int kv_dtype, hipStream_t s);
+// fp32 [n] -> dtype [n]
+hipError_t launch_cast(const float* x, void* y, int y_dtype, int64_t n, hipStream_t s);
 
 // ---- beam reorder: cache-row gather -----------------------------------------------------------
 struct BeamIdx { int32_t v[64]; };
