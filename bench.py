@@ -248,6 +248,65 @@ def run_qwen(args, w):
     print(json.dumps(out), flush=True)
 
 
+def run_encoder(args, w):
+    """The audio encoder of one window: every encoder set's 3000 synthetic mel frames through
+    the stem and the encoder layers to its 1500 states (wd_encode), with seeded random-init
+    weights generated on the device.  value = encoder states per second."""
+    import torch
+
+    import kv_cached_autoregressive_amd as K
+    dev = torch.device("cuda:0")
+    layers = args.encoder_layers or w.layers
+    mels, frames, d, ff, n = args.mels, 2 * w.frames, w.d, w.d_ff, w.n_enc
+    P = (frames - 1) // 2 + 1
+    wdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.w_dtype]
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed * 1000 + 17)
+    rnd = lambda *shape, std=0.02, mean=0.0: (torch.randn(*shape, generator=g, device=dev) * std + mean).to(wdt)
+    W = {"enc.conv1.w": rnd(d, mels, 3), "enc.conv1.b": rnd(d), "enc.conv2.w": rnd(d, d, 3), "enc.conv2.b": rnd(d),
+         "enc.pos": rnd(P, d, std=1.0), "enc.ln_post.g": rnd(d, mean=1.0), "enc.ln_post.b": rnd(d)}
+    for i in range(layers):
+        p = f"enc.{i}."
+        for ln in ("ln1", "ln2"):
+            W[p + ln + ".g"], W[p + ln + ".b"] = rnd(d, mean=1.0), rnd(d)
+        for proj in ("q", "k", "v", "o"):
+            W[p + f"attn.{proj}.w"] = rnd(d, d)
+            if proj != "k":
+                W[p + f"attn.{proj}.b"] = rnd(d)
+        W[p + "fc1.w"], W[p + "fc1.b"], W[p + "fc2.w"], W[p + "fc2.b"] = rnd(ff, d), rnd(ff), rnd(d, ff), rnd(d)
+    wr = WL.reduced(w, layers=1, vocab=1024)   # a decoder context to hold the encoder
+    dec = K.Decoder(wr, WL.make_weights(wr))
+    dec.load_encoder(W, mels, frames, layers, ff, max_sets=n)
+    del W
+    mel = torch.randn(n, frames, mels, generator=g, device=dev).to(wdt)
+    out = torch.empty(n, P, d, dtype=wdt, device=dev)
+    torch.cuda.synchronize()
+    torch.cuda.set_stream(dec.stream)
+    for _ in range(args.warmup):
+        dec.encode(mel, out)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(dec.stream)
+    for _ in range(args.steps):
+        dec.encode(mel, out)
+    t1.record(dec.stream)
+    torch.cuda.synchronize()
+    if dec.check() != 0:
+        raise RuntimeError(dec.last_error())
+    ms = t0.elapsed_time(t1) / args.steps
+    # algorithmic flops: the two convolutions and, per layer, q|k|v, the attention, o, fc1, fc2
+    per_set = 2 * frames * 3 * mels * d + 2 * P * 3 * d * d + \
+        layers * (2 * P * d * 3 * d + 4 * P * P * d + 2 * P * d * d + 4 * P * d * ff)
+    print(json.dumps({
+        "metric": "encoder states/sec (audio encoder, one window of every encoder set)",
+        "value": n * P / (ms / 1e3), "unit": "states/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "dtype": w.w_dtype,
+        "data": "synthetic (seeded random-init weights N(0,0.02), mel N(0,1))",
+        "config": {"workload": w.name + " encoder", "sets": n, "mel_frames": frames, "states": P, "mels": mels,
+                   "layers": layers, "d": d, "heads": w.heads, "d_ff": ff},
+        "tflops": n * per_set / (ms / 1e3) / 1e12}), flush=True)
+
+
 def cpu_baseline(w, budget_s: float):
     """The oracle as it is, on the host cores: one stream of the workload, its
     cross K/V and as many decode steps as fit the time budget."""
@@ -295,6 +354,10 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the cross-attention traffic summary under profiles/ from two --pmc runs and exit")
     ap.add_argument("--commands", nargs="*", default=[], help="the profiler commands, recorded in the summary")
+    ap.add_argument("--encoder", action="store_true",
+                    help="time the audio encoder (wd_encode) of the workload's encoder sets instead of the decoder")
+    ap.add_argument("--encoder-layers", type=int, default=0, help="encoder layers (default: the decoder's)")
+    ap.add_argument("--mels", type=int, default=80, help="mel channels of the encoder's input")
     args = ap.parse_args()
     if args.summarize_traffic:
         out = summarize_traffic(*args.summarize_traffic, args.commands)
@@ -320,6 +383,9 @@ def main():
     torch.cuda.set_device(dev)
     if w.arch == "qwen3":
         run_qwen(args, w)
+        return
+    if args.encoder:
+        run_encoder(args, w)
         return
     if w.mode != "greedy":
         print(f"bench.py times greedy windows; {w.name} is a beam-search workload", file=sys.stderr)
