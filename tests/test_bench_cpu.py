@@ -1,0 +1,53 @@
+"""bench.py host logic on the CPU: the one-GPU refusal, the counter scaling of the traffic
+summary (on small fabricated counter files), and the algorithmic byte model's parts."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import workloads as WL  # noqa: E402
+
+pytestmark = pytest.mark.filterwarnings("ignore")
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def _counter_file(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for name, v in rows:
+            wr.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": v})
+
+
+def test_traffic_summary_scales_by_the_copy_probe(tmp_path):
+    attn = "void wd::k_attn<wd::bf16_t, 64, 1, true, 4>(wd::AttnParams)"
+    selfattn = "void wd::k_attn<wd::bf16_t, 64, 1, false, 4>(wd::AttnParams)"
+    copy_kib = bench.COPY_PROBE_BYTES / 1024
+    # the counter reads half of the copy's bytes for fetches and all of them for writes
+    _counter_file(tmp_path / "f.csv", "FETCH_SIZE", [(attn, 1000.0), (attn, 3000.0), (selfattn, 7.0),
+                                                     ("__amd_rocclr_copyBuffer", copy_kib / 2),
+                                                     ("__amd_rocclr_copyBuffer", 1.0)])
+    _counter_file(tmp_path / "w.csv", "WRITE_SIZE", [(attn, 10.0), (attn, 30.0),
+                                                     ("__amd_rocclr_copyBuffer", copy_kib)])
+    out = bench.summarize_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), ["cmd"])
+    assert out["dispatches"] == 2
+    assert out["fetch_scale"] == pytest.approx(0.5) and out["write_scale"] == pytest.approx(1.0)
+    assert out["hbm_fetch_bytes_per_launch"] == int(2000.0 * 1024 / 0.5)
+    assert out["hbm_write_bytes_per_launch"] == int(20.0 * 1024)
+    assert out["kernel_source_sha256"] == bench.attn_source_sha()
+
+
+def test_cross_attention_bytes_per_launch_large_v3():
+    w = WL.by_name("whisper_large_bf16_b64")
+    assert bench.cross_attn_bytes_per_launch(w) == 64 * 20 * 1500 * 64 * 2 * 2 == 491_520_000
