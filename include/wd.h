@@ -171,6 +171,11 @@ wd_status wd_load_encoder(wd_ctx* ctx, int32_t n_mels, int32_t frames, int32_t n
  * w_dtype -> enc dev [n_sets, P, d] in w_dtype, ready for wd_cross_kv(ctx, enc, P).
  * Asynchronous on the context's stream.  Errors: ARG, STATE (no encoder loaded), HIP. */
 wd_status wd_encode(wd_ctx* ctx, const void* mel, int32_t n_sets, void* enc);
+/* wd_encode of all n_enc sets into the encoder workspace, then wd_cross_kv of its P states:
+ * one window from mel frames to the cross caches (Nest whisper-tiny model page, README
+ * "Transcribing with caches", entry `listen`).  Needs an encoder
+ * loaded with max_sets == n_enc.  Errors: ARG, STATE, HIP. */
+wd_status wd_listen(wd_ctx* ctx, const void* mel);
 
 /* One decoder step for rows 0..B-1 (1 <= B <= max_batch).
  *   tokens    dev int32 [B]   token id per row (may alias `argmax` for

@@ -19,7 +19,7 @@ from typing import Dict, Iterable, Optional, Sequence
 __all__ = [
     "WdError", "WdConfig", "WdTensor", "lib", "lib_path", "declared_functions",
     "wd_abi_version", "wd_workspace_bytes", "wd_load", "wd_cross_kv", "wd_cross_kv_ragged", "wd_step", "wd_reorder",
-    "wd_topk", "wd_prefill", "wd_encoder_workspace_bytes", "wd_load_encoder", "wd_encode", "wd_check", "wd_last_error", "wd_free", "wd_profile", "wd_profile_read",
+    "wd_topk", "wd_prefill", "wd_encoder_workspace_bytes", "wd_load_encoder", "wd_encode", "wd_listen", "wd_check", "wd_last_error", "wd_free", "wd_profile", "wd_profile_read",
     "wd_debug_cache",
     "config_from", "Decoder", "DTYPES", "STATUS",
 ]
@@ -82,6 +82,7 @@ def lib():
             "wd_encoder_workspace_bytes": (sz, [vp, i32, i32, i32, i32, i32]),
             "wd_load_encoder": (i32, [vp, i32, i32, i32, i32, i32, ctypes.POINTER(WdTensor), i32, vp, sz]),
             "wd_encode": (i32, [vp, vp, i32, vp]),
+            "wd_listen": (i32, [vp, vp]),
             "wd_prefill": (i32, [vp, vp, i32, i32, vp, i32, i32, vp, vp]),
             "wd_check": (i32, [vp]),
             "wd_last_error": (ctypes.c_char_p, [vp]),
@@ -168,6 +169,10 @@ def wd_load_encoder(ctx, n_mels: int, frames: int, n_layers: int, d_ff: int, max
 
 def wd_encode(ctx, mel: int, n_sets: int, enc: int):
     _check(lib().wd_encode(ctx, ctypes.c_void_p(mel), n_sets, ctypes.c_void_p(enc)), ctx)
+
+
+def wd_listen(ctx, mel: int):
+    _check(lib().wd_listen(ctx, ctypes.c_void_p(mel)), ctx)
 
 
 def wd_prefill(ctx, tokens: int, B: int, T: int, embeds: int, A: int, offset: int, logits: int,
@@ -297,6 +302,14 @@ class Decoder:
         wd_encode(self.ctx, mel.data_ptr(), n, out.data_ptr())
         self._leave(cur)
         return out
+
+    def listen(self, mel):
+        """mel: device tensor [n_enc, frames, n_mels]; encodes and fills the cross caches."""
+        assert mel.shape[0] == self.w.n_enc and mel.is_contiguous()
+        assert mel.shape[1] == getattr(self, "enc_frames", mel.shape[1])
+        cur = self._enter()
+        wd_listen(self.ctx, mel.data_ptr())
+        self._leave(cur)
 
     def close(self):
         if getattr(self, "ctx", None):

@@ -266,6 +266,7 @@ struct EncPlan {
   // buffers: rows of the stem's first convolution (sets x frames) and of the layers (sets x P),
   // both rounded up to the GEMM's 128-row tiles
   size_t x1 = 0, x = 0, ah = 0, al = 0, hh = 0, hl = 0, qkv = 0, q = 0, K = 0, V = 0;
+  size_t states = 0;         // encoder states [max_sets, P, d] in w_dtype (wd_listen)
   size_t total = 0;
 };
 
@@ -298,6 +299,7 @@ EncPlan make_enc_plan(const wd_config& c, int mels, int frames, int layers, int 
   p.qkv = b.take(r * 3 * d * f4);
   p.q = b.take(r * d * f4);
   p.K = b.take((size_t)max_sets * p.P * d * wb); p.V = b.take((size_t)max_sets * p.P * d * wb);
+  p.states = b.take((size_t)max_sets * p.P * d * wb);
   p.total = (b.off + 255) & ~size_t(255);
   return p;
 }
@@ -1375,6 +1377,22 @@ wd_status wd_encode(wd_ctx* ctx, const void* mel, int32_t n_sets, void* enc) {
     return WD_OK;
   } catch (...) {
     return fail(ctx, WD_ERR_INTERNAL, "wd_encode: internal error");
+  }
+}
+
+wd_status wd_listen(wd_ctx* ctx, const void* mel) {
+  if (!ctx) return WD_ERR_ARG;
+  try {
+    const wd_config& g = ctx->cfg;
+    const EncPlan* E = ctx->enc;
+    if (!E) return fail(ctx, WD_ERR_STATE, "wd_listen: no encoder loaded (wd_load_encoder)");
+    if (E->max_sets != g.n_enc) return fail(ctx, WD_ERR_STATE, "wd_listen: the encoder's max_sets must equal n_enc");
+    void* states = ctx->enc_ws + E->states;
+    const wd_status st = wd_encode(ctx, mel, g.n_enc, states);
+    if (st != WD_OK) return st;
+    return wd_cross_kv(ctx, states, E->P);
+  } catch (...) {
+    return fail(ctx, WD_ERR_INTERNAL, "wd_listen: internal error");
   }
 }
 

@@ -110,6 +110,7 @@ def test_null_context_calls_return_arg():
     assert L.wd_cross_kv_ragged(None, None, None) == 1
     assert L.wd_topk(None, None, 1, 1, None, None, None) == 1
     assert L.wd_encode(None, None, 1, None) == 1
+    assert L.wd_listen(None, None) == 1
     assert L.wd_load_encoder(None, 80, 3000, 1, 128, 1, None, 0, None, 0) == 1
     assert L.wd_encoder_workspace_bytes(None, 80, 3000, 1, 128, 1) == 0
     assert L.wd_reorder(None, None, 1, 1) == 1

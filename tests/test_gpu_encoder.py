@@ -68,3 +68,36 @@ def test_encoder_3000_frames_two_sets(w_dtype):
     assert worst < 8 * unit * scale, worst
     assert G.check() == 0
     G.close()
+
+
+def test_listen_equals_encode_then_cross_kv():
+    """wd_listen is wd_encode of every set followed by wd_cross_kv of its states: the step
+    after it gives the same logits, bit for bit, as the step after the two separate calls
+    (each of those is checked against the oracle on its own).  Before an encoder is loaded
+    it is refused."""
+    need_gpu()
+    K = pytest.importorskip("kv_cached_autoregressive_amd")
+    base = WL.by_name("whisper_large_bf16_b64")
+    w = WL.reduced(base, layers=2, batch=4, n_enc=2, d=256, heads=4, kv_heads=4, d_ff=512, vocab=3001)
+    mels, frames, layers, d_ff = 80, 3000, 1, 1024
+    P = (frames - 1) // 2 + 1
+    say(f"[listen] d={w.d} mels={mels} frames={frames} layers={layers} sets={w.n_enc} batch={w.batch}")
+    W = _enc_weights(w.d, mels, layers, d_ff, P, w.w_dtype, seed=11)
+    td = torch_dtype(w.w_dtype)
+    mel = torch.from_numpy(np.random.default_rng(12).standard_normal((w.n_enc, frames, mels))).to(td).cuda()
+    G = GpuRun(w, WL.make_weights(w))
+    with pytest.raises(K.WdError):
+        G.dec.listen(mel)
+    G.dec.load_encoder(W, mels, frames, layers, d_ff, max_sets=w.n_enc)
+    toks = np.arange(w.batch) * 7 + 3
+    G.dec.listen(mel)
+    torch.cuda.synchronize()
+    lg1, am1 = G.step(toks, 0)
+    states = G.dec.encode(mel)
+    G.dec.cross_kv(states, P)
+    torch.cuda.synchronize()
+    lg2, am2 = G.step(toks, 0)
+    assert np.all(np.isfinite(lg1))
+    assert np.array_equal(lg1, lg2) and np.array_equal(am1, am2)
+    assert G.check() == 0
+    G.close()
