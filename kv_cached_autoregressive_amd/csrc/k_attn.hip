@@ -69,10 +69,10 @@ __device__ __forceinline__ void write_o(float* out, int out_ld, void* o_hi, void
   }
 }
 
-// One query per block (NQ == 1) is kept to <= 96 VGPRs: 5 waves per SIMD, so 5 blocks of 4
-// waves per CU and 1280 blocks (64 rows x 20 heads) resident at once, with no second
-// partial round.  With fewer slabs the blocks have NW = 8 waves (more rows in flight per
-// slab).  CROSS only separates the two uses into distinct kernels for profiling (the cross
+// One query per block (NQ == 1) is kept to <= 96 VGPRs: 5 waves per SIMD, so the self
+// attention's 1280 blocks of 4 waves (64 rows x 20 heads) are resident at once, with no
+// second partial round.  The cross attention, 1500 rows per slab, and any launch with fewer
+// slabs take NW = 8 waves (more rows in flight per slab).  CROSS only separates the two uses into distinct kernels for profiling (the cross
 // attention over the encoder frames has no positions; the self attention reads rows 0..pos).
 template <typename CT, int HD, int NQ, bool CROSS, int NW>
 __global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {

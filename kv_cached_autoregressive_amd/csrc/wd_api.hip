@@ -109,21 +109,24 @@ std::string check_config(const wd_config& c) {
 
 // Launch shape of an attention over `rows` cache rows of `slabs` K/V slabs (measured on the
 // three batched workloads):
-//  * >= 512 slabs: blocks of 4 waves, one per slab (5 resident per CU at <= 96 VGPRs);
+//  * >= 512 slabs: one block per slab, of 4 waves for the self-attention (5 resident per CU
+//    at <= 96 VGPRs) and of 8 for the cross-attention over all encoder frames (its 1500 rows
+//    per slab want more rows in flight: 74.8 against 76.0 us per large-v3 launch);
 //  * otherwise blocks of 8 waves and about 256 blocks in total, so a slab is split only
 //    below ~170 slabs (each split costs a combine launch, about 4 us): one split at the
 //    192 slabs of the whisper-small step, 4 splits of 256 rows at the 64 of the Qwen3 step;
 //  * splits of at least 64 rows, at most 64 splits (the combine's limit).
-// Tuning override for sweeps: WD_ATTN_ROWS="self_rows,cross_rows[,waves]" (0 keeps the
-// policy; waves 4 or 8 per block).
-int attn_rows_override(int which) {   // 0 self rows, 1 cross rows, 2 waves
-  static int v[3] = {0, 0, 0};
+// Tuning override for sweeps: WD_ATTN_ROWS="self_rows,cross_rows[,waves[,cross_waves]]" (0
+// keeps the policy; waves 4 or 8 per block, for both attentions unless cross_waves is given).
+int attn_rows_override(int which) {   // 0 self rows, 1 cross rows, 2 waves, 3 cross waves
+  static int v[4] = {0, 0, 0, 0};
   static bool read = false;
   if (!read) {
     read = true;
     if (const char* e = getenv("WD_ATTN_ROWS"))
-      if (sscanf(e, "%d,%d,%d", &v[0], &v[1], &v[2]) < 2) v[0] = v[1] = v[2] = 0;
+      if (sscanf(e, "%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3]) < 2) v[0] = v[1] = v[2] = v[3] = 0;
     if (v[2] != 4 && v[2] != 8) v[2] = 0;
+    if (v[3] != 4 && v[3] != 8) v[3] = v[2];
   }
   return v[which];
 }
@@ -140,8 +143,8 @@ void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits, int*
   r = std::max(r, 1);
   *split_rows = r;
   *n_splits = std::max(1, (rows + r - 1) / r);
-  *nw = wide ? 8 : 4;
-  if (const int o = attn_rows_override(2)) *nw = o;
+  *nw = (wide || cross) ? 8 : 4;
+  if (const int o = attn_rows_override(cross ? 3 : 2)) *nw = o;
 }
 
 // Rows per chunk of the batched prefill (streams x positions): they feed dense MFMA GEMMs;
