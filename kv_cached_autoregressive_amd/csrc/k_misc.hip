@@ -204,8 +204,10 @@ __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, float
 // sum_g part[g][row][:] (the G <= GMAX partial slabs of a split-K residual projection,
 // added in order g = 0..G-1, all loads in flight together) and the new x is written back.
 // Mean and mean square come from one block reduction; the output goes to the split
-// fragment layout (4 consecutive k are contiguous there).
-template <typename OT, int PASS, int GMAX>
+// fragment layout (4 consecutive k are contiguous there).  With SKIP (d not a multiple of
+// 1024) a wave whose 256 columns of pass j all lie past d loads nothing for that pass, and
+// every live pass's loads are issued before any is summed; the sums keep the same order.
+template <typename OT, int PASS, int GMAX, bool SKIP>
 __global__ __launch_bounds__(256) void k_norm4(float* __restrict__ x, OT* __restrict__ yh, OT* __restrict__ yl,
                                                const float* __restrict__ g, const float* __restrict__ bvec, int d,
                                                float eps, const float* __restrict__ part, int G, int B,
@@ -214,6 +216,41 @@ __global__ __launch_bounds__(256) void k_norm4(float* __restrict__ x, OT* __rest
   const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
   float* xr = x + (int64_t)row * d;
   float4 v[PASS], gv[PASS], bv[PASS];
+  if constexpr (SKIP) {
+    const int wcol = 4 * __builtin_amdgcn_readfirstlane(t & ~63);   // first column of this wave
+    constexpr int GL = GMAX > 0 ? GMAX : 1;
+    float4 pb[PASS], q[PASS][GL];
+#pragma unroll
+    for (int j = 0; j < PASS; ++j) {
+      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (wcol + 1024 * j < d) {   // uniform over the wave; lanes past d load the last chunk
+        const int c = min(4 * t + 1024 * j, d - 4);
+        v[j] = *reinterpret_cast<const float4*>(xr + c);
+        gv[j] = *reinterpret_cast<const float4*>(g + c);
+        bv[j] = bvec ? *reinterpret_cast<const float4*>(bvec + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (GMAX > 0) {
+          pb[j] = pbias ? *reinterpret_cast<const float4*>(pbias + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int k = 0; k < GMAX; ++k)
+            q[j][k] = __builtin_bit_cast(float4, __builtin_nontemporal_load(
+                reinterpret_cast<const nt4f*>(part + ((int64_t)min(k, G - 1) * B + row) * d + c)));
+        }
+      }
+    }
+    if constexpr (GMAX > 0) {
+#pragma unroll
+      for (int j = 0; j < PASS; ++j) {
+        if (wcol + 1024 * j < d) {   // x, then the bias, then the partials g = 0..G-1
+          float4 a = v[j];
+          if (pbias) { a.x += pb[j].x; a.y += pb[j].y; a.z += pb[j].z; a.w += pb[j].w; }
+#pragma unroll
+          for (int k = 0; k < GMAX; ++k)
+            if (k < G) { a.x += q[j][k].x; a.y += q[j][k].y; a.z += q[j][k].z; a.w += q[j][k].w; }
+          v[j] = a;
+        }
+      }
+    }
+  } else {
 #pragma unroll
   for (int j = 0; j < PASS; ++j) {   // loads clamped to the last chunk; chunks past d are not used
     const int c = min(4 * t + 1024 * j, d - 4);
@@ -235,6 +272,7 @@ __global__ __launch_bounds__(256) void k_norm4(float* __restrict__ x, OT* __rest
         if (k < G) { a.x += q[k].x; a.y += q[k].y; a.z += q[k].z; a.w += q[k].w; }
     }
     v[j] = a;
+  }
   }
   float s1 = 0.f, s2 = 0.f;
 #pragma unroll
@@ -368,8 +406,11 @@ static hipError_t norm4(float* x, void* yh, void* yl, const float* g, const floa
                         const float* part, int G, const float* pbias, hipStream_t s) {
   if (d > 4096 || (part && (G < 1 || G > 8))) return hipErrorInvalidValue;
   const int pass = (d + 1023) / 1024;
-#define WD_N4(P_, GM_) \
-  k_norm4<OT, P_, GM_><<<B, 256, 0, s>>>(x, (OT*)yh, (OT*)yl, g, b, d, eps, part, G, B, pbias)
+#define WD_N4(P_, GM_)                                                                                  \
+  do {                                                                                                   \
+    if (d % 1024) k_norm4<OT, P_, GM_, true><<<B, 256, 0, s>>>(x, (OT*)yh, (OT*)yl, g, b, d, eps, part, G, B, pbias); \
+    else k_norm4<OT, P_, GM_, false><<<B, 256, 0, s>>>(x, (OT*)yh, (OT*)yl, g, b, d, eps, part, G, B, pbias); \
+  } while (0)
 #define WD_N4P(P_) \
   if (!part) WD_N4(P_, 0); else WD_N4(P_, 8);
   if (pass == 1) { WD_N4P(1) } else if (pass == 2) { WD_N4P(2) } else { WD_N4P(4) }
