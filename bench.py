@@ -47,7 +47,8 @@ def attn_source_sha() -> str:
     for f in ATTN_SRC:
         h.update(open(f, "rb").read())
     return h.hexdigest()
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_cross_whisper_large_bf16_b64_traffic.json")
+TRAFFIC_WORKLOAD = "whisper_large_bf16_b64"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", f"k_attn_cross_{TRAFFIC_WORKLOAD}_traffic.json")
 
 
 def whisper_bytes_per_step(w, pos: int) -> int:
@@ -70,9 +71,12 @@ def cross_attn_bytes_per_launch(w) -> int:
     return w.n_enc * w.heads * w.frames * w.head_dim * 2 * DT_BYTES[w.cache_dtype]
 
 
-def traffic_per_launch():
+def traffic_per_launch(workload: str):
     """HBM bytes per cross-attention launch from the committed rocprofv3 counter
-    summary, or None when absent or taken on a different kernel source."""
+    summary, or None when absent, taken on a different kernel source, or taken on
+    another workload (the counters cover the large-v3 window only)."""
+    if workload != TRAFFIC_WORKLOAD:
+        return None
     try:
         t = json.load(open(TRAFFIC_FILE))
         if t.get("kernel_source_sha256") != attn_source_sha():
@@ -466,7 +470,7 @@ def main():
     attn_avg_s = attn_ms / 1e3 / max(attn_n, 1)
     achieved = attn_bytes / attn_avg_s
     xkv_flops = 2.0 * w.n_enc * w.frames * w.d * 2 * w.d * w.layers
-    traffic = traffic_per_launch()
+    traffic = traffic_per_launch(w.name)
     out = {
         "metric": "decoder tokens/sec at batch B; achieved HBM GB/s as % of MI355X peak",
         "value": tokens / (ms_window / 1e3),

@@ -51,3 +51,12 @@ def test_traffic_summary_scales_by_the_copy_probe(tmp_path):
 def test_cross_attention_bytes_per_launch_large_v3():
     w = WL.by_name("whisper_large_bf16_b64")
     assert bench.cross_attn_bytes_per_launch(w) == 64 * 20 * 1500 * 64 * 2 * 2 == 491_520_000
+
+
+def test_traffic_summary_applies_to_its_own_workload_only():
+    """The counter summary was taken on the large-v3 window's cross-attention; a
+    bench line of any other workload reports no traffic figure."""
+    assert bench.traffic_per_launch("whisper_small_f16_b16") is None
+    assert bench.traffic_per_launch("qwen3asr_bf16_b8") is None
+    t = bench.traffic_per_launch(bench.TRAFFIC_WORKLOAD)
+    assert t is None or t > 0
