@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define WD_ABI_VERSION 3
+#define WD_ABI_VERSION 4
 #define WD_MAX_BATCH 64
 
 typedef struct wd_ctx wd_ctx;
@@ -226,6 +226,20 @@ wd_status wd_prefill(wd_ctx* ctx, const int32_t* tokens, int32_t B, int32_t T,
                      const void* embeds, int32_t A, int32_t offset,
                      float* logits, int32_t* argmax);
 
+/* Run options of a context (wd_set_option / wd_get_option):
+ *   WD_OPT_GRAPHS  1 (default): each distinct step (output buffers, row count, current self
+ *                  cache, frame count) is captured once into a HIP graph and replayed, since
+ *                  positions and tokens live in device memory and the step's launches never
+ *                  change (the static-shape step-graph reuse of transcribe.cpp
+ *                  qwen3_asr/decoder.h, `build_step_graph` comment); 0: every kernel is
+ *                  launched eagerly, on every call.  Both run the same kernels in the same
+ *                  order and give bit-identical results.  A context on the null stream never
+ *                  captures.
+ * Errors: ARG (unknown option, value out of range, null value pointer). */
+typedef enum { WD_OPT_GRAPHS = 0 } wd_option;
+wd_status wd_set_option(wd_ctx* ctx, int32_t option, int32_t value);
+wd_status wd_get_option(wd_ctx* ctx, int32_t option, int32_t* value);
+
 /* Synchronises the stream, reads and clears the sticky device flag:
  * WD_OK, WD_ERR_RANGE (flag was set) or WD_ERR_HIP. */
 wd_status wd_check(wd_ctx* ctx);
@@ -234,7 +248,9 @@ wd_status wd_check(wd_ctx* ctx);
  * wd_load on this thread).  Valid until the next call on ctx. */
 const char* wd_last_error(const wd_ctx* ctx);
 
-/* Releases the host-side context (events); never touches caller memory. */
+/* Waits for the context's stream, then releases the host-side context (captured
+ * step graphs, events); never touches caller memory.  After it returns, the caller
+ * may free the workspace. */
 void wd_free(wd_ctx* ctx);
 
 /* --- measurement support ------------------------------------------------

@@ -20,7 +20,7 @@ __all__ = [
     "WdError", "WdConfig", "WdTensor", "lib", "lib_path", "declared_functions",
     "wd_abi_version", "wd_workspace_bytes", "wd_load", "wd_cross_kv", "wd_cross_kv_ragged", "wd_step", "wd_reorder",
     "wd_topk", "wd_prefill", "wd_encoder_workspace_bytes", "wd_load_encoder", "wd_encode", "wd_listen", "wd_check", "wd_last_error", "wd_free", "wd_profile", "wd_profile_read",
-    "wd_debug_cache",
+    "wd_debug_cache", "wd_set_option", "wd_get_option", "WD_OPT_GRAPHS",
     "config_from", "Decoder", "DTYPES", "STATUS",
 ]
 
@@ -33,6 +33,8 @@ STATUS = {0: "WD_OK", 1: "WD_ERR_ARG", 2: "WD_ERR_STATE", 3: "WD_ERR_RANGE", 4: 
           5: "WD_ERR_OOM", 6: "WD_ERR_INTERNAL"}
 # kernel classes for wd_profile
 K_CROSS_ATTN, K_SELF_ATTN, K_LOGITS, K_XKV_GEMM, K_FC1 = 0, 1, 2, 3, 4
+# context options (wd_set_option)
+WD_OPT_GRAPHS = 0
 
 
 class WdError(RuntimeError):
@@ -90,6 +92,8 @@ def lib():
             "wd_profile": (i32, [vp, i32, i32, i32]),
             "wd_profile_read": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
             "wd_debug_cache": (i32, [vp, i32, i32, ctypes.POINTER(vp)]),
+            "wd_set_option": (i32, [vp, i32, i32]),
+            "wd_get_option": (i32, [vp, i32, ctypes.POINTER(i32)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -213,6 +217,16 @@ def wd_debug_cache(ctx, which: int, layer: int) -> int:
     return p.value
 
 
+def wd_set_option(ctx, option: int, value: int):
+    _check(lib().wd_set_option(ctx, option, value), ctx)
+
+
+def wd_get_option(ctx, option: int) -> int:
+    v = ctypes.c_int32()
+    _check(lib().wd_get_option(ctx, option, ctypes.byref(v)), ctx)
+    return v.value
+
+
 # ---- convenience: config and a torch-backed holder -------------------------------------------
 
 def config_from(w, max_batch: Optional[int] = None) -> WdConfig:
@@ -312,7 +326,10 @@ class Decoder:
         self._leave(cur)
 
     def close(self):
+        """Frees the context (wd_free waits for its stream first); the workspace is
+        released only after that, when this object goes away."""
         if getattr(self, "ctx", None):
+            self.stream.synchronize()
             wd_free(self.ctx)
             self.ctx = None
 
@@ -393,6 +410,10 @@ class Decoder:
 
     def check(self) -> int:
         return wd_check(self.ctx)
+
+    def set_graphs(self, on: bool):
+        """Step graphs on (capture once, replay) or off (eager launches)."""
+        wd_set_option(self.ctx, WD_OPT_GRAPHS, 1 if on else 0)
 
     def cache(self, which: int, layer: int):
         """A torch view of one cache block (test hook): which 0/1 self K/V

@@ -293,13 +293,9 @@ hipError_t launch_cross_kv_gemm(const void* X, const void* W, const float* bias,
   // 256-row blocks with LDS-shared operands once they fill the chip twice over (large-v3: 7500
   // blocks, 902 -> 704 us per layer; whisper-small 1128, 84.6 -> 81.0 us), else 128-row blocks
   // (whisper-base, one encoder set: 48 blocks of 256 rows took 17.4 us against 13.5 us).
-  // Tuning override: WD_XKV_LDS=0|1.
-  static int force = -2;
-  if (force == -2) { const char* e = getenv("WD_XKV_LDS"); force = e ? (atoi(e) != 0) : -1; }
-  const bool lds = force >= 0 ? force == 1 : (int64_t)((M + 255) / 256) * (2 * d / 128) >= 512;
+  const bool lds = (int64_t)((M + 255) / 256) * (2 * d / 128) >= 512;
   if (lds) {
-    static int pg = -1;   // row panels per L2 group (tuning override WD_XKV_PG)
-    if (pg < 0) { const char* e = getenv("WD_XKV_PG"); pg = e ? std::max(1, std::min(16, atoi(e))) : 4; }
+    constexpr int pg = 4;   // row panels per L2 group
     const int n_mt = (M + 255) / 256, n_nt = 2 * d / 128;
     const int per_xcd = ((n_mt + 7) / 8 + pg - 1) / pg * pg;   // panels per XCD, whole groups
     const dim3 grid(8 * per_xcd * n_nt);

@@ -656,32 +656,21 @@ hipError_t mrun_f16(const MGemvParams& p, hipStream_t st);
 // Split-K shape: 4 waves per workgroup, NBW = 2 (128 outputs) for the wide or deep
 // projections; S K steps per group so that ~256 workgroups cover the shape (2 <= S <= 8),
 // G = ceil(K steps / S), and the LDS chunk is 4 or 8 steps (no padded steps for S <= 4).
-// Tuning overrides: WD_MGEMV_SK=0 disables the variant; WD_MGEMV_SKS=<S> forces S.
 static bool sk_pick(int N, int K, int B, int epi, SkShape& s) {
-  static int mode = -1, forces = 0, forcew = 0;
-  if (mode < 0) {
-    const char* e = getenv("WD_MGEMV_SK");
-    mode = e ? atoi(e) : 1;
-    const char* f = getenv("WD_MGEMV_SKS");
-    forces = f ? atoi(f) : 0;
-    const char* w = getenv("WD_MGEMV_SKW");
-    forcew = w ? atoi(w) : 0;
-  }
-  if (!mode || epi == EPI_LOGITS) return false;
+  if (epi == EPI_LOGITS) return false;
   const int NB = (N + 15) / 16, KST = K / 32;
   s.NBB = B <= 16 ? 1 : B <= 32 ? 2 : 4;
+  // (SwiGLU's in-kernel epilogue needs gate and up in one wave: NBW = 2)
   s.NBW = (NB >= 256 || KST >= 128 || epi == EPI_SWIGLU_SPLIT) ? 2 : 1;
-  // (SwiGLU's in-kernel epilogue needs gate and up in one wave: NBW = 1 only with K groups)
-  if ((forcew == 1 && (epi != EPI_SWIGLU_SPLIT || KST > 8)) || forcew == 2) s.NBW = forcew;
   // up to 16 rows and at least 8 MB of 16-bit weights: 16-column tiles and K groups of up to
   // 16 steps (half the partial slabs of 8-step groups; measured 14.4 -> 13.3 us on the Qwen3
   // gate|up, 4.7% on its step)
-  const bool narrow = s.NBB == 1 && !forcew && (epi != EPI_SWIGLU_SPLIT || KST > 16) &&
+  const bool narrow = s.NBB == 1 && (epi != EPI_SWIGLU_SPLIT || KST > 16) &&
                       (int64_t)KST * ((NB + 3) / 4) >= 8 * 256;
   if (narrow) s.NBW = 1;
   int ncg = (NB + 4 * s.NBW - 1) / (4 * s.NBW);
-  int S = forces > 0 ? forces : (KST * ncg + 255) / 256;
-  S = std::max(2, std::min(S, (narrow || forces > 8) && s.NBB == 1 ? 16 : 8));
+  int S = (KST * ncg + 255) / 256;
+  S = std::max(2, std::min(S, narrow ? 16 : 8));
   int G = (KST + S - 1) / S;
   if (narrow) {
     if (G > 32) return false;
@@ -690,7 +679,7 @@ static bool sk_pick(int N, int K, int B, int epi, SkShape& s) {
     if (s.NSC > 8) s.NSC = 16;   // instantiated: 4..8 and 16 (steps past a group's end are padding)
     return true;
   }
-  if (ncg * G > 256 && s.NBW == 1 && !forces && !forcew) {   // past one workgroup per CU: wider column groups
+  if (ncg * G > 256 && s.NBW == 1) {   // past one workgroup per CU: wider column groups
     s.NBW = 2;
     ncg = (NB + 7) / 8;
     S = std::max(2, std::min((KST * ncg + 255) / 256, 8));
@@ -698,7 +687,7 @@ static bool sk_pick(int N, int K, int B, int epi, SkShape& s) {
   }
   // narrow outputs (N <= 2048): every XCD would fetch all the activations, which weigh as
   // much as the partials; with G a multiple of 8 each XCD fetches one K eighth of them
-  if (N <= 2048 && KST >= 16 && !forces) G = 8 * ((KST + 63) / 64);
+  if (N <= 2048 && KST >= 16) G = 8 * ((KST + 63) / 64);
   if (G > 32) return false;             // the consumers add at most 32 partial slabs
   s.G = G;
   s.NSC = std::max(4, (KST + G - 1) / G);   // the longest group's steps (4..8): at most one padded step
@@ -712,14 +701,6 @@ int mgemv_groups(int N, int K, int B, int epi) {
 }
 #endif  // WD_MG_MAIN
 
-// K slices per column tile inside a split-K workgroup (1: 4 waves, 2: 8 waves).
-// Tuning override: WD_MGEMV_SKK=1|2.
-static int sk_slices() {
-  static int ks = -1;
-  if (ks < 0) { const char* e = getenv("WD_MGEMV_SKK"); ks = e ? atoi(e) : 1; if (ks != 2) ks = 1; }
-  return ks;
-}
-
 template <typename T>
 static hipError_t skrun(const MGemvParams& p0, const SkShape& s, hipStream_t st) {
   const int NB = (p0.N + 15) / 16;
@@ -728,11 +709,9 @@ static hipError_t skrun(const MGemvParams& p0, const SkShape& s, hipStream_t st)
   MGemvParams p = p0;
   p.part_G = s.G;
   const dim3 grid(ncg * s.G);
-  const int KS = sk_slices();
 #define WD_SK(NBW_, NBB_, NSC_)                                                  \
   if (s.NBW == NBW_ && s.NBB == NBB_ && s.NSC == NSC_) {                         \
-    if (KS == 2) k_mgemv_sk<T, NBW_, NBB_, NSC_, 2><<<grid, 512, 0, st>>>(p);   \
-    else k_mgemv_sk<T, NBW_, NBB_, NSC_, 1><<<grid, 256, 0, st>>>(p);            \
+    k_mgemv_sk<T, NBW_, NBB_, NSC_, 1><<<grid, 256, 0, st>>>(p);                 \
     return hipGetLastError();                                                    \
   }
 #define WD_SK_S(S_) WD_SK(1, 1, S_) WD_SK(2, 1, S_) WD_SK(1, 2, S_) WD_SK(2, 2, S_) WD_SK(1, 4, S_) WD_SK(2, 4, S_)
@@ -766,22 +745,6 @@ struct MShape { int NBW, NBB, KS; };
 // Shape per projection: enough waves in flight for a weight stream of a few MB, K split
 // over the waves of a workgroup so each walks at most ~10 K steps, and several 16-row
 // blocks per wave where N is large (fewer activation re-reads per weight byte).
-// Tuning override for shape sweeps: WD_MGEMV_SHAPE="nbw,ks" (read once; ignored if invalid).
-static bool shape_override(MShape& s) {
-  static int nbw = -1, ks = -1;
-  static bool read = false;
-  if (!read) {
-    read = true;
-    if (const char* e = getenv("WD_MGEMV_SHAPE")) {
-      if (sscanf(e, "%d,%d", &nbw, &ks) != 2) nbw = ks = -1;
-    }
-  }
-  if (nbw < 0) return false;
-  s.NBW = nbw;
-  s.KS = ks;
-  return true;
-}
-
 static MShape mpick(int N, int K, int B, int epi) {
   MShape s;
   s.NBB = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
@@ -797,10 +760,6 @@ static MShape mpick(int N, int K, int B, int epi) {
     s.KS = ksteps >= 96 ? 16 : (ksteps >= 32 ? 8 : 4);
     if (s.NBB == 4 && s.KS > 8) s.KS = 8;   // 16 waves x 64-wide tiles would spill
   }
-  if (epi != EPI_LOGITS) {
-    MShape o = s;
-    if (shape_override(o) && !(epi == EPI_SWIGLU_SPLIT && o.NBW % 2)) s = o;
-  }
   if (s.KS > ksteps) { s.NBW = 2; s.KS = 1; }   // every wave needs at least one K step
   return s;
 }
@@ -811,16 +770,7 @@ static LShape lpick(int N, int K, int epi);
 static int lds_blocks(const LShape& s, int N);
 // The LDS-shared variant pays off where many waves re-read the same activation
 // tiles: the large-N shapes (the tied head) at B > 16.
-static bool use_lds(int N, int NBB) {
-  static int force = -1;
-  static bool read = false;
-  if (!read) {
-    read = true;
-    if (const char* e = getenv("WD_MGEMV_LDS")) force = atoi(e) > 0 ? 1 : 0;
-  }
-  if (force == 1 && getenv("WD_MGEMV_LDS")[0] != '0') return NBB > 1;
-  return NBB > 1 && (N + 15) / 16 >= 1024;
-}
+static bool use_lds(int N, int NBB) { return NBB > 1 && (N + 15) / 16 >= 1024; }
 #ifdef WD_MG_MAIN
 int mgemv_blocks_k(int N, int K, int B) {
   const MShape s = mpick(N, K, B, EPI_LOGITS);
@@ -857,19 +807,11 @@ static hipError_t mrun_b(const MGemvParams& p, const MShape& s, hipStream_t st) 
 // Shapes of the LDS-shared variant (B > 16): NBW rows-blocks per wave, KS K groups,
 // RT waves sharing each group's activation tiles.
 static LShape lpick(int N, int K, int epi) {
-  static int ov[3] = {-1, -1, -1};
-  static bool read = false;
-  if (!read) {
-    read = true;
-    if (const char* e = getenv("WD_MGEMV_LDS"))
-      if (sscanf(e, "%d,%d,%d", &ov[0], &ov[1], &ov[2]) != 3) ov[0] = -1;
-  }
   const int nblocks = (N + 15) / 16;
   LShape s;
   if (nblocks >= 1024) s = {2, 1, 4};
   else if (nblocks >= 128 || epi == EPI_SWIGLU_SPLIT) s = {2, 4, 2};
   else s = {1, 8, 2};
-  if (ov[0] > 0 && epi != EPI_LOGITS && !(epi == EPI_SWIGLU_SPLIT && ov[0] % 2)) s = {ov[0], ov[1], ov[2]};
   if (s.KS > K / 32) s = {2, 1, 4};   // every K group needs at least one step
   return s;
 }
@@ -893,10 +835,8 @@ static hipError_t lrun(const MGemvParams& p, const LShape& s, hipStream_t st) {
 // an exact split (or B in 17..32) take the ring kernel.
 struct PShape { int NBW, NBB, KS, NS; };
 static bool pf_pick(int N, int K, int B, int epi, PShape& s) {
-  static int mode = -1;
-  if (mode < 0) { const char* e = getenv("WD_MGEMV_PF"); mode = e ? atoi(e) : 1; }
   const int nblocks = (N + 15) / 16, kst = K / 32;
-  if (!mode || nblocks >= 1024) return false;
+  if (nblocks >= 1024) return false;
   s.NBB = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
   if (s.NBB == 2) return false;
   s.NBW = (nblocks >= 128 || epi == EPI_SWIGLU_SPLIT) ? 2 : 1;

@@ -203,8 +203,10 @@ __global__ __launch_bounds__(256) void k_norm(const float* __restrict__ x, float
 // and pass (PASS passes of 1024 columns; d % 32 == 0).  With GMAX > 0, first x += pbias +
 // sum_g part[g][row][:] (the G <= GMAX partial slabs of a split-K residual projection,
 // added in order g = 0..G-1, all loads in flight together) and the new x is written back.
-// Mean and mean square come from one block reduction; the output goes to the split
-// fragment layout (4 consecutive k are contiguous there).  With SKIP (d not a multiple of
+// The row stays in registers: the mean comes from a first block reduction and the variance
+// from a second one over the centred values (no cancellation when the mean is large against
+// the spread).  The output goes to the split fragment layout (4 consecutive k are
+// contiguous there).  With SKIP (d not a multiple of
 // 1024) a wave whose 256 columns of pass j all lie past d loads nothing for that pass, and
 // every live pass's loads are issued before any is summed; the sums keep the same order.
 template <typename OT, int PASS, int GMAX, bool SKIP>
@@ -274,24 +276,31 @@ __global__ __launch_bounds__(256) void k_norm4(float* __restrict__ x, OT* __rest
     v[j] = a;
   }
   }
-  float s1 = 0.f, s2 = 0.f;
+  float mean = 0.f;   // LayerNorm (bvec given), or RMSNorm without bias (mean 0)
+  if (bvec) {
+    float s1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < PASS; ++j)
+      if (4 * t + 1024 * j < d) s1 += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+    s1 = wave_sum(s1);
+    if (lane == 0) red[0][w] = s1;
+    __syncthreads();
+    mean = ((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) / (float)d;
+  }
+  float s2 = 0.f;
 #pragma unroll
   for (int j = 0; j < PASS; ++j) {
     const int c = 4 * t + 1024 * j;
     if (c < d) {
       if constexpr (GMAX > 0) *reinterpret_cast<float4*>(xr + c) = v[j];
-      s1 += (v[j].x + v[j].y) + (v[j].z + v[j].w);
-      s2 += (v[j].x * v[j].x + v[j].y * v[j].y) + (v[j].z * v[j].z + v[j].w * v[j].w);
+      const float a = v[j].x - mean, b = v[j].y - mean, e = v[j].z - mean, f = v[j].w - mean;
+      s2 += (a * a + b * b) + (e * e + f * f);
     }
   }
-  s1 = wave_sum(s1);
   s2 = wave_sum(s2);
-  if (lane == 0) { red[0][w] = s1; red[1][w] = s2; }
+  if (lane == 0) red[1][w] = s2;
   __syncthreads();
-  s1 = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
-  s2 = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
-  const float mean = bvec ? s1 / (float)d : 0.f;                     // LayerNorm, or RMSNorm without bias
-  const float var = fmaxf(s2 / (float)d - mean * mean, 0.f);
+  const float var = ((red[1][0] + red[1][1]) + (red[1][2] + red[1][3])) / (float)d;
   const float rs = 1.0f / sqrtf(var + eps);
 #pragma unroll
   for (int j = 0; j < PASS; ++j) {

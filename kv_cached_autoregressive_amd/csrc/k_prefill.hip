@@ -246,12 +246,9 @@ hipError_t launch_fgemm(const FgParams& p, hipStream_t s) {
   // 128-row blocks unless they leave CUs idle (then 64-row blocks; A is padded to 128 rows)
   const bool wide = (int64_t)((p.R + 127) / 128) * (p.N / 128) >= 256;
   const dim3 grid(wide ? (p.R + 127) / 128 : (p.R + 63) / 64, p.N / 128);
-  // 128-row blocks: operands staged through LDS unless WD_FGEMM_LDS=0 (tuning override)
-  static int lds = -1;
-  if (lds < 0) { const char* e = getenv("WD_FGEMM_LDS"); lds = e ? atoi(e) != 0 : 1; }
+  // 128-row blocks stage their operands through LDS
 #define WD_FG1(T_, E_)                                                                                   \
-  if (wide && lds) k_fgemm_lds<T_, E_><<<grid, 256, 0, s>>>(p);                                          \
-  else if (wide) k_fgemm<T_, E_, 4><<<grid, 256, 0, s>>>(p);                                             \
+  if (wide) k_fgemm_lds<T_, E_><<<grid, 256, 0, s>>>(p);                                                 \
   else k_fgemm<T_, E_, 2><<<grid, 256, 0, s>>>(p);
 #define WD_FG(T_)                                                                                        \
   switch (p.epi) {                                                                                       \

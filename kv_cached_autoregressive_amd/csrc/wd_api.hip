@@ -116,35 +116,18 @@ std::string check_config(const wd_config& c) {
 //    below ~170 slabs (each split costs a combine launch, about 4 us): one split at the
 //    192 slabs of the whisper-small step, 4 splits of 256 rows at the 64 of the Qwen3 step;
 //  * splits of at least 64 rows, at most 64 splits (the combine's limit).
-// Tuning override for sweeps: WD_ATTN_ROWS="self_rows,cross_rows[,waves[,cross_waves]]" (0
-// keeps the policy; waves 4 or 8 per block, for both attentions unless cross_waves is given).
-int attn_rows_override(int which) {   // 0 self rows, 1 cross rows, 2 waves, 3 cross waves
-  static int v[4] = {0, 0, 0, 0};
-  static bool read = false;
-  if (!read) {
-    read = true;
-    if (const char* e = getenv("WD_ATTN_ROWS"))
-      if (sscanf(e, "%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3]) < 2) v[0] = v[1] = v[2] = v[3] = 0;
-    if (v[2] != 4 && v[2] != 8) v[2] = 0;
-    if (v[3] != 4 && v[3] != 8) v[3] = v[2];
-  }
-  return v[which];
-}
-
 void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits, int* nw, bool cross = false) {
   const bool wide = slabs < 512;
   const int want = wide ? std::max(1, (256 + slabs / 2) / slabs) : 1;
   int r = (rows + want - 1) / want;
   r = std::max(r, (rows + 63) / 64);   // at most 64 splits (the combine's limit)
   r = std::max(r, 64);
-  if (const int o = attn_rows_override(cross ? 1 : 0)) r = std::max(o, (rows + 63) / 64);
   r = (r + 31) & ~31;
   r = std::min(r, std::max(12288 / std::max(nq, 1), (rows + 63) / 64));
   r = std::max(r, 1);
   *split_rows = r;
   *n_splits = std::max(1, (rows + r - 1) / r);
   *nw = (wide || cross) ? 8 : 4;
-  if (const int o = attn_rows_override(cross ? 3 : 2)) *nw = o;
 }
 
 // Rows per chunk of the batched prefill (streams x positions): they feed dense MFMA GEMMs;
@@ -154,15 +137,6 @@ void split_for(int rows, int slabs, int nq, int* split_rows, int* n_splits, int*
 constexpr int PF_ROWS = 4096, PF_MAX_POS = 512;
 int pf_positions(int max_batch) {
   return std::max(16, std::min(PF_MAX_POS, PF_ROWS / max_batch / 16 * 16));
-}
-// positions per chunk: the plan's, or fewer with WD_PF_CHUNK (sweeps)
-int pf_chunk(int plan_positions) {
-  static int v = -1;
-  if (v < 0) {
-    v = 0;
-    if (const char* e = getenv("WD_PF_CHUNK")) v = atoi(e) / 16 * 16;
-  }
-  return v >= 16 && v <= plan_positions ? v : plan_positions;
 }
 
 Plan make_plan(const wd_config& c) {
@@ -347,8 +321,8 @@ struct wd_ctx {
   EncPlan* enc = nullptr;    // the audio encoder, once wd_load_encoder ran
   char* enc_ws = nullptr;
   std::string err;
-  // captured steps (small cache, oldest evicted first); off when WD_GRAPHS=0, while
-  // profiling, or on the legacy null stream
+  // captured steps (small cache, least recently used evicted first); off with
+  // wd_set_option(WD_OPT_GRAPHS, 0), while profiling, or on the legacy null stream
   bool use_graphs = true;
   std::vector<GraphEntry> graphs;
   // measurement
@@ -844,7 +818,6 @@ wd_status wd_load(const wd_config* cfg, const wd_tensor* weights, int32_t n_weig
     c->plan = plan;
     c->stream = reinterpret_cast<hipStream_t>(stream);
     c->ws = reinterpret_cast<char*>(workspace);
-    if (const char* g = getenv("WD_GRAPHS")) c->use_graphs = atoi(g) != 0;
     hipStream_t s = c->stream;
     const int wdt = cfg->w_dtype;
     auto T = [&](const std::string& nm) { return byname[nm]; };
@@ -1027,9 +1000,12 @@ static wd_status staged_step(wd_ctx* ctx, int32_t B, float* logits, int32_t* arg
   if (!ctx->use_graphs || ctx->prof_kernel >= 0 || ctx->stream == nullptr)
     return run_step(ctx, tok, 1, pos, ovp, ovs, B, logits, argmax, head);
   const GraphKey key{logits, argmax, B, ctx->cur, ctx->frames, head ? 0 : (ov ? 2 : 1), ctx->ragged};
-  for (auto& e : ctx->graphs)
-    if (e.key == key) {
-      HIPCHK(ctx, hipGraphLaunch(e.exec, ctx->stream), "step: graph launch");
+  for (size_t i = 0; i < ctx->graphs.size(); ++i)
+    if (ctx->graphs[i].key == key) {   // least recently used order: a hit moves to the back
+      const GraphEntry hit = ctx->graphs[i];
+      ctx->graphs.erase(ctx->graphs.begin() + (ptrdiff_t)i);
+      ctx->graphs.push_back(hit);
+      HIPCHK(ctx, hipGraphLaunch(hit.exec, ctx->stream), "step: graph launch");
       return WD_OK;
     }
   HIPCHK(ctx, hipStreamBeginCapture(ctx->stream, hipStreamCaptureModeThreadLocal), "step: begin capture");
@@ -1046,6 +1022,9 @@ static wd_status staged_step(wd_ctx* ctx, int32_t B, float* logits, int32_t* arg
   (void)hipGraphDestroy(graph);
   if (ei != hipSuccess) return fail(ctx, WD_ERR_HIP, std::string("step: instantiate: ") + hipGetErrorString(ei));
   if (ctx->graphs.size() >= 8) {
+    // the least recently used graph may still be running (launched by an earlier step on
+    // this stream): wait for the stream before destroying it
+    HIPCHK(ctx, hipStreamSynchronize(ctx->stream), "step: graph cache eviction");
     (void)hipGraphExecDestroy(ctx->graphs.front().exec);
     ctx->graphs.erase(ctx->graphs.begin());
   }
@@ -1102,7 +1081,7 @@ wd_status prefill_batched(wd_ctx* c, const int32_t* tokens, int B, int T, const 
   const Plan& P = c->plan;
   hipStream_t s = c->stream;
   const int d = g.d_model, hd = g.head_dim, hq = g.n_heads, hkv = g.n_kv_heads, ff = g.d_ff;
-  const int nqkv = (hq + 2 * hkv) * hd, CH = pf_chunk(P.pf_pos_chunk);
+  const int nqkv = (hq + 2 * hkv) * hd, CH = P.pf_pos_chunk;
   const int adt = g.w_dtype;
   const float qscale = 1.0f / sqrtf((float)hd);
   const int64_t kv_bstride = (int64_t)hkv * g.context * hd;
@@ -1154,15 +1133,9 @@ wd_status prefill_batched(wd_ctx* c, const int32_t* tokens, int B, int T, const 
   return WD_OK;
 }
 
-// Batched prefill unless WD_PF_BATCHED=0 (then every position runs as a decode step).
-bool prefill_batched_on(const wd_ctx* c) {
-  static int mode = -1;
-  if (mode < 0) {
-    const char* e = getenv("WD_PF_BATCHED");
-    mode = e ? atoi(e) : 1;
-  }
-  return mode != 0 && c->plan.pf_rows > 0;
-}
+// The batched prefill serves 16-bit Qwen3 contexts (the plan has its chunk buffers); any other
+// context runs every prompt position as a decode step.
+bool prefill_batched_on(const wd_ctx* c) { return c->plan.pf_rows > 0; }
 
 }  // namespace
 
@@ -1438,6 +1411,10 @@ const char* wd_last_error(const wd_ctx* ctx) {
 
 void wd_free(wd_ctx* ctx) {
   if (!ctx) return;
+  // launched graphs and kernels may still be running on the context's stream: wait for it
+  // before their graphs are destroyed (and before the caller can release the workspace)
+  if (ctx->stream) (void)hipStreamSynchronize(ctx->stream);
+  else (void)hipDeviceSynchronize();
   for (auto& e : ctx->graphs) (void)hipGraphExecDestroy(e.exec);
   delete ctx->enc;
   for (auto& pr : ctx->prof) {
@@ -1445,6 +1422,27 @@ void wd_free(wd_ctx* ctx) {
     (void)hipEventDestroy(pr.b);
   }
   delete ctx;
+}
+
+wd_status wd_set_option(wd_ctx* ctx, int32_t option, int32_t value) {
+  if (!ctx) return WD_ERR_ARG;
+  switch (option) {
+    case WD_OPT_GRAPHS:
+      if (value != 0 && value != 1) return fail(ctx, WD_ERR_ARG, "wd_set_option: WD_OPT_GRAPHS takes 0 or 1");
+      ctx->use_graphs = value == 1;
+      return WD_OK;
+    default:
+      return fail(ctx, WD_ERR_ARG, "wd_set_option: unknown option");
+  }
+}
+
+wd_status wd_get_option(wd_ctx* ctx, int32_t option, int32_t* value) {
+  if (!ctx) return WD_ERR_ARG;
+  if (!value) return fail(ctx, WD_ERR_ARG, "wd_get_option: value must not be null");
+  switch (option) {
+    case WD_OPT_GRAPHS: *value = ctx->use_graphs ? 1 : 0; return WD_OK;
+    default: return fail(ctx, WD_ERR_ARG, "wd_get_option: unknown option");
+  }
 }
 
 wd_status wd_profile(wd_ctx* ctx, int32_t kernel, int32_t layer, int32_t repeats) {

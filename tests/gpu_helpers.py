@@ -42,9 +42,12 @@ def to_dev(a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device="cuda", dtype=dtype)
 
 
-def compare_logits(w, gpu, ref, where=""):
+def compare_logits(w, gpu, ref, where="", gpu_argmax=None):
     """gpu (float32) and ref (float64) logits [..., V]; asserts the parity bar and
-    returns (max error, argmax rows checked)."""
+    returns (max error, argmax rows checked).  gpu_argmax: the ids the library
+    returned for these rows, which must equal the lowest-index argmax of its own
+    logits everywhere and the oracle's wherever the oracle's top-2 margin exceeds
+    the bar."""
     gpu = np.asarray(gpu, np.float64).reshape(-1, ref.shape[-1])
     ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
     assert np.all(np.isfinite(gpu)), f"non-finite GPU logits {where}"
@@ -63,7 +66,23 @@ def compare_logits(w, gpu, ref, where=""):
     ga, oa = argmax_lowest(gpu), argmax_lowest(ref)
     mism = np.nonzero(sel & (ga != oa))[0]
     assert mism.size == 0, f"{where}: argmax differs at rows {mism[:8]} (margins {m[mism[:8]]})"
+    if gpu_argmax is not None:
+        da = np.asarray(gpu_argmax, np.int32).reshape(-1)
+        bad = np.nonzero(da != ga)[0]
+        assert bad.size == 0, f"{where}: device argmax {da[bad[:8]]} != argmax of its logits {ga[bad[:8]]}"
+        mism = np.nonzero(sel & (da != oa))[0]
+        assert mism.size == 0, f"{where}: device argmax differs from the oracle's at rows {mism[:8]}"
     return emax, int(sel.sum())
+
+
+def check_device_argmax(logits, amax, where=""):
+    """Every row: the id the library returned equals the lowest-index argmax of the
+    logits it wrote (device tensors [B, V] fp32 and [B] int32)."""
+    lg = logits.cpu().numpy()
+    want = argmax_lowest(lg)
+    got = amax.cpu().numpy()
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{where}: device argmax {got[bad[:8]]} != argmax of its logits {want[bad[:8]]} at rows {bad[:8]}"
 
 
 class GpuRun:
@@ -87,13 +106,17 @@ class GpuRun:
         self.dec.cross_kv(e, F)
         torch.cuda.synchronize()
 
-    def step(self, tokens, pos, rows=None, B=None):
-        """Feeds tokens [B] at position(s) pos; returns (logits of `rows`, argmax)."""
+    def step(self, tokens, pos, rows=None, B=None, check_all=False):
+        """Feeds tokens [B] at position(s) pos; returns (logits of `rows`, argmax of all B
+        rows).  check_all: also assert, for every row, that the returned argmax is the
+        lowest-index argmax of the logits the step wrote."""
         B = self.w.batch if B is None else B
         self.tok[:B].copy_(torch.as_tensor(np.asarray(tokens, np.int32)))
         p = np.broadcast_to(np.asarray(pos, np.int32), (B,))
         self.pos[:B].copy_(torch.as_tensor(np.ascontiguousarray(p)))
         self.dec.step(self.tok[:B], self.pos[:B], self.logits[:B], self.amax[:B])
+        if check_all:
+            check_device_argmax(self.logits[:B], self.amax[:B], f"position(s) {np.unique(p)}")
         lg = self.logits[:B] if rows is None else self.logits[rows]
         return lg.cpu().numpy(), self.amax[:B].cpu().numpy()
 

@@ -7,7 +7,7 @@ import torch
 import workloads as WL
 from oracle import qwen3 as OQ
 
-from .gpu_helpers import GpuRun, compare_logits, need_gpu, say, to_dev, torch_dtype
+from .gpu_helpers import GpuRun, check_device_argmax, compare_logits, need_gpu, say, to_dev, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -15,7 +15,9 @@ pytestmark = pytest.mark.gpu
 def _qwen_parity(w, T, steps, streams):
     """Prefill T rows (audio at rows audio_offset.. of the workload, clipped to T)
     on all rows, then `steps` teacher-forced decode steps; the sampled rows are
-    compared at the prefill's last position and at every decode step."""
+    compared at the prefill's last position and at every decode step.  The argmax
+    the prefill and every step return is checked for every row against the logits
+    they wrote, and for the sampled rows against the oracle's."""
     need_gpu()
     say(f"[qwen3] {w.describe()} T={T} steps={steps} rows={streams}")
     W = WL.make_weights(w)
@@ -29,12 +31,16 @@ def _qwen_parity(w, T, steps, streams):
     tok = torch.from_numpy(np.ascontiguousarray(ids)).to(device="cuda", dtype=torch.int32)
     emb = to_dev(audio, torch_dtype(w.w_dtype)) if A > 0 else None
     logits = torch.empty(w.batch, w.vocab, dtype=torch.float32, device="cuda")
-    G.dec.prefill(tok, emb, off, logits)
+    _, pam = G.dec.prefill(tok, emb, off, logits)
+    check_device_argmax(logits, pam, "prefill")
+    pam = pam.cpu().numpy()
     got = {b: [logits[b].cpu().numpy()] for b in streams}
+    amx = {b: [pam[b]] for b in streams}
     for s in range(steps):
-        lg, _ = G.step(dec_ids[:, s], T + s, rows=list(streams))
+        lg, am = G.step(dec_ids[:, s], T + s, rows=list(streams), check_all=True)
         for i, b in enumerate(streams):
             got[b].append(lg[i])
+            amx[b].append(am[b])
     assert G.check() == 0
     G.close()
     del G
@@ -45,7 +51,7 @@ def _qwen_parity(w, T, steps, streams):
         say(f"  oracle full prefix, row {b}")
         seq = np.concatenate([ids[b], dec_ids[b]])
         ref = OQ.decode_full(D, W, seq, round_cache=True, embeds=audio[b] if A else None, offset=off)
-        e, _ = compare_logits(w, np.stack(got[b]), ref[T - 1:], f"row {b}")
+        e, _ = compare_logits(w, np.stack(got[b]), ref[T - 1:], f"row {b}", gpu_argmax=np.array(amx[b]))
         worst = max(worst, e)
     say(f"  worst err {worst:.3e}")
 
@@ -93,3 +99,38 @@ def test_qwen3_prefill_mha_odd_rows():
     w = WL.reduced(WL.by_name("qwen3asr_bf16_b8"), layers=2, d=256, heads=4, kv_heads=4, d_ff=512, vocab=7001,
                    context=96, batch=3, audio_offset=4, audio_rows=30)
     _qwen_parity(w, T=70, steps=3, streams=(0, 2))
+
+
+def test_qwen3_argmax_exact_ties_full_vocab():
+    """Exact ties through the 16-bit tied head over the full 151936-id vocabulary at 8 rows:
+    every embedding row equals row 7 except ids 100000, 100001 and 151935 (twice row 7), so
+    each row's logits take two values; the argmax is 100000 where those win and 0 otherwise
+    (lowest index on ties, across every output block of the head)."""
+    need_gpu()
+    w = WL.reduced(WL.by_name("qwen3asr_bf16_b8"), layers=1, d=256, heads=4, kv_heads=2, d_ff=512, context=16)
+    top = [100000, 100001, 151935]
+    W = WL.make_weights(w)
+    E = W["embed"].copy()
+    E[:] = E[7]
+    for t in top:
+        E[t] = 2 * E[7]
+    W["embed"] = E
+    O = OQ.QwenOracle(OQ.dims_of(w), W, round_cache=True)
+    O.reset(w.batch)
+    G = GpuRun(w, W)
+    ids = WL.random_ids(w, 4)
+    decided = 0
+    for p in range(4):
+        ref = O.step(ids[:, p], [p] * w.batch)
+        lg, am = G.step(ids[:, p], p, check_all=True)
+        for t in top[1:]:
+            np.testing.assert_array_equal(lg[:, t], lg[:, top[0]], err_msg=f"tied logits, pos {p}")
+        hi, lo = ref[:, top[0]], ref[:, 0]
+        want = np.where(hi - lo > 1e-2, top[0], np.where(lo - hi > 1e-2, 0, -1))
+        sel = want >= 0
+        np.testing.assert_array_equal(am[sel], want[sel], err_msg=f"tie winner, pos {p}")
+        decided += int(sel.sum())
+    assert G.check() == 0
+    G.close()
+    say(f"  tie winners checked {decided}")
+    assert decided > 0

@@ -37,9 +37,8 @@ def _greedy_parity(w, steps=None, frames=None, B=None):
             toks = prompt[:, p]
         ref = O.step(toks, np.full(B, p))
         lg, am = G.step(toks, p, B=B)
-        e, n = compare_logits(w, lg, ref, f"pos {p}")
+        e, n = compare_logits(w, lg, ref, f"pos {p}", gpu_argmax=am)
         worst, checked = max(worst, e), checked + n
-        np.testing.assert_array_equal(am, argmax_lowest(lg), err_msg=f"device argmax vs its logits, pos {p}")
         toks = argmax_lowest(ref)
     assert G.check() == 0
     G.close()
@@ -72,7 +71,9 @@ def test_bf16_small_dims_frames_1499():
 def _sampled_parity(w, steps, streams, frames=None):
     """All rows step on the GPU, teacher-forced with seeded ids after the prompt;
     the oracle recomputes the sampled rows' full prefix once (identical to the
-    cached step, pinned on the CPU) and every position of them is compared."""
+    cached step, pinned on the CPU) and every position of them is compared.  At
+    every step the argmax the library returns is checked for every row against
+    its own logits, and for the sampled rows against the oracle's."""
     need_gpu()
     say(f"[whisper sampled] {w.describe()} steps={steps} rows={streams}")
     W = WL.make_weights(w)
@@ -83,10 +84,12 @@ def _sampled_parity(w, steps, streams, frames=None):
     G = GpuRun(w, W)
     G.cross(enc, F)
     got = {b: [] for b in streams}
+    amx = {b: [] for b in streams}
     for p in range(steps):
-        lg, _ = G.step(ids[:, p], p, rows=list(streams))
+        lg, am = G.step(ids[:, p], p, rows=list(streams), check_all=True)
         for i, b in enumerate(streams):
             got[b].append(lg[i])
+            amx[b].append(am[b])
     assert G.check() == 0
     G.close()
     del G
@@ -97,7 +100,7 @@ def _sampled_parity(w, steps, streams, frames=None):
         say(f"  oracle full prefix, row {b}")
         e = b // (w.batch // w.n_enc)
         ref = OW.decode_full(D, W, ids[b], enc[e, :F], round_cache=True)
-        err, _ = compare_logits(w, np.stack(got[b]), ref, f"row {b}")
+        err, _ = compare_logits(w, np.stack(got[b]), ref, f"row {b}", gpu_argmax=np.array(amx[b]))
         worst = max(worst, err)
     say(f"  worst err {worst:.3e}")
 
@@ -114,9 +117,10 @@ def test_large_bf16_b64_reduced_layers():
 @pytest.mark.slow
 def test_large_bf16_b64_full_window_sampled_rows():
     """The large-v3 workload at its full size: 32 layers, 64 rows with their own encoder
-    sets, all 448 positions (teacher-forced ids); rows 0 and 63 against the oracle's
-    full-prefix recompute at every position."""
-    _sampled_parity(WL.by_name("whisper_large_bf16_b64"), steps=448, streams=(0, 63))
+    sets, all 448 positions (teacher-forced ids); rows 0, 9, ..., 63 (one in every 16-row
+    tile of the projections and the head) against the oracle's full-prefix recompute at
+    every position, and every row's returned argmax against its logits."""
+    _sampled_parity(WL.by_name("whisper_large_bf16_b64"), steps=448, streams=(0, 9, 18, 27, 36, 45, 54, 63))
 
 
 @pytest.mark.slow
@@ -159,8 +163,8 @@ def test_ragged_window_sets_of_different_lengths():
     for p in range(8):
         toks = prompt[:, p] if p < prompt.shape[1] else toks
         ref = O.step(toks, np.full(w.batch, p))
-        lg, _ = G.step(toks, p)
-        e, _ = compare_logits(w, lg, ref, f"pos {p}")
+        lg, am = G.step(toks, p)
+        e, _ = compare_logits(w, lg, ref, f"pos {p}", gpu_argmax=am)
         worst = max(worst, e)
         toks = argmax_lowest(ref)
     assert G.check() == 0
@@ -168,8 +172,8 @@ def test_ragged_window_sets_of_different_lengths():
     G.cross(enc)
     O.cross_kv(enc)
     ref = O.step(toks, np.full(w.batch, 8))
-    lg, _ = G.step(toks, 8)
-    compare_logits(w, lg, ref, "uniform window after a ragged one")
+    lg, am = G.step(toks, 8)
+    compare_logits(w, lg, ref, "uniform window after a ragged one", gpu_argmax=am)
     G.close()
     say(f"  worst err {worst:.3e}")
 
@@ -195,8 +199,8 @@ def test_rows_at_different_positions():
         pos = np.maximum(0, st - delays).astype(np.int32)
         toks = ids[np.arange(w.batch), pos]
         ref = O.step(toks, pos)
-        lg, _ = G.step(toks, pos)
-        e, _ = compare_logits(w, lg, ref, f"step {st} positions {pos}")
+        lg, am = G.step(toks, pos)
+        e, _ = compare_logits(w, lg, ref, f"step {st} positions {pos}", gpu_argmax=am)
         worst = max(worst, e)
     assert G.check() == 0
     G.close()
@@ -282,8 +286,8 @@ def test_base_f16_beam5_full():
             O.reorder(beam_idx)
             G.dec.reorder(beam_idx, p)
         ref = O.step(toks, np.full(w.batch, p))
-        lg, _ = G.step(toks, p)
-        e, _ = compare_logits(w, lg, ref, f"pos {p}")
+        lg, am = G.step(toks, p)
+        e, _ = compare_logits(w, lg, ref, f"pos {p}", gpu_argmax=am)
         worst = max(worst, e)
         if p >= prompt.shape[1] - 1:
             first = p == prompt.shape[1] - 1
@@ -365,6 +369,126 @@ def test_argmax_exact_ties_lowest_index():
         assert want in (0, 1234)
         assert am[0] == want, (am[0], want)
     G.close()
+
+
+def _tied_embedding(W, base, top):
+    """Every embedding row equal to row `base`, and the rows in `top` equal to twice it:
+    all logits E.h of a row tie exactly on two values (equal rows give bit-identical dot
+    products), so the argmax is min(top) when E[base].h > 0 and 0 otherwise."""
+    E = W["embed"].copy()
+    E[:] = E[base]
+    for t in top:
+        E[t] = 2 * E[base]
+    W["embed"] = E
+    return W
+
+
+def _tie_winner(ref, top):
+    """The lowest-index argmax the tied logits must give (from the oracle's values), or -1
+    where the two tied values are too close to decide."""
+    hi, lo = ref[:, top[0]], ref[:, 0]
+    return np.where(hi - lo > 1e-2, min(top), np.where(lo - hi > 1e-2, 0, -1))
+
+
+def test_argmax_exact_ties_mfma_head_b64():
+    """Exact ties through the 16-bit tied head at 64 rows (the LDS-shared MFMA kernel, rows in
+    all four 16-row tiles, per-block argmax keys merged in a second kernel) over the full
+    51866-id vocabulary: ties inside one output block (1234, 1235), across blocks (2345) and
+    across every block at once (all other ids)."""
+    need_gpu()
+    w = WL.reduced(WL.by_name("whisper_large_bf16_b64"), layers=1, d=256, heads=4, kv_heads=4, d_ff=512,
+                   frames=64)
+    top = [1234, 1235, 2345]
+    W = _tied_embedding(WL.make_weights(w), 5, top)
+    enc = WL.make_encoder_states(w)
+    O = OW.WhisperOracle(OW.dims_of(w), W)
+    O.cross_kv(enc)
+    O.reset(w.batch, enc_of=np.arange(w.batch))
+    G = GpuRun(w, W)
+    G.cross(enc)
+    ids = WL.random_ids(w, 3)
+    decided = 0
+    for p in range(3):
+        ref = O.step(ids[:, p], np.full(w.batch, p))
+        lg, am = G.step(ids[:, p], p, check_all=True)
+        for t in top[1:]:
+            np.testing.assert_array_equal(lg[:, t], lg[:, top[0]], err_msg=f"tied logits, pos {p}")
+        np.testing.assert_array_equal(lg[:, 1], lg[:, 0], err_msg=f"tied logits, pos {p}")
+        want = _tie_winner(ref, top)
+        sel = want >= 0
+        np.testing.assert_array_equal(am[sel], want[sel], err_msg=f"tie winner, pos {p}")
+        decided += int(sel.sum())
+    assert G.check() == 0
+    G.close()
+    say(f"  tie winners checked {decided}")
+    assert decided > 0
+
+
+def test_step_graph_cache_many_output_buffers():
+    """A step is captured once per output-buffer set and replayed; more distinct buffers
+    than the cache holds evict the least recently used graphs (after the stream has passed
+    them).  Re-stepping one position with the same tokens rewrites the same cache row, so
+    every call must give the same logits and ids, whichever graph serves it."""
+    need_gpu()
+    w = WL.reduced(WL.by_name("whisper_small_f16_b16"), layers=2, batch=4, n_enc=4, d=256, heads=4, kv_heads=4,
+                   d_ff=512, vocab=3001, frames=100)
+    W = WL.make_weights(w)
+    enc = WL.make_encoder_states(w)
+    G = GpuRun(w, W)
+    G.cross(enc)
+    ids = WL.random_ids(w, 2)
+    G.step(ids[:, 0], 0)
+    ref_lg, ref_am = G.step(ids[:, 1], 1)
+    outs = [(torch.empty(w.batch, w.vocab, dtype=torch.float32, device="cuda"),
+             torch.empty(w.batch, dtype=torch.int32, device="cuda")) for _ in range(12)]
+    tok = torch.from_numpy(ids[:, 1].copy()).cuda()
+    pos = torch.ones(w.batch, dtype=torch.int32, device="cuda")
+    order = list(range(12)) + [0, 11, 3, 7] + list(range(12))
+    for i in order:
+        G.dec.step(tok, pos, outs[i][0], outs[i][1])
+    torch.cuda.synchronize()
+    for i in set(order):
+        np.testing.assert_array_equal(outs[i][0].cpu().numpy(), ref_lg, err_msg=f"buffer set {i}")
+        np.testing.assert_array_equal(outs[i][1].cpu().numpy(), ref_am, err_msg=f"buffer set {i}")
+    assert G.check() == 0
+    G.close()
+
+
+@pytest.mark.parametrize("name", ["whisper_large_bf16_b64", "whisper_small_f16_b16", "qwen3asr_bf16_b8"])
+def test_graph_replay_equals_eager_launches(name):
+    """wd_set_option(WD_OPT_GRAPHS): the captured-and-replayed step and the eagerly launched one
+    run the same kernels in the same order, so logits and ids must be bit-identical; two
+    contexts with the same weights and inputs step side by side, one with graphs, one
+    without, at full batch and width (reduced depth and vocabulary)."""
+    need_gpu()
+    w0 = WL.by_name(name)
+    kw = dict(layers=2, vocab=20011)
+    if w0.arch == "whisper":
+        kw["frames"] = 300
+    w = WL.reduced(w0, **kw)
+    W = WL.make_weights(w)
+    A, E = GpuRun(w, W), GpuRun(w, W)
+    E.dec.set_graphs(False)
+    assert G_opt(E) == 0 and G_opt(A) == 1
+    if w.arch == "whisper":
+        enc = WL.make_encoder_states(w)
+        A.cross(enc)
+        E.cross(enc)
+    ids = WL.random_ids(w, 6)
+    for p in range(6):
+        la, aa = A.step(ids[:, p], p)
+        le, ae = E.step(ids[:, p], p)
+        np.testing.assert_array_equal(la, le, err_msg=f"logits, position {p}")
+        np.testing.assert_array_equal(aa, ae, err_msg=f"argmax, position {p}")
+    assert A.check() == 0 and E.check() == 0
+    with pytest.raises(A.K.WdError):
+        A.K.wd_set_option(A.dec.ctx, A.K.WD_OPT_GRAPHS, 2)
+    A.close()
+    E.close()
+
+
+def G_opt(G):
+    return G.K.wd_get_option(G.dec.ctx, G.K.WD_OPT_GRAPHS)
 
 
 def test_out_of_range_inputs_set_device_flag():
