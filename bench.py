@@ -141,33 +141,223 @@ def qwen_bytes_per_step(w, pos: int) -> int:
     return L * per_layer + glob + kv
 
 
-def qwen_cpu_baseline(w, budget_s: float):
-    """The Qwen3 oracle on the host cores: one stream's decode steps from position 0 for
-    about `budget_s` seconds (no prefill; bounded sample)."""
+def host_info() -> dict:
+    """The host the CPU baseline ran on: CPU model, cores available to this process, and
+    the BLAS libraries numpy uses with their thread counts."""
     from threadpoolctl import threadpool_info
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = [{"library": p.get("internal_api"), "version": p.get("version"), "threads": p.get("num_threads")}
+            for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {"cpu_model": model, "cores_available": len(os.sched_getaffinity(0)), "blas": blas}
 
+
+def _blas_threads() -> int:
+    from threadpoolctl import threadpool_info
+    return int(max([p.get("num_threads", 1) for p in threadpool_info()] + [1]))
+
+
+def _sample_positions(first: int, last: int, n: int):
+    """n positions spread evenly over first..last (inclusive)."""
+    return sorted({int(round(first + (last - first) * i / max(n - 1, 1))) for i in range(n)})
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle as it is (float64 numpy) on the host cores: one stream of the workload,
+    its cross K/V, then single decode steps at positions spread over the whole window
+    (the self-cache rows below each sampled position hold seeded values of the cache dtype:
+    a step's cost does not depend on them), as many as fit the time budget.  tokens/s =
+    sampled steps / their time, i.e. the mean step cost over the window."""
+    from oracle import whisper as OW
+    W = WL.make_weights(w)
+    enc = WL.make_encoder_states(w, streams=[0])
+    O = OW.WhisperOracle(OW.dims_of(w), W)
+    del W
+    t0 = time.perf_counter()
+    O.cross_kv(enc)
+    t_cross = time.perf_counter() - t0
+    O.reset(1)
+    rng = np.random.default_rng(w.seed)
+    for l in range(w.layers):
+        O.Ks[l][:] = rng.standard_normal(O.Ks[l].shape).astype(np.float32)
+        O.Vs[l][:] = rng.standard_normal(O.Vs[l].shape).astype(np.float32)
+    tok = WL.make_prompt(w)[:1, 0]
+    times = []
+    for n in (128, 64, 32, 16, 8, 4, 2):   # as many spread positions as fit the budget
+        pos = _sample_positions(0, w.steps - 1, n)
+        t0 = time.perf_counter()
+        O.step(tok, [pos[0]])
+        one = time.perf_counter() - t0
+        if one * n <= budget_s or n == 2:
+            times = [one]
+            for p_ in pos[1:]:
+                t0 = time.perf_counter()
+                O.step(tok, [p_])
+                times.append(time.perf_counter() - t0)
+            break
+    hi = host_info()
+    return {"value": len(times) / sum(times), "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"1 of {w.batch} streams, one decode step at each of {len(pos)} positions spread evenly over "
+                      f"0..{w.steps - 1} (float64 numpy); its cross K/V took {t_cross:.2f} s on top, not counted",
+            "cpu_model": hi["cpu_model"], "cores_available": hi["cores_available"], "blas": hi["blas"],
+            "s_per_step": sum(times) / len(times)}
+
+
+def qwen_cpu_baseline(w, budget_s: float):
+    """The Qwen3 oracle on the host cores: one stream's decode steps at positions spread over
+    the decode window (the K/V rows below each hold seeded values of the cache dtype; no
+    prefill), as many as fit about `budget_s` seconds."""
     from oracle import qwen3 as OQ
     W = WL.make_weights(w)
     O = OQ.QwenOracle(OQ.dims_of(w), W, round_cache=True)
     del W
     O.reset(1)
-    ids = WL.random_ids(w, 64)[:1]
-    n, t = 0, 0.0
-    while n < ids.shape[1] and (n < 2 or t < budget_s):
+    rng = np.random.default_rng(w.seed)
+    for l in range(w.layers):
+        O.K[l][:] = rng.standard_normal(O.K[l].shape).astype(np.float16)
+        O.V[l][:] = rng.standard_normal(O.V[l].shape).astype(np.float16)
+    ids = WL.random_ids(w, 1)[:1, 0]
+    first, last = w.prefill_len, w.prefill_len + w.steps - 1
+    times = []
+    for n in (64, 32, 16, 8, 4, 2):
+        pos = _sample_positions(first, last, n)
         t0 = time.perf_counter()
-        O.step(ids[:, n], [n])
-        t += time.perf_counter() - t0
-        n += 1
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": n / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"1 of {w.batch} streams, decode steps at positions 0..{n - 1} (float64 numpy, no prefill)"}
+        O.step(ids, [pos[0]])
+        one = time.perf_counter() - t0
+        if one * n <= budget_s or n == 2:
+            times = [one]
+            for p_ in pos[1:]:
+                t0 = time.perf_counter()
+                O.step(ids, [p_])
+                times.append(time.perf_counter() - t0)
+            break
+    hi = host_info()
+    return {"value": len(times) / sum(times), "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"1 of {w.batch} streams, one decode step at each of {len(pos)} positions spread evenly over "
+                      f"{first}..{last} (float64 numpy, no prefill)", "cpu_model": hi["cpu_model"], "cores_available": hi["cores_available"],
+            "blas": hi["blas"], "s_per_step": sum(times) / len(times)}
 
 
-def run_qwen(args, w):
-    """Qwen3-ASR: prefill of 900 positions (audio rows spliced in), then the greedy decode
-    steps to the context end, argmax on the device.  value = decode tokens/s; the prefill
-    (batched: chunks of positions through dense MFMA GEMMs and a causal prefill attention)
-    is timed separately."""
+WDT = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
+
+
+def _tdt(name):
+    import torch
+    return getattr(torch, WDT[name])
+
+
+def bench_whisper_greedy(w, windows: int, warmup: int, args, graphs_off_windows: int = 0):
+    """Greedy windows of a Whisper workload: each window is wd_cross_kv of every layer, then
+    every position for all rows, the argmax of a step feeding the next (after the prompt).
+    Returns the measured figures and the decoder (for the kernel timing)."""
+    import torch
+
+    import kv_cached_autoregressive_amd as K
+    dev = torch.device("cuda:0")
+    W = WL.make_weights(w)
+    enc_np = WL.make_encoder_states(w)
+    dec = K.Decoder(w, W)
+    del W
+    enc = torch.from_numpy(enc_np).to(dev, _tdt(w.w_dtype))
+    del enc_np
+    B, S = w.batch, w.steps
+    prompt = torch.from_numpy(WL.make_prompt(w).T.copy()).to(dev)          # [4, B]
+    pos_all = torch.arange(S, dtype=torch.int32, device=dev)[:, None].repeat(1, B).contiguous()
+    amax = torch.zeros(B, dtype=torch.int32, device=dev)
+    stream, ctx = dec.stream, dec.ctx
+
+    def steps(n):
+        for p in range(n):
+            tok = prompt[p] if p < prompt.shape[0] else amax
+            K.wd_step(ctx, tok.data_ptr(), pos_all[p].data_ptr(), B, 0, amax.data_ptr())
+
+    def window(ev=None):
+        K.wd_cross_kv(ctx, enc.data_ptr(), w.frames)
+        if ev is not None:
+            ev.record(stream)
+        steps(S)
+
+    torch.cuda.synchronize()
+    torch.cuda.set_stream(stream)          # everything below is queued on the decoder's stream
+    for _ in range(warmup):
+        window()
+    torch.cuda.synchronize()
+    if dec.check() != 0:
+        raise RuntimeError(dec.last_error())
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(windows)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(windows):
+        ev[i][0].record(stream)
+        window(ev[i][1])
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    if dec.check() != 0:
+        raise RuntimeError(dec.last_error())
+    win_ms = [e[0].elapsed_time(e[2]) for e in ev]
+    xkv_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    dec_ms = [a - b for a, b in zip(win_ms, xkv_ms)]
+    total_ms = ev[0][0].elapsed_time(ev[-1][2])
+    bytes_window = sum(whisper_bytes_per_step(w, p) for p in range(S))
+    mean_dec = sum(dec_ms) / windows
+    out = {"workload": w.name, "batch": B, "positions": S,
+           "tokens_per_s": B * S * windows / (total_ms / 1e3), "ms_per_window": total_ms / windows,
+           "ms_per_window_median": float(np.median(win_ms)),
+           "decode_tokens_per_s": B * S / (mean_dec / 1e3), "decode_ms_per_window": mean_dec,
+           "decode_ms_per_window_median": float(np.median(dec_ms)),
+           "hbm_bytes_per_window": bytes_window,
+           "hbm_gbps_decode": bytes_window / (mean_dec / 1e3) / 1e9,
+           "hbm_frac_decode": bytes_window / (mean_dec / 1e3) / HBM_PEAK,
+           "cross_kv_ms": sum(xkv_ms) / windows,
+           "cross_kv_tflops": 2.0 * w.n_enc * w.frames * w.d * 2 * w.d * w.layers / (sum(xkv_ms) / windows / 1e3) / 1e12,
+           "windows": windows, "wall_s": wall}
+    if graphs_off_windows:
+        # the same windows with every kernel launched eagerly (no captured step graphs)
+        dec.set_graphs(False)
+        window()
+        torch.cuda.synchronize()
+        off = []
+        for _ in range(graphs_off_windows):
+            e1, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            window(e1)
+            e2.record(stream)
+            torch.cuda.synchronize()
+            off.append(e1.elapsed_time(e2))
+        dec.set_graphs(True)
+        off_dec = sum(off) / len(off)
+        out["graphs_off"] = {"decode_tokens_per_s": B * S / (off_dec / 1e3), "decode_ms_per_window": off_dec,
+                             "hbm_frac_decode": bytes_window / (off_dec / 1e3) / HBM_PEAK,
+                             "windows": graphs_off_windows}
+        if dec.check() != 0:
+            raise RuntimeError(dec.last_error())
+    # the dominant kernel: HIP events on the decoder's stream around the cross-attention of
+    # one layer, issued `repeats` times back to back per step (the launch is idempotent),
+    # over the first positions of a window run right after the timed ones (steps are
+    # launched one by one there: a captured step replays without per-launch host hooks);
+    # the cross-attention reads all frames at every position, so any positions will do
+    K.wd_profile(ctx, K.K_CROSS_ATTN, args.profile_layer, args.profile_repeats)
+    steps(min(S, args.profile_positions))
+    attn_ms, attn_n = K.wd_profile_read(ctx)
+    K.wd_profile(ctx, -1, -1, 1)
+    attn_bytes = cross_attn_bytes_per_launch(w)
+    attn_avg_s = attn_ms / 1e3 / max(attn_n, 1)
+    out["roofline"] = {"kernel": "k_attn (cross-attention, one layer per launch)", "bound": "hbm",
+                       "achieved": attn_bytes / attn_avg_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                       "frac": attn_bytes / attn_avg_s / HBM_PEAK, "traffic": traffic_per_launch(w.name),
+                       "bytes_per_launch": attn_bytes, "avg_launch_us": attn_avg_s * 1e6, "launches_timed": attn_n}
+    return out, dec, enc
+
+
+def bench_qwen(w, runs: int, warmup: int, args):
+    """Qwen3-ASR: a 900-position prefill (audio rows spliced in), then the greedy decode steps
+    to the context end, argmax on the device.  The prefill is timed separately."""
     import torch
 
     import kv_cached_autoregressive_amd as K
@@ -176,10 +366,9 @@ def run_qwen(args, w):
     ids_np, audio_np = WL.make_qwen_prefill(w)
     dec = K.Decoder(w, W)
     del W
-    wdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.w_dtype]
     B, T, S = w.batch, w.prefill_len, w.steps
     ids = torch.from_numpy(np.ascontiguousarray(ids_np)).to(dev, torch.int32)
-    audio = torch.from_numpy(np.ascontiguousarray(audio_np)).to(dev, wdt)
+    audio = torch.from_numpy(np.ascontiguousarray(audio_np)).to(dev, _tdt(w.w_dtype))
     pos_all = (T + torch.arange(S, dtype=torch.int32, device=dev))[:, None].repeat(1, B).contiguous()
     amax = torch.zeros(B, dtype=torch.int32, device=dev)
     stream, ctx = dec.stream, dec.ctx
@@ -194,26 +383,25 @@ def run_qwen(args, w):
 
     torch.cuda.synchronize()
     torch.cuda.set_stream(stream)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         prefill()
         steps(S)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
-    pre_ms, dec_ms = 0.0, 0.0
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(runs)]
     wall0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[3 * i].record(stream)
+    for i in range(runs):
+        ev[i][0].record(stream)
         prefill()
-        ev[3 * i + 1].record(stream)
+        ev[i][1].record(stream)
         steps(S)
-        ev[3 * i + 2].record(stream)
+        ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    for i in range(args.steps):
-        pre_ms += ev[3 * i].elapsed_time(ev[3 * i + 1]) / args.steps
-        dec_ms += ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) / args.steps
     if dec.check() != 0:
         raise RuntimeError(dec.last_error())
+    pre = [e[0].elapsed_time(e[1]) for e in ev]
+    dms = [e[1].elapsed_time(e[2]) for e in ev]
+    dec_ms = sum(dms) / runs
     # kernel timing: the gate|up projection of one layer (the largest weight stream of a layer)
     prefill()
     K.wd_profile(ctx, K.K_FC1, args.profile_layer, args.profile_repeats)
@@ -223,33 +411,129 @@ def run_qwen(args, w):
     gu_bytes = 2 * w.d_ff * w.d * DT_BYTES[w.w_dtype]
     k_avg = k_ms / 1e3 / max(k_n, 1)
     bytes_dec = sum(qwen_bytes_per_step(w, T + p) for p in range(S))
-    out = {
-        "metric": "decoder tokens/sec at batch B; achieved HBM GB/s as % of MI355X peak",
-        "value": B * S / (dec_ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": dec_ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.w_dtype,
-        "data": "synthetic (seeded random-init weights N(0,0.02), N(0,1) audio rows, uniform ids)",
-        "config": {"workload": w.name, "batch": B, "prefill": T, "positions": S, "layers": w.layers,
-                   "d": w.d, "q_heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
-                   "d_ff": w.d_ff, "vocab": w.vocab, "w_dtype": w.w_dtype, "cache_dtype": w.cache_dtype,
-                   "step": "124 greedy decode steps after the prefill (prefill timed separately)"},
-        "decode_tokens_per_s": B * S / (dec_ms / 1e3),
-        "prefill_ms": pre_ms,
-        "hbm_bytes_decode": bytes_dec,
-        "hbm_gbps_decode": bytes_dec / (dec_ms / 1e3) / 1e9,
-        "hbm_frac_decode": bytes_dec / (dec_ms / 1e3) / HBM_PEAK,
-        "wall_s": wall,
-        "roofline": {"kernel": "gate|up projection (MFMA skinny GEMM, one layer per launch)", "bound": "hbm",
-                     "achieved": gu_bytes / k_avg / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": gu_bytes / k_avg / HBM_PEAK, "traffic": None, "bytes_per_launch": gu_bytes,
-                     "avg_launch_us": k_avg * 1e6, "launches_timed": k_n},
-        "cpu_baseline": None,
-    }
+    out = {"workload": w.name, "batch": B, "prefill": T, "positions": S,
+           "tokens_per_s": B * S / (dec_ms / 1e3), "decode_tokens_per_s": B * S / (dec_ms / 1e3),
+           "decode_ms": dec_ms, "decode_ms_median": float(np.median(dms)),
+           "prefill_ms": sum(pre) / runs, "prefill_ms_median": float(np.median(pre)),
+           "hbm_bytes_decode": bytes_dec, "hbm_gbps_decode": bytes_dec / (dec_ms / 1e3) / 1e9,
+           "hbm_frac_decode": bytes_dec / (dec_ms / 1e3) / HBM_PEAK, "runs": runs, "wall_s": wall,
+           "roofline": {"kernel": "gate|up projection (MFMA skinny GEMM, one layer per launch)", "bound": "hbm",
+                        "achieved": gu_bytes / k_avg / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                        "frac": gu_bytes / k_avg / HBM_PEAK, "traffic": None, "bytes_per_launch": gu_bytes,
+                        "avg_launch_us": k_avg * 1e6, "launches_timed": k_n}}
+    return out, dec
+
+
+def _beam_merge(scores, vals, ids, lse, V, first):
+    """One width-W beam step from per-row device candidates: scores S_b + (logit - lse_b) of
+    the W x W candidates (only row 0 at the first generated position, where every row holds
+    the same prefix), the W best kept, ties to the lower flat index b * V + v."""
+    W = vals.shape[0]
+    rows = 1 if first else W
+    cand = np.asarray(scores, np.float64)[:rows, None] + (vals[:rows].astype(np.float64) -
+                                                          lse[:rows, None].astype(np.float64))
+    flat = (np.arange(rows)[:, None] * V + ids[:rows]).reshape(-1)
+    c = cand.reshape(-1)
+    keep = np.lexsort((flat, -c))[:W]
+    return (flat[keep] // V).astype(np.int32), (flat[keep] % V).astype(np.int32), c[keep]
+
+
+def bench_beam(w, runs: int, warmup: int):
+    """Width-W beam search over one broadcast encoder set: per position wd_step (logits), the
+    per-row candidates on the device (wd_topk: W values, ids and the log-sum-exp per row),
+    the W x W merge on the host, wd_reorder of the self caches and the chosen tokens fed
+    back.  tokens/s counts every row of every step; GPU-only time excludes the host merge."""
+    import torch
+
+    import kv_cached_autoregressive_amd as K
+    dev = torch.device("cuda:0")
+    W = WL.make_weights(w)
+    enc = torch.from_numpy(WL.make_encoder_states(w)).to(dev, _tdt(w.w_dtype))
+    dec = K.Decoder(w, W)
+    del W
+    B, S, V = w.batch, w.steps, w.vocab
+    prompt = WL.make_prompt(w)
+    logits = torch.empty(B, V, dtype=torch.float32, device=dev)
+    amax = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.zeros(B, dtype=torch.int32, device=dev)
+    pos_all = torch.arange(S, dtype=torch.int32, device=dev)[:, None].repeat(1, B).contiguous()
+    vals = torch.empty(B, B, dtype=torch.float32, device=dev)
+    ids = torch.empty(B, B, dtype=torch.int32, device=dev)
+    lse = torch.empty(B, dtype=torch.float32, device=dev)
+    host = torch.empty(2 * B * B + B, dtype=torch.float32).pin_memory()
+    stream, ctx = dec.stream, dec.ctx
+    torch.cuda.set_stream(stream)
+    gpu_ms = 0.0
+
+    def run(timed):
+        nonlocal gpu_ms
+        K.wd_cross_kv(ctx, enc.data_ptr(), w.frames)
+        scores = np.zeros(B)
+        toks = prompt[:, 0]
+        for p in range(S):
+            if p < prompt.shape[1]:
+                toks = prompt[:, p]
+            tok.copy_(torch.from_numpy(np.ascontiguousarray(toks, dtype=np.int32)), non_blocking=False)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            K.wd_step(ctx, tok.data_ptr(), pos_all[p].data_ptr(), B, logits.data_ptr(), amax.data_ptr())
+            if p >= prompt.shape[1] - 1:
+                K.wd_topk(ctx, logits.data_ptr(), B, B, vals.data_ptr(), ids.data_ptr(), lse.data_ptr())
+                host[:B * B].copy_(vals.view(-1), non_blocking=True)
+                host[B * B:2 * B * B].copy_(ids.view(torch.float32).view(-1), non_blocking=True)
+                host[2 * B * B:].copy_(lse, non_blocking=True)
+            e1.record(stream)
+            stream.synchronize()
+            if timed:
+                gpu_ms += e0.elapsed_time(e1)
+            if p >= prompt.shape[1] - 1:
+                h = host.numpy()
+                hv = h[:B * B].reshape(B, B)
+                hi = h[B * B:2 * B * B].view(np.int32).reshape(B, B)
+                bi, tk, sc = _beam_merge(scores, hv, hi, h[2 * B * B:], V, p == prompt.shape[1] - 1)
+                if p + 1 < S:
+                    K.wd_reorder(ctx, bi.tolist(), p + 1)
+                scores, toks = sc, tk
+
+    for _ in range(warmup):
+        run(False)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for _ in range(runs):
+        run(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    if dec.check() != 0:
+        raise RuntimeError(dec.last_error())
+    bytes_run = sum(whisper_bytes_per_step(w, p) for p in range(S))
+    gpu_s = gpu_ms / 1e3 / runs
+    out = {"workload": w.name, "beams": B, "positions": S,
+           "tokens_per_s": B * S * runs / wall, "tokens_per_s_gpu": B * S / gpu_s,
+           "ms_per_run_wall": wall / runs * 1e3, "ms_per_run_gpu": gpu_s * 1e3,
+           "hbm_bytes_per_run": bytes_run, "hbm_frac_decode_gpu": bytes_run / gpu_s / HBM_PEAK,
+           "runs": runs,
+           "step": "wd_step + wd_topk on the device, W x W merge and wd_reorder from the host every position; "
+                   "GPU time excludes the host merge and the per-step synchronisation"}
     del dec
-    torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = qwen_cpu_baseline(w, args.cpu_budget)
-    print(json.dumps(out), flush=True)
+    return out
+
+
+def _extra_workloads(args):
+    """The other four workloads, at a fixed small number of windows each (their figures ride
+    along the headline line)."""
+    import torch
+    out = {}
+    for name, fn in (("whisper_small_f16_b16", lambda w: bench_whisper_greedy(w, 3, 1, args, graphs_off_windows=1)),
+                     ("whisper_tiny_f32_b1", lambda w: bench_whisper_greedy(w, 5, 1, args, graphs_off_windows=1)),
+                     ("qwen3asr_bf16_b8", lambda w: bench_qwen(w, 3, 1, args)),
+                     ("whisper_base_f16_beam5", lambda w: (bench_beam(w, 2, 1),))):
+        w = WL.by_name(name)
+        r = fn(w)
+        out[name] = r[0]
+        del r
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
 
 
 def run_encoder(args, w):
@@ -311,35 +595,6 @@ def run_encoder(args, w):
         "tflops": n * per_set / (ms / 1e3) / 1e12}), flush=True)
 
 
-def cpu_baseline(w, budget_s: float):
-    """The oracle as it is, on the host cores: one stream of the workload, its
-    cross K/V and as many decode steps as fit the time budget."""
-    from threadpoolctl import threadpool_info
-
-    from oracle import whisper as OW
-    W = WL.make_weights(w)
-    enc = WL.make_encoder_states(w, streams=[0])
-    O = OW.WhisperOracle(OW.dims_of(w), W)
-    del W
-    t0 = time.perf_counter()
-    O.cross_kv(enc)
-    t_cross = time.perf_counter() - t0
-    O.reset(1)
-    prompt = WL.make_prompt(w)[:1]
-    tok = prompt[:, 0]
-    n, t_steps = 0, 0.0
-    while n < w.steps and (n < 2 or t_steps < budget_s):
-        t0 = time.perf_counter()
-        lg = O.step(tok, [n])
-        t_steps += time.perf_counter() - t0
-        tok = prompt[:, n + 1] if n + 1 < prompt.shape[1] else np.argmax(lg, -1)
-        n += 1
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": n / t_steps, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"1 of {w.batch} streams, positions 0..{n - 1} of {w.steps} (float64 numpy); "
-                      f"the stream's cross K/V took {t_cross:.2f} s on top, not counted"}
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,8 +602,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=1, help="untimed windows")
     ap.add_argument("--config", default=DEFAULT)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time the --config workload only (the default run also times the other four)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle decode steps")
-    ap.add_argument("--profile-layer", type=int, default=0, help="layer whose cross-attention launches are timed")
+    ap.add_argument("--profile-layer", type=int, default=0, help="layer whose dominant-kernel launches are timed")
     ap.add_argument("--profile-positions", type=int, default=16, help="positions of the kernel-timing run")
     ap.add_argument("--profile-repeats", type=int, default=8, help="back-to-back launches per timed event pair")
     ap.add_argument("--positions", type=int, default=0,
@@ -385,75 +642,40 @@ def main():
     K.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if w.arch == "qwen3":
-        run_qwen(args, w)
-        return
     if args.encoder:
         run_encoder(args, w)
         return
+    metric = "decoder tokens/sec at batch B; achieved HBM GB/s as % of MI355X peak"
+    common = {"metric": metric, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.w_dtype}
+    if w.arch == "qwen3":
+        r, dec = bench_qwen(w, args.steps, args.warmup, args)
+        del dec
+        out = dict(common, value=r["decode_tokens_per_s"], ms_per_step=r["decode_ms"],
+                   data="synthetic (seeded random-init weights N(0,0.02), N(0,1) audio rows, uniform ids)",
+                   config={"workload": w.name, "batch": w.batch, "prefill": w.prefill_len, "positions": w.steps,
+                           "layers": w.layers, "d": w.d, "q_heads": w.heads, "kv_heads": w.kv_heads,
+                           "head_dim": w.head_dim, "d_ff": w.d_ff, "vocab": w.vocab, "w_dtype": w.w_dtype,
+                           "cache_dtype": w.cache_dtype,
+                           "step": "124 greedy decode steps after the prefill (prefill timed separately)"})
+        out.update({k: v for k, v in r.items() if k not in ("workload", "batch", "positions", "tokens_per_s")})
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = None if args.no_cpu_baseline else qwen_cpu_baseline(w, args.cpu_budget)
+        print(json.dumps(out), flush=True)
+        return
     if w.mode != "greedy":
-        print(f"bench.py times greedy windows; {w.name} is a beam-search workload", file=sys.stderr)
-        sys.exit(2)
+        r = bench_beam(w, args.steps, args.warmup)
+        out = dict(common, value=r["tokens_per_s"], ms_per_step=r["ms_per_run_wall"],
+                   data="synthetic (seeded random-init weights N(0,0.02), encoder states N(0,1))",
+                   config={"workload": w.name, "beams": w.batch, "positions": w.steps, "layers": w.layers,
+                           "d": w.d, "vocab": w.vocab, "w_dtype": w.w_dtype, "cache_dtype": w.cache_dtype})
+        out.update(r)
+        out["cpu_baseline"] = None
+        print(json.dumps(out), flush=True)
+        return
 
-    W = WL.make_weights(w)
-    enc_np = WL.make_encoder_states(w)
-    dec = K.Decoder(w, W)
-    del W
-    wdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.w_dtype]
-    enc = torch.from_numpy(enc_np).to(dev, wdt)
-    del enc_np
-    B, S = w.batch, w.steps
-    prompt = torch.from_numpy(WL.make_prompt(w).T.copy()).to(dev)          # [4, B]
-    pos_all = torch.arange(S, dtype=torch.int32, device=dev)[:, None].repeat(1, B).contiguous()
-    amax = torch.zeros(B, dtype=torch.int32, device=dev)
-    stream = dec.stream
-    ctx = dec.ctx
-
-    def steps(n):
-        for p in range(n):
-            tok = prompt[p] if p < prompt.shape[0] else amax
-            K.wd_step(ctx, tok.data_ptr(), pos_all[p].data_ptr(), B, 0, amax.data_ptr())
-
-    def window(ev=None):
-        K.wd_cross_kv(ctx, enc.data_ptr(), w.frames)
-        if ev is not None:
-            ev.record(stream)
-        steps(S)
-
-    torch.cuda.synchronize()
-    torch.cuda.set_stream(stream)          # everything below is queued on the decoder's stream
-    for _ in range(args.warmup):
-        window()
-    torch.cuda.synchronize()
-    if dec.check() != 0:
-        raise RuntimeError(dec.last_error())
-
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
-        window(mids[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    xkv_ms = sum(starts[i].elapsed_time(mids[i]) for i in range(args.steps)) / args.steps
-    if dec.check() != 0:
-        raise RuntimeError(dec.last_error())
-    # kernel timing: HIP events on the decoder's stream around the cross-attention of one
-    # layer, issued `repeats` times back to back per step (the launch is idempotent), over
-    # the first positions of a window run right after the timed ones (steps are launched
-    # one by one there, since a captured step replays without per-launch host hooks); the
-    # cross-attention reads all frames at every position, so any positions will do
-    K.wd_profile(ctx, K.K_CROSS_ATTN, args.profile_layer, args.profile_repeats)
-    steps(min(S, args.profile_positions))
-    attn_ms, attn_n = K.wd_profile_read(ctx)
-    K.wd_profile(ctx, -1, -1, 1)
+    r, dec, enc = bench_whisper_greedy(w, args.steps, args.warmup, args,
+                                       graphs_off_windows=0 if args.no_extra else 1)
     if args.traffic_probe:
         src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.zeros_like(src)
@@ -461,53 +683,19 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-
-    ms_window = total_ms / args.steps
-    dec_ms = ms_window - xkv_ms
-    tokens = B * S
-    bytes_window = sum(whisper_bytes_per_step(w, p) for p in range(S))
-    attn_bytes = cross_attn_bytes_per_launch(w)
-    attn_avg_s = attn_ms / 1e3 / max(attn_n, 1)
-    achieved = attn_bytes / attn_avg_s
-    xkv_flops = 2.0 * w.n_enc * w.frames * w.d * 2 * w.d * w.layers
-    traffic = traffic_per_launch(w.name)
-    out = {
-        "metric": "decoder tokens/sec at batch B; achieved HBM GB/s as % of MI355X peak",
-        "value": tokens / (ms_window / 1e3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_window,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.w_dtype,
-        "data": "synthetic (seeded random-init weights N(0,0.02), encoder states N(0,1))",
-        "config": {"workload": w.name, "batch": B, "positions": S, "frames": w.frames,
-                   "layers": w.layers, "d": w.d, "heads": w.heads, "d_ff": w.d_ff,
-                   "vocab": w.vocab, "w_dtype": w.w_dtype, "cache_dtype": w.cache_dtype,
-                   "step": "one window: cross K/V projection + all positions, greedy on device"},
-        "decode_tokens_per_s": tokens / (dec_ms / 1e3),
-        "decode_ms_per_window": dec_ms,
-        "hbm_bytes_per_window": bytes_window,
-        "hbm_gbps_decode": bytes_window / (dec_ms / 1e3) / 1e9,
-        "hbm_frac_decode": bytes_window / (dec_ms / 1e3) / HBM_PEAK,
-        "cross_kv_ms": xkv_ms,
-        "cross_kv_tflops": xkv_flops / (xkv_ms / 1e3) / 1e12,
-        "wall_s": wall,
-        "roofline": {"kernel": "k_attn (cross-attention, one layer per launch)", "bound": "hbm",
-                     "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK,
-                     "traffic": traffic,
-                     "bytes_per_launch": attn_bytes, "avg_launch_us": attn_avg_s * 1e6,
-                     "launches_timed": attn_n},
-        "cpu_baseline": None,
-    }
     del dec, enc
     torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    out = dict(common, value=r["tokens_per_s"], ms_per_step=r["ms_per_window"],
+               data="synthetic (seeded random-init weights N(0,0.02), encoder states N(0,1))",
+               config={"workload": w.name, "batch": w.batch, "positions": w.steps, "frames": w.frames,
+                       "layers": w.layers, "d": w.d, "heads": w.heads, "d_ff": w.d_ff,
+                       "vocab": w.vocab, "w_dtype": w.w_dtype, "cache_dtype": w.cache_dtype,
+                       "step": "one window: cross K/V projection + all positions, greedy on device"})
+    out.update({k: v for k, v in r.items() if k not in ("workload", "batch", "positions", "tokens_per_s",
+                                                        "ms_per_window", "windows")})
+    if not args.no_extra and w.name == DEFAULT:
+        out["workloads"] = _extra_workloads(args)
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 
