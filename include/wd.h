@@ -213,6 +213,20 @@ wd_status wd_reorder(wd_ctx* ctx, const int32_t* beam_idx, int32_t B, int32_t n_
 wd_status wd_topk(wd_ctx* ctx, const float* logits, int32_t B, int32_t W, float* top_val,
                   int32_t* top_id, float* lse);
 
+/* wd_topk for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation) and hold no decoder context: the same
+ * candidates and log-sum-exp from logits dev fp32 [B, ld] (rows of V logits, ld >= V), launched
+ * on `stream` (a hipStream_t; NULL = the null stream).  It allocates nothing: its partial lists
+ * live in a static device array of the library (147,456 bytes per GPU, held until the process
+ * ends), which is why B is limited to WD_TOPK_NOALLOC_MAX_ROWS.  Every call on one GPU shares
+ * that array: calls that overlap on one GPU (concurrent streams or threads) race and give
+ * undefined results; calls ordered on one stream are safe.  Errors (message from
+ * wd_last_error(NULL)): ARG (null pointer, B outside [1, WD_TOPK_NOALLOC_MAX_ROWS], V < 1,
+ * ld < V, W outside [1, min(8, V)]), HIP. */
+#define WD_TOPK_NOALLOC_MAX_ROWS 64
+wd_status wd_topk_noalloc(const float* logits, int32_t B, int32_t V, int64_t ld, int32_t W, float* top_val,
+                          int32_t* top_id, float* lse, void* stream);
+
 /* Prompt prefill for rows 0..B-1 at positions 0..T-1 (Nest entry `prefill`;
  * decoder.h `PrefillBuild`).  tokens dev int32 [B, T]; embeds dev [B, A, d]
  * in w_dtype or NULL: rows offset..offset+A-1 take these embeddings instead of

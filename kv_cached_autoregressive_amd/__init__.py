@@ -20,7 +20,7 @@ __all__ = [
     "WdError", "WdConfig", "WdTensor", "lib", "lib_path", "declared_functions",
     "wd_abi_version", "wd_workspace_bytes", "wd_load", "wd_cross_kv", "wd_cross_kv_ragged", "wd_step", "wd_reorder",
     "wd_topk", "wd_prefill", "wd_encoder_workspace_bytes", "wd_load_encoder", "wd_encode", "wd_listen", "wd_check", "wd_last_error", "wd_free", "wd_profile", "wd_profile_read",
-    "wd_debug_cache", "wd_set_option", "wd_get_option", "WD_OPT_GRAPHS",
+    "wd_debug_cache", "wd_set_option", "wd_get_option", "WD_OPT_GRAPHS", "wd_topk_noalloc",
     "config_from", "Decoder", "DTYPES", "STATUS",
 ]
 
@@ -93,6 +93,7 @@ def lib():
             "wd_profile_read": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
             "wd_debug_cache": (i32, [vp, i32, i32, ctypes.POINTER(vp)]),
             "wd_set_option": (i32, [vp, i32, i32]),
+            "wd_topk_noalloc": (i32, [vp, i32, i32, i64, i32, vp, vp, vp, vp]),
             "wd_get_option": (i32, [vp, i32, ctypes.POINTER(i32)]),
         }
         for name, (res, args) in sig.items():
@@ -215,6 +216,12 @@ def wd_debug_cache(ctx, which: int, layer: int) -> int:
     p = ctypes.c_void_p()
     _check(lib().wd_debug_cache(ctx, which, layer, ctypes.byref(p)), ctx)
     return p.value
+
+
+def wd_topk_noalloc(logits: int, B: int, V: int, ld: int, W: int, top_val: int, top_id: int, lse: int,
+                    stream: int = 0):
+    _check(lib().wd_topk_noalloc(ctypes.c_void_p(logits), B, V, ld, W, ctypes.c_void_p(top_val),
+                                 ctypes.c_void_p(top_id), ctypes.c_void_p(lse), ctypes.c_void_p(stream)))
 
 
 def wd_set_option(ctx, option: int, value: int):

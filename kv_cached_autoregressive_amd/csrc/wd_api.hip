@@ -18,6 +18,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -757,6 +758,40 @@ std::vector<Need> required(const wd_config& c) {
 
 }  // namespace
 
+// ---- device scratch of wd_topk_noalloc ----------------------------------------------------------
+// The per-part candidate lists of up to WD_TOPK_NOALLOC_MAX_ROWS rows (at most 32 parts per row,
+// each W <= 8 (value, id) pairs and a (max, sum) pair): a file-scope device array, so the entry
+// point needs no workspace and allocates nothing.  Each GPU holds its own copy until the
+// process ends; its device address is looked up once per device, with that device current.
+// The array has external linkage: the runtime resolves a registered device variable by its
+// symbol name in the code object, and an internal-linkage (static) one stays a local symbol
+// that lookup cannot find.
+constexpr size_t kTopkScratchBytes = (size_t)WD_TOPK_NOALLOC_MAX_ROWS * 32 * (8 * 8 + 8);
+__device__ __align__(256) unsigned char scratch[kTopkScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The current device's address of `scratch` (the host-side symbol is only a stand-in).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+}  // namespace
+
 extern "C" {
 
 int32_t wd_abi_version(void) { return WD_ABI_VERSION; }
@@ -1385,6 +1420,29 @@ wd_status wd_topk(wd_ctx* ctx, const float* logits, int32_t B, int32_t W, float*
     return WD_OK;
   } catch (...) {
     return fail(ctx, WD_ERR_INTERNAL, "wd_topk: internal error");
+  }
+}
+
+wd_status wd_topk_noalloc(const float* logits, int32_t B, int32_t V, int64_t ld, int32_t W, float* top_val,
+                          int32_t* top_id, float* lse, void* stream) {
+  try {
+    if (!logits || !top_val || !top_id || !lse) return fail(nullptr, WD_ERR_ARG, "wd_topk_noalloc: null pointer");
+    if (B < 1 || B > WD_TOPK_NOALLOC_MAX_ROWS)
+      return fail(nullptr, WD_ERR_ARG, "wd_topk_noalloc: B outside [1, " + std::to_string(WD_TOPK_NOALLOC_MAX_ROWS) +
+                                           "] (the size of its static scratch)");
+    if (V < 1 || ld < V) return fail(nullptr, WD_ERR_ARG, "wd_topk_noalloc: V < 1 or ld < V");
+    if (W < 1 || W > 8 || W > V) return fail(nullptr, WD_ERR_ARG, "wd_topk_noalloc: W outside [1, min(8, V)]");
+    if (wd::topk_scratch_bytes(B, V) > kTopkScratchBytes)
+      return fail(nullptr, WD_ERR_INTERNAL, "wd_topk_noalloc: scratch too small for this shape");
+    void* sp = nullptr;
+    const hipError_t e = scratch_address(&sp);
+    if (e != hipSuccess) return fail(nullptr, WD_ERR_HIP, std::string("wd_topk_noalloc: scratch address: ") + hipGetErrorString(e));
+    const hipError_t l = wd::launch_topk_lse(logits, B, V, ld, W, top_val, top_id, lse, sp,
+                                             reinterpret_cast<hipStream_t>(stream));
+    if (l != hipSuccess) return fail(nullptr, WD_ERR_HIP, std::string("wd_topk_noalloc: launch: ") + hipGetErrorString(l));
+    return WD_OK;
+  } catch (...) {
+    return fail(nullptr, WD_ERR_INTERNAL, "wd_topk_noalloc: internal error");
   }
 }
 

@@ -117,6 +117,13 @@ def test_null_context_calls_return_arg():
     assert L.wd_prefill(None, None, 1, 1, None, 0, 0, None, None) == 1
     assert L.wd_check(None) == 1
     assert L.wd_set_option(None, K.WD_OPT_GRAPHS, 0) == 1
+    # the allocation-free candidates entry point checks its arguments before any device call
+    fake = ctypes.c_void_p(FAKE_DATA)
+    assert L.wd_topk_noalloc(None, 1, 10, 10, 1, fake, fake, fake, None) == 1
+    assert L.wd_topk_noalloc(fake, 65, 10, 10, 1, fake, fake, fake, None) == 1
+    assert "scratch" in K.wd_last_error(None)
+    assert L.wd_topk_noalloc(fake, 4, 10, 9, 1, fake, fake, fake, None) == 1
+    assert L.wd_topk_noalloc(fake, 4, 10, 10, 9, fake, fake, fake, None) == 1
     v = ctypes.c_int32()
     assert L.wd_get_option(None, K.WD_OPT_GRAPHS, ctypes.byref(v)) == 1
     L.wd_free(None)
