@@ -128,6 +128,187 @@ def summarize_traffic(fetch_csv: str, write_csv: str, commands: list) -> dict:
             "commands": commands}
 
 
+# ---- per-kernel HBM traffic against algorithmic bytes (two rocprofv3 --pmc runs) ----------------
+EPI = {"store": 0, "resid": 1, "qkv": 3, "gelu_split": 5, "swiglu_split": 6}
+
+
+def sk_shape(N: int, K: int, B: int, epi: int):
+    """The split-K skinny GEMM's launch shape for a projection (the library's policy, restated
+    for labelling counter rows): (NBW, NBB, NSC, G, workgroups) or None when the projection
+    takes another kernel."""
+    NB, KST = (N + 15) // 16, K // 32
+    NBB = 1 if B <= 16 else 2 if B <= 32 else 4
+    NBW = 2 if (NB >= 256 or KST >= 128 or epi == EPI["swiglu_split"]) else 1
+    narrow = NBB == 1 and (epi != EPI["swiglu_split"] or KST > 16) and KST * ((NB + 3) // 4) >= 8 * 256
+    if narrow:
+        NBW = 1
+    ncg = (NB + 4 * NBW - 1) // (4 * NBW)
+    S = max(2, min((KST * ncg + 255) // 256, 16 if narrow else 8))
+    G = (KST + S - 1) // S
+    if narrow:
+        if G > 32:
+            return None
+        nsc = max(4, (KST + G - 1) // G)
+        return NBW, NBB, (16 if nsc > 8 else nsc), G, ncg * G
+    if ncg * G > 256 and NBW == 1:
+        NBW = 2
+        ncg = (NB + 7) // 8
+        S = max(2, min((KST * ncg + 255) // 256, 8))
+        G = (KST + S - 1) // S
+    if N <= 2048 and KST >= 16:
+        G = 8 * ((KST + 63) // 64)
+    if G > 32:
+        return None
+    nsc = max(4, (KST + G - 1) // G)
+    return NBW, NBB, (16 if nsc > 8 else nsc), G, ncg * G
+
+
+def projections(w):
+    """(role, N, K, epilogue) of one layer's projections, in launch order."""
+    d, ff = w.d, w.d_ff
+    if w.arch == "whisper":
+        return [("q|k|v", 3 * d, d, EPI["qkv"]), ("self out", d, d, EPI["resid"]), ("cross q", d, d, EPI["store"]),
+                ("cross out", d, d, EPI["resid"]), ("fc1", ff, d, EPI["gelu_split"]), ("fc2", d, ff, EPI["resid"])]
+    qd, kvd = w.heads * w.head_dim, w.kv_heads * w.head_dim
+    return [("q|k|v", qd + 2 * kvd, d, EPI["store"]), ("out", d, qd, EPI["resid"]),
+            ("gate|up", 2 * ff, d, EPI["swiglu_split"]), ("down", d, ff, EPI["resid"])]
+
+
+def canon_kernel(name: str) -> str:
+    """'base<int and bool template arguments>' of a kernel name, demangled by the profiler or
+    not (instantiations over _Float16 come out mangled): the type arguments are dropped."""
+    m = re.match(r"_ZN2wd(\d+)(\w+)", name)
+    if m:
+        base = m.group(2)[:int(m.group(1))]
+        rest = m.group(2)[int(m.group(1)):]
+        args = [("true" if a == "b1" else "false") if a.startswith("b") else a[1:]
+                for a in re.findall(r"L(i\d+|b[01])E", rest)]
+        return f"{base}<{','.join(args)}>" if args else base
+    m = re.search(r"(?:wd::)?(\w+)<([^()]*)>\(", name)
+    if m:
+        args = [a.strip() for a in m.group(2).split(",") if re.fullmatch(r"\s*(-?\d+|true|false)\s*", a)]
+        return f"{m.group(1)}<{','.join(args)}>"
+    m = re.search(r"(?:wd::)?(\w+)\(", name)
+    return m.group(1) if m else name[:60]
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, w, positions: int, commands: list,
+                       mfma_csv: str = None) -> str:
+    """Markdown table of HBM bytes per dispatch (FETCH_SIZE + WRITE_SIZE, each scaled by what it
+    reads for the run's device copy of COPY_PROBE_BYTES) per kernel and launch shape, against the
+    kernel's algorithmic bytes (weights read once, cache rows read) and the activation and
+    partial-slab bytes its design adds."""
+    import csv
+    import collections
+
+    def load(path, counter):
+        groups, copies = collections.defaultdict(list), []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if "copyBuffer" in r["Kernel_Name"]:
+                copies.append(v)
+                continue
+            wg = max(1, int(r.get("Workgroup_Size", 1) or 1))
+            grid = int(r.get("Grid_Size", 0) or 0) // wg
+            groups[(r["Kernel_Name"], grid)].append(v)
+        return groups, max(copies) / (COPY_PROBE_BYTES / 1024)
+
+    fg, ff_ = load(fetch_csv, "FETCH_SIZE")
+    wg_, wf = load(write_csv, "WRITE_SIZE")
+    mf = {}
+    if mfma_csv:
+        for r in csv.DictReader(open(mfma_csv)):
+            if r["Counter_Name"] != "MfmaUtil" or "copyBuffer" in r["Kernel_Name"]:
+                continue
+            wgs = max(1, int(r.get("Workgroup_Size", 1) or 1))
+            mf.setdefault((r["Kernel_Name"], int(r.get("Grid_Size", 0) or 0) // wgs), []).append(float(r["Counter_Value"]))
+    wb, cb = DT_BYTES[w.w_dtype], DT_BYTES[w.cache_dtype]
+    B, d = w.batch, w.d
+    Bp = 16 if B <= 16 else 32 if B <= 32 else 64
+    # labels of the projection shapes
+    label = {}
+    for role, N, K, epi in projections(w):
+        sh = sk_shape(N, K, B, epi)
+        if sh is None:
+            continue
+        NBW, NBB, NSC, G, grid = sh
+        key = (f"k_mgemv_sk<{NBW},{NBB},{NSC},1>", grid)
+        alg = N * K * wb
+        extra = G * B * N * 4 if G > 1 else 0   # fp32 partial slabs written (read by the consumer)
+        prev = label.get(key)
+        if prev is None:
+            label[key] = (f"{role} (K groups {G})", alg, extra, G)
+        else:   # two projections with one launch shape: their mean
+            label[key] = (f"{prev[0]}, {role} (K groups {G})", (prev[1] + alg) // 2, (prev[2] + extra) // 2, G)
+    # partial slabs the attention prologues read (q, and the appended k, v) when the q
+    # projection is split
+    qkv_G = [sk_shape(N, K, B, e)[3] for r, N, K, e in projections(w) if r == "q|k|v"][0]
+    cq_G = [sk_shape(N, K, B, e)[3] for r, N, K, e in projections(w) if r == "cross q"] if w.arch == "whisper" else [1]
+    mean_rows = (positions + 1) / 2 if w.arch == "whisper" else w.prefill_len + (positions + 1) / 2
+    rows = []
+    for key in sorted(set(fg) | set(wg_), key=lambda k: -sum(fg.get(k, [0]))):
+        name, grid = key
+        f = fg.get(key, [])
+        wr = wg_.get(key, [])
+        n = max(len(f), len(wr))
+        fb = (sum(f) / max(len(f), 1)) * 1024 / ff_
+        wb_ = (sum(wr) / max(len(wr), 1)) * 1024 / wf
+        short = canon_kernel(name)
+        role, alg, extra = "", None, None
+        if (short, grid) in label:
+            role, alg, extra, G = label[(short, grid)]
+        if "k_attn<" in short and ",true," in short:
+            role, alg = "cross-attention", cross_attn_bytes_per_launch(w)
+            if cq_G[0] > 1:
+                extra = cq_G[0] * B * d * 4
+                role += " (+ cross-q partials read)"
+        elif "k_attn<" in short:
+            role = "self-attention"
+            alg = int(B * w.kv_heads * mean_rows * w.head_dim * 2 * cb)
+            if qkv_G > 1:
+                nqkv = 3 * d if w.arch == "whisper" else (w.heads + 2 * w.kv_heads) * w.head_dim
+                extra = qkv_G * B * nqkv * 4
+                role += " (+ q|k|v partials read)"
+        elif "k_mgemv_lds" in short or "k_mgemv<" in short:
+            role, alg = "tied head (logits + argmax keys)", w.vocab * d * wb
+        elif "k_norm" in short:
+            role = "row norm (+ partial fold)"
+        elif "k_mgemv_finish" in short:
+            role = "split-K finish (GELU / SwiGLU)"
+        elif "k_attn_combine" in short:
+            role = "attention split combine"
+        mu = mf.get(key)
+        rows.append((short, grid, n, fb, wb_, role, alg, extra, None if not mu else sum(mu) / len(mu)))
+    out = [f"# HBM traffic per kernel: {w.name} (decode window of positions "
+           f"{'0' if w.arch == 'whisper' else w.prefill_len}..{(0 if w.arch == 'whisper' else w.prefill_len) + positions - 1})",
+           "",
+           "Commands (run from /tmp with TMPDIR=/tmp, repository at $R):", ""]
+    out += [f"    {c}" for c in commands]
+    out += ["",
+            f"FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what each reads for the run's "
+            f"{COPY_PROBE_BYTES >> 20} MiB device copy (fetch scale {ff_:.3f}, write scale {wf:.3f}).  "
+            "`algorithmic` is the kernel's share of the step's bytes (weights read once; self-cache rows "
+            "0..pos; the cross cache); `design extra` is what the launch shape adds in HBM traffic: "
+            "the fp32 partial slabs a split-K projection writes, or the ones an attention prologue "
+            "reads (activation tiles re-read by many workgroups come from the L2 and do not show "
+            "here).  Kernels without an algorithmic figure move activations and partial slabs only "
+            "(the norms fold the residual projections' slabs, the finish kernel the fc1 / gate|up "
+            "slabs).", "",
+            "| kernel | workgroups | dispatches | fetch B | write B | role | algorithmic B | design extra B | "
+            "measured / (alg + extra) | MfmaUtil % |",
+            "|---|---|---|---|---|---|---|---|---|---|"]
+    for short, grid, n, fb, wb_, role, alg, extra, mu in rows:
+        ratio = ""
+        if alg:
+            ratio = f"{(fb + wb_) / (alg + (extra or 0)):.2f}"
+        out.append(f"| `{short[:70]}` | {grid} | {n} | {fb:,.0f} | {wb_:,.0f} | {role} | "
+                   f"{'' if alg is None else f'{alg:,}'} | {'' if extra is None else f'{extra:,}'} | {ratio} | "
+                   f"{'' if mu is None else f'{mu:.1f}'} |")
+    return "\n".join(out) + "\n"
+
+
 def qwen_bytes_per_step(w, pos: int) -> int:
     """Algorithmic HBM bytes of one Qwen3 decode step at position `pos`: every weight once
     (q, k, v, o, gate, up, down, the norms, the tied head), the B embedding rows and the
@@ -615,11 +796,22 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the cross-attention traffic summary under profiles/ from two --pmc runs and exit")
     ap.add_argument("--commands", nargs="*", default=[], help="the profiler commands, recorded in the summary")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/counters_<config>.md (HBM bytes per kernel against algorithmic bytes) "
+                         "from two --pmc runs of the --config workload with --positions and exit")
+    ap.add_argument("--mfma-csv", default=None, help="with --summarize-counters: a third --pmc MfmaUtil run")
     ap.add_argument("--encoder", action="store_true",
                     help="time the audio encoder (wd_encode) of the workload's encoder sets instead of the decoder")
     ap.add_argument("--encoder-layers", type=int, default=0, help="encoder layers (default: the decoder's)")
     ap.add_argument("--mels", type=int, default=80, help="mel channels of the encoder's input")
     args = ap.parse_args()
+    if args.summarize_counters:
+        w = WL.by_name(args.config)
+        md = summarize_counters(*args.summarize_counters, w, args.positions or w.steps, args.commands, args.mfma_csv)
+        with open(os.path.join(ROOT, "profiles", f"counters_{w.name}.md"), "w") as f:
+            f.write(md)
+        print(md)
+        return
     if args.summarize_traffic:
         out = summarize_traffic(*args.summarize_traffic, args.commands)
         with open(TRAFFIC_FILE, "w") as f:
