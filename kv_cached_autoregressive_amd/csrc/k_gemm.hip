@@ -141,9 +141,12 @@ __global__ __launch_bounds__(256) void k_xkv_frag(const T* __restrict__ Xf, cons
 
 // Block tile 256 rows of X x 128 output columns; eight waves as 4 x 2, each 64 x 64 (4 x 4 MFMA
 // tiles).  Per 32-deep K step the block's 16 + 8 operand tiles (1 KB each, fragment order) are
-// staged once through LDS (double-buffered, next step's loads in flight) and every wave reads
-// its 4 + 4 tiles from there, so each fragment leaves L2 once per block instead of once per
-// wave.  Same XCD panel order and epilogue as k_xkv_frag, the 256 rows in two halves.
+// staged once through LDS (double-buffered) and every wave reads its 4 + 4 tiles from there,
+// so each fragment leaves L2 once per block instead of once per wave.  Loads run two K steps
+// ahead of the MFMAs (two register sets in front of the two LDS slots), unconditionally: a
+// load under a branch made the compiler wait for every load at the branch (23.2 -> 22.0 ms per
+// large-v3 window branch-free, 32.3 ms with the branches).  Same XCD panel order and epilogue
+// as k_xkv_frag, the 256 rows in two halves.
 template <typename T, typename CT>
 __global__ __launch_bounds__(512) void k_xkv_lds(const T* __restrict__ Xf, const T* __restrict__ Wf, int K,
                                                  XkvOut o, int n_mt, int n_nt, int pg) {
@@ -164,41 +167,51 @@ __global__ __launch_bounds__(512) void k_xkv_lds(const T* __restrict__ Xf, const
   const int KST = K >> 5, lr = lane & 15, lq = lane >> 4;
   const v4u* __restrict__ A = reinterpret_cast<const v4u*>(Xf) + (int64_t)mt * RT * KST * 64;
   const v4u* __restrict__ B = reinterpret_cast<const v4u*>(Wf) + (int64_t)nt * CTL * KST * 64;
-  v4u g[3];
-  auto gload = [&](int st) __attribute__((always_inline)) {
+  // a thread's share of one K step's 24 tiles: 3 16-byte loads (step clamped: no load under a
+  // branch, so the compiler's wait counts stay exact)
+  auto gload = [&](int st, v4u (&g)[3]) __attribute__((always_inline)) {
+    st = min(st, KST - 1);
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       const int q = t + 512 * u, tl = q >> 6, w = q & 63;
       g[u] = tl < RT ? A[((int64_t)tl * KST + st) * 64 + w] : B[((int64_t)(tl - RT) * KST + st) * 64 + w];
     }
   };
+  auto gstore = [&](int slot, const v4u (&g)[3]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) stage[slot][t + 512 * u] = g[u];
+  };
   f32x4_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) acc[i][jn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  gload(0);
-#pragma unroll
-  for (int u = 0; u < 3; ++u) stage[0][t + 512 * u] = g[u];
-  __syncthreads();
-  for (int st = 0; st < KST; ++st) {
-    const int cur = st & 1;
-    const bool more = st + 1 < KST;
-    if (more) gload(st + 1);
+  auto mma_step = [&](int slot) __attribute__((always_inline)) {
     v4u a[4], b[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = stage[cur][(wm * 4 + i) * 64 + lane];
+    for (int i = 0; i < 4; ++i) a[i] = stage[slot][(wm * 4 + i) * 64 + lane];
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn) b[jn] = stage[cur][(RT + wn * 4 + jn) * 64 + lane];
+    for (int jn = 0; jn < 4; ++jn) b[jn] = stage[slot][(RT + wn * 4 + jn) * 64 + lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int jn = 0; jn < 4; ++jn)
         acc[i][jn] = mfma16x16x32(__builtin_bit_cast(uint4, a[i]), __builtin_bit_cast(uint4, b[jn]), acc[i][jn], (T*)nullptr);
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < 3; ++u) stage[cur ^ 1][t + 512 * u] = g[u];
-    }
+  };
+  v4u ga[3], gb[3];
+  gload(0, ga);
+  gstore(0, ga);
+  gload(1, ga);
+  __syncthreads();
+  // KST even (K % 64 == 0 for every 16-bit Whisper width): two steps per trip
+  for (int st = 0; st < KST; st += 2) {
+    gload(st + 2, gb);
+    mma_step(0);
+    gstore(1, ga);
+    __syncthreads();
+    gload(st + 3, ga);
+    mma_step(1);
+    gstore(0, gb);
     __syncthreads();
   }
   // epilogue through LDS (the staging buffers, free after the loop's last barrier), 128 rows
@@ -289,6 +302,7 @@ hipError_t launch_cross_kv_gemm(const void* X, const void* W, const float* bias,
   }
   // 16-bit: X already in fragment order (launch_pack_rows, rows padded to 256), W in fragment
   // order; 128 / hd heads per 128-column tile
+  // (d % 128 == 0 also makes the K step count even, which k_xkv_lds's two-step trips assume)
   if ((hd != 64 && hd != 128) || d % 128 || (cache_dtype != DT_F16 && cache_dtype != DT_BF16)) return hipErrorInvalidValue;
   // 256-row blocks with LDS-shared operands once they fill the chip twice over (large-v3: 7500
   // blocks, 902 -> 704 us per layer; whisper-small 1128, 84.6 -> 81.0 us), else 128-row blocks
