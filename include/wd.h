@@ -116,7 +116,10 @@ typedef struct {
 int32_t wd_abi_version(void);
 
 /* Bytes of workspace wd_load needs for cfg (repacked weights, self caches,
- * cross caches, step scratch, device error word); 0 if cfg is invalid. */
+ * cross caches, step scratch, device error word); 0 if cfg is invalid.  The
+ * pages' decoders allocate the same state themselves when they load (wavo
+ * decoder.rs `Decoder::load` sizes the self and cross caches from the model
+ * dimensions); here the caller allocates it, so the size is a call of its own. */
 size_t wd_workspace_bytes(const wd_config* cfg);
 
 /* Validates cfg and the weight list, repacks the weights into `workspace`
@@ -255,19 +258,26 @@ wd_status wd_set_option(wd_ctx* ctx, int32_t option, int32_t value);
 wd_status wd_get_option(wd_ctx* ctx, int32_t option, int32_t* value);
 
 /* Synchronises the stream, reads and clears the sticky device flag:
- * WD_OK, WD_ERR_RANGE (flag was set) or WD_ERR_HIP. */
+ * WD_OK, WD_ERR_RANGE (flag was set) or WD_ERR_HIP.  The pages report bad
+ * input as a returned error (wavo decoder.rs: `Decoder::load` and the step
+ * return `Result`) or a thrown one (mlx-bun whisper.ts); a fault seen only on
+ * the device cannot return from an asynchronous launch, so it is collected here. */
 wd_status wd_check(wd_ctx* ctx);
 
 /* Message for the last non-OK status of ctx (ctx NULL: of the last failed
- * wd_load on this thread).  Valid until the next call on ctx. */
+ * wd_load on this thread).  Valid until the next call on ctx.  (The text that
+ * the pages' `Result` errors and exceptions carry, as a C string.) */
 const char* wd_last_error(const wd_ctx* ctx);
 
 /* Waits for the context's stream, then releases the host-side context (captured
  * step graphs, events); never touches caller memory.  After it returns, the caller
- * may free the workspace. */
+ * may free the workspace.  (The pages' decoders drop their state with the object
+ * that owns it, wavo `Decoder`; a C caller releases it explicitly.) */
 void wd_free(wd_ctx* ctx);
 
-/* --- measurement support ------------------------------------------------
+/* --- measurement support (not part of the decoding method) ----------------
+ * For benchmarks and profilers only: a decoder never needs these calls, and
+ * with recording off (the default) they change nothing on the step path.
  * Records a pair of HIP events on the context's stream around the launches
  * of kernel class `kernel` in layer `layer` (-1: all layers) during later
  * wd_step / wd_cross_kv calls; each such launch is issued `repeats` times back
@@ -281,7 +291,8 @@ void wd_free(wd_ctx* ctx);
 wd_status wd_profile(wd_ctx* ctx, int32_t kernel, int32_t layer, int32_t repeats);
 wd_status wd_profile_read(wd_ctx* ctx, double* total_ms, int64_t* launches);
 
-/* --- test hook ------------------------------------------------------------
+/* --- test hook (not part of the decoding method) ---------------------------
+ * For parity tests only; a decoder never needs it.
  * Device address of one cache block of the current buffer, for checking the
  * caches element by element (in the spirit of named intermediate dumps,
  * transcribe.cpp qwen3_asr/decoder.h `DecoderDumps`).  which: 0 self K,

@@ -29,6 +29,19 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
+// One 16-byte load per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane i's bytes land at lds_wave + 16 i, so `lds_wave` is the wave's (uniform) 1 KB slot.
+// The load counts in vmcnt like any vector load and writes no VGPR.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave, 16, 0, 0);
+}
+// s_waitcnt with vmcnt = N (N < 16) and the other counters left alone
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 struct XkvOut {
   const float* bias; int M, N, d, frames, max_frames, H, hd;
   void* Kc; void* Vc;
@@ -141,19 +154,20 @@ __global__ __launch_bounds__(256) void k_xkv_frag(const T* __restrict__ Xf, cons
 
 // Block tile 256 rows of X x 128 output columns; eight waves as 4 x 2, each 64 x 64 (4 x 4 MFMA
 // tiles).  Per 32-deep K step the block's 16 + 8 operand tiles (1 KB each, fragment order) are
-// staged once through LDS (double-buffered) and every wave reads its 4 + 4 tiles from there,
-// so each fragment leaves L2 once per block instead of once per wave.  Loads run two K steps
-// ahead of the MFMAs (two register sets in front of the two LDS slots), unconditionally: a
-// load under a branch made the compiler wait for every load at the branch (23.2 -> 22.0 ms per
-// large-v3 window branch-free, 32.3 ms with the branches).  Same XCD panel order and epilogue
-// as k_xkv_frag, the 256 rows in two halves.
+// loaded once into LDS and every wave reads its 4 + 4 tiles from there, so each fragment
+// leaves L2 once per block instead of once per wave.  The loads go straight from global
+// memory into a ring of three LDS slots, two K steps ahead of the MFMAs (no staging
+// registers, no LDS stores); each step waits for its own loads by count and meets the other
+// waves at a bare barrier (a full __syncthreads would also wait for the loads still in
+// flight).  Same XCD panel order and epilogue as k_xkv_frag, the 256 rows in two halves.
 template <typename T, typename CT>
 __global__ __launch_bounds__(512) void k_xkv_lds(const T* __restrict__ Xf, const T* __restrict__ Wf, int K,
                                                  XkvOut o, int n_mt, int n_nt, int pg) {
   constexpr int RT = 16, CTL = 8, NTL = RT + CTL;   // tiles per block and K step
   constexpr int CLD = 128 + 8;
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-  __shared__ __align__(16) v4u stage[2][NTL * 64];            // 2 x 24 KB
+  constexpr int NSLOT = 3;
+  __shared__ __align__(16) v4u stage[NSLOT][NTL * 64];        // 3 x 24 KB
   static_assert(sizeof(stage) >= 128 * CLD * sizeof(CT), "epilogue tile fits the staging buffers");
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   // workgroup L runs on XCD L % 8; that XCD's j-th workgroup takes, within a group of pg of
@@ -167,55 +181,46 @@ __global__ __launch_bounds__(512) void k_xkv_lds(const T* __restrict__ Xf, const
   const int KST = K >> 5, lr = lane & 15, lq = lane >> 4;
   const v4u* __restrict__ A = reinterpret_cast<const v4u*>(Xf) + (int64_t)mt * RT * KST * 64;
   const v4u* __restrict__ B = reinterpret_cast<const v4u*>(Wf) + (int64_t)nt * CTL * KST * 64;
-  // a thread's share of one K step's 24 tiles: 3 16-byte loads (step clamped: no load under a
-  // branch, so the compiler's wait counts stay exact)
-  auto gload = [&](int st, v4u (&g)[3]) __attribute__((always_inline)) {
+  // a K step's 24 tiles go straight to LDS, wave wv loading tiles wv, 8 + wv (X) and 16 + wv
+  // (W); the step index is clamped so every thread issues exactly 3 loads per step and the
+  // vmcnt arithmetic below stays exact
+  auto issue = [&](int st) __attribute__((always_inline)) {
+    const int slot = st % NSLOT;
     st = min(st, KST - 1);
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int q = t + 512 * u, tl = q >> 6, w = q & 63;
-      g[u] = tl < RT ? A[((int64_t)tl * KST + st) * 64 + w] : B[((int64_t)(tl - RT) * KST + st) * 64 + w];
-    }
-  };
-  auto gstore = [&](int slot, const v4u (&g)[3]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < 3; ++u) stage[slot][t + 512 * u] = g[u];
+    const int64_t so = (int64_t)st * 64 + lane;
+    lds_dma16(A + (int64_t)wv * KST * 64 + so, &stage[slot][wv * 64]);
+    lds_dma16(A + (int64_t)(8 + wv) * KST * 64 + so, &stage[slot][(8 + wv) * 64]);
+    lds_dma16(B + (int64_t)wv * KST * 64 + so, &stage[slot][(16 + wv) * 64]);
   };
   f32x4_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) acc[i][jn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto mma_step = [&](int slot) __attribute__((always_inline)) {
+  // three slots, loads two K steps ahead: at step st the slot of st - 1 is free once every
+  // wave is past the barrier (its MFMAs of st - 1 have consumed their LDS reads)
+  issue(0);
+  issue(1);
+  for (int st = 0; st < KST; ++st) {
+    wait_vmcnt<3>();                  // this thread's loads of step st have landed
+    __builtin_amdgcn_s_barrier();     // ... and every thread's
+    issue(st + 2);
+    const v4u* S = stage[st % NSLOT];
     v4u a[4], b[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = stage[slot][(wm * 4 + i) * 64 + lane];
+    for (int i = 0; i < 4; ++i) a[i] = S[(wm * 4 + i) * 64 + lane];
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn) b[jn] = stage[slot][(RT + wn * 4 + jn) * 64 + lane];
+    for (int jn = 0; jn < 4; ++jn) b[jn] = S[(RT + wn * 4 + jn) * 64 + lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int jn = 0; jn < 4; ++jn)
         acc[i][jn] = mfma16x16x32(__builtin_bit_cast(uint4, a[i]), __builtin_bit_cast(uint4, b[jn]), acc[i][jn], (T*)nullptr);
-  };
-  v4u ga[3], gb[3];
-  gload(0, ga);
-  gstore(0, ga);
-  gload(1, ga);
-  __syncthreads();
-  // KST even (K % 64 == 0 for every 16-bit Whisper width): two steps per trip
-  for (int st = 0; st < KST; st += 2) {
-    gload(st + 2, gb);
-    mma_step(0);
-    gstore(1, ga);
-    __syncthreads();
-    gload(st + 3, ga);
-    mma_step(1);
-    gstore(0, gb);
-    __syncthreads();
   }
-  // epilogue through LDS (the staging buffers, free after the loop's last barrier), 128 rows
-  // at a time: waves 0, 1 (rows 0..127) then waves 2, 3 of each column half
+  wait_vmcnt<0>();                    // the clamped loads past the end land before LDS is reused
+  __syncthreads();
+  // epilogue through LDS (the staging buffers), 128 rows at a time: waves 0, 1 (rows 0..127)
+  // then waves 2, 3 of each column half
   CT* Cs = reinterpret_cast<CT*>(&stage[0][0]);
   const int n0 = nt * 128;
   const bool isv = n0 >= o.d;
@@ -302,7 +307,6 @@ hipError_t launch_cross_kv_gemm(const void* X, const void* W, const float* bias,
   }
   // 16-bit: X already in fragment order (launch_pack_rows, rows padded to 256), W in fragment
   // order; 128 / hd heads per 128-column tile
-  // (d % 128 == 0 also makes the K step count even, which k_xkv_lds's two-step trips assume)
   if ((hd != 64 && hd != 128) || d % 128 || (cache_dtype != DT_F16 && cache_dtype != DT_BF16)) return hipErrorInvalidValue;
   // 256-row blocks with LDS-shared operands once they fill the chip twice over (large-v3: 7500
   // blocks, 902 -> 704 us per layer; whisper-small 1128, 84.6 -> 81.0 us), else 128-row blocks

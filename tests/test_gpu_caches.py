@@ -91,3 +91,38 @@ def test_cross_and_self_caches_match_oracle(w_dtype, cache_dtype, batch, frames)
             worst = max(worst, _cmp(g, r, cache_dtype, f"self {'KV'[which]} pos {p}", 2e-2))
     G.close()
     say(f"  largest one-ulp fraction {worst:.2e}")
+
+
+@pytest.mark.parametrize("name", ["whisper_large_bf16_b64", "whisper_small_f16_b16"])
+def test_cross_kv_full_size_sampled_rows(name):
+    """The cross K/V projection at the full benchmark shapes (large-v3: 96000 x 1280 x 2560,
+    256 x 256 blocks; whisper-small: 24000 x 768 x 1536, 256 x 128 blocks), one layer, in
+    the launch configuration of the benchmark: sampled rows of both caches, every column,
+    against the oracle's projection of the same rows (each cache row depends only on its
+    own encoder row).  The rows cover the first and last sets, the first and last frames and
+    256-row panel edges."""
+    need_gpu()
+    base = WL.by_name(name)
+    w = WL.reduced(base, layers=1)
+    say(f"[cross K/V full size] {w.describe()}")
+    W = WL.make_weights(w)
+    enc = WL.make_encoder_states(w)
+    G = GpuRun(w, W)
+    G.cross(enc)
+    rng = np.random.default_rng(5)
+    sets = sorted({0, 1, w.n_enc // 2, w.n_enc - 2, w.n_enc - 1})
+    frames = sorted({0, 1, 255, 256, 511, 777, 1023, 1024, w.frames - 2, w.frames - 1,
+                     *rng.integers(0, w.frames, 12).tolist()})
+    O = OW.WhisperOracle(OW.dims_of(w), W)
+    O.cross_kv([enc[e][frames] for e in sets])
+    worst = 0.0
+    fi = torch.tensor(frames, device="cuda")
+    for which, ref in ((2, O.Kc[0]), (3, O.Vc[0])):
+        c = G.dec.cache(which, 0)
+        for k, e in enumerate(sets):
+            g = c[e].index_select(1, fi).float().cpu().numpy()          # [H, n_frames, hd]
+            g = g.transpose(1, 0, 2).reshape(len(frames), w.d)
+            worst = max(worst, _cmp(g, ref[k], w.cache_dtype, f"cross {'KV'[which - 2]} set {e}", 2e-3))
+    assert G.check() == 0
+    G.close()
+    say(f"  {len(sets)} sets x {len(frames)} frames x {2 * w.d} columns; largest one-ulp fraction {worst:.2e}")

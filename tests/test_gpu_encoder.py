@@ -101,3 +101,33 @@ def test_listen_equals_encode_then_cross_kv():
     assert np.array_equal(lg1, lg2) and np.array_equal(am1, am2)
     assert G.check() == 0
     G.close()
+
+
+def test_encoder_large_v3_dims_one_layer():
+    """The encoder at the large-v3 widths the decoder benchmark runs behind (d = 1280, 20
+    heads, 128 mels, d_ff = 5120), one layer, 3000 frames, one set: every output compared
+    with the oracle's."""
+    need_gpu()
+    base = WL.by_name("whisper_large_bf16_b64")
+    w = WL.reduced(base, layers=1, batch=1, n_enc=1, vocab=3001)
+    assert (w.d, w.heads) == (1280, 20)
+    mels, frames, layers, d_ff = 128, 3000, 1, 5120
+    P = (frames - 1) // 2 + 1
+    say(f"[encoder large-v3 dims] d={w.d} heads={w.heads} mels={mels} frames={frames} layers={layers}")
+    W = _enc_weights(w.d, mels, layers, d_ff, P, w.w_dtype, seed=21)
+    td = torch_dtype(w.w_dtype)
+    mel = torch.from_numpy(np.random.default_rng(22).standard_normal((1, frames, mels))).to(td)
+    G = GpuRun(w, WL.make_weights(w))
+    G.dec.load_encoder(W, mels, frames, layers, d_ff, max_sets=1)
+    out = G.dec.encode(mel.cuda()).float().cpu().numpy()
+    torch.cuda.synchronize()
+    ref = OE.encode(W, mel[0].double().numpy(), w.heads, layers)
+    err = np.abs(out[0] - ref)
+    scale = float(np.abs(ref).max())
+    rms = float(np.sqrt((err ** 2).mean()) / np.sqrt((ref ** 2).mean()))
+    say(f"  max abs err {float(err.max()):.3e} (max |ref| {scale:.2f}), relative rms err {rms:.3e}")
+    unit = 2.0 ** -8   # bf16 output and K/V rounding, as in the two-set test
+    assert rms < 4 * unit, rms
+    assert float(err.max()) < 8 * unit * scale, float(err.max())
+    assert G.check() == 0
+    G.close()
