@@ -29,19 +29,6 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// One 16-byte load per lane from global memory straight into LDS (global_load_lds_dwordx4):
-// lane i's bytes land at lds_wave + 16 i, so `lds_wave` is the wave's (uniform) 1 KB slot.
-// The load counts in vmcnt like any vector load and writes no VGPR.
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave, 16, 0, 0);
-}
-// s_waitcnt with vmcnt = N (N < 16) and the other counters left alone
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
 struct XkvOut {
   const float* bias; int M, N, d, frames, max_frames, H, hd;
   void* Kc; void* Vc;

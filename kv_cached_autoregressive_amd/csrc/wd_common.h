@@ -162,4 +162,17 @@ __device__ __forceinline__ float sum_parts(const float* __restrict__ p, int64_t 
   return s;
 }
 
+// One 16-byte load per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane i's bytes land at lds_wave + 16 i, so `lds_wave` is the wave's (uniform) 1 KB slot.
+// The load counts in vmcnt like any vector load and writes no VGPR.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave, 16, 0, 0);
+}
+// s_waitcnt with vmcnt = N (N < 16) and the other counters left alone
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 }  // namespace wd
