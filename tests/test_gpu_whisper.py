@@ -15,12 +15,12 @@ from .gpu_helpers import GpuRun, compare_logits, need_gpu, say, to_dev, torch_dt
 pytestmark = pytest.mark.gpu
 
 
-def _greedy_parity(w, steps=None, frames=None, B=None):
+def _greedy_parity(w, steps=None, frames=None, B=None, W=None):
     """Oracle-driven greedy decode (the oracle's argmax is the next token of both
     sides); compares every step's logits of every row."""
     need_gpu()
     say(f"[whisper greedy] {w.describe()} steps={steps or w.steps}")
-    W = WL.make_weights(w)
+    W = WL.make_weights(w) if W is None else W
     enc = WL.make_encoder_states(w)
     F = w.frames if frames is None else frames
     O = OW.WhisperOracle(OW.dims_of(w), W)
@@ -66,6 +66,20 @@ def test_bf16_small_dims_frames_1499():
     w = WL.reduced(WL.by_name("whisper_large_bf16_b64"), layers=2, batch=4, n_enc=4, d=256,
                    heads=4, kv_heads=4, d_ff=1024, vocab=5003)
     _greedy_parity(w, steps=8, frames=1499)
+
+
+@pytest.mark.parametrize("B", [4, 24])
+def test_layernorm_rows_with_large_mean(B):
+    """Rows whose mean is large against their spread: layer 0's self-attention output bias
+    carries +20 on every channel (exactly 20 after bf16 rounding for all but a few
+    channels), so every LayerNorm after it sees rows of mean about 20 and spread about
+    0.05, where a one-pass E[x^2] - mean^2 in fp32 would lose the variance.  At 24 rows the
+    norms also fold split-K partial slabs."""
+    w = WL.reduced(WL.by_name("whisper_large_bf16_b64"), layers=2, batch=B, n_enc=B, d=256, heads=4,
+                   kv_heads=4, d_ff=512, vocab=3001, frames=64)
+    W = WL.make_weights(w)
+    W["dec.0.self.o.b"] = torch.from_numpy(W["dec.0.self.o.b"] + 20.0).to(torch.bfloat16).float().numpy()
+    _greedy_parity(w, steps=5, W=W)
 
 
 def _sampled_parity(w, steps, streams, frames=None):
