@@ -91,6 +91,30 @@ COPY_PROBE_BYTES = 256 << 20
 CROSS_ATTN_NAME = re.compile(r"k_attn<[^<>]*?,\s*true\s*,")
 
 
+def probe_scale(copy_kib: list, path: str, counter: str) -> float:
+    """Counter reading of the probe's COPY_PROBE_BYTES device copy (its largest copy dispatch)
+    over the copy's true KiB.  The counters read 0.5 (FETCH_SIZE) and 1.0 (WRITE_SIZE) of the
+    copy on this GPU; a run without the probe has only small copies and would give a scale
+    thousands of times too small, so it is refused."""
+    ref_kib = COPY_PROBE_BYTES / 1024
+    scale = max(copy_kib, default=0.0) / ref_kib
+    if scale < 0.25:
+        raise SystemExit(f"{path}: no {COPY_PROBE_BYTES >> 20} MiB copy probe among the {counter} dispatches "
+                         "(run bench.py with --traffic-probe)")
+    return scale
+
+
+def traffic_probe_copy(dev) -> None:
+    """The device copy of COPY_PROBE_BYTES that calibrates FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.zeros_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def summarize_traffic(fetch_csv: str, write_csv: str, commands: list) -> dict:
     """HBM bytes per cross-attention launch from two rocprofv3 --pmc runs of
     `bench.py --traffic-probe` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).
@@ -116,7 +140,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, commands: list) -> dict:
     fa, fc, n = per_kernel(fetch_csv, "FETCH_SIZE")
     wa, wc, _ = per_kernel(write_csv, "WRITE_SIZE")
     ref_kib = COPY_PROBE_BYTES / 1024
-    f_fac, w_fac = fc / ref_kib, wc / ref_kib
+    f_fac, w_fac = probe_scale([fc], fetch_csv, "FETCH_SIZE"), probe_scale([wc], write_csv, "WRITE_SIZE")
     fetch_b, write_b = fa * 1024 / f_fac, wa * 1024 / w_fac
     return {"kernel": "k_attn (cross-attention)", "dispatches": n,
             "fetch_kib_per_dispatch": fa, "write_kib_per_dispatch": wa,
@@ -213,7 +237,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, w, positions: int, comman
             wg = max(1, int(r.get("Workgroup_Size", 1) or 1))
             grid = int(r.get("Grid_Size", 0) or 0) // wg
             groups[(r["Kernel_Name"], grid)].append(v)
-        return groups, max(copies) / (COPY_PROBE_BYTES / 1024)
+        return groups, probe_scale(copies, path, counter)
 
     fg, ff_ = load(fetch_csv, "FETCH_SIZE")
     wg_, wf = load(write_csv, "WRITE_SIZE")
@@ -279,6 +303,13 @@ def summarize_counters(fetch_csv: str, write_csv: str, w, positions: int, comman
             role = "split-K finish (GELU / SwiGLU)"
         elif "k_attn_combine" in short:
             role = "attention split combine"
+        elif "k_fgemm" in short:
+            role = "prefill GEMM (" + {"<0>": "q|k|v", "<1>": "out / down + residual", "<2>": "gate|up + SwiGLU"}.get(
+                short[short.index("<"):], "epilogue " + short[short.index("<"):]) + ")"
+        elif "k_pf_attn" in short:
+            role = "prefill causal attention"
+        elif "k_qk_rope_append" in short:
+            role = "prefill q/k norm + RoPE + K/V append"
         mu = mf.get(key)
         rows.append((short, grid, n, fb, wb_, role, alg, extra, None if not mu else sum(mu) / len(mu)))
     out = [f"# HBM traffic per kernel: {w.name} (decode window of positions "
@@ -295,7 +326,9 @@ def summarize_counters(fetch_csv: str, write_csv: str, w, positions: int, comman
             "reads (activation tiles re-read by many workgroups come from the L2 and do not show "
             "here).  Kernels without an algorithmic figure move activations and partial slabs only "
             "(the norms fold the residual projections' slabs, the finish kernel the fc1 / gate|up "
-            "slabs).", "",
+            "slabs)." + ("  The run also holds the 900-position prefill that precedes the decode "
+                         "window: its dense GEMMs, causal attention and q/k norm + RoPE + append, "
+                         "one dispatch per chunk and layer." if w.arch == "qwen3" else ""), "",
             "| kernel | workgroups | dispatches | fetch B | write B | role | algorithmic B | design extra B | "
             "measured / (alg + extra) | MfmaUtil % |",
             "|---|---|---|---|---|---|---|---|---|---|"]
@@ -842,6 +875,8 @@ def main():
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.w_dtype}
     if w.arch == "qwen3":
         r, dec = bench_qwen(w, args.steps, args.warmup, args)
+        if args.traffic_probe:
+            traffic_probe_copy(dev)
         del dec
         out = dict(common, value=r["decode_tokens_per_s"], ms_per_step=r["decode_ms"],
                    data="synthetic (seeded random-init weights N(0,0.02), N(0,1) audio rows, uniform ids)",
@@ -869,12 +904,7 @@ def main():
     r, dec, enc = bench_whisper_greedy(w, args.steps, args.warmup, args,
                                        graphs_off_windows=0 if args.no_extra else 1)
     if args.traffic_probe:
-        src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.zeros_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        traffic_probe_copy(dev)
     del dec, enc
     torch.cuda.empty_cache()
     out = dict(common, value=r["tokens_per_s"], ms_per_step=r["ms_per_window"],

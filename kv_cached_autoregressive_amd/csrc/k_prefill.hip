@@ -179,17 +179,25 @@ __global__ __launch_bounds__(256) void k_fgemm(FgParams p) {
 // 128 x 128 blocks (waves 2 x 2 of 4 x 4 tiles) with the block's operand tiles of a K step
 // (8 Ahi + 8 Alo + 8 W, 1 KB each) staged once through LDS, double-buffered with the next
 // step's loads in flight: each fragment leaves L2 once per block instead of once per wave.
+// Block order: the (row panel, column tile) units are numbered panel by panel and cut into 8
+// equal runs, one per XCD (workgroup L runs on XCD L % 8), so a row panel of A is fetched into
+// one XCD's L2 (two at a run boundary) whatever the row count; with the plain 2-D grid a row
+// count that is not a multiple of 8 panels sent every panel to every XCD (the 3104-row prefill
+// chunk fetched 2.7 GB per gate|up launch against 0.8 GB for the 4096-row chunk).
 template <typename T, int EPI>
-__global__ __launch_bounds__(256) void k_fgemm_lds(FgParams p) {
+__global__ __launch_bounds__(256) void k_fgemm_lds(FgParams p, int n_mt, int n_nt, int per_xcd) {
   constexpr int WR = 4, WC = 4, NTL = 24;
   __shared__ __align__(16) pv4u stage[2][NTL * 64];   // 2 x 24 KB
+  const int u = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (u >= n_mt * n_nt) return;
+  const int mt = u / n_nt, nt = u - mt * n_nt;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w & 1, wn = w >> 1;
-  const int rt0 = blockIdx.x * 8 + wm * 4, ct0 = blockIdx.y * 8 + wn * 4;
+  const int rt0 = mt * 8 + wm * 4, ct0 = nt * 8 + wn * 4;
   const int KST = p.K >> 5;
-  const pv4u* __restrict__ Ah = reinterpret_cast<const pv4u*>(p.Ahi) + (int64_t)blockIdx.x * 8 * KST * 64;
-  const pv4u* __restrict__ Al = reinterpret_cast<const pv4u*>(p.Alo) + (int64_t)blockIdx.x * 8 * KST * 64;
-  const pv4u* __restrict__ Wt = reinterpret_cast<const pv4u*>(p.W) + (int64_t)blockIdx.y * 8 * KST * 64;
+  const pv4u* __restrict__ Ah = reinterpret_cast<const pv4u*>(p.Ahi) + (int64_t)mt * 8 * KST * 64;
+  const pv4u* __restrict__ Al = reinterpret_cast<const pv4u*>(p.Alo) + (int64_t)mt * 8 * KST * 64;
+  const pv4u* __restrict__ Wt = reinterpret_cast<const pv4u*>(p.W) + (int64_t)nt * 8 * KST * 64;
   pv4u g[6];
   auto gload = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
@@ -246,9 +254,11 @@ hipError_t launch_fgemm(const FgParams& p, hipStream_t s) {
   // 128-row blocks unless they leave CUs idle (then 64-row blocks; A is padded to 128 rows)
   const bool wide = (int64_t)((p.R + 127) / 128) * (p.N / 128) >= 256;
   const dim3 grid(wide ? (p.R + 127) / 128 : (p.R + 63) / 64, p.N / 128);
-  // 128-row blocks stage their operands through LDS
+  // 128-row blocks stage their operands through LDS, in XCD runs of (panel, tile) units
+  const int n_mt = (p.R + 127) / 128, n_nt = p.N / 128;
+  const int per_xcd = (n_mt * n_nt + 7) / 8;
 #define WD_FG1(T_, E_)                                                                                   \
-  if (wide) k_fgemm_lds<T_, E_><<<grid, 256, 0, s>>>(p);                                                 \
+  if (wide) k_fgemm_lds<T_, E_><<<8 * per_xcd, 256, 0, s>>>(p, n_mt, n_nt, per_xcd);                     \
   else k_fgemm<T_, E_, 2><<<grid, 256, 0, s>>>(p);
 #define WD_FG(T_)                                                                                        \
   switch (p.epi) {                                                                                       \

@@ -100,3 +100,17 @@ def test_counter_summary_scales_and_labels(tmp_path):
     assert "self out" in line and f"{3200 * 1024 * 2:,}" in line and f"{1280 * 1280 * 2:,}" in line
     line = [l for l in md.splitlines() if "k_attn<64,1,true,8>" in l][0]
     assert "cross-attention" in line and f"{bench.cross_attn_bytes_per_launch(w):,}" in line
+
+
+def test_counter_summary_refuses_a_run_without_the_copy_probe(tmp_path):
+    """Without the 256 MiB probe copy the scale would come from a small copy and inflate every
+    figure thousands of times: both summaries refuse such a run."""
+    w = WL.reduced(WL.by_name("qwen3asr_bf16_b8"), layers=1)
+    sk = "void wd::k_mgemv_sk<wd::bf16_t, 1, 1, 16, 1>(wd::MGemvParams)"
+    attn = "void wd::k_attn<wd::bf16_t, 64, 1, true, 8>(wd::AttnParams)"
+    for path, counter in ((tmp_path / "f.csv", "FETCH_SIZE"), (tmp_path / "w.csv", "WRITE_SIZE")):
+        _counter_file(path, counter, [(sk, 100.0), (attn, 100.0), ("__amd_rocclr_copyBuffer", 44.5)])
+    with pytest.raises(SystemExit, match="copy probe"):
+        bench.summarize_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), w, 4, ["cmd"])
+    with pytest.raises(SystemExit, match="copy probe"):
+        bench.summarize_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), ["cmd"])
