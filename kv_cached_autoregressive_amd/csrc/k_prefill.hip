@@ -304,8 +304,13 @@ __device__ __forceinline__ uint32_t pa_pack2(float a, float b, uint32_t& lo) {
   return pa_bits(ha) | (pa_bits(hb) << 16);
 }
 
+// Block order: the (stream, kv head, query block) units are numbered query block fastest and
+// cut into 8 equal runs, one per XCD (workgroup L runs on XCD L % 8), so the query blocks that
+// stream one (stream, kv head) slab of K and V share one XCD's L2 instead of pulling the slab
+// into all eight.
 template <typename CT, typename OT, int HD>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) void k_pf_attn(PfAttnParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) void k_pf_attn(PfAttnParams p, int n_qb,
+                                                                                            int per_xcd) {
   constexpr int KLD = HD + 8;                 // K tile row stride (elements): conflict-free 16 B reads
   constexpr int VLD = PA_KT + 4;              // transposed V tile row stride
   constexpr int NCH = PA_KT * HD / 8;         // 16-byte chunks per tile (K or V)
@@ -314,21 +319,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
   constexpr int HT = HD / 16;                 // output channel tiles
   __shared__ __align__(16) CT Ks[PA_KT * KLD];
   __shared__ __align__(16) CT Vt[HD * VLD];
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int u = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (u >= n_qb * p.Hkv * p.B) return;
+  const int qb = u % n_qb, g = (u / n_qb) % p.Hkv, b = u / (n_qb * p.Hkv);
   const int G = p.Hq / p.Hkv;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int col = lane & 15, grp = lane >> 4;
 
   // this lane's query (column col of the wave's 16)
-  const int qidx = blockIdx.x * PA_QB + wv * 16 + col;
+  const int qidx = qb * PA_QB + wv * 16 + col;
   const int jq = qidx / G, hq = g * G + (qidx - jq * G);
   const bool active = jq < p.Cn;
   const int jc = min(jq, p.Cn - 1);
   const int tq = p.t0 + jc;
   const int r = b * p.C + jc;
   // key ranges: the block's (staged) and the wave's (computed)
-  const int rows_blk = p.full ? p.t0 + p.Cn : p.t0 + min(p.Cn - 1, (blockIdx.x * PA_QB + PA_QB - 1) / G) + 1;
-  const int rows_w = p.full ? rows_blk : p.t0 + min(p.Cn - 1, (blockIdx.x * PA_QB + wv * 16 + 15) / G) + 1;
+  const int rows_blk = p.full ? p.t0 + p.Cn : p.t0 + min(p.Cn - 1, (qb * PA_QB + PA_QB - 1) / G) + 1;
+  const int rows_w = p.full ? rows_blk : p.t0 + min(p.Cn - 1, (qb * PA_QB + wv * 16 + 15) / G) + 1;
   const int tmax = p.full ? rows_blk - 1 : tq;   // the last key this lane's query sees
 
   // q^T as the B operand: lane (col, grp) holds channels 32 ks + 8 grp .. +8 of its query
@@ -462,10 +469,12 @@ hipError_t launch_pf_attn(const PfAttnParams& p, hipStream_t s) {
   if (p.B <= 0 || p.C <= 0 || p.Cn <= 0 || p.Cn > p.C || G <= 0 || p.Hq % p.Hkv ||
       p.t0 < 0 || p.t0 + p.Cn > p.ctx || !p.q || !p.K || !p.V || !p.o_hi || !p.o_lo)
     return hipErrorInvalidValue;
-  const dim3 grid((p.Cn * G + PA_QB - 1) / PA_QB, p.Hkv, p.B);
+  const int n_qb = (p.Cn * G + PA_QB - 1) / PA_QB;
+  const int per_xcd = (n_qb * p.Hkv * p.B + 7) / 8;
+  const dim3 grid(8 * per_xcd);
 #define WD_PFA(CT_, HD_)                                                                        \
-  if (p.o_dtype == DT_BF16) k_pf_attn<CT_, bf16_t, HD_><<<grid, 256, 0, s>>>(p);               \
-  else if (p.o_dtype == DT_F16) k_pf_attn<CT_, f16_t, HD_><<<grid, 256, 0, s>>>(p);            \
+  if (p.o_dtype == DT_BF16) k_pf_attn<CT_, bf16_t, HD_><<<grid, 256, 0, s>>>(p, n_qb, per_xcd);   \
+  else if (p.o_dtype == DT_F16) k_pf_attn<CT_, f16_t, HD_><<<grid, 256, 0, s>>>(p, n_qb, per_xcd); \
   else return hipErrorInvalidValue;
   if (p.hd == 128 && p.cache_dtype == DT_F16) { WD_PFA(f16_t, 128) }
   else if (p.hd == 128 && p.cache_dtype == DT_BF16) { WD_PFA(bf16_t, 128) }
