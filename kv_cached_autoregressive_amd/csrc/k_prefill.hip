@@ -179,18 +179,34 @@ __global__ __launch_bounds__(256) void k_fgemm(FgParams p) {
 // 128 x 128 blocks (waves 2 x 2 of 4 x 4 tiles) with the block's operand tiles of a K step
 // (8 Ahi + 8 Alo + 8 W, 1 KB each) staged once through LDS, double-buffered with the next
 // step's loads in flight: each fragment leaves L2 once per block instead of once per wave.
-// Block order: the (row panel, column tile) units are numbered panel by panel and cut into 8
-// equal runs, one per XCD (workgroup L runs on XCD L % 8), so a row panel of A is fetched into
-// one XCD's L2 (two at a run boundary) whatever the row count; with the plain 2-D grid a row
-// count that is not a multiple of 8 panels sent every panel to every XCD (the 3104-row prefill
-// chunk fetched 2.7 GB per gate|up launch against 0.8 GB for the 4096-row chunk).
+// Block order (workgroup L runs on XCD L % 8): with n_mt = 8 q + r row panels, XCD x owns
+// panels x, x + 8, ..., x + 8 (q - 1) and takes them in groups of pg, column tile by column
+// tile within a group, so a group's A panels stay in the XCD's L2 while each W tile is used pg
+// times in a row; the (panel, tile) units of the last r panels are then shared out evenly, so
+// every XCD gets the same work at any row count.  (A plain 2-D grid sent every panel to every
+// XCD whenever n_mt % 8 != 0: the 3104-row prefill chunk fetched 2.7 GB per gate|up launch
+// against 0.8 GB for the 4096-row chunk; plain panel-major runs fixed that but re-read W for
+// every panel.)
+struct FgOrder { int n_mt, n_nt, pg, per_xcd; };
 template <typename T, int EPI>
-__global__ __launch_bounds__(256) void k_fgemm_lds(FgParams p, int n_mt, int n_nt, int per_xcd) {
+__global__ __launch_bounds__(256) void k_fgemm_lds(FgParams p, FgOrder od) {
   constexpr int WR = 4, WC = 4, NTL = 24;
   __shared__ __align__(16) pv4u stage[2][NTL * 64];   // 2 x 24 KB
-  const int u = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (u >= n_mt * n_nt) return;
-  const int mt = u / n_nt, nt = u - mt * n_nt;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int q = od.n_mt >> 3, bulk = q * od.n_nt;
+  int mt, nt;
+  if (j < bulk) {
+    const int gi = j / (od.pg * od.n_nt), within = j - gi * od.pg * od.n_nt;
+    const int gsz = min(od.pg, q - gi * od.pg);
+    nt = within / gsz;
+    mt = xcd + 8 * (gi * od.pg + (within - nt * gsz));
+  } else {
+    const int r = od.n_mt - 8 * q, tail = r * od.n_nt, per = (tail + 7) >> 3;
+    const int tu = xcd * per + (j - bulk);
+    if (tu >= tail) return;
+    mt = 8 * q + tu / od.n_nt;
+    nt = tu - (tu / od.n_nt) * od.n_nt;
+  }
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w & 1, wn = w >> 1;
   const int rt0 = mt * 8 + wm * 4, ct0 = nt * 8 + wn * 4;
@@ -254,11 +270,15 @@ hipError_t launch_fgemm(const FgParams& p, hipStream_t s) {
   // 128-row blocks unless they leave CUs idle (then 64-row blocks; A is padded to 128 rows)
   const bool wide = (int64_t)((p.R + 127) / 128) * (p.N / 128) >= 256;
   const dim3 grid(wide ? (p.R + 127) / 128 : (p.R + 63) / 64, p.N / 128);
-  // 128-row blocks stage their operands through LDS, in XCD runs of (panel, tile) units
-  const int n_mt = (p.R + 127) / 128, n_nt = p.N / 128;
-  const int per_xcd = (n_mt * n_nt + 7) / 8;
+  // 128-row blocks stage their operands through LDS, in XCD-owned panel groups; a group's A
+  // panels (128 rows x K, hi and lo) take about 3 MB of the XCD's 4 MB L2
+  FgOrder od;
+  od.n_mt = (p.R + 127) / 128;
+  od.n_nt = p.N / 128;
+  od.pg = std::max(1, std::min(8, (3 << 20) / (128 * p.K * 4)));
+  od.per_xcd = (od.n_mt >> 3) * od.n_nt + ((od.n_mt & 7) * od.n_nt + 7) / 8;
 #define WD_FG1(T_, E_)                                                                                   \
-  if (wide) k_fgemm_lds<T_, E_><<<8 * per_xcd, 256, 0, s>>>(p, n_mt, n_nt, per_xcd);                     \
+  if (wide) k_fgemm_lds<T_, E_><<<8 * od.per_xcd, 256, 0, s>>>(p, od);                                   \
   else k_fgemm<T_, E_, 2><<<grid, 256, 0, s>>>(p);
 #define WD_FG(T_)                                                                                        \
   switch (p.epi) {                                                                                       \
