@@ -653,10 +653,11 @@ def _beam_merge(scores, vals, ids, lse, V, first):
 
 
 def bench_beam(w, runs: int, warmup: int):
-    """Width-W beam search over one broadcast encoder set: per position wd_step (logits), the
-    per-row candidates on the device (wd_topk: W values, ids and the log-sum-exp per row),
-    the W x W merge on the host, wd_reorder of the self caches and the chosen tokens fed
-    back.  tokens/s counts every row of every step; GPU-only time excludes the host merge."""
+    """Width-W beam search over one broadcast encoder set, all on the device: per position
+    wd_step (logits) and wd_beam_step (candidates, W x W merge, cache rearrangement, the next
+    tokens written into the step's token buffer), with no host round trip inside a run.
+    tokens/s counts every row of every step.  One more run takes the candidates to the host
+    for the merge and calls wd_reorder (the step without wd_beam_step), for comparison."""
     import torch
 
     import kv_cached_autoregressive_amd as K
@@ -667,67 +668,88 @@ def bench_beam(w, runs: int, warmup: int):
     del W
     B, S, V = w.batch, w.steps, w.vocab
     prompt = WL.make_prompt(w)
+    P = prompt.shape[1]
+    prompt_dev = torch.from_numpy(np.ascontiguousarray(prompt.T, dtype=np.int32)).to(dev)   # [P, B]
     logits = torch.empty(B, V, dtype=torch.float32, device=dev)
     amax = torch.empty(B, dtype=torch.int32, device=dev)
     tok = torch.zeros(B, dtype=torch.int32, device=dev)
     pos_all = torch.arange(S, dtype=torch.int32, device=dev)[:, None].repeat(1, B).contiguous()
+    scores = torch.zeros(B, dtype=torch.float64, device=dev)
+    bidx = torch.zeros(B, dtype=torch.int32, device=dev)
+    stream, ctx = dec.stream, dec.ctx
+    torch.cuda.set_stream(stream)
+
+    def run():
+        K.wd_cross_kv(ctx, enc.data_ptr(), w.frames)
+        scores.zero_()
+        for p in range(S):
+            if p < P:
+                tok.copy_(prompt_dev[p])
+            K.wd_step(ctx, tok.data_ptr(), pos_all[p].data_ptr(), B, logits.data_ptr(), amax.data_ptr())
+            if p >= P - 1:
+                K.wd_beam_step(ctx, logits.data_ptr(), B, p == P - 1, scores.data_ptr(), bidx.data_ptr(),
+                               tok.data_ptr(), p + 1 if p + 1 < S else 0)
+
     vals = torch.empty(B, B, dtype=torch.float32, device=dev)
     ids = torch.empty(B, B, dtype=torch.int32, device=dev)
     lse = torch.empty(B, dtype=torch.float32, device=dev)
     host = torch.empty(2 * B * B + B, dtype=torch.float32).pin_memory()
-    stream, ctx = dec.stream, dec.ctx
-    torch.cuda.set_stream(stream)
-    gpu_ms = 0.0
 
-    def run(timed):
-        nonlocal gpu_ms
+    def run_host_merge():
         K.wd_cross_kv(ctx, enc.data_ptr(), w.frames)
-        scores = np.zeros(B)
+        sc_h = np.zeros(B)
         toks = prompt[:, 0]
         for p in range(S):
-            if p < prompt.shape[1]:
+            if p < P:
                 toks = prompt[:, p]
             tok.copy_(torch.from_numpy(np.ascontiguousarray(toks, dtype=np.int32)), non_blocking=False)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
             K.wd_step(ctx, tok.data_ptr(), pos_all[p].data_ptr(), B, logits.data_ptr(), amax.data_ptr())
-            if p >= prompt.shape[1] - 1:
+            if p >= P - 1:
                 K.wd_topk(ctx, logits.data_ptr(), B, B, vals.data_ptr(), ids.data_ptr(), lse.data_ptr())
                 host[:B * B].copy_(vals.view(-1), non_blocking=True)
                 host[B * B:2 * B * B].copy_(ids.view(torch.float32).view(-1), non_blocking=True)
                 host[2 * B * B:].copy_(lse, non_blocking=True)
-            e1.record(stream)
-            stream.synchronize()
-            if timed:
-                gpu_ms += e0.elapsed_time(e1)
-            if p >= prompt.shape[1] - 1:
+                stream.synchronize()
                 h = host.numpy()
-                hv = h[:B * B].reshape(B, B)
-                hi = h[B * B:2 * B * B].view(np.int32).reshape(B, B)
-                bi, tk, sc = _beam_merge(scores, hv, hi, h[2 * B * B:], V, p == prompt.shape[1] - 1)
+                bi, tk, sc = _beam_merge(sc_h, h[:B * B].reshape(B, B), h[B * B:2 * B * B].view(np.int32).reshape(B, B),
+                                         h[2 * B * B:], V, p == P - 1)
                 if p + 1 < S:
                     K.wd_reorder(ctx, bi.tolist(), p + 1)
-                scores, toks = sc, tk
+                sc_h, toks = sc, tk
+        return np.asarray(toks)
 
     for _ in range(warmup):
-        run(False)
+        run()
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
+    e0.record(stream)
     for _ in range(runs):
-        run(True)
+        run()
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gpu_s = e0.elapsed_time(e1) / 1e3 / runs
+    dev_tokens = tok.cpu().numpy().copy()
+    run_host_merge()
+    torch.cuda.synchronize()
+    hm0 = time.perf_counter()
+    host_tokens = run_host_merge()
+    torch.cuda.synchronize()
+    host_wall = time.perf_counter() - hm0
     if dec.check() != 0:
         raise RuntimeError(dec.last_error())
     bytes_run = sum(whisper_bytes_per_step(w, p) for p in range(S))
-    gpu_s = gpu_ms / 1e3 / runs
     out = {"workload": w.name, "beams": B, "positions": S,
            "tokens_per_s": B * S * runs / wall, "tokens_per_s_gpu": B * S / gpu_s,
            "ms_per_run_wall": wall / runs * 1e3, "ms_per_run_gpu": gpu_s * 1e3,
            "hbm_bytes_per_run": bytes_run, "hbm_frac_decode_gpu": bytes_run / gpu_s / HBM_PEAK,
            "runs": runs,
-           "step": "wd_step + wd_topk on the device, W x W merge and wd_reorder from the host every position; "
-                   "GPU time excludes the host merge and the per-step synchronisation"}
+           "host_merge": {"tokens_per_s": B * S / host_wall, "ms_per_run_wall": host_wall * 1e3,
+                          "same_final_tokens": bool(np.array_equal(dev_tokens, host_tokens))},
+           "step": "wd_step + wd_beam_step (candidates, merge and cache rearrangement on the device) every "
+                   "position, no host round trip; host_merge: the candidates merged on the host and "
+                   "wd_reorder, one run"}
     del dec
     return out
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define WD_ABI_VERSION 4
+#define WD_ABI_VERSION 5
 #define WD_MAX_BATCH 64
 
 typedef struct wd_ctx wd_ctx;
@@ -215,6 +215,26 @@ wd_status wd_reorder(wd_ctx* ctx, const int32_t* beam_idx, int32_t B, int32_t n_
  * stream.  Errors: ARG (null, B or W out of range), HIP. */
 wd_status wd_topk(wd_ctx* ctx, const float* logits, int32_t B, int32_t W, float* top_val,
                   int32_t* top_id, float* lse);
+
+/* One whole width-W beam step on the device, with no host round trip: the candidates of
+ * rows 0..W-1 of `logits` (dev fp32 [W, vocab], as written by wd_step) as in wd_topk, then
+ * the W best of the W x W candidates, then the self-cache rearrangement (mlx-bun
+ * `WhisperKvCache.rearrange`).  The selection is the plain width-W beam step with no length
+ * penalty and no end token: candidate (b, v) scores scores[b] + logit(b, v) - lse[b] in
+ * float64; the W best are kept, best first, equal scores going to the lower b * vocab + v
+ * (NaN scores last); with first != 0 (the first generated position, where every beam holds
+ * the same prefix) only row 0 is expanded.
+ *   scores    dev float64 [W]  in: the beams' scores; out: the kept candidates' scores
+ *   beam_idx  dev int32 [W]    out: source beam of each kept candidate
+ *   tokens    dev int32 [W]    out: its token, ready as the next wd_step's `tokens`
+ *   n_rows    self-cache rows 0..n_rows-1 are copied from beam_idx's rows as by wd_reorder
+ *             (0: no copy, as after the last position)
+ * 1 <= W <= min(8, max_batch, vocab).  A rearrangement needs n_enc == 1 and max_batch > 1;
+ * it always copies (the indices are not known on the host) and makes the spare cache
+ * current.  Asynchronous on the context's stream.  Errors: ARG (null, W, first or n_rows out
+ * of range), STATE, HIP. */
+wd_status wd_beam_step(wd_ctx* ctx, const float* logits, int32_t W, int32_t first, double* scores,
+                       int32_t* beam_idx, int32_t* tokens, int32_t n_rows);
 
 /* wd_topk for callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation) and hold no decoder context: the same

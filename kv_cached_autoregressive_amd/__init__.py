@@ -20,7 +20,7 @@ __all__ = [
     "WdError", "WdConfig", "WdTensor", "lib", "lib_path", "declared_functions",
     "wd_abi_version", "wd_workspace_bytes", "wd_load", "wd_cross_kv", "wd_cross_kv_ragged", "wd_step", "wd_reorder",
     "wd_topk", "wd_prefill", "wd_encoder_workspace_bytes", "wd_load_encoder", "wd_encode", "wd_listen", "wd_check", "wd_last_error", "wd_free", "wd_profile", "wd_profile_read",
-    "wd_debug_cache", "wd_set_option", "wd_get_option", "WD_OPT_GRAPHS", "wd_topk_noalloc",
+    "wd_debug_cache", "wd_set_option", "wd_get_option", "WD_OPT_GRAPHS", "wd_topk_noalloc", "wd_beam_step",
     "config_from", "Decoder", "DTYPES", "STATUS",
 ]
 
@@ -81,6 +81,7 @@ def lib():
             "wd_step": (i32, [vp, vp, vp, i32, vp, vp]),
             "wd_reorder": (i32, [vp, ctypes.POINTER(i32), i32, i32]),
             "wd_topk": (i32, [vp, vp, i32, i32, vp, vp, vp]),
+            "wd_beam_step": (i32, [vp, vp, i32, i32, vp, vp, vp, i32]),
             "wd_encoder_workspace_bytes": (sz, [vp, i32, i32, i32, i32, i32]),
             "wd_load_encoder": (i32, [vp, i32, i32, i32, i32, i32, ctypes.POINTER(WdTensor), i32, vp, sz]),
             "wd_encode": (i32, [vp, vp, i32, vp]),
@@ -159,6 +160,11 @@ def wd_reorder(ctx, beam_idx: Iterable[int], n_rows: int):
 def wd_topk(ctx, logits: int, B: int, W: int, top_val: int, top_id: int, lse: int):
     _check(lib().wd_topk(ctx, ctypes.c_void_p(logits), B, W, ctypes.c_void_p(top_val), ctypes.c_void_p(top_id),
                          ctypes.c_void_p(lse)), ctx)
+
+
+def wd_beam_step(ctx, logits: int, W: int, first: bool, scores: int, beam_idx: int, tokens: int, n_rows: int):
+    _check(lib().wd_beam_step(ctx, ctypes.c_void_p(logits), W, 1 if first else 0, ctypes.c_void_p(scores),
+                              ctypes.c_void_p(beam_idx), ctypes.c_void_p(tokens), n_rows), ctx)
 
 
 def wd_encoder_workspace_bytes(ctx, n_mels: int, frames: int, n_layers: int, d_ff: int, max_sets: int) -> int:
@@ -399,6 +405,18 @@ class Decoder:
     def reorder(self, beam_idx, n_rows: int):
         cur = self._enter()
         wd_reorder(self.ctx, [int(i) for i in beam_idx], n_rows)
+        self._leave(cur)
+
+    def beam_step(self, logits, W: int, first: bool, scores, beam_idx, tokens, n_rows: int):
+        """One beam step on the device (wd_beam_step): logits fp32 [>= W, vocab], scores float64
+        [W] (updated in place), beam_idx and tokens int32 [W] (written), then the self-cache
+        rearrangement of rows 0..n_rows-1."""
+        import torch
+        assert logits.dtype == torch.float32 and logits.is_contiguous() and logits.shape[1] == self.w.vocab
+        assert scores.dtype == torch.float64 and beam_idx.dtype == torch.int32 and tokens.dtype == torch.int32
+        cur = self._enter()
+        wd_beam_step(self.ctx, logits.data_ptr(), W, first, scores.data_ptr(), beam_idx.data_ptr(),
+                     tokens.data_ptr(), n_rows)
         self._leave(cur)
 
     def topk(self, logits, W: int):

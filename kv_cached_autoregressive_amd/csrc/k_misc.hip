@@ -852,4 +852,90 @@ hipError_t launch_reorder(const void* src, void* dst, int elt_bytes, const BeamI
   return hipGetLastError();
 }
 
+template <bool DEV>
+__global__ __launch_bounds__(256) void k_reorder_dev(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                     const int32_t* __restrict__ idx, int B, int H, int64_t slab_vec,
+                                                     int64_t copy_vec, int64_t block_vec) {
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh - (bh / H) * H;
+  const int from = min(max(idx[b], 0), B - 1);
+  const int64_t blk = (int64_t)blockIdx.z * block_vec;
+  const int64_t so = blk + ((int64_t)from * H + h) * slab_vec;
+  const int64_t dof = blk + ((int64_t)b * H + h) * slab_vec;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < copy_vec; i += (int64_t)gridDim.x * 256)
+    dst[dof + i] = src[so + i];
+}
+
+hipError_t launch_reorder_dev(const void* src, void* dst, int elt_bytes, const int32_t* idx, int B, int Bmax,
+                              int H, int ctx, int hd, int n_rows, int n_blocks, hipStream_t s) {
+  if (!idx || B <= 0 || B > Bmax || n_rows < 0 || n_rows > ctx || n_blocks <= 0) return hipErrorInvalidValue;
+  if (((int64_t)hd * elt_bytes) % 16) return hipErrorInvalidValue;
+  if (n_rows == 0) return hipSuccess;
+  const int64_t row_vec = (int64_t)hd * elt_bytes / 16;
+  const int64_t slab_vec = (int64_t)ctx * row_vec;
+  const int64_t copy_vec = (int64_t)n_rows * row_vec;
+  const int64_t block_vec = (int64_t)Bmax * H * slab_vec;
+  dim3 grid((unsigned)std::min<int64_t>((copy_vec + 255) / 256, 64), B * H, n_blocks);
+  k_reorder_dev<true><<<grid, 256, 0, s>>>((const uint4*)src, (uint4*)dst, idx, B, H, slab_vec, copy_vec, block_vec);
+  return hipGetLastError();
+}
+
+// Beam selection in one wave: lane i < rows * W holds candidate (i / W, i % W).  Each of the W
+// rounds takes the best remaining candidate by a butterfly over the 64 lanes (a total order:
+// not NaN before NaN, then higher score, then lower flat index), and the lane holding it drops
+// out.  Every score is read before any is written, so `scores` is updated in place.
+struct BeamKey { double c; long long flat; int live; };
+__device__ __forceinline__ bool beam_better(const BeamKey& a, const BeamKey& b) {
+  if (a.live != b.live) return a.live > b.live;
+  const bool an = a.c != a.c, bn = b.c != b.c;
+  if (an != bn) return bn;
+  if (!an && a.c != b.c) return a.c > b.c;
+  return a.flat < b.flat;
+}
+__global__ __launch_bounds__(64) void k_beam_merge(const float* __restrict__ top_val, const int32_t* __restrict__ top_id,
+                                                   const float* __restrict__ lse, double* scores,
+                                                   int32_t* __restrict__ beam_idx, int32_t* __restrict__ tokens, int W,
+                                                   int rows, int V) {
+  const int lane = threadIdx.x;
+  BeamKey me{-INFINITY, 0x7fffffffffffffffLL, 0};
+  if (lane < rows * W) {
+    const int b = lane / W;
+    me.c = scores[b] + ((double)top_val[lane] - (double)lse[b]);
+    me.flat = (long long)b * V + top_id[lane];
+    me.live = 1;
+  }
+  double out_c = 0.0;
+  long long out_flat = 0;
+  for (int r = 0; r < W; ++r) {
+    BeamKey best = me;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      BeamKey other;
+      other.c = __shfl_xor(best.c, o, 64);
+      other.flat = __shfl_xor(best.flat, o, 64);
+      other.live = __shfl_xor(best.live, o, 64);
+      if (beam_better(other, best)) best = other;
+    }
+    if (me.live && me.flat == best.flat) me.live = 0;   // flat indices are distinct
+    if (lane == r) {
+      out_c = best.c;
+      out_flat = best.flat;
+    }
+  }
+  if (lane < W) {
+    scores[lane] = out_c;
+    beam_idx[lane] = (int32_t)(out_flat / V);
+    tokens[lane] = (int32_t)(out_flat % V);
+  }
+}
+
+hipError_t launch_beam_merge(const float* top_val, const int32_t* top_id, const float* lse, double* scores,
+                             int32_t* beam_idx, int32_t* tokens, int W, int rows, int V, hipStream_t s) {
+  if (!top_val || !top_id || !lse || !scores || !beam_idx || !tokens || W < 1 || W > 8 || V < 1 ||
+      (rows != 1 && rows != W))
+    return hipErrorInvalidValue;
+  k_beam_merge<<<1, 64, 0, s>>>(top_val, top_id, lse, scores, beam_idx, tokens, W, rows, V);
+  return hipGetLastError();
+}
+
 }  // namespace wd

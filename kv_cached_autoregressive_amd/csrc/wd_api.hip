@@ -59,6 +59,7 @@ struct Plan {
   size_t x = 0, y = 0, q = 0, qkv = 0, o = 0, h = 0, part = 0, amax = 0, err = 0, pos_tmp = 0;
   size_t rope = 0;           // Qwen3: cos [context][hd/2], then sin [context][hd/2]
   size_t topk = 0;           // wd_topk partial lists
+  size_t beam = 0;           // wd_beam_step candidates: values [8][8] f32, ids [8][8] i32, lse [8] f32
   size_t gpart = 0; int64_t gpart_cap = 0;   // split-K GEMM partials [G][B][N] fp32
   size_t tok_in = 0, ov_in = 0;              // staged tokens [B] and embedding override rows [B, d]
   int max_splits = 1, amax_parts = 1;
@@ -215,6 +216,7 @@ Plan make_plan(const wd_config& c) {
   p.amax_parts = std::max(wd::gemv_blocks(c.vocab, c.max_batch), wd::mgemv_blocks(c.vocab, c.max_batch));
   p.amax = b.take((size_t)p.amax_parts * Bm * 8);
   p.topk = b.take(wd::topk_scratch_bytes((int)Bm, c.vocab));   // beam-candidate partial lists
+  p.beam = b.take(8 * 8 * 4 * 2 + 8 * 4);
   p.err = b.take(64);
   p.pos_tmp = b.take(Bm * 4);
   p.tok_in = b.take(Bm * 4);
@@ -1420,6 +1422,40 @@ wd_status wd_topk(wd_ctx* ctx, const float* logits, int32_t B, int32_t W, float*
     return WD_OK;
   } catch (...) {
     return fail(ctx, WD_ERR_INTERNAL, "wd_topk: internal error");
+  }
+}
+
+wd_status wd_beam_step(wd_ctx* ctx, const float* logits, int32_t W, int32_t first, double* scores,
+                       int32_t* beam_idx, int32_t* tokens, int32_t n_rows) {
+  if (!ctx) return WD_ERR_ARG;
+  try {
+    const wd_config& g = ctx->cfg;
+    if (!logits || !scores || !beam_idx || !tokens) return fail(ctx, WD_ERR_ARG, "wd_beam_step: null pointer");
+    if (W < 1 || W > 8 || W > g.max_batch || W > g.vocab)
+      return fail(ctx, WD_ERR_ARG, "wd_beam_step: W outside [1, min(8, max_batch, vocab)]");
+    if (first != 0 && first != 1) return fail(ctx, WD_ERR_ARG, "wd_beam_step: first must be 0 or 1");
+    if (n_rows < 0 || n_rows > g.context) return fail(ctx, WD_ERR_ARG, "wd_beam_step: n_rows outside [0, context]");
+    if (n_rows > 0 && ctx->plan.n_bufs < 2)
+      return fail(ctx, WD_ERR_STATE, "wd_beam_step: the reorder needs n_enc == 1 and max_batch > 1");
+    float* tv = ctx->at<float>(ctx->plan.beam);
+    int32_t* ti = reinterpret_cast<int32_t*>(tv + 64);
+    float* lse = tv + 128;
+    const int rows = first ? 1 : W;
+    HIPCHK(ctx, wd::launch_topk_lse(logits, rows, g.vocab, g.vocab, W, tv, ti, lse, ctx->at(ctx->plan.topk),
+                                    ctx->stream), "beam candidates");
+    HIPCHK(ctx, wd::launch_beam_merge(tv, ti, lse, scores, beam_idx, tokens, W, rows, g.vocab, ctx->stream),
+           "beam merge");
+    if (n_rows > 0) {
+      const int nxt = 1 - ctx->cur;
+      HIPCHK(ctx, wd::launch_reorder_dev(ctx->ws + ctx->plan.self[ctx->cur], ctx->ws + ctx->plan.self[nxt],
+                                         dtype_bytes(g.cache_dtype), beam_idx, W, g.max_batch, g.n_kv_heads,
+                                         g.context, g.head_dim, n_rows, 2 * g.n_layers, ctx->stream),
+             "beam reorder");
+      ctx->cur = nxt;
+    }
+    return WD_OK;
+  } catch (...) {
+    return fail(ctx, WD_ERR_INTERNAL, "wd_beam_step: internal error");
   }
 }
 

@@ -214,6 +214,17 @@ struct BeamIdx { int32_t v[64]; };
 hipError_t launch_reorder(const void* src, void* dst, int elt_bytes, const BeamIdx& idx, int B,
                           int Bmax, int H, int ctx, int hd, int n_rows, int n_blocks,
                           hipStream_t s);
+// The same copy with the beam indices read from device memory (idx dev int32 [B], each in
+// [0, B); an index outside that range is clamped into it).
+hipError_t launch_reorder_dev(const void* src, void* dst, int elt_bytes, const int32_t* idx, int B,
+                              int Bmax, int H, int ctx, int hd, int n_rows, int n_blocks, hipStream_t s);
+// One width-W beam selection from the per-row candidates of launch_topk_lse (top_val, top_id
+// [rows, W], lse [rows]): candidate (b, k) scores scores[b] + (top_val[b][k] - lse[b]) in
+// float64, the W best kept (score descending, then flat index b * V + id ascending; NaN
+// scores last), written as beam_idx[i] = b, tokens[i] = id, scores[i] = its score.  rows is
+// 1 at the first generated position (every beam holds the same prefix), else W.  W <= 8.
+hipError_t launch_beam_merge(const float* top_val, const int32_t* top_id, const float* lse, double* scores,
+                             int32_t* beam_idx, int32_t* tokens, int W, int rows, int V, hipStream_t s);
 
 // ---- cross K/V projection (dense GEMM) with cache scatter ------------------------------------
 // C[m, n] = sum_k X[m,k] W[n,k] (+ bias[n]); m = e*frames + f; n < d -> K cache, else V cache;

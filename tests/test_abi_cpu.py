@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
             "wd_free", "wd_workspace_bytes", "wd_last_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert K.wd_abi_version() == 4
+    assert K.wd_abi_version() == 5
 
 
 def test_workspace_bytes_plan():
@@ -114,6 +114,7 @@ def test_null_context_calls_return_arg():
     assert L.wd_load_encoder(None, 80, 3000, 1, 128, 1, None, 0, None, 0) == 1
     assert L.wd_encoder_workspace_bytes(None, 80, 3000, 1, 128, 1) == 0
     assert L.wd_reorder(None, None, 1, 1) == 1
+    assert L.wd_beam_step(None, None, 1, 0, None, None, None, 0) == 1
     assert L.wd_prefill(None, None, 1, 1, None, 0, 0, None, None) == 1
     assert L.wd_check(None) == 1
     assert L.wd_set_option(None, K.WD_OPT_GRAPHS, 0) == 1

@@ -1,6 +1,8 @@
 """GPU parity of the Whisper decoder step against the oracle (teacher-forced:
 both sides are fed the same tokens and beam indices, so one legitimate flip at
 a low-margin step does not invalidate the steps after it)."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -231,7 +233,7 @@ def _merge_candidates(scores, vals, ids, lse, V, first):
     flat = (np.arange(rows)[:, None] * V + ids[:rows]).reshape(-1)
     c = cand.reshape(-1)
     keep = np.lexsort((flat, -c))[:W]
-    return (flat[keep] // V).astype(np.int32), (flat[keep] % V).astype(np.int32)
+    return (flat[keep] // V).astype(np.int32), (flat[keep] % V).astype(np.int32), c[keep]
 
 
 def _topk_definition(lg, W):
@@ -313,8 +315,8 @@ def test_base_f16_beam5_full():
                 decided += 1
             # the same choice from the device candidates (wd_topk: W per row + lse), merged here
             vals, ids, lse = G.dec.topk(G.logits[:w.batch], w.batch)
-            tbi, ttk = _merge_candidates(scores, vals.cpu().numpy(), ids.cpu().numpy(), lse.cpu().numpy(),
-                                         w.vocab, first)
+            tbi, ttk, _ = _merge_candidates(scores, vals.cpu().numpy(), ids.cpu().numpy(), lse.cpu().numpy(),
+                                            w.vocab, first)
             if np.all(ggaps > 1e-4):
                 np.testing.assert_array_equal(tbi, gbi, err_msg=f"device-candidate beams at pos {p}")
                 np.testing.assert_array_equal(ttk, gtk, err_msg=f"device-candidate tokens at pos {p}")
@@ -324,6 +326,62 @@ def test_base_f16_beam5_full():
     G.close()
     say(f"  worst err {worst:.3e}; beam decisions compared {decided}, from device candidates {merged}")
     assert decided > 0 and merged > 0
+
+
+def test_beam_step_on_device_matches_host_merge():
+    """wd_beam_step (candidates, W x W merge and cache rearrangement, all on the device, the
+    next tokens written straight into the token buffer) against the same step taken from the
+    device candidates with the merge in float64 on the host and wd_reorder: over 64 positions of
+    a width-5 search the two decoders write bit-identical logits, and the beam indices, tokens
+    and float64 scores agree exactly (the same operations in the same order).  The host merge
+    is the rule that test_base_f16_beam5_full checks against the oracle."""
+    need_gpu()
+    w = WL.reduced(WL.by_name("whisper_base_f16_beam5"), layers=2)
+    say(f"[beam step on device] {w.describe()}")
+    W = WL.make_weights(w)
+    enc = WL.make_encoder_states(w)
+    A, H = GpuRun(w, W), GpuRun(w, W)
+    A.cross(enc)
+    H.cross(enc)
+    nb, steps = w.batch, 64
+    prompt = WL.make_prompt(w)
+    scores_dev = torch.zeros(nb, dtype=torch.float64, device="cuda")
+    bi_dev = torch.zeros(nb, dtype=torch.int32, device="cuda")
+    scores, toks = np.zeros(nb), prompt[:, 0]
+    merged = 0
+    for p in range(steps):
+        if p < prompt.shape[1]:
+            toks = prompt[:, p]
+            A.tok.copy_(torch.as_tensor(np.asarray(toks, np.int32)))
+        A.pos.fill_(p)
+        A.dec.step(A.tok, A.pos, A.logits, A.amax)
+        lg_h, _ = H.step(toks, p)
+        np.testing.assert_array_equal(A.logits.cpu().numpy(), lg_h, err_msg=f"logits at pos {p}")
+        if p >= prompt.shape[1] - 1:
+            first = p == prompt.shape[1] - 1
+            n_rows = p + 1 if p + 1 < steps else 0
+            A.dec.beam_step(A.logits, nb, first, scores_dev, bi_dev, A.tok, n_rows)
+            vals, ids, lse = H.dec.topk(H.logits, nb)
+            hbi, htk, hsc = _merge_candidates(scores, vals.cpu().numpy(), ids.cpu().numpy(), lse.cpu().numpy(),
+                                              w.vocab, first)
+            np.testing.assert_array_equal(bi_dev.cpu().numpy(), hbi, err_msg=f"beam indices at pos {p}")
+            np.testing.assert_array_equal(A.tok.cpu().numpy(), htk, err_msg=f"tokens at pos {p}")
+            np.testing.assert_array_equal(scores_dev.cpu().numpy(), hsc, err_msg=f"scores at pos {p}")
+            if n_rows:
+                H.dec.reorder(hbi, n_rows)
+            toks, scores = htk, hsc
+            merged += 1
+    K = A.K
+    for bad in (dict(W=nb + 1), dict(first=2), dict(n_rows=w.context + 1)):
+        args = {**dict(W=nb, first=0, n_rows=1), **bad}
+        st = K.lib().wd_beam_step(A.dec.ctx, ctypes.c_void_p(A.logits.data_ptr()), args["W"], args["first"],
+                                  ctypes.c_void_p(scores_dev.data_ptr()), ctypes.c_void_p(bi_dev.data_ptr()),
+                                  ctypes.c_void_p(A.tok.data_ptr()), args["n_rows"])
+        assert st == 1, (bad, st)
+    assert A.check() == 0 and H.check() == 0
+    A.close()
+    H.close()
+    say(f"  device beam steps compared {merged}")
 
 
 def test_reorder_identity_and_inverse_restore_cache():
