@@ -56,6 +56,8 @@ class WdTensor(ctypes.Structure):
 
 
 def lib_path() -> str:
+    """The in-tree build, or the library the WD_LIB environment variable names (another build
+    of the same sources, e.g. one compiled with different flags); there is no other fallback."""
     return os.environ.get("WD_LIB", os.path.join(HERE, "libwd.so"))
 
 
