@@ -750,7 +750,9 @@ static MShape mpick(int N, int K, int B, int epi) {
   s.NBB = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
   const int nblocks = (N + 15) / 16, ksteps = K / 32;
   if (nblocks >= 1024) {
-    s.NBW = s.NBB == 4 ? 2 : 4;
+    // the tied head: 2 row blocks per wave, twice the workgroups of 4 (whisper-small head 19.1
+    // -> 17.1 us, 203 -> 406 workgroups on 256 CUs; Qwen3 head 112.2 -> 111.1 us)
+    s.NBW = 2;
     s.KS = (s.NBW == 2 && ksteps >= 32) ? 2 : 1;
   } else if (nblocks >= 128 || epi == EPI_SWIGLU_SPLIT) {
     s.NBW = 2;
