@@ -315,14 +315,27 @@ __device__ __forceinline__ uint32_t pa_bits(CT v) {
   if constexpr (sizeof(CT) == 2 && std::is_same<CT, bf16_t>::value) return v.x;
   else return (uint32_t)__builtin_bit_cast(uint16_t, v);
 }
+// Two floats -> packed hi and lo 16-bit pairs (hi = round(v), lo = round(v - hi)).  bf16 takes
+// the hardware round-to-nearest-even convert (v_cvt_pk_bf16_f32, two values per instruction;
+// the same bits as the integer rounding of from_f for every finite value): the attention's
+// inner loop is bound by its VALU work, and the integer rounding took about 7 instructions a
+// value.
 template <typename CT>
 __device__ __forceinline__ uint32_t pa_pack2(float a, float b, uint32_t& lo) {
-  CT ha, la, hb, lb;
-  split_hi_lo<CT>(a, ha, la);
-  split_hi_lo<CT>(b, hb, lb);
-  lo = pa_bits(la) | (pa_bits(lb) << 16);
-  return pa_bits(ha) | (pa_bits(hb) << 16);
+  if constexpr (std::is_same<CT, bf16_t>::value) {
+    const __bf16 ha = (__bf16)a, hb = (__bf16)b;
+    const __bf16 la = (__bf16)(a - (float)ha), lb = (__bf16)(b - (float)hb);
+    lo = (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+  } else {
+    CT ha, la, hb, lb;
+    split_hi_lo<CT>(a, ha, la);
+    split_hi_lo<CT>(b, hb, lb);
+    lo = pa_bits(la) | (pa_bits(lb) << 16);
+    return pa_bits(ha) | (pa_bits(hb) << 16);
+  }
 }
+constexpr float PA_LOG2E = 1.4426950408889634f;
 
 // Block order: the (stream, kv head, query block) units are numbered query block fastest and
 // cut into 8 equal runs, one per XCD (workgroup L runs on XCD L % 8), so the query blocks that
@@ -367,8 +380,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
       const float4 u0 = *reinterpret_cast<const float4*>(qr + 32 * ks);
       const float4 u1 = *reinterpret_cast<const float4*>(qr + 32 * ks + 4);
       uint32_t l0, l1, l2, l3;
-      qh[ks][0] = pa_pack2<CT>(u0.x, u0.y, l0); qh[ks][1] = pa_pack2<CT>(u0.z, u0.w, l1);
-      qh[ks][2] = pa_pack2<CT>(u1.x, u1.y, l2); qh[ks][3] = pa_pack2<CT>(u1.z, u1.w, l3);
+      // scores in log2 units (q times log2 e), so the softmax exponentials are bare exp2
+      qh[ks][0] = pa_pack2<CT>(u0.x * PA_LOG2E, u0.y * PA_LOG2E, l0);
+      qh[ks][1] = pa_pack2<CT>(u0.z * PA_LOG2E, u0.w * PA_LOG2E, l1);
+      qh[ks][2] = pa_pack2<CT>(u1.x * PA_LOG2E, u1.y * PA_LOG2E, l2);
+      qh[ks][3] = pa_pack2<CT>(u1.z * PA_LOG2E, u1.w * PA_LOG2E, l3);
       ql[ks][0] = l0; ql[ks][1] = l1; ql[ks][2] = l2; ql[ks][3] = l3;
     }
   }
@@ -432,7 +448,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
       mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
       mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
       const float mn = fmaxf(m, mx);          // finite: key 0 counts for every query
-      const float f = expf(m - mn);
+      const float f = __builtin_amdgcn_exp2f(m - mn);   // 2^(m - mn): 0 while m is -inf
       m = mn;
       lsum *= f;
 #pragma unroll
@@ -442,7 +458,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
       float pv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        pv[i] = expf(sv[i] - mn);
+        pv[i] = __builtin_amdgcn_exp2f(sv[i] - mn);
         lsum += pv[i];
       }
       pv4u ph, pl;
