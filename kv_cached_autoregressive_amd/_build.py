@@ -31,9 +31,15 @@ def hipcc() -> str:
     return "hipcc"
 
 
+# Per-file additions.  The prefill and encoder kernels keep their MFMA accumulators in
+# ordinary VGPRs: with the default accumulator registers the attention's per-tile rescale of
+# its output accumulators cost 32 register moves a tile on top of its softmax arithmetic.
+FILE_FLAGS = {"k_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
