@@ -104,7 +104,31 @@ __device__ __forceinline__ void fg_epilogue(const FgParams& p, const pf32x4_t (&
                                             int lane) {
   // tile (i, j): lane holds rows (rt0+i)*16 + 4*(lane/16) + e of column (ct0+j)*16 + lane%16
   const int rsub = (lane >> 4) * 4, col = lane & 15;
-  if constexpr (EPI == FG_SWIGLU) {
+  if constexpr (EPI == FG_ENC_QKV) {
+    const int d = p.N / 3;
+#pragma unroll
+    for (int j = 0; j < WC; ++j) {
+      const int n = (ct0 + j) * 16 + col, sec = n / d, c = n - sec * d;
+      const int h = c / p.kv_hd, ch = c - h * p.kv_hd;
+      const float bn = sec == 0 ? (p.bias ? p.bias[c] : 0.f) : sec == 2 ? (p.bias2 ? p.bias2[c] : 0.f) : 0.f;
+#pragma unroll
+      for (int i = 0; i < WR; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = (rt0 + i) * 16 + rsub + e;
+          if (r < p.R) {
+            const float v = acc[i][j][e] + bn;
+            if (sec == 0) {
+              p.out[(int64_t)r * d + c] = v * p.scale;
+            } else {
+              const int b = r / p.kv_P, fr = r - b * p.kv_P;
+              const int64_t kv = (((int64_t)b * p.kv_H + h) * p.kv_P + fr) * p.kv_hd + ch;
+              reinterpret_cast<T*>(sec == 1 ? p.Kc : p.Vc)[kv] = from_f<T>(v);
+            }
+          }
+        }
+    }
+  } else if constexpr (EPI == FG_SWIGLU) {
     // weight row blocks alternate gate, up for the same 16 outputs: tiles (0,1), (2,3)
     const int half = p.N >> 1;
 #pragma unroll
@@ -280,6 +304,8 @@ hipError_t launch_fgemm(const FgParams& p, hipStream_t s) {
   if (p.R <= 0 || p.N <= 0 || p.N % 128 || p.K <= 0 || p.K % 32 || !p.W || !p.Ahi || !p.Alo) return hipErrorInvalidValue;
   if (p.epi == FG_SWIGLU ? (!p.Ohi || !p.Olo || p.N % 256)
       : p.epi == FG_GELU_SPLIT ? (!p.Ohi || !p.Olo)
+      : p.epi == FG_ENC_QKV ? (!p.out || !p.Kc || !p.Vc || p.N % 3 || p.kv_P <= 0 || p.kv_H <= 0 || p.kv_hd <= 0 ||
+                               p.kv_H * p.kv_hd != p.N / 3 || p.R % p.kv_P)
       : (!p.out || p.ldo < p.N || (p.epi == FG_GELU && p.pos && p.pos_rows <= 0)))
     return hipErrorInvalidValue;
   // 128-row blocks unless they leave CUs idle (then 64-row blocks; A is padded to 128 rows)
@@ -302,6 +328,7 @@ hipError_t launch_fgemm(const FgParams& p, hipStream_t s) {
     case FG_SWIGLU: WD_FG1(T_, FG_SWIGLU) break;                                                         \
     case FG_GELU: WD_FG1(T_, FG_GELU) break;                                                             \
     case FG_GELU_SPLIT: WD_FG1(T_, FG_GELU_SPLIT) break;                                                 \
+    case FG_ENC_QKV: WD_FG1(T_, FG_ENC_QKV) break;                                                       \
     default: return hipErrorInvalidValue;                                                                \
   }
   if (p.w_dtype == DT_BF16) { WD_FG(bf16_t) }
@@ -600,35 +627,6 @@ hipError_t launch_pack_pad(const void* src, int src_dtype, int64_t rows, int Ks,
   else return hipErrorInvalidValue;
 #undef WD_PP_S
 #undef WD_PP
-  return hipGetLastError();
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void k_enc_qkv(const float* __restrict__ qkv, const float* __restrict__ bq,
-                                                 const float* __restrict__ bv, int nb, int P, int H, int hd,
-                                                 float qscale, float* __restrict__ q, T* __restrict__ K,
-                                                 T* __restrict__ V) {
-  const int d = H * hd;
-  const int64_t n = (int64_t)nb * P * d;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / d;
-    const int c = (int)(i - r * d);
-    const int b = (int)(r / P), pp = (int)(r - (int64_t)b * P), h = c / hd, ch = c - h * hd;
-    const float* row = qkv + r * 3 * d;
-    q[i] = (row[c] + (bq ? bq[c] : 0.f)) * qscale;
-    const int64_t kv = (((int64_t)b * H + h) * P + pp) * hd + ch;
-    K[kv] = from_f<T>(row[d + c]);
-    V[kv] = from_f<T>(row[2 * d + c] + (bv ? bv[c] : 0.f));
-  }
-}
-
-hipError_t launch_enc_qkv(const float* qkv, const float* bq, const float* bv, int nb, int P, int H, int hd,
-                          float qscale, float* q, void* K, void* V, int kv_dtype, hipStream_t s) {
-  if (!qkv || !q || !K || !V || nb <= 0 || P <= 0 || H <= 0 || hd <= 0) return hipErrorInvalidValue;
-  const int blocks = (int)std::min<int64_t>(((int64_t)nb * P * H * hd + 255) / 256, 65536);
-  if (kv_dtype == DT_BF16) k_enc_qkv<bf16_t><<<blocks, 256, 0, s>>>(qkv, bq, bv, nb, P, H, hd, qscale, q, (bf16_t*)K, (bf16_t*)V);
-  else if (kv_dtype == DT_F16) k_enc_qkv<f16_t><<<blocks, 256, 0, s>>>(qkv, bq, bv, nb, P, H, hd, qscale, q, (f16_t*)K, (f16_t*)V);
-  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -276,7 +276,7 @@ EncPlan make_enc_plan(const wd_config& c, int mels, int frames, int layers, int 
   p.x = b.take(r * d * f4);
   p.ah = b.take(ka * wb); p.al = b.take(ka * wb);
   p.hh = b.take(r * dff * wb); p.hl = b.take(r * dff * wb);
-  p.qkv = b.take(r * 3 * d * f4);
+  p.qkv = b.take(r * d * f4);   // the final norm's fp32 output (q, K and V come from the GEMM's epilogue)
   p.q = b.take(r * d * f4);
   p.K = b.take((size_t)max_sets * p.P * d * wb); p.V = b.take((size_t)max_sets * p.P * d * wb);
   p.states = b.take((size_t)max_sets * p.P * d * wb);
@@ -1365,10 +1365,13 @@ wd_status wd_encode(wd_ctx* ctx, const void* mel, int32_t n_sets, void* enc) {
       const EncLayer& L = E->L[l];
       HIPCHK(ctx, wd::launch_norm_split(atf(E->x), at(E->ah), at(E->al), wdt, atf(L.ln1g), atf(L.ln1b), R, d,
                                         g.norm_eps, s), "wd_encode: ln1");
-      WDCHK(gemm(at(L.wqkv), 3 * d, d, at(E->ah), at(E->al), R, wd::FG_STORE, atf(E->qkv), nullptr, nullptr,
-                 nullptr, nullptr, "wd_encode: q|k|v"));
-      HIPCHK(ctx, wd::launch_enc_qkv(atf(E->qkv), atf(L.bq), atf(L.bv), n_sets, P, H, hd, qscale, atf(E->q),
-                                     at(E->K), at(E->V), wdt, s), "wd_encode: q, K, V");
+      {   // q|k|v with its biases, the q scale and the K/V layout in the GEMM's epilogue
+        wd::FgParams f{};
+        f.W = at(L.wqkv); f.w_dtype = wdt; f.N = 3 * d; f.K = d; f.Ahi = at(E->ah); f.Alo = at(E->al); f.R = R;
+        f.epi = wd::FG_ENC_QKV; f.out = atf(E->q); f.ldo = d; f.bias = atf(L.bq); f.bias2 = atf(L.bv);
+        f.scale = qscale; f.Kc = at(E->K); f.Vc = at(E->V); f.kv_P = P; f.kv_H = H; f.kv_hd = hd;
+        HIPCHK(ctx, wd::launch_fgemm(f, s), "wd_encode: q|k|v");
+      }
       wd::PfAttnParams pa{};
       pa.q = atf(E->q); pa.K = at(E->K); pa.V = at(E->V); pa.cache_dtype = wdt;
       pa.kv_bstride = (int64_t)H * P * hd; pa.ctx = P; pa.B = n_sets; pa.C = P; pa.Cn = P; pa.t0 = 0;

@@ -170,7 +170,7 @@ hipError_t launch_pf_embed(float* x, int32_t* pos, const void* E, int w_dtype, c
                            const void* emb, int A, int offset, int t0, int B, int C, int Cn, int d, int V,
                            unsigned* err, hipStream_t s);
 // Dense GEMM over fragment-layout operands: C[R, N] = (Ahi + Alo)[R, K] . W[N, K]^T.
-enum FgEpi : int { FG_STORE = 0, FG_RESID = 1, FG_SWIGLU = 2, FG_GELU = 3, FG_GELU_SPLIT = 4 };
+enum FgEpi : int { FG_STORE = 0, FG_RESID = 1, FG_SWIGLU = 2, FG_GELU = 3, FG_GELU_SPLIT = 4, FG_ENC_QKV = 5 };
 struct FgParams {
   const void* W; int w_dtype; int N; int K;   // W fragment layout (N % 128 == 0)
   const void* Ahi; const void* Alo; int R;    // A fragment layout [R rounded up to 128, K]
@@ -181,6 +181,10 @@ struct FgParams {
                                               // GELU_SPLIT: GELU(C), fragment layout [R_pad, N]
   const float* bias;                          // optional [N], added to C first (STORE, RESID, GELU*)
   const float* pos; int pos_rows;             // GELU: optional [pos_rows, N] added after the GELU
+  // ENC_QKV (the encoder's fused q|k|v, N = 3 d, d = kv_H kv_hd, rows r = set * kv_P + frame):
+  // columns < d -> out[r][c] = (C + bias[c]) * scale (fp32 [R, d]); the next d -> K, the last d
+  // (+ bias2[c]) -> V, both [set][head][frame][hd] in the weight dtype
+  const float* bias2; float scale; void* Kc; void* Vc; int kv_P; int kv_H; int kv_hd;
 };
 hipError_t launch_fgemm(const FgParams& p, hipStream_t s);
 // Causal attention of a chunk's rows over cache rows 0..t of their stream (GQA).
@@ -202,10 +206,6 @@ hipError_t launch_conv_windows(const void* x, int x_dtype, int nb, int L, int C,
 // Row-major [rows, Ks] (any wd dtype) -> fragment layout [rows, Kp] (Kp >= Ks, columns >= Ks zero).
 hipError_t launch_pack_pad(const void* src, int src_dtype, int64_t rows, int Ks, void* dst, int dst_dtype, int Kp,
                            hipStream_t s);
-// q|k|v rows [nb * P, 3 d] fp32 -> q [nb * P, d] fp32 ((q + bq) * qscale), K and V [nb][H][P][hd]
-// in kv_dtype (K as is, V + bv).
-hipError_t launch_enc_qkv(const float* qkv, const float* bq, const float* bv, int nb, int P, int H, int hd,
-                          float qscale, float* q, void* K, void* V, int kv_dtype, hipStream_t s);
 // fp32 [n] -> dtype [n]
 hipError_t launch_cast(const float* x, void* y, int y_dtype, int64_t n, hipStream_t s);
 
