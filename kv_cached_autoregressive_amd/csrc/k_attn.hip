@@ -10,13 +10,20 @@
 //
 // Per block, one pass over its rows: K and V rows stream together (16 B per
 // lane; a wave covers 4 or 8 whole rows per load, fully coalesced), the lanes of
-// a row reduce the q.k dot product with shuffles, and each lane keeps an online
+// a row reduce the q.k dot product with DPP adds, and each lane keeps an online
 // softmax state (running max, running exp-sum and its slice of the weighted V
 // sum), rescaled when the max grows.  The lanes' states are merged at the end
-// (shuffles within a wave, LDS across waves).  With one split the block
+// (DPP moves and permlane swaps within a wave, LDS across waves).
+//
+// Scores are kept in base 2: q is scaled by log2(e) once, so every exponential
+// is a bare v_exp_f32 and the softmax weights are unchanged.  With a 16-bit
+// cache q is split into (hi, lo) halves of the cache type (q = hi + lo to about
+// 16 bits, each half's products exact in fp32), so the 8 channels a lane holds
+// take 8 packed dot2 instructions and the K row is never unpacked.  With one split the block
 // normalises and writes o; otherwise it writes (o, max, sum) partials that a
 // combine kernel rescales and adds.
 #include <algorithm>
+#include <type_traits>
 
 #include "wd_common.h"
 #include "wd_kernels.h"
@@ -55,6 +62,114 @@ __device__ __forceinline__ Raw8<T> fetch8_nt(const T* p) {
   const nt4u a = __builtin_nontemporal_load(reinterpret_cast<const nt4u*>(p));
   r.v = __builtin_bit_cast(uint4, a);
   return r;
+}
+
+constexpr float ATT_LOG2E = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP lane moves within a 16-lane row (all rows and banks enabled; every source lane exists)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i of 8 <- lane 7 - i
+constexpr int DPP_ROR8 = 0x128;        // lane i of 16 <- lane (i + 8) mod 16
+
+// Sum over the SEGS (8 or 16) consecutive lanes that hold one cache row; every lane of the
+// group gets the same bits (each step adds a value and its partner's in either order).
+template <int SEGS>
+__device__ __forceinline__ float seg_sum(float d) {
+  static_assert(SEGS == 8 || SEGS == 16, "lanes per row");
+  d += dpp_mov<DPP_XOR1>(d);
+  d += dpp_mov<DPP_XOR2>(d);
+  d += dpp_mov<DPP_HALF_MIRROR>(d);   // quads hold equal values: the mirror brings the other quad's
+  if constexpr (SEGS == 16) d += dpp_mov<DPP_ROR8>(d);
+  return d;
+}
+
+// The values of lanes i and i ^ OFF (OFF = 8, 16, 32): own and partner for OFF = 8 (a DPP
+// rotation), the lower and upper lane of the pair for 16 and 32 (the gfx950 permlane swaps
+// hand both to both lanes).  The merge below is symmetric in the two, so either order serves.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float x, float& u, float& w) {
+  if constexpr (OFF == 8) {
+    u = x;
+    w = dpp_mov<DPP_ROR8>(x);
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+    const int r0 = r[0], r1 = r[1];   // (bit-casting r[1] in place reads r[0] with this hipcc)
+    u = __int_as_float(r0);
+    w = __int_as_float(r1);
+  } else {
+    static_assert(OFF == 32, "pair distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    const int r0 = r[0], r1 = r[1];   // (bit-casting r[1] in place reads r[0] with this hipcc)
+    u = __int_as_float(r0);
+    w = __int_as_float(r1);
+  }
+}
+
+// q in the form the score takes: fp32 for a float cache, else (hi, lo) pairs of the cache type
+template <typename CT> struct QOp { uint32_t h[4], l[4]; };
+template <> struct QOp<float> { float v[8]; };
+template <typename CT>
+__device__ __forceinline__ QOp<CT> make_qop(const float (&f)[8]) {
+  QOp<CT> q;
+  if constexpr (sizeof(CT) == 4) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q.v[j] = f[j];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t hb[2], lb[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float v = f[2 * i + e];
+        if constexpr (std::is_same<CT, bf16_t>::value) {
+          const __bf16 h = (__bf16)v, l = (__bf16)(v - (float)h);
+          hb[e] = __builtin_bit_cast(uint16_t, h);
+          lb[e] = __builtin_bit_cast(uint16_t, l);
+        } else {
+          const f16_t h = (f16_t)v, l = (f16_t)(v - (float)h);
+          hb[e] = __builtin_bit_cast(uint16_t, h);
+          lb[e] = __builtin_bit_cast(uint16_t, l);
+        }
+      }
+      q.h[i] = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
+      q.l[i] = (uint32_t)lb[0] | ((uint32_t)lb[1] << 16);
+    }
+  }
+  return q;
+}
+// this lane's part of q.k over its 8 channels
+template <typename CT>
+__device__ __forceinline__ float qk8(const QOp<CT>& q, const Raw8<CT>& k) {
+  if constexpr (sizeof(CT) == 4) {
+    float kf[8];
+    unpack8(k, kf);
+    float d = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d = fmaf(q.v[j], kf[j], d);
+    return d;
+  } else {
+    const uint32_t kw[4] = {k.v.x, k.v.y, k.v.z, k.v.w};
+    float dh = 0.f, dl = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (std::is_same<CT, bf16_t>::value) {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        dh = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, q.h[i]), __builtin_bit_cast(b2, kw[i]), dh, false);
+        dl = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, q.l[i]), __builtin_bit_cast(b2, kw[i]), dl, false);
+      } else {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        dh = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, q.h[i]), __builtin_bit_cast(h2, kw[i]), dh, false);
+        dl = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, q.l[i]), __builtin_bit_cast(h2, kw[i]), dl, false);
+      }
+    }
+    return dh + dl;
+  }
 }
 
 // o for (row bq, head h, channel c): fp32 row-major, or split fragment layout
@@ -246,20 +361,24 @@ __global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {
       }
   }
 
-  float qv[NQ][8];
+  QOp<CT> qv[NQ];
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
+    float f[8];
     if (qi < nq) {
       if (p.qpart) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) qv[qi][j] = qs[qi * HD + seg * 8 + j];
+        for (int j = 0; j < 8; ++j) f[j] = qs[qi * HD + seg * 8 + j];
       } else {
-        load8(p.q + (int64_t)qrow(qi) * p.q_ld + qhead(qi) * HD + seg * 8, qv[qi]);
+        load8(p.q + (int64_t)qrow(qi) * p.q_ld + qhead(qi) * HD + seg * 8, f);
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qv[qi][j] = 0.f;
+      for (int j = 0; j < 8; ++j) f[j] = 0.f;
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] *= ATT_LOG2E;
+    qv[qi] = make_qop<CT>(f);
   }
 
   // one pass over the rows: each lane keeps, per query, the running max m, the
@@ -277,25 +396,20 @@ __global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const bool live = r + u * RPP < r_hi;
-      float kf[8], vf[8];
-      unpack8(kr[u], kf);
+      float vf[8];
       unpack8(vr[u], vf);
 #pragma unroll
       for (int qi = 0; qi < NQ; ++qi) {
-        float d = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) d = fmaf(qv[qi][j], kf[j], d);
-#pragma unroll
-        for (int o = 1; o < SEGS; o <<= 1) d += __shfl_xor(d, o, WAVE);
+        const float d = seg_sum<SEGS>(qk8<CT>(qv[qi], kr[u]));
         if (live && qi < nq) {
           if (d > m[qi]) {  // new running max: rescale what was accumulated
-            const float sc = expf(m[qi] - d);
+            const float sc = exp2_fast(m[qi] - d);
             l[qi] *= sc;
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[qi][j] *= sc;
             m[qi] = d;
           }
-          const float e = expf(d - m[qi]);
+          const float e = exp2_fast(d - m[qi]);
           l[qi] += e;
 #pragma unroll
           for (int j = 0; j < 8; ++j) acc[qi][j] = fmaf(e, vf[j], acc[qi][j]);
@@ -320,24 +434,29 @@ __global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {
   pass(r);
   // merge the (m, l, acc) of the lanes holding the same segment: within the wave,
   // then across the NW waves through LDS
+  auto merge = [&](auto off) __attribute__((always_inline)) {
+    constexpr int OFF = decltype(off)::value;
 #pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) {
-#pragma unroll
-    for (int o = SEGS; o < 64; o <<= 1) {
-      const float m2 = __shfl_xor(m[qi], o, WAVE);
-      const float l2 = __shfl_xor(l[qi], o, WAVE);
-      const float mn = fmaxf(m[qi], m2);
-      const float f1 = mn == -INFINITY ? 0.f : expf(m[qi] - mn);
-      const float f2 = mn == -INFINITY ? 0.f : expf(m2 - mn);
-      l[qi] = l[qi] * f1 + l2 * f2;
+    for (int qi = 0; qi < NQ; ++qi) {
+      float mu, mw, lu, lw;
+      lane_pair<OFF>(m[qi], mu, mw);
+      lane_pair<OFF>(l[qi], lu, lw);
+      const float mn = fmaxf(mu, mw);
+      const float fu = mn == -INFINITY ? 0.f : exp2_fast(mu - mn);
+      const float fw = mn == -INFINITY ? 0.f : exp2_fast(mw - mn);
+      l[qi] = lu * fu + lw * fw;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float a2 = __shfl_xor(acc[qi][j], o, WAVE);
-        acc[qi][j] = acc[qi][j] * f1 + a2 * f2;
+        float au, aw;
+        lane_pair<OFF>(acc[qi][j], au, aw);
+        acc[qi][j] = au * fu + aw * fw;
       }
       m[qi] = mn;
     }
-  }
+  };
+  if constexpr (SEGS == 8) merge(std::integral_constant<int, 8>());
+  merge(std::integral_constant<int, 16>());
+  merge(std::integral_constant<int, 32>());
   if (lane < SEGS) {
 #pragma unroll
     for (int qi = 0; qi < NQ; ++qi) {
@@ -355,7 +474,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {
     float L = 0.f, o = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < NW; ++w2) {
-      const float f = red[w2][qi][HD] == -INFINITY ? 0.f : expf(red[w2][qi][HD] - M);
+      const float f = red[w2][qi][HD] == -INFINITY ? 0.f : exp2_fast(red[w2][qi][HD] - M);
       L += f * red[w2][qi][HD + 1];
       o += f * red[w2][qi][c];
     }
@@ -393,7 +512,7 @@ __global__ __launch_bounds__(HD) void k_attn_combine(const float* __restrict__ p
   float L = 0.f, o = 0.f;
 #pragma unroll
   for (int s = 0; s < MAXS; ++s) {
-    const float w = (s < n_splits && M != -INFINITY) ? expf(m[s] - M) : 0.f;
+    const float w = (s < n_splits && M != -INFINITY) ? exp2_fast(m[s] - M) : 0.f;
     L += w * l[s];
     o += w * ov[s];
   }
