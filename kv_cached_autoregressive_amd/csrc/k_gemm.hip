@@ -143,10 +143,12 @@ __global__ __launch_bounds__(256) void k_xkv_frag(const T* __restrict__ Xf, cons
 // tiles).  Per 32-deep K step the block's 16 + 8 operand tiles (1 KB each, fragment order) are
 // loaded once into LDS and every wave reads its 4 + 4 tiles from there, so each fragment
 // leaves L2 once per block instead of once per wave.  The loads go straight from global
-// memory into a ring of three LDS slots, two K steps ahead of the MFMAs (no staging
-// registers, no LDS stores); each step waits for its own loads by count and meets the other
-// waves at a bare barrier (a full __syncthreads would also wait for the loads still in
-// flight).  Same XCD panel order and epilogue as k_xkv_frag, the 256 rows in two halves.
+// memory (buffer loads with the LDS destination) into a ring of three LDS slots, two K steps
+// ahead of the MFMAs (no staging registers, no LDS stores); each step waits for its own loads
+// by count and meets the other waves at a bare barrier (a full __syncthreads would also wait
+// for the loads still in flight).  Same XCD panel order and epilogue as k_xkv_frag, the 256
+// rows in two halves.  (256 x 256 blocks of eight 128 x 64 waves, one workgroup per CU,
+// measured slower: 22.3 against 21.0 ms per large-v3 window.)
 template <typename T, typename CT>
 __global__ __launch_bounds__(512) void k_xkv_lds(const T* __restrict__ Xf, const T* __restrict__ Wf, int K,
                                                  XkvOut o, int n_mt, int n_nt, int pg) {
@@ -171,13 +173,14 @@ __global__ __launch_bounds__(512) void k_xkv_lds(const T* __restrict__ Xf, const
   // a K step's 24 tiles go straight to LDS, wave wv loading tiles wv, 8 + wv (X) and 16 + wv
   // (W); the step index is clamped so every thread issues exactly 3 loads per step and the
   // vmcnt arithmetic below stays exact
+  const __amdgpu_buffer_rsrc_t ra = buf_rsrc(A, RT * KST * 1024), rb = buf_rsrc(B, CTL * KST * 1024);
   auto issue = [&](int st) __attribute__((always_inline)) {
     const int slot = st % NSLOT;
     st = min(st, KST - 1);
-    const int64_t so = (int64_t)st * 64 + lane;
-    lds_dma16(A + (int64_t)wv * KST * 64 + so, &stage[slot][wv * 64]);
-    lds_dma16(A + (int64_t)(8 + wv) * KST * 64 + so, &stage[slot][(8 + wv) * 64]);
-    lds_dma16(B + (int64_t)wv * KST * 64 + so, &stage[slot][(16 + wv) * 64]);
+    const uint32_t so = (uint32_t)(st * 64 + lane) * 16;
+    lds_dma16(ra, (uint32_t)wv * KST * 1024 + so, &stage[slot][wv * 64]);
+    lds_dma16(ra, (uint32_t)(8 + wv) * KST * 1024 + so, &stage[slot][(8 + wv) * 64]);
+    lds_dma16(rb, (uint32_t)wv * KST * 1024 + so, &stage[slot][(16 + wv) * 64]);
   };
   f32x4_t acc[4][4];
 #pragma unroll

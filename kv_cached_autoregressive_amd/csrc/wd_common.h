@@ -162,11 +162,18 @@ __device__ __forceinline__ float sum_parts(const float* __restrict__ p, int64_t 
   return s;
 }
 
-// One 16-byte load per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// A raw buffer resource over `bytes` bytes at `base` (32-bit byte offsets; a load past the
+// end returns zeros instead of touching memory).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// One 16-byte load per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds):
 // lane i's bytes land at lds_wave + 16 i, so `lds_wave` is the wave's (uniform) 1 KB slot.
-// The load counts in vmcnt like any vector load and writes no VGPR.
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave, 16, 0, 0);
+// The load counts in vmcnt like any vector load and writes no VGPR.  (The buffer form, not
+// global_load_lds: with the latter in a loop, hipcc waits for every outstanding LDS read
+// before the first use of any of them; with this one it counts them.)
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t off, void* lds_wave) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave, 16, off, 0, 0, 0);
 }
 // s_waitcnt with vmcnt = N (N < 16) and the other counters left alone
 template <int N>
