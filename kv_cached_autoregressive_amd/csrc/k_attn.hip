@@ -67,50 +67,6 @@ __device__ __forceinline__ Raw8<T> fetch8_nt(const T* p) {
 constexpr float ATT_LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// DPP lane moves within a 16-lane row (all rows and banks enabled; every source lane exists)
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
-constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
-constexpr int DPP_HALF_MIRROR = 0x141; // lane i of 8 <- lane 7 - i
-constexpr int DPP_ROR8 = 0x128;        // lane i of 16 <- lane (i + 8) mod 16
-
-// Sum over the SEGS (8 or 16) consecutive lanes that hold one cache row; every lane of the
-// group gets the same bits (each step adds a value and its partner's in either order).
-template <int SEGS>
-__device__ __forceinline__ float seg_sum(float d) {
-  static_assert(SEGS == 8 || SEGS == 16, "lanes per row");
-  d += dpp_mov<DPP_XOR1>(d);
-  d += dpp_mov<DPP_XOR2>(d);
-  d += dpp_mov<DPP_HALF_MIRROR>(d);   // quads hold equal values: the mirror brings the other quad's
-  if constexpr (SEGS == 16) d += dpp_mov<DPP_ROR8>(d);
-  return d;
-}
-
-// The values of lanes i and i ^ OFF (OFF = 8, 16, 32): own and partner for OFF = 8 (a DPP
-// rotation), the lower and upper lane of the pair for 16 and 32 (the gfx950 permlane swaps
-// hand both to both lanes).  The merge below is symmetric in the two, so either order serves.
-template <int OFF>
-__device__ __forceinline__ void lane_pair(float x, float& u, float& w) {
-  if constexpr (OFF == 8) {
-    u = x;
-    w = dpp_mov<DPP_ROR8>(x);
-  } else if constexpr (OFF == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
-    const int r0 = r[0], r1 = r[1];   // (bit-casting r[1] in place reads r[0] with this hipcc)
-    u = __int_as_float(r0);
-    w = __int_as_float(r1);
-  } else {
-    static_assert(OFF == 32, "pair distance");
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-    const int r0 = r[0], r1 = r[1];   // (bit-casting r[1] in place reads r[0] with this hipcc)
-    u = __int_as_float(r0);
-    w = __int_as_float(r1);
-  }
-}
-
 // q in the form the score takes: fp32 for a float cache, else (hi, lo) pairs of the cache type
 template <typename CT> struct QOp { uint32_t h[4], l[4]; };
 template <> struct QOp<float> { float v[8]; };

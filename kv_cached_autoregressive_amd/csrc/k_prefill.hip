@@ -492,8 +492,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
           sv[kt * 4 + e] = key <= tmax ? sc[kt][e] : -INFINITY;
           mx = fmaxf(mx, sv[kt * 4 + e]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+      {   // over the four 16-lane key groups of the query (permlane swaps, no LDS)
+        float u, w;
+        lane_pair<16>(mx, u, w);
+        lane_pair<32>(fmaxf(u, w), u, w);
+        mx = fmaxf(u, w);
+      }
       const float mn = fmaxf(m, mx);          // finite: key 0 counts for every query
       const float f = __builtin_amdgcn_exp2f(m - mn);   // 2^(m - mn): 0 while m is -inf
       m = mn;
@@ -527,8 +531,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
       }
     }
   }
-  lsum += __shfl_xor(lsum, 16, WAVE);
-  lsum += __shfl_xor(lsum, 32, WAVE);
+  {
+    float u, w;
+    lane_pair<16>(lsum, u, w);
+    lane_pair<32>(u + w, u, w);
+    lsum = u + w;
+  }
   if (!active) return;
   const float inv = 1.0f / lsum;
   const int K = p.Hq * HD;

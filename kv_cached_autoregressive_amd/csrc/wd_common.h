@@ -95,16 +95,71 @@ __device__ __forceinline__ void store_split(void* hi_base, void* lo_base, int64_
   reinterpret_cast<T*>(lo_base)[off] = l;
 }
 
-// Butterfly sum / max over the 64 lanes of a wave (every lane gets the result).
+// DPP lane moves within a 16-lane row (all rows and banks enabled; every source lane exists)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i of 8 <- lane 7 - i
+constexpr int DPP_ROR8 = 0x128;        // lane i of 16 <- lane (i + 8) mod 16
+
+// Sum over SEGS (8 or 16) consecutive lanes (one cache row of the decode attention, one DPP
+// row); every lane of the group gets the same bits (each step adds a value and its partner's
+// in either order).
+template <int SEGS>
+__device__ __forceinline__ float seg_sum(float d) {
+  static_assert(SEGS == 8 || SEGS == 16, "lanes per row");
+  d += dpp_mov<DPP_XOR1>(d);
+  d += dpp_mov<DPP_XOR2>(d);
+  d += dpp_mov<DPP_HALF_MIRROR>(d);   // quads hold equal values: the mirror brings the other quad's
+  if constexpr (SEGS == 16) d += dpp_mov<DPP_ROR8>(d);
+  return d;
+}
+
+// The values of lanes i and i ^ OFF (OFF = 8, 16, 32): own and partner for OFF = 8 (a DPP
+// rotation), the lower and upper lane of the pair for 16 and 32 (the gfx950 permlane swaps
+// hand both to both lanes).  Callers combine the two symmetrically, so either order serves.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float x, float& u, float& w) {
+  if constexpr (OFF == 8) {
+    u = x;
+    w = dpp_mov<DPP_ROR8>(x);
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+    const int r0 = r[0], r1 = r[1];   // (bit-casting r[1] in place reads r[0] with this hipcc)
+    u = __int_as_float(r0);
+    w = __int_as_float(r1);
+  } else {
+    static_assert(OFF == 32, "pair distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    const int r0 = r[0], r1 = r[1];   // (bit-casting r[1] in place reads r[0] with this hipcc)
+    u = __int_as_float(r0);
+    w = __int_as_float(r1);
+  }
+}
+
+// Sum / max over the 64 lanes of a wave without LDS round trips: DPP steps within each
+// 16-lane row, then the two permlane swaps; every lane gets the same bits.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int s = 32; s > 0; s >>= 1) v += __shfl_xor(v, s, WAVE);
-  return v;
+  v = seg_sum<16>(v);
+  float u, w;
+  lane_pair<16>(v, u, w);
+  v = u + w;
+  lane_pair<32>(v, u, w);
+  return u + w;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int s = 32; s > 0; s >>= 1) v = fmaxf(v, __shfl_xor(v, s, WAVE));
-  return v;
+  v = fmaxf(v, dpp_mov<DPP_XOR1>(v));
+  v = fmaxf(v, dpp_mov<DPP_XOR2>(v));
+  v = fmaxf(v, dpp_mov<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_mov<DPP_ROR8>(v));
+  float u, w;
+  lane_pair<16>(v, u, w);
+  v = fmaxf(u, w);
+  lane_pair<32>(v, u, w);
+  return fmaxf(u, w);
 }
 
 // Block-wide sum for blockDim.x == NT (multiple of 64); `red` holds NT/64 floats.
