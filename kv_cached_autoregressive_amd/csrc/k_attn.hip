@@ -150,9 +150,9 @@ __global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {
   constexpr int NT = 64 * NW;
   constexpr int SEGS = HD / 8;          // lanes per cache row (16 bytes each)
   constexpr int RPP = NT / SEGS;        // rows per block pass
-  // rows per pass per lane (x2 in flight), for K and for V; 8 queries per block keep 3 so that
-  // nothing spills (the 5-beam cross-attention)
-  constexpr int UNR = NQ == 1 || NQ >= 8 ? 3 : 4;
+  // rows per pass per lane (x2 in flight), for K and for V; 8 queries per block keep 3 (2 in
+  // 4-wave blocks) so that nothing spills (the 5-beam cross-attention)
+  constexpr int UNR = NQ >= 8 && NW == 4 ? 2 : NQ == 1 || NQ >= 8 ? 3 : 4;
   __shared__ float red[NW][NQ][HD + 2];
 
   const int s = blockIdx.x, g = blockIdx.y, kvb = blockIdx.z;
