@@ -93,6 +93,16 @@ def test_qwen3_prefill_two_chunks_hd64_bf16_cache_gqa4():
     _qwen_parity(w, T=600, steps=4, streams=(0, 1))
 
 
+@pytest.mark.parametrize("batch", [6, 64])
+def test_qwen3_gqa8_decode_attention(batch):
+    """8 query heads per kv head: the decode attention serves all 8 from one block (8 queries
+    per block), split over rows in 8-wave blocks at 6 rows (48 slabs) and unsplit in 4-wave
+    blocks at 64 rows (512 slabs, 2 rows per pass per lane)."""
+    w = WL.reduced(WL.by_name("qwen3asr_bf16_b8"), layers=1, d=256, heads=64, kv_heads=8, head_dim=64,
+                   d_ff=512, vocab=7001, context=40, batch=batch, audio_offset=2, audio_rows=6)
+    _qwen_parity(w, T=12, steps=4, streams=(0, batch - 1))
+
+
 def test_qwen3_prefill_mha_odd_rows():
     """One query head per kv head (no GQA) and 3 streams of 70 positions: the prefill
     attention's query tiles mix positions across a partial last block."""
