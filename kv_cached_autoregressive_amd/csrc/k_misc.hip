@@ -340,26 +340,33 @@ __global__ __launch_bounds__(1024) void k_norm_part(float* __restrict__ x, OT* _
   float v[PE];
   if constexpr (SKIP) {
     const int wbase = __builtin_amdgcn_readfirstlane(t & ~63);   // first column of this wave
-    // every live pass's loads are issued before any of them is summed (one round trip)
-    float xb[PE], pv[PE][GMAX];
+    // every live pass's loads are issued before any of them is summed (one round trip; two
+    // when the 4-pass, 32-slab case would not fit the 128 registers of a 1024-thread block)
+    constexpr int JB = PE * GMAX > 96 ? PE / 2 : PE;
 #pragma unroll
-    for (int j = 0; j < PE; ++j) {
-      if (wbase + j * 1024 < d) {   // uniform over the wave
-        const int i = min(t + j * 1024, d - 1);
-        xb[j] = xr[i] + (pbias ? pbias[i] : 0.f);
-        const float* pp = part + (int64_t)row * d + i;
+    for (int j0 = 0; j0 < PE; j0 += JB) {
+      float xb[JB], pv[JB][GMAX];
 #pragma unroll
-        for (int k = 0; k < GMAX; ++k) pv[j][k] = __builtin_nontemporal_load(pp + (int64_t)min(k, G - 1) * pstride);
+      for (int jj = 0; jj < JB; ++jj) {
+        const int j = j0 + jj;
+        if (wbase + j * 1024 < d) {   // uniform over the wave
+          const int i = min(t + j * 1024, d - 1);
+          xb[jj] = xr[i] + (pbias ? pbias[i] : 0.f);
+          const float* pp = part + (int64_t)row * d + i;
+#pragma unroll
+          for (int k = 0; k < GMAX; ++k) pv[jj][k] = __builtin_nontemporal_load(pp + (int64_t)min(k, G - 1) * pstride);
+        }
       }
-    }
 #pragma unroll
-    for (int j = 0; j < PE; ++j) {
-      v[j] = 0.f;
-      if (wbase + j * 1024 < d) {
-        float sp = 0.f;   // g = 0..G-1 in order, then onto x + bias (as sum_parts adds them)
+      for (int jj = 0; jj < JB; ++jj) {
+        const int j = j0 + jj;
+        v[j] = 0.f;
+        if (wbase + j * 1024 < d) {
+          float sp = 0.f;   // g = 0..G-1 in order, then onto x + bias (as sum_parts adds them)
 #pragma unroll
-        for (int k = 0; k < GMAX; ++k) sp += k < G ? pv[j][k] : 0.f;
-        v[j] = xb[j] + sp;
+          for (int k = 0; k < GMAX; ++k) sp += k < G ? pv[jj][k] : 0.f;
+          v[j] = xb[jj] + sp;
+        }
       }
     }
   } else {
