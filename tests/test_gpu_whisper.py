@@ -154,6 +154,15 @@ def test_split_k_projections_above_16_rows(batch):
     _sampled_parity(w, steps=6, streams=(0, batch - 1))
 
 
+def test_wide_model_32_k_groups_into_the_norm():
+    """d = 2560 (not a multiple of 1024) and d_ff = 8192 at 24 rows: fc2 splits K into 32
+    groups, and the final norm folds 32 partial slabs over 4 passes per thread, loading them
+    in two halves."""
+    w = WL.reduced(WL.by_name("whisper_large_bf16_b64"), layers=1, batch=24, n_enc=24, d=2560, heads=40,
+                   kv_heads=40, d_ff=8192, vocab=5001, frames=100)
+    _sampled_parity(w, steps=5, streams=(0, 23))
+
+
 def test_ragged_window_sets_of_different_lengths():
     """wd_cross_kv_ragged: encoder sets of 1500, 777, 1 and 1024 frames in one window, the
     padding rows filled with large values that must never be read; every row's logits
