@@ -347,12 +347,12 @@ hipError_t launch_fgemm(const FgParams& p, hipStream_t s) {
 // ---- causal prefill attention ------------------------------------------------------------------
 // Flash attention on the matrix cores.  A block takes 64 queries of one kv head g and stream b,
 // enumerated (position j, query head g*G + i) as q = j*G + i; wave w holds 16 of them.  Cache
-// rows stream through LDS in tiles of 32 keys: K as stored ([key][hd], rows padded), V
-// transposed ([hd][key]).  Per tile a wave computes S^T = K Q^T (16 keys x 16 queries per MFMA
-// tile, q split into hi + lo in the cache type), so a lane holds 4 keys of one query; the online
-// softmax state of that query lives in the lane; P^T (split hi + lo) is the B operand of
-// O^T += V^T P^T as it stands, with the A operand read from the transposed V tile in the same
-// key order.  Causal: key k counts for the query at position t when k <= t.  q is the scaled,
+// rows stream through LDS in tiles of 32 keys, K and V as stored ([key][hd], rows padded).
+// Per tile a wave computes S^T = K Q^T (16 keys x 16 queries per MFMA tile, q split into hi + lo
+// in the cache type), so a lane holds 4 keys of one query; the online softmax state of that
+// query lives in the lane; P^T (split hi + lo) is the B operand of O^T += V^T P^T as it stands,
+// with the A operand (V^T in the same key order) read from the V tile by the transposing LDS
+// load (ds_read_b64_tr_b16).  Causal: key k counts for the query at position t when k <= t.  q is the scaled,
 // normed and rotated query [R, Hq*hd] fp32; o goes to the split fragment layout [Rp, Hq*hd].
 constexpr int PA_KT = 32;    // keys per tile
 constexpr int PA_QB = 64;    // queries per block (4 waves x 16)
@@ -392,13 +392,13 @@ template <typename CT, typename OT, int HD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) void k_pf_attn(PfAttnParams p, int n_qb,
                                                                                             int per_xcd) {
   constexpr int KLD = HD + 8;                 // K tile row stride (elements): conflict-free 16 B reads
-  constexpr int VLD = PA_KT + 4;              // transposed V tile row stride
+  constexpr int VLD = HD + 8;                 // V tile row stride (elements), rows = keys
   constexpr int NCH = PA_KT * HD / 8;         // 16-byte chunks per tile (K or V)
   constexpr int CPT = NCH / 256;              // chunks per thread
   constexpr int KS = HD / 32;                 // MFMA k-steps over the head dim
   constexpr int HT = HD / 16;                 // output channel tiles
   __shared__ __align__(16) CT Ks[PA_KT * KLD];
-  __shared__ __align__(16) CT Vt[HD * VLD];
+  __shared__ __align__(16) CT Vs[PA_KT * VLD];
   const int u = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (u >= n_qb * p.Hkv * p.B) return;
   const int qb = u % n_qb, g = (u / n_qb) % p.Hkv, b = u / (n_qb * p.Hkv);
@@ -460,12 +460,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
       const int i = t + 256 * u;
       const int kk = i / (HD / 8), c0 = (i % (HD / 8)) * 8;
       *reinterpret_cast<uint4*>(Ks + kk * KLD + c0) = kst[u];
-      // 16-bit halves of the chunk's words, taken with shifts (no address of a register array)
-      unsigned short* vt = reinterpret_cast<unsigned short*>(Vt);
-      const uint32_t wds[4] = {vst[u].x, vst[u].y, vst[u].z, vst[u].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vt[(c0 + e) * VLD + kk] = (unsigned short)((e & 1) ? (wds[e >> 1] >> 16) : (wds[e >> 1] & 0xFFFFu));
+      *reinterpret_cast<uint4*>(Vs + kk * VLD + c0) = vst[u];
     }
     __syncthreads();
     if (k0 + PA_KT < rows_blk) fetch(k0 + PA_KT);   // next tile in flight during the math
@@ -519,12 +514,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
         ph[i] = pa_pack2<CT>(pv[2 * i], pv[2 * i + 1], lo);
         pl[i] = lo;
       }
-      // O^T += V^T P^T; A operand: channel row col of tile h, keys 4 grp .. +4 and 16 + 4 grp .. +4
+      // O^T += V^T P^T; A operand: channel row col of tile h, keys 4 grp .. +4 and 16 + 4 grp .. +4,
+      // read from the row-major V tile by the gfx950 transposing LDS load: within each 16-lane
+      // group, lane r points at key 4 grp + r / 4, channels h*16 + 4 (r % 4) .. +4, and lane i
+      // gets channel h*16 + i of the group's 4 keys
 #pragma unroll
       for (int h = 0; h < HT; ++h) {
-        const CT* vr = Vt + (h * 16 + col) * VLD + 4 * grp;
-        const uint2 v0 = *reinterpret_cast<const uint2*>(vr);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16);
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const CT* vr = Vs + (4 * grp + (col >> 2)) * VLD + h * 16 + 4 * (col & 3);
+        const v4s t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vr));
+        const v4s t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vr + 16 * VLD));
+        const uint2 v0 = __builtin_bit_cast(uint2, t0), v1 = __builtin_bit_cast(uint2, t1);
         const pv4u a = pv4u{v0.x, v0.y, v1.x, v1.y};
         acc[h] = pmma(a, ph, acc[h], (CT*)nullptr);
         acc[h] = pmma(a, pl, acc[h], (CT*)nullptr);
