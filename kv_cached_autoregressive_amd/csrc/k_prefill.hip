@@ -305,6 +305,81 @@ __global__ __launch_bounds__(256) void k_fgemm_lds(FgParams p, FgOrder od) {
   fg_epilogue<T, EPI, WR, WC>(p, acc, rt0, ct0, lane);
 }
 
+// 256 x 128 blocks of eight 64 x 64 waves (4 x 2), the block's 16 Ahi + 16 Alo + 8 W tiles of
+// a K step through two 40 KB LDS slots (buffer loads, five per thread and step), two blocks per
+// CU.  Same XCD block order as k_fgemm_lds over 256-row panels; A is padded to 128 rows only,
+// so the last panel's buffer resource ends at the padded rows (reads past it return zeros).
+template <typename T, int EPI>
+__global__ __launch_bounds__(512) void k_fgemm_lds8(FgParams p, FgOrder od) {
+  constexpr int WR = 4, WC = 4, NTL = 40, NSLOT = 2;
+  __shared__ __align__(16) pv4u stage[NSLOT][NTL * 64];   // 2 x 40 KB
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int q = od.n_mt >> 3, bulk = q * od.n_nt;
+  int mt, nt;
+  if (j < bulk) {
+    const int gi = j / (od.pg * od.n_nt), within = j - gi * od.pg * od.n_nt;
+    const int gsz = min(od.pg, q - gi * od.pg);
+    nt = within / gsz;
+    mt = xcd + 8 * (gi * od.pg + (within - nt * gsz));
+  } else {
+    const int r = od.n_mt - 8 * q, tail = r * od.n_nt, per = (tail + 7) >> 3;
+    const int tu = xcd * per + (j - bulk);
+    if (tu >= tail) return;
+    mt = 8 * q + tu / od.n_nt;
+    nt = tu - (tu / od.n_nt) * od.n_nt;
+  }
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w & 3, wn = w >> 2;
+  const int rt0 = mt * 16 + wm * 4, ct0 = nt * 8 + wn * 4;
+  const int KST = p.K >> 5;
+  const pv4u* __restrict__ Ah = reinterpret_cast<const pv4u*>(p.Ahi) + (int64_t)mt * 16 * KST * 64;
+  const pv4u* __restrict__ Al = reinterpret_cast<const pv4u*>(p.Alo) + (int64_t)mt * 16 * KST * 64;
+  const pv4u* __restrict__ Wt = reinterpret_cast<const pv4u*>(p.W) + (int64_t)nt * 8 * KST * 64;
+  const int rpad = (p.R + 127) & ~127, a_tiles = min(16, (rpad - mt * 256) >> 4);
+  const uint32_t abytes = (uint32_t)(a_tiles * KST) * 1024, wbytes = (uint32_t)(8 * KST) * 1024;
+  const __amdgpu_buffer_rsrc_t rh = buf_rsrc(Ah, abytes), rl = buf_rsrc(Al, abytes), rw = buf_rsrc(Wt, wbytes);
+  auto issue = [&](int st) __attribute__((always_inline)) {
+    pv4u* S = stage[st % NSLOT];
+    st = min(st, KST - 1);
+    const uint32_t so = (uint32_t)(st * 64 + lane) * 16, t0 = (uint32_t)w * KST * 1024, t8 = (uint32_t)(8 + w) * KST * 1024;
+    lds_dma16(rh, t0 + so, S + w * 64);
+    lds_dma16(rh, t8 + so, S + (8 + w) * 64);
+    lds_dma16(rl, t0 + so, S + (16 + w) * 64);
+    lds_dma16(rl, t8 + so, S + (24 + w) * 64);
+    lds_dma16(rw, t0 + so, S + (32 + w) * 64);
+  };
+  pf32x4_t acc[WR][WC];
+#pragma unroll
+  for (int i = 0; i < WR; ++i)
+#pragma unroll
+    for (int jj = 0; jj < WC; ++jj) acc[i][jj] = pf32x4_t{0.f, 0.f, 0.f, 0.f};
+  issue(0);
+  for (int st = 0; st < KST; ++st) {
+    wait_vmcnt<0>();                  // this thread's loads of step st have landed
+    __builtin_amdgcn_s_barrier();     // ... and every thread's; every wave is done with step st - 1
+    issue(st + 1);                    // into the slot of step st - 1
+    const pv4u* S = stage[st % NSLOT];
+    pv4u ah[WR], al[WR], wf[WC];
+#pragma unroll
+    for (int jj = 0; jj < WC; ++jj) wf[jj] = S[(32 + wn * 4 + jj) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < WR; ++i) {
+      ah[i] = S[(wm * 4 + i) * 64 + lane];
+      al[i] = S[(16 + wm * 4 + i) * 64 + lane];
+    }
+#pragma unroll
+    for (int i = 0; i < WR; ++i)
+#pragma unroll
+      for (int jj = 0; jj < WC; ++jj) {
+        acc[i][jj] = pmma(ah[i], wf[jj], acc[i][jj], (T*)nullptr);
+        acc[i][jj] = pmma(al[i], wf[jj], acc[i][jj], (T*)nullptr);
+      }
+  }
+  wait_vmcnt<0>();   // the clamped loads past the end land before the workgroup's LDS is released
+  fg_epilogue<T, EPI, WR, WC>(p, acc, rt0, ct0, lane);
+}
+
+
 hipError_t launch_fgemm(const FgParams& p, hipStream_t s) {
   if (p.R <= 0 || p.N <= 0 || p.N % 128 || p.K <= 0 || p.K % 32 || !p.W || !p.Ahi || !p.Alo) return hipErrorInvalidValue;
   if (p.epi == FG_SWIGLU ? (!p.Ohi || !p.Olo || p.N % 256)
@@ -323,8 +398,17 @@ hipError_t launch_fgemm(const FgParams& p, hipStream_t s) {
   od.n_nt = p.N / 128;
   od.pg = std::max(1, std::min(8, (3 << 20) / (128 * p.K * 4)));
   od.per_xcd = (od.n_mt >> 3) * od.n_nt + ((od.n_mt & 7) * od.n_nt + 7) / 8;
+  // 256-row blocks once they fill the chip twice over
+  // (encoder window 341 -> 328 ms, Qwen3 prefill 46.4 -> 45.9 ms against 128-row blocks only)
+  const bool wide8 = (int64_t)((p.R + 255) / 256) * (p.N / 128) >= 512;
+  FgOrder od8;
+  od8.n_mt = (p.R + 255) / 256;
+  od8.n_nt = p.N / 128;
+  od8.pg = std::max(1, std::min(8, (3 << 20) / (256 * p.K * 4)));
+  od8.per_xcd = (od8.n_mt >> 3) * od8.n_nt + ((od8.n_mt & 7) * od8.n_nt + 7) / 8;
 #define WD_FG1(T_, E_)                                                                                   \
-  if (wide) k_fgemm_lds<T_, E_><<<8 * od.per_xcd, 256, 0, s>>>(p, od);                                   \
+  if (wide8) k_fgemm_lds8<T_, E_><<<8 * od8.per_xcd, 512, 0, s>>>(p, od8);                            \
+  else if (wide) k_fgemm_lds<T_, E_><<<8 * od.per_xcd, 256, 0, s>>>(p, od);                            \
   else k_fgemm<T_, E_, 2><<<grid, 256, 0, s>>>(p);
 #define WD_FG(T_)                                                                                        \
   switch (p.epi) {                                                                                       \
