@@ -143,14 +143,16 @@ __global__ __launch_bounds__(256) void k_xkv_frag(const T* __restrict__ Xf, cons
 // tiles).  Per 32-deep K step the block's 16 + 8 operand tiles (1 KB each, fragment order) are
 // loaded once into LDS and every wave reads its 4 + 4 tiles from there, so each fragment
 // leaves L2 once per block instead of once per wave.  The loads go straight from global
-// memory (buffer loads with the LDS destination) into a ring of three LDS slots, two K steps
-// ahead of the MFMAs (no staging registers, no LDS stores); each step waits for its own loads
-// by count and meets the other waves at a bare barrier (a full __syncthreads would also wait
-// for the loads still in flight).  Same XCD panel order and epilogue as k_xkv_frag, the 256
-// rows in two halves.  (256 x 256 blocks of eight 128 x 64 waves, one workgroup per CU,
-// measured slower: 22.3 against 21.0 ms per large-v3 window.)
+// memory (buffer loads with the LDS destination) into a ring of three LDS slots (no staging
+// registers, no LDS stores); each step waits for its own loads by count and meets the other
+// waves at a bare barrier (a full __syncthreads would also wait for the loads still in
+// flight), and half of a step's MFMAs hide the fragment reads of the next.  Same XCD panel
+// order and epilogue as k_xkv_frag, the 256 rows in two halves.  At most 128 VGPRs, so two
+// workgroups share a CU.  (256 x 256 blocks of eight 128 x 64 waves, one workgroup per CU,
+// measured slower: 22.3 against 21.0 ms per large-v3 window; reading each step's fragments
+// after its barrier, loads two steps ahead: 20.6 against 20.1 ms.)
 template <typename T, typename CT>
-__global__ __launch_bounds__(512) void k_xkv_lds(const T* __restrict__ Xf, const T* __restrict__ Wf, int K,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_xkv_lds(const T* __restrict__ Xf, const T* __restrict__ Wf, int K,
                                                  XkvOut o, int n_mt, int n_nt, int pg) {
   constexpr int RT = 16, CTL = 8, NTL = RT + CTL;   // tiles per block and K step
   constexpr int CLD = 128 + 8;
@@ -187,26 +189,59 @@ __global__ __launch_bounds__(512) void k_xkv_lds(const T* __restrict__ Xf, const
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) acc[i][jn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // three slots, loads two K steps ahead: at step st the slot of st - 1 is free once every
-  // wave is past the barrier (its MFMAs of st - 1 have consumed their LDS reads)
-  issue(0);
-  issue(1);
-  for (int st = 0; st < KST; ++st) {
-    wait_vmcnt<3>();                  // this thread's loads of step st have landed
-    __builtin_amdgcn_s_barrier();     // ... and every thread's
-    issue(st + 2);
+  // Three slots, loads three K steps ahead of the MFMAs.  Step st: the reads of row tiles 2, 3
+  // and the MFMAs of row tiles 0, 1 (their fragments and the column fragments read during
+  // step st - 1); a barrier at which every thread's loads of step st + 1 have landed and every
+  // wave has read all of slot st, so that slot takes the loads of st + 3; then the reads of
+  // step st + 1's row tiles 0, 1 and column tiles, hidden behind the MFMAs of row tiles 2, 3.
+  // Two register sets alternate by step (no copies, which would wait for the reads).
+  auto rd_rows = [&](int st, int i0, v4u (&fa)[2]) __attribute__((always_inline)) {
     const v4u* S = stage[st % NSLOT];
-    v4u a[4], b[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = S[(wm * 4 + i) * 64 + lane];
+    for (int i = 0; i < 2; ++i) fa[i] = S[(wm * 4 + i0 + i) * 64 + lane];
+  };
+  auto rd_cols = [&](int st, v4u (&fb)[4]) __attribute__((always_inline)) {
+    const v4u* S = stage[st % NSLOT];
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn) b[jn] = S[(RT + wn * 4 + jn) * 64 + lane];
+    for (int jn = 0; jn < 4; ++jn) fb[jn] = S[(RT + wn * 4 + jn) * 64 + lane];
+  };
+  auto mfmas = [&](int i0, const v4u (&fa)[2], const v4u (&fb)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int jn = 0; jn < 4; ++jn)
-        acc[i][jn] = mfma16x16x32(__builtin_bit_cast(uint4, a[i]), __builtin_bit_cast(uint4, b[jn]), acc[i][jn], (T*)nullptr);
+        acc[i0 + i][jn] = mfma16x16x32(__builtin_bit_cast(uint4, fa[i]), __builtin_bit_cast(uint4, fb[jn]), acc[i0 + i][jn], (T*)nullptr);
+  };
+  auto step = [&](int st, const v4u (&pa)[2], const v4u (&pb)[4], v4u (&na)[2], v4u (&nb)[4]) __attribute__((always_inline)) {
+    v4u qa[2];
+    rd_rows(st, 2, qa);
+    mfmas(0, pa, pb);
+    __builtin_amdgcn_sched_barrier(0);    // (the scheduler would move MFMAs across the barrier)
+    wait_vmcnt<3>();                      // this thread's loads of step st + 1 have landed
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of slot st are done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(st + 3);
+    rd_rows(st + 1, 0, na);               // past the end: a slot's stale tiles, never used
+    rd_cols(st + 1, nb);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(2, qa, pb);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  issue(0);
+  issue(1);
+  issue(2);
+  wait_vmcnt<6>();                    // this thread's loads of step 0 have landed
+  __builtin_amdgcn_s_barrier();       // ... and every thread's
+  v4u a0[2], b0[4], a1[2], b1[4];
+  rd_rows(0, 0, a0);
+  rd_cols(0, b0);
+  int st = 0;
+  for (; st + 1 < KST; st += 2) {
+    step(st, a0, b0, a1, b1);
+    step(st + 1, a1, b1, a0, b0);
   }
+  if (st < KST) step(st, a0, b0, a1, b1);
   wait_vmcnt<0>();                    // the clamped loads past the end land before LDS is reused
   __syncthreads();
   // epilogue through LDS (the staging buffers), 128 rows at a time: waves 0, 1 (rows 0..127)
