@@ -215,6 +215,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   auto step = [&](int st, const v4u (&pa)[2], const v4u (&pb)[4], v4u (&na)[2], v4u (&nb)[4]) __attribute__((always_inline)) {
     v4u qa[2];
     rd_rows(st, 2, qa);
+    __builtin_amdgcn_sched_barrier(0);
     mfmas(0, pa, pb);
     __builtin_amdgcn_sched_barrier(0);    // (the scheduler would move MFMAs across the barrier)
     wait_vmcnt<3>();                      // this thread's loads of step st + 1 have landed
