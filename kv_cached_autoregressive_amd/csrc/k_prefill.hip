@@ -367,6 +367,7 @@ __global__ __launch_bounds__(512) void k_fgemm_lds8(FgParams p, FgOrder od) {
       ah[i] = S[(wm * 4 + i) * 64 + lane];
       al[i] = S[(16 + wm * 4 + i) * 64 + lane];
     }
+    __builtin_amdgcn_s_setprio(1);   // MFMA issue first while this wave has operands (encoder window -0.5%)
 #pragma unroll
     for (int i = 0; i < WR; ++i)
 #pragma unroll
@@ -374,6 +375,7 @@ __global__ __launch_bounds__(512) void k_fgemm_lds8(FgParams p, FgOrder od) {
         acc[i][jj] = pmma(ah[i], wf[jj], acc[i][jj], (T*)nullptr);
         acc[i][jj] = pmma(al[i], wf[jj], acc[i][jj], (T*)nullptr);
       }
+    __builtin_amdgcn_s_setprio(0);
   }
   wait_vmcnt<0>();   // the clamped loads past the end land before the workgroup's LDS is released
   fg_epilogue<T, EPI, WR, WC>(p, acc, rt0, ct0, lane);
