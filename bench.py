@@ -772,6 +772,34 @@ def _extra_workloads(args):
     return out
 
 
+def run_floors(w):
+    """The costs the decode kernels are bounded by on this device, from wd_probe: the per-launch
+    cost of a graph of dependent empty kernels (1280 blocks, like the large-v3 attention grids),
+    and one kernel that only streams the bytes of one cross-attention launch of the workload (its
+    K and V caches as two buffers, read with the attention's 16-byte nontemporal lane loads).
+    Medians of five measurements each; the two buffers are allocated once and stay resident."""
+    import torch
+    import kv_cached_autoregressive_amd as K
+    kv = w.n_enc * w.heads * w.frames * (w.d // w.heads) * {"f32": 4, "f16": 2, "bf16": 2}[w.cache_dtype]
+    a = torch.empty(kv, dtype=torch.uint8, device="cuda")
+    b = torch.empty(kv, dtype=torch.uint8, device="cuda")
+    a.random_(0, 256)
+    b.random_(0, 256)
+    sink = torch.zeros(4096, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    launch = float(np.median([K.wd_probe(0, iters=1000) for _ in range(5)]))
+    stream = float(np.median([K.wd_probe(1, a.data_ptr(), b.data_ptr(), kv, 20, sink.data_ptr()) for _ in range(5)]))
+    rate = 2 * kv / stream / 1e3   # GB/s
+    print(json.dumps({"metric": "machine floors", "workload": w.name,
+                      "empty_dependent_launch_us": launch,
+                      "stream_bytes": 2 * kv, "stream_us": stream, "stream_gbps": rate,
+                      "stream_frac_of_8tbps": rate / 8000.0,
+                      # repeated reads of less than the 256 MB MALL come from it, not from HBM
+                      "stream_fits_mall": 2 * kv <= 256 * 2**20,
+                      "probe": "wd_probe kind 0 (1000 graph-captured launches of 1280 empty blocks) and "
+                               "kind 1 (20 launches reading the K and V bytes of one cross-attention launch)"}))
+
+
 def run_encoder(args, w):
     """The audio encoder of one window: every encoder set's 3000 synthetic mel frames through
     the stem and the encoder layers to its 1500 states (wd_encode), with seeded random-init
@@ -859,6 +887,8 @@ def main():
                     help="time the audio encoder (wd_encode) of the workload's encoder sets instead of the decoder")
     ap.add_argument("--encoder-layers", type=int, default=0, help="encoder layers (default: the decoder's)")
     ap.add_argument("--mels", type=int, default=80, help="mel channels of the encoder's input")
+    ap.add_argument("--floors", action="store_true",
+                    help="measure the machine floors the decode kernels run against (wd_probe) and exit")
     args = ap.parse_args()
     if args.summarize_counters:
         w = WL.by_name(args.config)
@@ -891,6 +921,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.encoder:
         run_encoder(args, w)
+        return
+    if args.floors:
+        run_floors(w)
         return
     metric = "decoder tokens/sec at batch B; achieved HBM GB/s as % of MI355X peak"
     common = {"metric": metric, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -311,6 +311,26 @@ void wd_free(wd_ctx* ctx);
 wd_status wd_profile(wd_ctx* ctx, int32_t kernel, int32_t layer, int32_t repeats);
 wd_status wd_profile_read(wd_ctx* ctx, double* total_ms, int64_t* launches);
 
+/* --- machine floors (measurement support, not part of the decoding method) --
+ * For benchmarks only: the costs that bound the step's kernels on the device
+ * at hand, measured with HIP events on a stream of its own (created and
+ * destroyed by the call, default priority; the call synchronises it).
+ * kind 0: `iters` dependent launches of an empty kernel of 1280 blocks of 256
+ *         threads, captured in one HIP graph and replayed as the decode step's
+ *         graph is; *us = time per launch (a, b, bytes, sink unused).
+ * kind 1: `iters` back-to-back launches of one kernel that reads `bytes`
+ *         bytes of a and `bytes` bytes of b (device buffers, 16-byte aligned,
+ *         bytes a positive multiple of 16): 1280 blocks of eight waves, block
+ *         i reading the i-th slab of each, with 16-byte nontemporal lane loads
+ *         (the large-v3 cross-attention's grid and K/V pattern, without its
+ *         arithmetic); *us = time per launch.  sink: device scratch of at
+ *         least 1280 floats (practically never written; it keeps the loads).
+ * No device buffer is allocated.  Errors: ARG (kind, iters outside
+ * [1, 100000], null us, or kind 1 with null, misaligned or empty buffers;
+ * wd_last_error(NULL) names it), HIP.                                       */
+wd_status wd_probe(int32_t kind, const void* a, const void* b, int64_t bytes, int32_t iters, float* sink,
+                   double* us);
+
 /* --- test hook (not part of the decoding method) ---------------------------
  * For parity tests only; a decoder never needs it.
  * Device address of one cache block of the current buffer, for checking the

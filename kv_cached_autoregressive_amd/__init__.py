@@ -19,7 +19,7 @@ from typing import Dict, Iterable, Optional, Sequence
 __all__ = [
     "WdError", "WdConfig", "WdTensor", "lib", "lib_path", "declared_functions",
     "wd_abi_version", "wd_workspace_bytes", "wd_load", "wd_cross_kv", "wd_cross_kv_ragged", "wd_step", "wd_reorder",
-    "wd_topk", "wd_prefill", "wd_encoder_workspace_bytes", "wd_load_encoder", "wd_encode", "wd_listen", "wd_check", "wd_last_error", "wd_free", "wd_profile", "wd_profile_read",
+    "wd_topk", "wd_prefill", "wd_encoder_workspace_bytes", "wd_load_encoder", "wd_encode", "wd_listen", "wd_check", "wd_last_error", "wd_free", "wd_profile", "wd_profile_read", "wd_probe",
     "wd_debug_cache", "wd_set_option", "wd_get_option", "WD_OPT_GRAPHS", "wd_topk_noalloc", "wd_beam_step",
     "config_from", "Decoder", "DTYPES", "STATUS",
 ]
@@ -94,6 +94,7 @@ def lib():
             "wd_free": (None, [vp]),
             "wd_profile": (i32, [vp, i32, i32, i32]),
             "wd_profile_read": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
+            "wd_probe": (i32, [i32, vp, vp, i64, i32, vp, ctypes.POINTER(ctypes.c_double)]),
             "wd_debug_cache": (i32, [vp, i32, i32, ctypes.POINTER(vp)]),
             "wd_set_option": (i32, [vp, i32, i32]),
             "wd_topk_noalloc": (i32, [vp, i32, i32, i64, i32, vp, vp, vp, vp]),
@@ -218,6 +219,14 @@ def wd_profile_read(ctx):
     n = ctypes.c_int64()
     _check(lib().wd_profile_read(ctx, ctypes.byref(t), ctypes.byref(n)), ctx)
     return t.value, n.value
+
+
+def wd_probe(kind: int, a: int = 0, b: int = 0, nbytes: int = 0, iters: int = 1, sink: int = 0) -> float:
+    """Microseconds per launch of a machine-floor probe (kind 0: empty dependent launches in a
+    graph; kind 1: one read of nbytes from each of the device buffers a and b)."""
+    us = ctypes.c_double()
+    _check(lib().wd_probe(kind, a or None, b or None, nbytes, iters, sink or None, ctypes.byref(us)), None)
+    return us.value
 
 
 def wd_debug_cache(ctx, which: int, layer: int) -> int:

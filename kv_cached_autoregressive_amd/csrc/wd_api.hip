@@ -794,6 +794,37 @@ hipError_t scratch_address(void** out) {
 }
 }  // namespace
 
+// ---- machine floors (measurement support) -------------------------------------------------------
+namespace {
+constexpr int kProbeEmptyBlocks = 1280;   // the large-v3 step's attention grids
+constexpr int kProbeStreamBlocks = 1280;  // slabs, as the cross-attention's (encoder set, head) blocks
+__global__ __launch_bounds__(256) void k_probe_empty() {}
+// Block i reads the i-th of gridDim.x equal slabs of a and of b (the cross-attention's K and V
+// slab of one block), eight waves, six 16-byte nontemporal lane loads of each array in flight per
+// lane; the words' xor reaches memory only in the (practically never taken) case it equals a
+// fixed constant, so no load is dropped.
+__global__ __launch_bounds__(512) void k_probe_stream(const uint4* __restrict__ a, const uint4* __restrict__ b,
+                                                      int64_t n16, float* __restrict__ sink) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  constexpr int UNR = 6;
+  const int64_t slab = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * slab, hi = min(lo + slab, n16);
+  uint32_t acc = 0;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 512 * UNR) {
+    u4 va[UNR], vb[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t j = min(i + u * 512, hi - 1);
+      va[u] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(a) + j);
+      vb[u] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(b) + j);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) acc ^= va[u].x ^ va[u].y ^ va[u].z ^ va[u].w ^ vb[u].x ^ vb[u].y ^ vb[u].z ^ vb[u].w;
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x] = 1.f;
+}
+}  // namespace
+
 extern "C" {
 
 int32_t wd_abi_version(void) { return WD_ABI_VERSION; }
@@ -1584,6 +1615,59 @@ wd_status wd_debug_cache(wd_ctx* ctx, int32_t which, int32_t layer, void** dev_p
   if (which >= 2 && ctx->cfg.arch != WD_ARCH_WHISPER) return fail(ctx, WD_ERR_ARG, "wd_debug_cache: no cross cache");
   *dev_ptr = which == 0 ? ctx->self_k(layer) : which == 1 ? ctx->self_v(layer)
            : which == 2 ? ctx->cross_k(layer) : ctx->cross_v(layer);
+  return WD_OK;
+}
+
+wd_status wd_probe(int32_t kind, const void* a, const void* b, int64_t bytes, int32_t iters, float* sink,
+                   double* us) {
+  if (!us || iters < 1 || iters > 100000 || (kind != 0 && kind != 1))
+    return fail(nullptr, WD_ERR_ARG, "wd_probe: kind must be 0 or 1, iters in [1, 100000], us not null");
+  if (kind == 1 && (!a || !b || !sink || bytes < 16 || bytes % 16 || (reinterpret_cast<uintptr_t>(a) % 16) ||
+                    (reinterpret_cast<uintptr_t>(b) % 16)))
+    return fail(nullptr, WD_ERR_ARG, "wd_probe: stream needs 16-byte aligned a, b, bytes a positive multiple of 16, a sink");
+  struct Res {   // released on every path
+    hipStream_t s = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipGraph_t g = nullptr;
+    hipGraphExec_t x = nullptr;
+    ~Res() {
+      if (s) (void)hipStreamSynchronize(s);
+      if (x) (void)hipGraphExecDestroy(x);
+      if (g) (void)hipGraphDestroy(g);
+      if (e0) (void)hipEventDestroy(e0);
+      if (e1) (void)hipEventDestroy(e1);
+      if (s) (void)hipStreamDestroy(s);
+    }
+  } r;
+#define PCHK(expr) do { const hipError_t e_ = (expr); if (e_ != hipSuccess) \
+    return fail(nullptr, WD_ERR_HIP, std::string("wd_probe: ") + hipGetErrorString(e_)); } while (0)
+  PCHK(hipStreamCreateWithFlags(&r.s, hipStreamNonBlocking));
+  PCHK(hipEventCreate(&r.e0));
+  PCHK(hipEventCreate(&r.e1));
+  float ms = 0.f;
+  if (kind == 0) {   // a graph of `iters` dependent empty launches, replayed like the step graph
+    PCHK(hipStreamBeginCapture(r.s, hipStreamCaptureModeThreadLocal));
+    for (int i = 0; i < iters; ++i) k_probe_empty<<<kProbeEmptyBlocks, 256, 0, r.s>>>();
+    PCHK(hipStreamEndCapture(r.s, &r.g));
+    PCHK(hipGraphInstantiate(&r.x, r.g, nullptr, nullptr, 0));
+    PCHK(hipGraphLaunch(r.x, r.s));   // warm-up replay
+    PCHK(hipEventRecord(r.e0, r.s));
+    PCHK(hipGraphLaunch(r.x, r.s));
+    PCHK(hipEventRecord(r.e1, r.s));
+  } else {           // `iters` back-to-back reads of a and b
+    const int64_t n16 = bytes / 16;
+    k_probe_stream<<<kProbeStreamBlocks, 512, 0, r.s>>>(static_cast<const uint4*>(a), static_cast<const uint4*>(b), n16, sink);
+    PCHK(hipGetLastError());
+    PCHK(hipEventRecord(r.e0, r.s));
+    for (int i = 0; i < iters; ++i)
+      k_probe_stream<<<kProbeStreamBlocks, 512, 0, r.s>>>(static_cast<const uint4*>(a), static_cast<const uint4*>(b), n16, sink);
+    PCHK(hipGetLastError());
+    PCHK(hipEventRecord(r.e1, r.s));
+  }
+  PCHK(hipEventSynchronize(r.e1));
+  PCHK(hipEventElapsedTime(&ms, r.e0, r.e1));
+#undef PCHK
+  *us = 1000.0 * ms / iters;
   return WD_OK;
 }
 

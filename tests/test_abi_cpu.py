@@ -125,6 +125,15 @@ def test_null_context_calls_return_arg():
     assert "scratch" in K.wd_last_error(None)
     assert L.wd_topk_noalloc(fake, 4, 10, 9, 1, fake, fake, fake, None) == 1
     assert L.wd_topk_noalloc(fake, 4, 10, 10, 9, fake, fake, fake, None) == 1
+    # the machine-floor probe checks its arguments before creating a stream
+    us = ctypes.c_double()
+    assert L.wd_probe(2, None, None, 0, 1, None, ctypes.byref(us)) == 1
+    assert L.wd_probe(0, None, None, 0, 0, None, ctypes.byref(us)) == 1
+    assert L.wd_probe(0, None, None, 0, 1, None, None) == 1
+    assert L.wd_probe(1, None, fake, 1 << 20, 1, fake, ctypes.byref(us)) == 1
+    assert L.wd_probe(1, fake, fake, 1000, 1, fake, ctypes.byref(us)) == 1
+    assert L.wd_probe(1, ctypes.c_void_p(FAKE_DATA + 8), fake, 1 << 20, 1, fake, ctypes.byref(us)) == 1
+    assert "wd_probe" in K.wd_last_error(None)
     v = ctypes.c_int32()
     assert L.wd_get_option(None, K.WD_OPT_GRAPHS, ctypes.byref(v)) == 1
     L.wd_free(None)
