@@ -790,14 +790,25 @@ def run_floors(w):
     launch = float(np.median([K.wd_probe(0, iters=1000) for _ in range(5)]))
     stream = float(np.median([K.wd_probe(1, a.data_ptr(), b.data_ptr(), kv, 20, sink.data_ptr()) for _ in range(5)]))
     rate = 2 * kv / stream / 1e3   # GB/s
+    # a decode step's hand-off: the B x d fp32 residual rows (rounded up to 4 KiB per 256 blocks)
+    act = -(-w.batch * w.d * 4 // 4096) * 4096
+    hand = {k: float(np.median([K.wd_probe(k, a.data_ptr(), b.data_ptr(), act, 1000) for _ in range(5)]))
+            for k in (2, 3)}
+    ctr = torch.zeros(2, dtype=torch.int32, device="cuda")
+    fence = {k: float(np.median([K.wd_probe(k, a.data_ptr(), ctr.data_ptr(), 4096, 200) for _ in range(5)]))
+             for k in (4, 5)}
     print(json.dumps({"metric": "machine floors", "workload": w.name,
                       "empty_dependent_launch_us": launch,
                       "stream_bytes": 2 * kv, "stream_us": stream, "stream_gbps": rate,
                       "stream_frac_of_8tbps": rate / 8000.0,
                       # repeated reads of less than the 256 MB MALL come from it, not from HBM
                       "stream_fits_mall": 2 * kv <= 256 * 2**20,
-                      "probe": "wd_probe kind 0 (1000 graph-captured launches of 1280 empty blocks) and "
-                               "kind 1 (20 launches reading the K and V bytes of one cross-attention launch)"}))
+                      "handoff_bytes": act, "handoff_same_xcd_us": hand[2], "handoff_cross_xcd_us": hand[3],
+                      "fence_reduce_256_blocks_us": fence[4], "fence_reduce_1024_blocks_us": fence[5],
+                      "probe": "wd_probe kind 0 (1000 graph-captured launches of 1280 empty blocks), "
+                               "kind 1 (20 launches reading the K and V bytes of one cross-attention launch), "
+                               "kinds 2, 3 (1000 graph-captured dependent hand-offs of the residual rows, same / "
+                               "other XCD) and kinds 4, 5 (200 in-kernel fence reductions over 256 / 1024 blocks)"}))
 
 
 def run_encoder(args, w):

@@ -325,9 +325,21 @@ wd_status wd_profile_read(wd_ctx* ctx, double* total_ms, int64_t* launches);
  *         (the large-v3 cross-attention's grid and K/V pattern, without its
  *         arithmetic); *us = time per launch.  sink: device scratch of at
  *         least 1280 floats (practically never written; it keeps the loads).
- * No device buffer is allocated.  Errors: ARG (kind, iters outside
- * [1, 100000], null us, or kind 1 with null, misaligned or empty buffers;
- * wd_last_error(NULL) names it), HIP.                                       */
+ * kind 2, 3: a graph of `iters` dependent launches of 256 blocks, each block
+ *         reading a slab of bytes / 256 of the previous launch's output (a and
+ *         b in turn; 16-byte aligned, bytes a multiple of 4096 up to 256 MiB)
+ *         and writing its own: kind 2 the slab its own block index wrote (the
+ *         same XCD), kind 3 the next block's (another XCD); *us = time per
+ *         launch.  (Both buffers are overwritten.)
+ * kind 4, 5: `iters` launches of a kernel of 256 (kind 4) or 1024 (kind 5)
+ *         blocks that reduces one value per block inside the kernel: each
+ *         block stores its value, fences (__threadfence) and counts itself on
+ *         an atomic counter, and the last block adds them up.  a: at least
+ *         4096 bytes (bytes >= 4096); b: 8 bytes, 8-byte aligned (counter and
+ *         result; zeroed first); *us = time per launch.
+ * No device buffer is allocated.  Errors: ARG (kind outside [0, 5], iters
+ * outside [1, 100000], null us, or null, misaligned or too small buffers for
+ * the kind; wd_last_error(NULL) names it), HIP.                             */
 wd_status wd_probe(int32_t kind, const void* a, const void* b, int64_t bytes, int32_t iters, float* sink,
                    double* us);
 

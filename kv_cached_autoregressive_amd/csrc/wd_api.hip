@@ -823,6 +823,43 @@ __global__ __launch_bounds__(512) void k_probe_stream(const uint4* __restrict__ 
   }
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = 1.f;
 }
+constexpr int kProbeHandoffBlocks = 256;
+// One hand-off between dependent kernels: block i reads the slab that block (i + shift) % grid
+// wrote in the previous launch (shift 0: the same block index, so the same XCD, as blocks reach
+// the XCDs round-robin by launch index; shift 1: the next XCD's) and writes its own slab.
+__global__ __launch_bounds__(256) void k_probe_handoff(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                       int slab16, int shift) {
+  const int from = (blockIdx.x + shift) % gridDim.x;
+  for (int i = threadIdx.x; i < slab16; i += 256) {
+    uint4 v = src[(int64_t)from * slab16 + i];
+    v.x ^= 1u;
+    dst[(int64_t)blockIdx.x * slab16 + i] = v;
+  }
+}
+// A cross-workgroup reduction inside one kernel: every block publishes one value, makes it
+// visible device-wide with a fence and counts itself in; the block that counts last adds the
+// values (nobody waits) and re-arms the counter for the next launch.
+__global__ __launch_bounds__(256) void k_probe_fence(float* __restrict__ part, unsigned* __restrict__ ctr) {
+  __shared__ bool last;
+  if (threadIdx.x == 0) {
+    part[blockIdx.x] = (float)blockIdx.x;
+    __threadfence();
+    last = atomicAdd(ctr, 1u) == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  __shared__ float red[256];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < (int)gridDim.x; i += 256) s += part[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < 256; ++i) s += red[i];
+    reinterpret_cast<float*>(ctr)[1] = s;
+    ctr[0] = 0u;
+  }
+}
 }  // namespace
 
 extern "C" {
@@ -1620,11 +1657,16 @@ wd_status wd_debug_cache(wd_ctx* ctx, int32_t which, int32_t layer, void** dev_p
 
 wd_status wd_probe(int32_t kind, const void* a, const void* b, int64_t bytes, int32_t iters, float* sink,
                    double* us) {
-  if (!us || iters < 1 || iters > 100000 || (kind != 0 && kind != 1))
-    return fail(nullptr, WD_ERR_ARG, "wd_probe: kind must be 0 or 1, iters in [1, 100000], us not null");
-  if (kind == 1 && (!a || !b || !sink || bytes < 16 || bytes % 16 || (reinterpret_cast<uintptr_t>(a) % 16) ||
-                    (reinterpret_cast<uintptr_t>(b) % 16)))
+  if (!us || iters < 1 || iters > 100000 || kind < 0 || kind > 5)
+    return fail(nullptr, WD_ERR_ARG, "wd_probe: kind must be in [0, 5], iters in [1, 100000], us not null");
+  const bool aligned = !(reinterpret_cast<uintptr_t>(a) % 16) && !(reinterpret_cast<uintptr_t>(b) % 16);
+  if (kind == 1 && (!a || !b || !sink || bytes < 16 || bytes % 16 || !aligned))
     return fail(nullptr, WD_ERR_ARG, "wd_probe: stream needs 16-byte aligned a, b, bytes a positive multiple of 16, a sink");
+  if ((kind == 2 || kind == 3) && (!a || !b || !aligned || bytes < 16 * kProbeHandoffBlocks ||
+                                   bytes % (16 * kProbeHandoffBlocks) || bytes > (int64_t(1) << 28)))
+    return fail(nullptr, WD_ERR_ARG, "wd_probe: hand-off needs 16-byte aligned a, b, bytes a multiple of 4096 up to 256 MiB");
+  if ((kind == 4 || kind == 5) && (!a || !b || bytes < 4096 || (reinterpret_cast<uintptr_t>(b) % 8)))
+    return fail(nullptr, WD_ERR_ARG, "wd_probe: fence needs a of at least 4096 bytes and an 8-byte aligned b");
   struct Res {   // released on every path
     hipStream_t s = nullptr;
     hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -1653,6 +1695,29 @@ wd_status wd_probe(int32_t kind, const void* a, const void* b, int64_t bytes, in
     PCHK(hipGraphLaunch(r.x, r.s));   // warm-up replay
     PCHK(hipEventRecord(r.e0, r.s));
     PCHK(hipGraphLaunch(r.x, r.s));
+    PCHK(hipEventRecord(r.e1, r.s));
+  } else if (kind == 2 || kind == 3) {   // a graph of `iters` dependent hand-offs, a -> b -> a ...
+    const int slab16 = (int)(bytes / 16 / kProbeHandoffBlocks);
+    uint4* bufs[2] = {static_cast<uint4*>(const_cast<void*>(a)), static_cast<uint4*>(const_cast<void*>(b))};
+    PCHK(hipStreamBeginCapture(r.s, hipStreamCaptureModeThreadLocal));
+    for (int i = 0; i < iters; ++i)
+      k_probe_handoff<<<kProbeHandoffBlocks, 256, 0, r.s>>>(bufs[i & 1], bufs[(i + 1) & 1], slab16, kind == 3 ? 1 : 0);
+    PCHK(hipStreamEndCapture(r.s, &r.g));
+    PCHK(hipGraphInstantiate(&r.x, r.g, nullptr, nullptr, 0));
+    PCHK(hipGraphLaunch(r.x, r.s));
+    PCHK(hipEventRecord(r.e0, r.s));
+    PCHK(hipGraphLaunch(r.x, r.s));
+    PCHK(hipEventRecord(r.e1, r.s));
+  } else if (kind == 4 || kind == 5) {   // `iters` back-to-back fence reductions over 256 / 1024 blocks
+    const int blocks = kind == 4 ? 256 : 1024;
+    float* part = static_cast<float*>(const_cast<void*>(a));
+    unsigned* ctr = static_cast<unsigned*>(const_cast<void*>(b));
+    PCHK(hipMemsetAsync(ctr, 0, 8, r.s));   // (a plain stream, not captured)
+    k_probe_fence<<<blocks, 256, 0, r.s>>>(part, ctr);
+    PCHK(hipGetLastError());
+    PCHK(hipEventRecord(r.e0, r.s));
+    for (int i = 0; i < iters; ++i) k_probe_fence<<<blocks, 256, 0, r.s>>>(part, ctr);
+    PCHK(hipGetLastError());
     PCHK(hipEventRecord(r.e1, r.s));
   } else {           // `iters` back-to-back reads of a and b
     const int64_t n16 = bytes / 16;

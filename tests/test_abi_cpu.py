@@ -127,7 +127,11 @@ def test_null_context_calls_return_arg():
     assert L.wd_topk_noalloc(fake, 4, 10, 10, 9, fake, fake, fake, None) == 1
     # the machine-floor probe checks its arguments before creating a stream
     us = ctypes.c_double()
-    assert L.wd_probe(2, None, None, 0, 1, None, ctypes.byref(us)) == 1
+    assert L.wd_probe(6, None, None, 0, 1, None, ctypes.byref(us)) == 1
+    assert L.wd_probe(2, fake, fake, 4095, 1, None, ctypes.byref(us)) == 1
+    assert L.wd_probe(3, fake, None, 4096, 1, None, ctypes.byref(us)) == 1
+    assert L.wd_probe(4, fake, fake, 100, 1, None, ctypes.byref(us)) == 1
+    assert L.wd_probe(5, fake, ctypes.c_void_p(FAKE_DATA + 4), 4096, 1, None, ctypes.byref(us)) == 1
     assert L.wd_probe(0, None, None, 0, 0, None, ctypes.byref(us)) == 1
     assert L.wd_probe(0, None, None, 0, 1, None, None) == 1
     assert L.wd_probe(1, None, fake, 1 << 20, 1, fake, ctypes.byref(us)) == 1

@@ -1,5 +1,5 @@
-"""The machine-floor probe (wd_probe) that bench.py --floors reports: both kinds run through the
-C ABI and return plausible per-launch times on the device."""
+"""The machine-floor probe (wd_probe) that bench.py --floors reports: every kind runs through the
+C ABI and returns a plausible per-launch time on the device."""
 import pytest
 import torch
 
@@ -21,6 +21,17 @@ def test_probe_empty_launch_and_stream():
     us = K.wd_probe(1, a.data_ptr(), b.data_ptr(), n, 5, sink.data_ptr())
     rate = 2 * n / us / 1e3   # bytes per us / 1000 = GB/s
     assert 500.0 < rate < 9000.0, rate
+    # hand-offs between dependent launches (same and other XCD), fence reductions in a kernel
+    for kind in (2, 3):
+        t = K.wd_probe(kind, a.data_ptr(), b.data_ptr(), 327680, 100)
+        assert 0.1 < t < 200.0, (kind, t)
+    ctr = torch.zeros(2, dtype=torch.int32, device="cuda")
+    for kind in (4, 5):
+        t = K.wd_probe(kind, a.data_ptr(), ctr.data_ptr(), 4096, 20)
+        assert 0.1 < t < 2000.0, (kind, t)
     torch.cuda.synchronize()
+    assert int(ctr[0].item()) == 0   # the last block re-arms the counter
+    # the reduction's sum of block indices 0..1023
+    assert float(ctr.view(torch.float32)[1].item()) == 1023 * 1024 / 2
     with pytest.raises(K.WdError):
         K.wd_probe(1, a.data_ptr() + 8, b.data_ptr(), n - 16, 1, sink.data_ptr())
