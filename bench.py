@@ -772,12 +772,14 @@ def _extra_workloads(args):
     return out
 
 
-def run_floors(w):
+def floors(w, full=True):
     """The costs the decode kernels are bounded by on this device, from wd_probe: the per-launch
     cost of a graph of dependent empty kernels (1280 blocks, like the large-v3 attention grids),
     and one kernel that only streams the bytes of one cross-attention launch of the workload (its
-    K and V caches as two buffers, read with the attention's 16-byte nontemporal lane loads).
-    Medians of five measurements each; the two buffers are allocated once and stay resident."""
+    K and V caches as two buffers, read with the attention's 16-byte nontemporal lane loads);
+    with full, also the hand-off of the residual rows between dependent launches (same / other
+    XCD) and an in-kernel fence reduction over 256 / 1024 workgroups.  Medians of five
+    measurements each; the buffers are allocated once and stay resident."""
     import torch
     import kv_cached_autoregressive_amd as K
     kv = w.n_enc * w.heads * w.frames * (w.d // w.heads) * {"f32": 4, "f16": 2, "bf16": 2}[w.cache_dtype]
@@ -790,25 +792,33 @@ def run_floors(w):
     launch = float(np.median([K.wd_probe(0, iters=1000) for _ in range(5)]))
     stream = float(np.median([K.wd_probe(1, a.data_ptr(), b.data_ptr(), kv, 20, sink.data_ptr()) for _ in range(5)]))
     rate = 2 * kv / stream / 1e3   # GB/s
-    # a decode step's hand-off: the B x d fp32 residual rows (rounded up to 4 KiB per 256 blocks)
-    act = -(-w.batch * w.d * 4 // 4096) * 4096
-    hand = {k: float(np.median([K.wd_probe(k, a.data_ptr(), b.data_ptr(), act, 1000) for _ in range(5)]))
-            for k in (2, 3)}
-    ctr = torch.zeros(2, dtype=torch.int32, device="cuda")
-    fence = {k: float(np.median([K.wd_probe(k, a.data_ptr(), ctr.data_ptr(), 4096, 200) for _ in range(5)]))
-             for k in (4, 5)}
-    print(json.dumps({"metric": "machine floors", "workload": w.name,
-                      "empty_dependent_launch_us": launch,
-                      "stream_bytes": 2 * kv, "stream_us": stream, "stream_gbps": rate,
-                      "stream_frac_of_8tbps": rate / 8000.0,
-                      # repeated reads of less than the 256 MB MALL come from it, not from HBM
-                      "stream_fits_mall": 2 * kv <= 256 * 2**20,
-                      "handoff_bytes": act, "handoff_same_xcd_us": hand[2], "handoff_cross_xcd_us": hand[3],
-                      "fence_reduce_256_blocks_us": fence[4], "fence_reduce_1024_blocks_us": fence[5],
-                      "probe": "wd_probe kind 0 (1000 graph-captured launches of 1280 empty blocks), "
-                               "kind 1 (20 launches reading the K and V bytes of one cross-attention launch), "
-                               "kinds 2, 3 (1000 graph-captured dependent hand-offs of the residual rows, same / "
-                               "other XCD) and kinds 4, 5 (200 in-kernel fence reductions over 256 / 1024 blocks)"}))
+    out = {"empty_dependent_launch_us": launch,
+           "stream_bytes": 2 * kv, "stream_us": stream, "stream_gbps": rate,
+           "stream_frac_of_8tbps": rate / 8000.0,
+           # repeated reads of less than the 256 MB MALL come from it, not from HBM
+           "stream_fits_mall": 2 * kv <= 256 * 2**20}
+    probe = ("wd_probe kind 0 (1000 graph-captured launches of 1280 empty blocks), "
+             "kind 1 (20 launches reading the K and V bytes of one cross-attention launch)")
+    if full:
+        # a decode step's hand-off: the B x d fp32 residual rows (rounded up to 4 KiB per 256 blocks)
+        act = -(-w.batch * w.d * 4 // 4096) * 4096
+        hand = {k: float(np.median([K.wd_probe(k, a.data_ptr(), b.data_ptr(), act, 1000) for _ in range(5)]))
+                for k in (2, 3)}
+        ctr = torch.zeros(2, dtype=torch.int32, device="cuda")
+        fence = {k: float(np.median([K.wd_probe(k, a.data_ptr(), ctr.data_ptr(), 4096, 200) for _ in range(5)]))
+                 for k in (4, 5)}
+        out.update({"handoff_bytes": act, "handoff_same_xcd_us": hand[2], "handoff_cross_xcd_us": hand[3],
+                    "fence_reduce_256_blocks_us": fence[4], "fence_reduce_1024_blocks_us": fence[5]})
+        probe += (", kinds 2, 3 (1000 graph-captured dependent hand-offs of the residual rows, same / other "
+                  "XCD) and kinds 4, 5 (200 in-kernel fence reductions over 256 / 1024 blocks)")
+    out["probe"] = probe
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_floors(w):
+    print(json.dumps({"metric": "machine floors", "workload": w.name, **floors(w)}))
 
 
 def run_encoder(args, w):
@@ -983,6 +993,11 @@ def main():
                                                         "ms_per_window", "windows")})
     if not args.no_extra and w.name == DEFAULT:
         out["workloads"] = _extra_workloads(args)
+        # the plain read of one cross-attention launch's bytes: the practical ceiling of roofline.frac
+        f = floors(w, full=False)
+        out["floors"] = f
+        if (out.get("roofline") or {}).get("avg_launch_us"):
+            out["roofline"]["frac_of_plain_read"] = f["stream_us"] / out["roofline"]["avg_launch_us"]
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
